@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs for the five gated-linear-attention workloads.
+
+This module only draws random numbers and casts them; it holds none of the
+attention arithmetic.  It serves both the HIP path and the CPU oracle: every test
+draws its inputs here once and hands the very same bits to both sides.
+
+Workload recipes (shapes and distributions as specified for the runs; the pages
+use the same symbols: q, k, v, per-key-dimension log-gates, the elu+1 feature map
+of the "Transformers are RNNs" notes and the Mamba2 scalar gate of "Gated Linear
+Attention", section "Motivation"):
+
+  fp32_single_head   fp32, B=1 H=1 L=256 d=16, q,k ~ N(0,1)/sqrt(d_k), v ~ N(0,1),
+                     key-dim log-gate g = logsigmoid(z)/16, z ~ N(0,1), chunk 16
+  linear_elu1        bf16, B=4 H=8 L=2048 d=64, q,k,v ~ N(0,1), no gate (alpha = 1),
+                     phi(x) = elu(x)+1 on q and k, chunk 64
+  gla_prefill        bf16, B=8 H=16 L=4096 d=128, q,k ~ N(0,1)/sqrt(d_k), v ~ N(0,1),
+                     key-dim g = logsigmoid(z)/16 in fp32, chunk 64
+  scalar_long        bf16, B=1 H=32 L=32768 d=128, q,k,v as gla_prefill, scalar gate
+                     log(gamma) = logsigmoid(z+4) per head and token, chunk 64
+  decode             B=256 H=32 d=128: a 512-token gla_prefill-style prefill fills the
+                     fp32 state, then 1024 single-token steps with bf16 q,k,v and
+                     key-dim gates drawn as in gla_prefill
+
+Draw order for one call: q, k, v, z, each standard normal in fp32 on the chosen
+device from ``torch.Generator(device).manual_seed(seed)``, then scaled and cast
+(bf16 casts round to nearest even).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+import torch.nn.functional as F
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: torch.dtype
+    B: int
+    H: int
+    L: int
+    d_k: int
+    d_v: int
+    chunk: int
+    gate: str | None            # None, "keydim" or "scalar"
+    feature_map: str | None     # None or "elu1"
+    scale_qk: bool              # q, k drawn as N(0,1)/sqrt(d_k)
+    decode_steps: int = 0       # > 0 only for the decode workload
+    seed: int = 0
+
+
+WORKLOADS = {
+    "fp32_single_head": Workload("fp32_single_head", torch.float32, 1, 1, 256, 16, 16, 16,
+                                 "keydim", None, True, seed=1),
+    "linear_elu1": Workload("linear_elu1", torch.bfloat16, 4, 8, 2048, 64, 64, 64,
+                            None, "elu1", False, seed=2),
+    "gla_prefill": Workload("gla_prefill", torch.bfloat16, 8, 16, 4096, 128, 128, 64,
+                            "keydim", None, True, seed=3),
+    "scalar_long": Workload("scalar_long", torch.bfloat16, 1, 32, 32768, 128, 128, 64,
+                            "scalar", None, True, seed=4),
+    "decode": Workload("decode", torch.bfloat16, 256, 32, 512, 128, 128, 64,
+                       "keydim", None, True, decode_steps=1024, seed=5),
+}
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _log_gate(z, gate):
+    """The configured log-gate recipes (input distributions, not attention math)."""
+    if gate == "keydim":
+        return F.logsigmoid(z) / 16.0
+    if gate == "scalar":
+        return F.logsigmoid(z + 4.0)
+    raise ValueError(gate)
+
+
+def draw(w: Workload, *, B=None, H=None, L=None, seed=None, device="cpu"):
+    """Draw q, k, v (and g) for a prefill over shape [B, H, L, d] of workload ``w``.
+
+    Sizes default to the workload's own; tests override them to get oracle-sized
+    cases of the same distributions.  Returns a dict of tensors on ``device``.
+    """
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    L = w.L if L is None else L
+    seed = w.seed if seed is None else seed
+    gen = _gen(device, seed)
+    f32 = dict(dtype=torch.float32, device=device, generator=gen)
+    qk_scale = 1.0 / math.sqrt(w.d_k) if w.scale_qk else 1.0
+    q = torch.randn(B, H, L, w.d_k, **f32) * qk_scale
+    k = torch.randn(B, H, L, w.d_k, **f32) * qk_scale
+    v = torch.randn(B, H, L, w.d_v, **f32)
+    g = None
+    if w.gate == "keydim":
+        g = _log_gate(torch.randn(B, H, L, w.d_k, **f32), "keydim")
+    elif w.gate == "scalar":
+        g = _log_gate(torch.randn(B, H, L, **f32), "scalar")
+    return dict(q=q.to(w.dtype), k=k.to(w.dtype), v=v.to(w.dtype),
+                g=None if g is None else g.contiguous())
+
+
+def draw_decode(w: Workload, *, steps=None, B=None, H=None, seed=None, device="cpu"):
+    """Draw the per-step decode inputs, step-major: q, k [T, B, H, d_k], v [T, B, H, d_v],
+    g [T, B, H, d_k] (key-dim) or [T, B, H] (scalar).  Seeded apart from ``draw``."""
+    T = w.decode_steps if steps is None else steps
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    seed = (w.seed if seed is None else seed) + 7919
+    gen = _gen(device, seed)
+    f32 = dict(dtype=torch.float32, device=device, generator=gen)
+    qk_scale = 1.0 / math.sqrt(w.d_k) if w.scale_qk else 1.0
+    q = torch.randn(T, B, H, w.d_k, **f32) * qk_scale
+    k = torch.randn(T, B, H, w.d_k, **f32) * qk_scale
+    v = torch.randn(T, B, H, w.d_v, **f32)
+    g = None
+    if w.gate == "keydim":
+        g = _log_gate(torch.randn(T, B, H, w.d_k, **f32), "keydim")
+    elif w.gate == "scalar":
+        g = _log_gate(torch.randn(T, B, H, **f32), "scalar")
+    return dict(q=q.to(w.dtype), k=k.to(w.dtype), v=v.to(w.dtype),
+                g=None if g is None else g.contiguous())
+
+
+def draw_state(B, H, d_k, d_v, *, seed, scale=1.0, device="cpu"):
+    """A random fp32 initial state [B, H, d_k, d_v] ~ scale * N(0,1)."""
+    gen = _gen(device, seed)
+    return torch.randn(B, H, d_k, d_v, dtype=torch.float32, device=device, generator=gen) * scale

@@ -1,0 +1,160 @@
+/*
+ * gla_oracle.c -- plain, slow CPU oracle for the causal gated-linear-attention
+ * forward pass, in double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load
+ * this file or the library built from it: only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, table or
+ * helper with the HIP implementation.
+ *
+ * What it computes, per (batch b, head h), token by token, with no chunking:
+ *
+ *   S_{-1} = S0 (or zero)                            d_k x d_v state
+ *   for t = 0 .. L-1:
+ *       q~ = phi(q_t),  k~ = phi(k_t)                 phi = identity or elu(x)+1
+ *       a  = exp(g_t)                                 per key dim / scalar / 1
+ *       S_t[i][j] = a_i * S_{t-1}[i][j] + k~_i * v_t[j]
+ *       o_t[j]    = sum_i q~_i * S_t[i][j]
+ *
+ * Sources (the pages, by title and section):
+ *  - "Attention is recurrent", section "Linear attention": with the softmax
+ *    removed the history collapses into one fixed-size state; the output of token
+ *    n is a function of the previous state and token n's q, k, v, and the state is
+ *    carried from step to step.  Section "Gated linear attention": the state
+ *    forgets through a gate alpha_n applied before the new write.
+ *  - "Gated Linear Attention", section "GLA / Recurrent Form": the gate
+ *    G_t = alpha_t 1^T, i.e. the update Diag(alpha_t) S_{t-1} + (outer product of
+ *    key and value), and the Mamba2 special case G_t = gamma_t 1 1^T with a scalar
+ *    gamma_t in (0,1) (also in "Motivation").
+ *  - "Transformers are RNNs" notes, feature-map paragraph: similarity written as
+ *    phi(Q_i)^T phi(K_j); the elu(x)+1 choice of phi.
+ *
+ * Readings taken where the pages are silent or garbled:
+ *  - orientation: S is d_k x d_v, the write is k v^T, the gate scales key rows and
+ *    the read-out is o_t = S_t^T q_t (the first page's row-vector k^T v form);
+ *  - the read-out is inclusive: o_t uses S_t, which already holds token t's write;
+ *  - alpha_0 also decays the initial state S0;
+ *  - no normaliser and no 1/sqrt(d) scaling inside the operation;
+ *  - gates are passed as natural-log values g = log(alpha) <= 0.
+ *
+ * Layouts: contiguous [B][H][L][d] for q, k, v, o; g is [B][H][L][d_k] (key-dim
+ * mode) or [B][H][L] (scalar mode) or unused; s0 / s_out are [B][H][d_k][d_v].
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_GATE_NONE = 0, ORACLE_GATE_KEYDIM = 1, ORACLE_GATE_SCALAR = 2 };
+enum { ORACLE_PHI_IDENTITY = 0, ORACLE_PHI_ELU1 = 1 };
+
+/* elu(x) + 1 with elu's alpha = 1: x + 1 for x > 0, exp(x) otherwise. */
+static double feature(double x, int phi)
+{
+    if (phi == ORACLE_PHI_IDENTITY) return x;
+    return x > 0.0 ? x + 1.0 : exp(x);
+}
+
+typedef struct {
+    const double *q, *k, *v, *g, *s0;
+    double *o, *s_out;
+    long B, H, L, dk, dv;
+    int gate_mode, phi;
+    long next_head;          /* shared work counter, guarded by lock */
+    pthread_mutex_t lock;
+} job_t;
+
+static void run_head(const job_t *jb, long head, double *S, double *qf, double *kf, double *a)
+{
+    const long L = jb->L, dk = jb->dk, dv = jb->dv;
+    const double *q = jb->q + head * L * dk;
+    const double *k = jb->k + head * L * dk;
+    const double *v = jb->v + head * L * dv;
+    double *o = jb->o + head * L * dv;
+
+    if (jb->s0) memcpy(S, jb->s0 + head * dk * dv, sizeof(double) * dk * dv);
+    else memset(S, 0, sizeof(double) * dk * dv);
+
+    for (long t = 0; t < L; ++t) {
+        for (long i = 0; i < dk; ++i) {
+            qf[i] = feature(q[t * dk + i], jb->phi);
+            kf[i] = feature(k[t * dk + i], jb->phi);
+        }
+        for (long i = 0; i < dk; ++i) {
+            if (jb->gate_mode == ORACLE_GATE_KEYDIM) a[i] = exp(jb->g[(head * L + t) * dk + i]);
+            else if (jb->gate_mode == ORACLE_GATE_SCALAR) a[i] = exp(jb->g[head * L + t]);
+            else a[i] = 1.0;
+        }
+        /* state update: decay the key rows, then add the outer product k~ v^T */
+        for (long i = 0; i < dk; ++i)
+            for (long j = 0; j < dv; ++j)
+                S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];
+        /* read-out from the updated state: o_t = S_t^T q~ */
+        for (long j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk; ++i) acc += qf[i] * S[i * dv + j];
+            o[t * dv + j] = acc;
+        }
+    }
+    if (jb->s_out) memcpy(jb->s_out + head * dk * dv, S, sizeof(double) * dk * dv);
+}
+
+static void *worker(void *arg)
+{
+    job_t *jb = (job_t *)arg;
+    double *S = (double *)malloc(sizeof(double) * jb->dk * jb->dv);
+    double *qf = (double *)malloc(sizeof(double) * jb->dk);
+    double *kf = (double *)malloc(sizeof(double) * jb->dk);
+    double *a = (double *)malloc(sizeof(double) * jb->dk);
+    if (S && qf && kf && a) {          /* on allocation failure take no head */
+        for (;;) {
+            pthread_mutex_lock(&jb->lock);
+            long head = jb->next_head++;
+            pthread_mutex_unlock(&jb->lock);
+            if (head >= jb->B * jb->H) break;
+            run_head(jb, head, S, qf, kf, a);
+        }
+    }
+    free(S); free(qf); free(kf); free(a);
+    return NULL;
+}
+
+/*
+ * Forward pass over all (b, h).  Returns 0 on success, -1 on bad arguments,
+ * -2 if scratch memory could not be allocated.  nthreads <= 0 means 1.
+ */
+int gla_oracle_forward(const double *q, const double *k, const double *v, const double *g,
+                       int gate_mode, int phi, const double *s0, double *o, double *s_out,
+                       long B, long H, long L, long dk, long dv, int nthreads)
+{
+    if (!q || !k || !v || !o || B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0) return -1;
+    if (gate_mode != ORACLE_GATE_NONE && gate_mode != ORACLE_GATE_KEYDIM &&
+        gate_mode != ORACLE_GATE_SCALAR) return -1;
+    if (gate_mode != ORACLE_GATE_NONE && !g) return -1;
+    if (phi != ORACLE_PHI_IDENTITY && phi != ORACLE_PHI_ELU1) return -1;
+
+    job_t jb;
+    jb.q = q; jb.k = k; jb.v = v; jb.g = g; jb.s0 = s0; jb.o = o; jb.s_out = s_out;
+    jb.B = B; jb.H = H; jb.L = L; jb.dk = dk; jb.dv = dv;
+    jb.gate_mode = gate_mode; jb.phi = phi; jb.next_head = 0;
+    pthread_mutex_init(&jb.lock, NULL);
+
+    long heads = B * H;
+    if (nthreads <= 0) nthreads = 1;
+    if (nthreads > heads) nthreads = heads > 0 ? (int)heads : 1;
+    /* The heads form a shared work queue: whichever threads start drain all of it,
+     * and if none can be started the calling thread does the whole job. */
+    pthread_t *th = nthreads > 1 ? (pthread_t *)malloc(sizeof(pthread_t) * nthreads) : NULL;
+    int started = 0;
+    for (int t = 0; th && t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, worker, &jb) != 0) break;
+        ++started;
+    }
+    if (started == 0) worker(&jb);
+    for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    free(th);
+    pthread_mutex_destroy(&jb.lock);
+    /* a worker that failed took no head: if none succeeded, heads are left over */
+    if (jb.next_head < B * H) return -2;
+    return 0;
+}

@@ -1,0 +1,119 @@
+"""Python binding of the fp64 CPU oracle (``gla_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  The product path never
+does, and this module imports nothing from the product package.
+
+The oracle is the token-by-token recurrence of the pages ("Attention is
+recurrent", sections "Linear attention" and "Gated linear attention"; "Gated
+Linear Attention", section "GLA / Recurrent Form"), run in double precision:
+
+    S_t = Diag(alpha_t) S_{t-1} + phi(k_t) v_t^T,   o_t = S_t^T phi(q_t)
+
+with alpha_t = exp(g_t) per key dimension, a scalar exp(g_t) for every key
+dimension, or 1.  Inputs are upcast exactly to float64 from whatever bits the
+caller holds (bf16 and fp32 both convert exactly).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+GATE_MODES = {None: 0, "none": 0, "keydim": 1, "scalar": 2}
+FEATURE_MAPS = {None: 0, "identity": 0, "elu1": 1}
+
+_libs = {}
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one C source of the oracle into a shared library with gcc (no fast-math)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
+                           "-o", tmp, src, "-lm", "-lpthread"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    """Compile ``gla_oracle.c`` into ``liboracle.so`` (always when ``force``)."""
+    if force or not os.path.exists(_LIB_PATH):
+        compile_source(_SRC, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load(lib_path=None):
+    if lib_path is None:
+        build()
+        lib_path = _LIB_PATH
+    if lib_path not in _libs:
+        lib = ctypes.CDLL(lib_path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.gla_oracle_forward.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, dp, dp, dp,
+                                           ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                           ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        lib.gla_oracle_forward.restype = ctypes.c_int
+        _libs[lib_path] = lib
+    return _libs[lib_path]
+
+
+def _f64(x):
+    """Exact upcast to a C-contiguous float64 numpy array (accepts torch tensors)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):                       # torch tensor, any device / dtype
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:                          # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def forward(q, k, v, g=None, gate=None, feature_map=None, s0=None, nthreads=None, lib_path=None):
+    """Run the recurrence over every (b, h).
+
+    q, k: [B, H, L, d_k]; v: [B, H, L, d_v]; g: [B, H, L, d_k] for gate="keydim",
+    [B, H, L] for gate="scalar", None for no gate; s0: [B, H, d_k, d_v] or None.
+    Returns (o [B, H, L, d_v], s_final [B, H, d_k, d_v]) as float64 arrays.
+    ``lib_path`` selects another build of the oracle source (the pin tests use it to
+    check that planted mistakes are caught); by default the committed source is used.
+    """
+    q, k, v, g, s0 = _f64(q), _f64(k), _f64(v), _f64(g), _f64(s0)
+    if q.ndim != 4 or k.shape != q.shape or v.ndim != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("oracle: q, k must be [B,H,L,d_k] and v [B,H,L,d_v]")
+    B, H, L, dk = q.shape
+    dv = v.shape[3]
+    mode = GATE_MODES[gate]
+    if mode == 1 and (g is None or g.shape != (B, H, L, dk)):
+        raise ValueError("oracle: key-dim gate needs g of shape [B,H,L,d_k]")
+    if mode == 2 and (g is None or g.shape != (B, H, L)):
+        raise ValueError("oracle: scalar gate needs g of shape [B,H,L]")
+    if mode == 0:
+        g = None
+    if s0 is not None and s0.shape != (B, H, dk, dv):
+        raise ValueError("oracle: s0 must be [B,H,d_k,d_v]")
+    o = np.zeros((B, H, L, dv), dtype=np.float64)
+    s = np.zeros((B, H, dk, dv), dtype=np.float64)
+    nthreads = default_threads() if nthreads is None else int(nthreads)
+    rc = _load(lib_path).gla_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), mode,
+                                    FEATURE_MAPS[feature_map], _ptr(s0), _ptr(o), _ptr(s),
+                                    B, H, L, dk, dv, nthreads)
+    if rc != 0:
+        raise RuntimeError("gla_oracle_forward failed with code %d" % rc)
+    return o, s

@@ -1,0 +1,274 @@
+"""Independent forms that pin the fp64 oracle to what the pages fix.
+
+Each ``pin_*`` function takes an oracle ``forward`` callable (the committed one, or
+a deliberately broken build in the mutant tests) and returns the worst error it
+found against a form of the computation that is *not* the token recurrence:
+
+- the quadratic masked form ``(phi(Q) phi(K)^T (.) L) V`` for alpha = 1
+  ("Attention is recurrent", note on non-causal linear attention: the causal case
+  needs the multiplicative 0/1 mask L; "Transformers are RNNs" notes: the numerator
+  as entry (i, m) of (A B^T) V with A = phi(Q), B = phi(K));
+- the cumulative-sum state and the last-token regrouping Q (K^T V) ("Attention is
+  recurrent", Prefill: the prefix states are a cumulative sum; note on non-causal
+  linear attention: O = Q (K^T V));
+- the unrolled gated form, where a write at position i reaches position n scaled
+  by the product of the gates after it ("Attention is recurrent", Gated linear
+  attention), evaluated with explicit products;
+- exact rational arithmetic for tiny cases;
+- the RetNet constant decay as a geometric mask and the Mamba2 scalar gate as the
+  key-dimension gate with equal entries ("Gated Linear Attention", Motivation and
+  Recurrent Form);
+- closed forms: elu(x)+1 at fixed points, geometric series, vanishing gates.
+
+Numpy and ``fractions`` only; nothing here calls the HIP path.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+
+def rel_err(x, ref):
+    """Normwise relative error max|x - ref| / max|ref| over the whole array."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    num = np.max(np.abs(x - ref)) if ref.size else 0.0
+    return float(num / den) if den > 0 else float(num)
+
+
+def _phi(x, fm):
+    if fm == "elu1":
+        return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+    return x
+
+
+def rng_inputs(seed, B, H, L, dk, dv, gate=None, s0=False, g_scale=0.3):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, H, L, dk))
+    k = r.standard_normal((B, H, L, dk))
+    v = r.standard_normal((B, H, L, dv))
+    g = None
+    if gate == "keydim":
+        g = -g_scale * r.random((B, H, L, dk))
+    elif gate == "scalar":
+        g = -g_scale * r.random((B, H, L))
+    S0 = r.standard_normal((B, H, dk, dv)) if s0 else None
+    return q, k, v, g, S0
+
+
+# --------------------------------------------------------------------------------------
+def pin_feature_map_points(fwd):
+    """elu(x)+1 at x = -2, 0, 3 is e^-2, 1, 4.  With k = 0 (phi(0) = 1), v = 1 and one
+    token, o_0 = phi(q)."""
+    xs = np.array([-2.0, 0.0, 3.0])
+    want = np.array([math.exp(-2.0), 1.0, 4.0])
+    q = xs.reshape(1, 3, 1, 1)
+    k = np.zeros((1, 3, 1, 1))
+    v = np.ones((1, 3, 1, 1))
+    o, _ = fwd(q, k, v, feature_map="elu1")
+    return float(np.max(np.abs(o.reshape(3) - want)))
+
+
+def pin_quadratic_masked(fwd, seed=0, fm=None, B=2, H=3, L=37, dk=5, dv=7):
+    """alpha = 1: O equals (phi(Q) phi(K)^T (.) L) V per head, L_ts = [s <= t]."""
+    q, k, v, _, _ = rng_inputs(seed, B, H, L, dk, dv)
+    o, _ = fwd(q, k, v, feature_map=fm)
+    mask = np.tril(np.ones((L, L)))
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            A = _phi(q[b, h], fm)
+            Bm = _phi(k[b, h], fm)
+            ref = ((A @ Bm.T) * mask) @ v[b, h]
+            worst = max(worst, rel_err(o[b, h], ref))
+    return worst
+
+
+def pin_cumsum_and_last_token(fwd, seed=1, fm=None, B=2, H=2, L=29, dk=6, dv=4):
+    """alpha = 1, S0 = 0: the final state is phi(K)^T V (a cumulative sum over all
+    tokens), and the last output equals phi(q_last)^T (phi(K)^T V), the non-causal
+    regrouping Q (K^T V) evaluated on the row that sees every token."""
+    q, k, v, _, _ = rng_inputs(seed, B, H, L, dk, dv)
+    o, s = fwd(q, k, v, feature_map=fm)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            KV = _phi(k[b, h], fm).T @ v[b, h]
+            worst = max(worst, rel_err(s[b, h], KV))
+            worst = max(worst, rel_err(o[b, h, L - 1], _phi(q[b, h, L - 1], fm) @ KV))
+    return worst
+
+
+def unrolled_reference(q, k, v, g, gate, S0):
+    """o_n = sum_{i<=n} (q_n . (k_i (.) prod_{m=i+1..n} alpha_m)) v_i
+             + q_n^T Diag(prod_{m=0..n} alpha_m) S0, with explicit products."""
+    B, H, L, dk = q.shape
+    out = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            if gate == "keydim":
+                alpha = np.exp(g[b, h])                          # [L, dk]
+            elif gate == "scalar":
+                alpha = np.repeat(np.exp(g[b, h])[:, None], dk, axis=1)
+            else:
+                alpha = np.ones((L, dk))
+            for n in range(L):
+                acc = np.zeros(v.shape[3])
+                for i in range(n + 1):
+                    w = np.prod(alpha[i + 1:n + 1], axis=0)      # empty product = 1
+                    acc += np.dot(q[b, h, n], k[b, h, i] * w) * v[b, h, i]
+                if S0 is not None:
+                    w0 = np.prod(alpha[0:n + 1], axis=0)
+                    acc += (q[b, h, n] * w0) @ S0[b, h]
+                out[b, h, n] = acc
+    return out
+
+
+def pin_unrolled(fwd, seed=2, gate="keydim", with_s0=True, B=2, H=2, L=23, dk=5, dv=3):
+    q, k, v, g, S0 = rng_inputs(seed, B, H, L, dk, dv, gate=gate, s0=with_s0)
+    o, _ = fwd(q, k, v, g=g, gate=gate, s0=S0)
+    return rel_err(o, unrolled_reference(q, k, v, g, gate, S0))
+
+
+def pin_exact_rational(fwd, seed=3):
+    """Tiny case (L=5, d_k=3, d_v=2, B=H=1) in exact rationals via the unrolled form
+    (outputs) and the expanded state sum (final state); the oracle must agree to
+    ~1e-15 relative (the gates reach it as log values, exp(log a) = a + O(ulp))."""
+    r = np.random.default_rng(seed)
+    L, dk, dv = 5, 3, 2
+    qi = r.integers(-3, 4, size=(L, dk))
+    ki = r.integers(-3, 4, size=(L, dk))
+    vi = r.integers(-3, 4, size=(L, dv))
+    ai = r.integers(1, 8, size=(L, dk))
+    a = [[Fraction(int(x), 8) for x in row] for row in ai]          # alpha in (0, 1)
+    s0i = r.integers(-2, 3, size=(dk, dv))
+    O = [[Fraction(0)] * dv for _ in range(L)]
+    for n in range(L):
+        for j in range(dv):
+            tot = Fraction(0)
+            for i in range(n + 1):
+                for c in range(dk):
+                    w = Fraction(1)
+                    for m in range(i + 1, n + 1):
+                        w *= a[m][c]
+                    tot += int(qi[n, c]) * int(ki[i, c]) * w * int(vi[i, j])
+            for c in range(dk):
+                w0 = Fraction(1)
+                for m in range(0, n + 1):
+                    w0 *= a[m][c]
+                tot += int(qi[n, c]) * w0 * int(s0i[c, j])
+            O[n][j] = tot
+    Sx = [[Fraction(0)] * dv for _ in range(dk)]
+    for c in range(dk):
+        for j in range(dv):
+            w0 = Fraction(1)
+            for m in range(L):
+                w0 *= a[m][c]
+            tot = w0 * int(s0i[c, j])
+            for i in range(L):
+                w = Fraction(1)
+                for m in range(i + 1, L):
+                    w *= a[m][c]
+                tot += int(ki[i, c]) * w * int(vi[i, j])
+            Sx[c][j] = tot
+    g = np.log(ai / 8.0).reshape(1, 1, L, dk)
+    o, s = fwd(qi.reshape(1, 1, L, dk).astype(float), ki.reshape(1, 1, L, dk).astype(float),
+               vi.reshape(1, 1, L, dv).astype(float), g=g, gate="keydim",
+               s0=s0i.reshape(1, 1, dk, dv).astype(float))
+    O_ex = np.array([[float(x) for x in row] for row in O])
+    S_ex = np.array([[float(x) for x in row] for row in Sx])
+    return max(rel_err(o[0, 0], O_ex), rel_err(s[0, 0], S_ex))
+
+
+def pin_scalar_is_broadcast_keydim(fwd, seed=4, B=2, H=3, L=31, dk=4, dv=5):
+    """The Mamba2 gate gamma_t 1 1^T equals the key-dim gate with all entries gamma_t."""
+    q, k, v, g, S0 = rng_inputs(seed, B, H, L, dk, dv, gate="scalar", s0=True)
+    o1, s1 = fwd(q, k, v, g=g, gate="scalar", s0=S0)
+    gk = np.repeat(g[..., None], dk, axis=3)
+    o2, s2 = fwd(q, k, v, g=gk, gate="keydim", s0=S0)
+    # the two must also differ from the ungated run, or the gate was ignored
+    o3, _ = fwd(q, k, v, s0=S0)
+    assert rel_err(o3, o2) > 1e-3
+    return max(rel_err(o1, o2), rel_err(s1, s2))
+
+
+def pin_retnet_geometric(fwd, seed=5, gamma=0.9, B=1, H=2, L=33, dk=4, dv=6):
+    """Constant gamma (RetNet's fixed decay): O = ((Q K^T) (.) D) V with D_ts = gamma^(t-s)
+    for s <= t, else 0."""
+    q, k, v, _, _ = rng_inputs(seed, B, H, L, dk, dv)
+    g = np.full((B, H, L), math.log(gamma))
+    o, _ = fwd(q, k, v, g=g, gate="scalar")
+    t = np.arange(L)
+    D = np.where(t[:, None] >= t[None, :], gamma ** (t[:, None] - t[None, :]).clip(min=0), 0.0)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            ref = ((q[b, h] @ k[b, h].T) * D) @ v[b, h]
+            worst = max(worst, rel_err(o[b, h], ref))
+    return worst
+
+
+def pin_vanishing_gate(fwd, seed=6, B=1, H=2, L=9, dk=3, dv=4):
+    """alpha -> 0 (g = -1000, exp underflows to 0): the state keeps only the current
+    write, so o_t = (q_t . k_t) v_t and S_final = k_last v_last^T."""
+    q, k, v, _, S0 = rng_inputs(seed, B, H, L, dk, dv, s0=True)
+    g = np.full((B, H, L, dk), -1000.0)
+    o, s = fwd(q, k, v, g=g, gate="keydim", s0=S0)
+    ref = np.einsum("bhtc,bhtc->bht", q, k)[..., None] * v
+    sref = np.einsum("bhc,bhj->bhcj", k[:, :, -1], v[:, :, -1])
+    return max(rel_err(o, ref), rel_err(s, sref))
+
+
+def pin_geometric_closed_form(fwd, alpha=0.75, s0=2.5, L=12):
+    """d_k = d_v = 1, q = k = v = 1, constant alpha, initial state s0:
+    o_t = alpha^(t+1) s0 + (1 - alpha^(t+1)) / (1 - alpha).  Pins the inclusive read-out
+    (token t's own write counts) and that alpha_0 decays the initial state."""
+    one = np.ones((1, 1, L, 1))
+    g = np.full((1, 1, L, 1), math.log(alpha))
+    o, s = fwd(one, one, one, g=g, gate="keydim", s0=np.full((1, 1, 1, 1), s0))
+    t = np.arange(L)
+    ref = alpha ** (t + 1) * s0 + (1 - alpha ** (t + 1)) / (1 - alpha)
+    return max(rel_err(o.reshape(L), ref), rel_err(s.reshape(1), ref[-1:]))
+
+
+def pin_chaining(fwd, seed=7, B=2, H=2, L1=17, L2=11, dk=4, dv=5):
+    """run(L1 + L2) equals run(L1) followed by run(L2) from its final state (the state
+    is the whole history).  Returns the max abs difference (0 in the same op order)."""
+    q, k, v, g, S0 = rng_inputs(seed, B, H, L1 + L2, dk, dv, gate="keydim", s0=True)
+    o, s = fwd(q, k, v, g=g, gate="keydim", s0=S0)
+    oa, sa = fwd(q[:, :, :L1], k[:, :, :L1], v[:, :, :L1], g=g[:, :, :L1], gate="keydim", s0=S0)
+    ob, sb = fwd(q[:, :, L1:], k[:, :, L1:], v[:, :, L1:], g=g[:, :, L1:], gate="keydim", s0=sa)
+    return float(max(np.max(np.abs(np.concatenate([oa, ob], axis=2) - o)), np.max(np.abs(sb - s))))
+
+
+def pin_positive_monotone(fwd, seed=8, L=40, dk=4, dv=3):
+    """phi = elu+1 is positive; with alpha = 1, v = 1 and the same query at every step,
+    each output entry is strictly increasing in t.  Returns the smallest increment
+    (must be > 0)."""
+    r = np.random.default_rng(seed)
+    q = np.repeat(r.standard_normal((1, 1, 1, dk)), L, axis=2)
+    k = r.standard_normal((1, 1, L, dk))
+    v = np.ones((1, 1, L, dv))
+    o, _ = fwd(q, k, v, feature_map="elu1")
+    return float(np.min(np.diff(o[0, 0], axis=0)))
+
+
+ALL_ERROR_PINS = {
+    # name: (callable, tolerance); each returns an error that must stay below tolerance
+    "feature_map_points": (pin_feature_map_points, 1e-15),
+    "quadratic_masked": (pin_quadratic_masked, 1e-12),
+    "quadratic_masked_elu1": (lambda f: pin_quadratic_masked(f, seed=10, fm="elu1"), 1e-12),
+    "cumsum_last_token": (pin_cumsum_and_last_token, 1e-12),
+    "cumsum_last_token_elu1": (lambda f: pin_cumsum_and_last_token(f, seed=11, fm="elu1"), 1e-12),
+    "unrolled_keydim": (pin_unrolled, 1e-12),
+    "unrolled_scalar": (lambda f: pin_unrolled(f, seed=12, gate="scalar"), 1e-12),
+    "exact_rational": (pin_exact_rational, 1e-14),
+    "scalar_broadcast": (pin_scalar_is_broadcast_keydim, 1e-15),
+    "retnet_geometric": (pin_retnet_geometric, 1e-12),
+    "vanishing_gate": (pin_vanishing_gate, 1e-15),
+    "geometric_closed_form": (pin_geometric_closed_form, 1e-14),
+    "chaining": (pin_chaining, 0.0),
+}

@@ -1,0 +1,85 @@
+"""CPU tests: the pins are strong enough to catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of ``oracle/gla_oracle.c`` (on the CPU, in a
+temporary directory), builds it, and requires that at least one pin of ``pins.py``
+rejects it.  The committed oracle itself must pass every pin (test_oracle_pins).
+"""
+import functools
+import os
+
+import pytest
+
+from oracle import oracle
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "gla_oracle.c")
+
+UPDATE = "S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];"
+READ = "acc += qf[i] * S[i * dv + j];"
+
+MUTANTS = {
+    "no_decay": [(UPDATE, "S[i * dv + j] = S[i * dv + j] + kf[i] * v[t * dv + j];")],
+    "gate_sign": [("a[i] = exp(jb->g[(head * L + t) * dk + i]);",
+                   "a[i] = exp(-jb->g[(head * L + t) * dk + i]);")],
+    "decay_after_write": [(UPDATE, "S[i * dv + j] = a[i] * (S[i * dv + j] + kf[i] * v[t * dv + j]);")],
+    "gate_on_value_axis": [(UPDATE, "S[i * dv + j] = a[j % dk] * S[i * dv + j] + kf[i] * v[t * dv + j];")],
+    "wrong_readout_column": [(READ, "acc += qf[i] * S[i * dv + (dv - 1 - j)];")],
+    "readout_uses_key": [(READ, "acc += kf[i] * S[i * dv + j];")],
+    "phi_on_value": [(UPDATE, "S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * feature(v[t * dv + j], jb->phi);")],
+    "phi_missing_on_query": [("qf[i] = feature(q[t * dk + i], jb->phi);", "qf[i] = q[t * dk + i];")],
+    "elu_without_plus_one": [("return x > 0.0 ? x + 1.0 : exp(x);", "return x > 0.0 ? x : exp(x);")],
+    "scalar_gate_head_offset": [("a[i] = exp(jb->g[head * L + t]);", "a[i] = exp(jb->g[t]);")],
+    "initial_state_ignored": [("if (jb->s0) memcpy", "if (0) memcpy")],
+    "exclusive_readout": [
+        ("""        /* state update: decay the key rows, then add the outer product k~ v^T */
+        for (long i = 0; i < dk; ++i)
+            for (long j = 0; j < dv; ++j)
+                S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];
+        /* read-out from the updated state: o_t = S_t^T q~ */
+        for (long j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk; ++i) acc += qf[i] * S[i * dv + j];
+            o[t * dv + j] = acc;
+        }""",
+         """        for (long j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk; ++i) acc += qf[i] * S[i * dv + j];
+            o[t * dv + j] = acc;
+        }
+        for (long i = 0; i < dk; ++i)
+            for (long j = 0; j < dv; ++j)
+                S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];""")],
+    "off_by_one_value_row": [(UPDATE, "S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[(t > 0 ? t - 1 : 0) * dv + j];")],
+}
+
+
+def _pin_results(fwd):
+    failed = []
+    for name, (fn, tol) in pins.ALL_ERROR_PINS.items():
+        try:
+            err = fn(fwd)
+        except AssertionError:
+            failed.append(name)
+            continue
+        if not err <= tol:                 # also catches NaN
+            failed.append(name)
+    try:
+        if not pins.pin_positive_monotone(fwd) > 0.0:
+            failed.append("positive_monotone")
+    except AssertionError:
+        failed.append("positive_monotone")
+    return failed
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_reject_planted_mistake(mutant, tmp_path):
+    src = open(SRC).read()
+    for old, new in MUTANTS[mutant]:
+        assert src.count(old) == 1, "mutation anchor not found: %r" % old
+        src = src.replace(old, new)
+    c_path = tmp_path / ("mutant_%s.c" % mutant)
+    c_path.write_text(src)
+    lib = oracle.compile_source(str(c_path), str(tmp_path / ("libmutant_%s.so" % mutant)))
+    fwd = functools.partial(oracle.forward, lib_path=lib)
+    failed = _pin_results(fwd)
+    assert failed, "planted mistake %r passed every pin" % mutant

@@ -1,0 +1,87 @@
+"""CPU tests: the fp64 oracle against the independent forms in ``pins.py`` and the
+stored worked example under ``golden/``."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from tests import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "prefill_4token.json")
+
+
+@pytest.mark.parametrize("name", sorted(pins.ALL_ERROR_PINS))
+def test_oracle_pin(name):
+    fn, tol = pins.ALL_ERROR_PINS[name]
+    err = fn(oracle.forward)
+    assert err <= tol, "%s: error %.3e above %.1e" % (name, err, tol)
+
+
+def test_oracle_positive_monotone():
+    assert pins.pin_positive_monotone(oracle.forward) > 0.0
+
+
+def test_oracle_threads_agree_bitwise():
+    q, k, v, g, S0 = pins.rng_inputs(21, 3, 5, 19, 6, 7, gate="keydim", s0=True)
+    o1, s1 = oracle.forward(q, k, v, g=g, gate="keydim", s0=S0, nthreads=1)
+    o8, s8 = oracle.forward(q, k, v, g=g, gate="keydim", s0=S0, nthreads=8)
+    assert np.array_equal(o1, o8) and np.array_equal(s1, s8)
+
+
+def test_oracle_empty_sequence_returns_initial_state():
+    q, k, v, g, S0 = pins.rng_inputs(22, 2, 2, 0, 4, 3, gate="keydim", s0=True)
+    o, s = oracle.forward(q, k, v, g=g, gate="keydim", s0=S0)
+    assert o.shape == (2, 2, 0, 3) and np.array_equal(s, S0)
+
+
+def test_oracle_rejects_bad_shapes():
+    q, k, v, g, _ = pins.rng_inputs(23, 1, 1, 4, 3, 2, gate="keydim")
+    with pytest.raises(ValueError):
+        oracle.forward(q, k, v, g=g[..., 0], gate="keydim")
+    with pytest.raises(ValueError):
+        oracle.forward(q, k[..., :2], v)
+
+
+def _exact_unrolled(case):
+    """Exact rational outputs of the stored example via the unrolled form."""
+    q, k, v = (np.array(case[x], dtype=object) for x in ("q", "k", "v"))
+    a = [[Fraction(x) for x in row] for row in case["alpha"]]
+    L, dk = q.shape
+    dv = v.shape[1]
+    out = []
+    for n in range(L):
+        row = []
+        for j in range(dv):
+            tot = Fraction(0)
+            for i in range(n + 1):
+                for c in range(dk):
+                    w = Fraction(1)
+                    for m in range(i + 1, n + 1):
+                        w *= a[m][c]
+                    tot += Fraction(q[n, c]) * Fraction(k[i, c]) * w * Fraction(v[i, j])
+            row.append(tot)
+        out.append(row)
+    return np.array([[float(x) for x in r] for r in out])
+
+
+def test_golden_prefill_4token():
+    """A four-token prompt x_0..x_3 prefilled in one pass (the shape of the worked
+    example in "Attention is recurrent", Prefill, whose numbers did not survive):
+    the stored outputs were written by ``golden/make_golden.py`` from the oracle; they
+    must match exact rational arithmetic and the oracle must still reproduce them."""
+    with open(GOLDEN) as f:
+        case = json.load(f)
+    want = np.array(case["o"], dtype=np.float64)
+    exact = _exact_unrolled(case)
+    assert pins.rel_err(want, exact) < 1e-14
+    L, dk = len(case["q"]), len(case["q"][0])
+    dv = len(case["v"][0])
+    alpha = np.array([[float(Fraction(x)) for x in r] for r in case["alpha"]])
+    o, _ = oracle.forward(np.array(case["q"], float).reshape(1, 1, L, dk),
+                          np.array(case["k"], float).reshape(1, 1, L, dk),
+                          np.array(case["v"], float).reshape(1, 1, L, dv),
+                          g=np.log(alpha).reshape(1, 1, L, dk), gate="keydim")
+    assert pins.rel_err(o[0, 0], want) < 1e-14
