@@ -1,0 +1,8 @@
+"""Causal gated linear attention (GLA) forward for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``include/gla.h`` (``libgla.so``, built in-tree); this package is its thin Python
+binding.  ``inputs`` holds the seeded synthetic workloads.
+"""
+from .api import DeviceState, decode_step, prefill, state_alloc, workspace_bytes  # noqa: F401
+from ._lib import GLAError  # noqa: F401

@@ -1,0 +1,276 @@
+// gla_api.cpp -- the C ABI declared in include/gla.h: host-only argument
+// validation (no HIP call happens before it passes), launch configuration, and the
+// state allocation helpers.  The operations themselves are the gated recurrence of
+// "Attention is recurrent" (Linear attention, Gated linear attention) and "Gated
+// Linear Attention" (Recurrent Form), computed by the kernels in gla_prefill.hpp
+// (chunkwise form) and gla_decode.hip (one recurrent step).
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "gla.h"
+#include "gla_launch.hpp"
+
+namespace gla {
+hipError_t launch_prefill_0_16(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_0_32(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_0_64(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_0_128(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_1_16(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_1_32(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_1_64(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_1_128(const PrefillArgs &, int, int, hipStream_t);
+
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, int nw,
+                          hipStream_t stream)
+{
+    if (dtype == 1) {
+        switch (d_k) {
+        case 16: return launch_prefill_1_16(a, chunk, nw, stream);
+        case 32: return launch_prefill_1_32(a, chunk, nw, stream);
+        case 64: return launch_prefill_1_64(a, chunk, nw, stream);
+        case 128: return launch_prefill_1_128(a, chunk, nw, stream);
+        }
+    } else {
+        switch (d_k) {
+        case 16: return launch_prefill_0_16(a, chunk, nw, stream);
+        case 32: return launch_prefill_0_32(a, chunk, nw, stream);
+        case 64: return launch_prefill_0_64(a, chunk, nw, stream);
+        case 128: return launch_prefill_0_128(a, chunk, nw, stream);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+// Value-column tile width is 16 * waves: 4 waves (64 columns) when d_v allows.
+int prefill_waves(int d_v, int BH)
+{
+    (void)BH;
+    return d_v >= 64 ? 4 : d_v / 16;
+}
+}  // namespace gla
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return status;
+}
+
+int ok()
+{
+    g_detail.clear();
+    return GLA_OK;
+}
+
+bool dim_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_supported(int c) { return c == 16 || c == 32 || c == 64; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+size_t elem_size(gla_dtype dt) { return dt == GLA_BF16 ? 2 : 4; }
+
+struct Span {
+    uintptr_t lo, hi;   // [lo, hi); empty when lo == hi
+    const char *name;
+};
+Span span(const void *p, size_t bytes, const char *name)
+{
+    const uintptr_t lo = (uintptr_t)p;
+    return Span{lo, p ? lo + bytes : lo, name};
+}
+bool overlap(const Span &a, const Span &b)
+{
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+int check_common(int B, int H, int d_k, int d_v, gla_dtype dtype, gla_gate_mode gate,
+                 gla_feature_map phi, const float *g, bool g_required)
+{
+    if (B <= 0 || H <= 0) return fail(GLA_ERR_SHAPE, "B=%d and H=%d must be positive", B, H);
+    if (d_k <= 0 || d_v <= 0)
+        return fail(GLA_ERR_SHAPE, "d_k=%d and d_v=%d must be positive", d_k, d_v);
+    if (!dim_supported(d_k) || !dim_supported(d_v))
+        return fail(GLA_ERR_UNSUPPORTED, "d_k=%d, d_v=%d: each must be 16, 32, 64 or 128", d_k, d_v);
+    if (dtype != GLA_F32 && dtype != GLA_BF16)
+        return fail(GLA_ERR_UNSUPPORTED, "dtype %d is not GLA_F32 or GLA_BF16", (int)dtype);
+    if (gate != GLA_GATE_NONE && gate != GLA_GATE_KEYDIM && gate != GLA_GATE_SCALAR)
+        return fail(GLA_ERR_UNSUPPORTED, "gate mode %d", (int)gate);
+    if (phi != GLA_PHI_IDENTITY && phi != GLA_PHI_ELU1)
+        return fail(GLA_ERR_UNSUPPORTED, "feature map %d", (int)phi);
+    if (gate == GLA_GATE_NONE && g != nullptr)
+        return fail(GLA_ERR_UNSUPPORTED, "g must be NULL with GLA_GATE_NONE");
+    if (gate != GLA_GATE_NONE && g == nullptr && g_required)
+        return fail(GLA_ERR_NULL, "g is NULL but a gate mode is set");
+    if (g && ((uintptr_t)g & (gate == GLA_GATE_SCALAR ? 3u : 15u)))
+        return fail(GLA_ERR_ALIGN, "g=%p is not %d-byte aligned", (const void *)g,
+                    gate == GLA_GATE_SCALAR ? 4 : 16);
+    return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gla_strerror(int status)
+{
+    switch (status) {
+    case GLA_OK: return "success";
+    case GLA_ERR_NULL: return "required pointer is NULL";
+    case GLA_ERR_SHAPE: return "invalid size";
+    case GLA_ERR_UNSUPPORTED: return "unsupported size, dtype, gate mode or feature map";
+    case GLA_ERR_ALIGN: return "pointer not suitably aligned";
+    case GLA_ERR_ALIAS: return "output overlaps an input";
+    case GLA_ERR_HIP: return "HIP runtime error";
+    case GLA_ERR_OOM: return "out of device memory";
+    case GLA_ERR_WORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+const char *gla_last_error_detail(void) { return g_detail.c_str(); }
+
+int gla_state_alloc(int B, int H, int d_k, int d_v, float **state, gla_stream_t stream)
+{
+    if (!state) return fail(GLA_ERR_NULL, "state out-pointer is NULL");
+    if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0)
+        return fail(GLA_ERR_SHAPE, "B=%d H=%d d_k=%d d_v=%d must be positive", B, H, d_k, d_v);
+    if (!dim_supported(d_k) || !dim_supported(d_v))
+        return fail(GLA_ERR_UNSUPPORTED, "d_k=%d, d_v=%d: each must be 16, 32, 64 or 128", d_k, d_v);
+    const size_t bytes = (size_t)B * H * d_k * d_v * sizeof(float);
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e == hipErrorOutOfMemory) {
+        (void)hipGetLastError();
+        return fail(GLA_ERR_OOM, "hipMalloc(%zu) failed: out of memory", bytes);
+    }
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "hipMalloc: %s", hipGetErrorString(e));
+    e = hipMemsetAsync(p, 0, bytes, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return fail(GLA_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
+    }
+    *state = (float *)p;
+    return ok();
+}
+
+int gla_state_free(float *state, gla_stream_t stream)
+{
+    if (!state) return ok();
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    e = hipFree(state);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t gla_prefill_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chunk,
+                                   gla_dtype dtype)
+{
+    (void)B; (void)H; (void)L; (void)d_k; (void)d_v; (void)chunk; (void)dtype;
+    return 0;
+}
+
+int gla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
+                        gla_gate_mode gate, const float *s0, void *o, float *s_final,
+                        int B, int H, int L, int d_k, int d_v, int chunk, gla_dtype dtype,
+                        gla_feature_map phi, void *workspace, size_t workspace_bytes,
+                        gla_stream_t stream)
+{
+    if (L < 0) return fail(GLA_ERR_SHAPE, "L=%d must be >= 0", L);
+    int st = check_common(B, H, d_k, d_v, dtype, gate, phi, g, L > 0);
+    if (st != GLA_OK) return st;
+    if (!chunk_supported(chunk))
+        return fail(GLA_ERR_UNSUPPORTED, "chunk=%d: must be 16, 32 or 64", chunk);
+    if (L > 0 && (!q || !k || !v || !o))
+        return fail(GLA_ERR_NULL, "q, k, v and o are required when L > 0");
+    const void *ptrs[] = {q, k, v, s0, o, s_final, workspace};
+    const char *names[] = {"q", "k", "v", "s0", "o", "s_final", "workspace"};
+    for (int i = 0; i < 7; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    const size_t need = gla_prefill_workspace_bytes(B, H, L, d_k, d_v, chunk, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    const size_t BH = (size_t)B * H, es = elem_size(dtype);
+    const size_t gbytes = gate == GLA_GATE_KEYDIM ? BH * L * d_k * 4 : BH * L * 4;
+    const size_t sbytes = BH * d_k * d_v * 4;
+    const Span sq = span(q, BH * L * d_k * es, "q"), sk = span(k, BH * L * d_k * es, "k");
+    const Span sv = span(v, BH * L * d_v * es, "v"), sg = span(g, g ? gbytes : 0, "g");
+    const Span ss0 = span(s0, sbytes, "s0"), so = span(o, BH * L * d_v * es, "o");
+    const Span ssf = span(s_final, sbytes, "s_final"), sw = span(workspace, need, "workspace");
+    const Span o_forbidden[] = {sq, sk, sv, sg, ss0, ssf, sw};
+    for (const Span &x : o_forbidden)
+        if (overlap(so, x)) return fail(GLA_ERR_ALIAS, "o overlaps %s", x.name);
+    const Span sf_forbidden[] = {sq, sk, sv, sg, sw};
+    for (const Span &x : sf_forbidden)
+        if (overlap(ssf, x)) return fail(GLA_ERR_ALIAS, "s_final overlaps %s", x.name);
+    if (overlap(ssf, ss0) && s_final != s0)
+        return fail(GLA_ERR_ALIAS, "s_final partially overlaps s0");
+
+    gla::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.s0 = s0; a.o = o; a.s_final = s_final;
+    a.BH = (int)BH; a.L = L; a.d_v = d_v;
+    a.gate = (int)gate; a.elu1 = phi == GLA_PHI_ELU1;
+    const int nw = gla::prefill_waves(d_v, a.BH);
+    a.n_vt = d_v / (16 * nw);
+    const long grid = (long)BH * a.n_vt;
+    if (grid > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H too large");
+    a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
+    if (L == 0 && !s_final) return ok();
+    hipError_t e = gla::launch_prefill(a, dtype == GLA_BF16 ? 1 : 0, d_k, chunk, nw,
+                                       (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int gla_decode_step(const void *q, const void *k, const void *v, const float *g,
+                    gla_gate_mode gate, float *state, void *o, int B, int H, int d_k, int d_v,
+                    gla_dtype dtype, gla_feature_map phi, gla_stream_t stream)
+{
+    int st = check_common(B, H, d_k, d_v, dtype, gate, phi, g, true);
+    if (st != GLA_OK) return st;
+    if (!q || !k || !v || !state || !o)
+        return fail(GLA_ERR_NULL, "q, k, v, state and o are required");
+    const void *ptrs[] = {q, k, v, state, o};
+    const char *names[] = {"q", "k", "v", "state", "o"};
+    for (int i = 0; i < 5; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    const size_t BH = (size_t)B * H, es = elem_size(dtype);
+    const size_t gbytes = gate == GLA_GATE_KEYDIM ? BH * d_k * 4 : BH * 4;
+    const Span sq = span(q, BH * d_k * es, "q"), sk = span(k, BH * d_k * es, "k");
+    const Span sv = span(v, BH * d_v * es, "v"), sg = span(g, g ? gbytes : 0, "g");
+    const Span sst = span(state, BH * d_k * d_v * 4, "state"), so = span(o, BH * d_v * es, "o");
+    const Span o_forbidden[] = {sq, sk, sv, sg, sst};
+    for (const Span &x : o_forbidden)
+        if (overlap(so, x)) return fail(GLA_ERR_ALIAS, "o overlaps %s", x.name);
+    const Span st_forbidden[] = {sq, sk, sv, sg};
+    for (const Span &x : st_forbidden)
+        if (overlap(sst, x)) return fail(GLA_ERR_ALIAS, "state overlaps %s", x.name);
+    if (BH > 0x7fffffffUL) return fail(GLA_ERR_SHAPE, "B*H too large");
+
+    gla::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.state = state; a.o = o;
+    a.BH = (int)BH; a.gate = (int)gate; a.elu1 = phi == GLA_PHI_ELU1;
+    hipError_t e = gla::launch_decode(a, dtype == GLA_BF16 ? 1 : 0, d_k, d_v, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+/*
+ * gla.h -- C ABI of the causal gated-linear-attention (GLA) forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per batch b and head h), following the pages:
+ *   "Attention is recurrent", sections "Linear attention" and "Gated linear
+ *   attention": once the softmax is removed, the history folds into a fixed-size
+ *   state that is updated once per token, and a gate alpha_n makes it forget;
+ *   "Gated Linear Attention", section "GLA / Recurrent Form": the gate
+ *   G_t = alpha_t 1^T acts as Diag(alpha_t) on the state, and the Mamba2 form
+ *   G_t = gamma_t 1 1^T uses one scalar gamma_t (also section "Motivation");
+ *   "Transformers are RNNs" notes, feature-map paragraph: phi applied to q and k.
+ *
+ *     S_t = Diag(alpha_t) S_{t-1} + phi(k_t) v_t^T          S_t is d_k x d_v, fp32
+ *     o_t = S_t^T phi(q_t)                                  (reads the updated state)
+ *
+ * with alpha_t = exp(g_t) (key-dimension gate), alpha_t = exp(g_t) * 1 (scalar
+ * gate) or alpha_t = 1 (no gate), and S_{-1} = s0 (zero when s0 is NULL).
+ * No normaliser and no 1/sqrt(d) scaling are applied; callers pre-scale q and k.
+ *
+ * gla_prefill_chunked computes all outputs of a known prompt with the chunkwise
+ * block-parallel form ("Gated Linear Attention", Summary: chunks of C tokens
+ * interpolate between the parallel and the recurrent form, cost
+ * O(L C d + L d^2)); gla_decode_step performs one token of the recurrence on a
+ * state held in device memory ("Attention is recurrent", Linear attention: o_n
+ * is a function of S_{n-1}, q_n, k_n, v_n only).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major arrays,
+ *    16-byte aligned (scalar-mode gates: 4-byte aligned).  The caller owns every
+ *    buffer; prefill and decode never allocate device memory and keep no state
+ *    between calls.
+ *  - Layouts: q, k: [B][H][L][d_k]; v, o: [B][H][L][d_v] (decode: L absent);
+ *    key-dim gates g: [B][H][L][d_k]; scalar gates g: [B][H][L]; states s0,
+ *    s_final, state: [B][H][d_k][d_v], always fp32; gates always fp32 natural-log
+ *    values g = log(alpha), finite and <= 0 (outside that domain results are
+ *    undefined; the library does not scan device data to check it).
+ *  - q, k, v and o share one dtype (GLA_F32 or GLA_BF16); bf16 results are rounded
+ *    to nearest even.  Arithmetic: fp32 accumulation and fp32 state; with bf16
+ *    inputs the matrix-core operands are bf16.
+ *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ *    B, H >= 1; L >= 0 (L need not be a multiple of chunk; L == 0 only copies the
+ *    initial state to s_final).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Argument validation is host-only and runs before any HIP call: on
+ *    any error nothing is launched and nothing is written.  Faults during
+ *    execution surface at the caller's next synchronisation of the stream.
+ *  - Every entry point returns GLA_OK (0) or a negative gla_status.
+ *    gla_last_error_detail() gives a message for the last failure on the calling
+ *    thread.
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GLA_OK = 0,
+    GLA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    GLA_ERR_SHAPE = -2,       /* a size is negative or zero where it must be positive */
+    GLA_ERR_UNSUPPORTED = -3, /* d_k, d_v, chunk, dtype, gate mode or feature map     */
+    GLA_ERR_ALIGN = -4,       /* a pointer is not aligned as documented below         */
+    GLA_ERR_ALIAS = -5,       /* an output overlaps an input it must not overlap      */
+    GLA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed           */
+    GLA_ERR_OOM = -7,         /* gla_state_alloc could not allocate                   */
+    GLA_ERR_WORKSPACE = -8    /* workspace missing or smaller than required           */
+} gla_status;
+
+typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+typedef enum {
+    GLA_GATE_NONE = 0,    /* alpha = 1 (plain linear attention); g must be NULL      */
+    GLA_GATE_KEYDIM = 1,  /* alpha_t = exp(g_t), one log-gate per key dimension      */
+    GLA_GATE_SCALAR = 2   /* alpha_t = exp(g_t) * 1, one log-gate per token and head */
+} gla_gate_mode;
+
+typedef enum {
+    GLA_PHI_IDENTITY = 0, /* phi(x) = x                                              */
+    GLA_PHI_ELU1 = 1      /* phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise    */
+} gla_feature_map;
+
+typedef void *gla_stream_t; /* a hipStream_t */
+
+/*
+ * gla_state_alloc -- allocate a zero-filled fp32 state [B][H][d_k][d_v] on the
+ * current device for gla_decode_step (the fixed-size state that replaces the
+ * KV cache: "Attention is recurrent", Linear attention).  The zero fill is
+ * enqueued on `stream`.  *state receives the device pointer; release it with
+ * gla_state_free.  Errors: GLA_ERR_NULL (state == NULL), GLA_ERR_SHAPE,
+ * GLA_ERR_UNSUPPORTED (d_k / d_v), GLA_ERR_OOM, GLA_ERR_HIP.  On error *state is
+ * left unchanged.
+ */
+int gla_state_alloc(int B, int H, int d_k, int d_v, float **state, gla_stream_t stream);
+
+/*
+ * gla_state_free -- synchronise `stream` and free a state from gla_state_alloc.
+ * NULL is accepted and ignored.  Errors: GLA_ERR_HIP.
+ */
+int gla_state_free(float *state, gla_stream_t stream);
+
+/*
+ * gla_prefill_workspace_bytes -- size in bytes of the device workspace that
+ * gla_prefill_chunked needs for these sizes (0 when none).  Returns 0 also for
+ * invalid sizes (gla_prefill_chunked reports those).
+ */
+size_t gla_prefill_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chunk,
+                                   gla_dtype dtype);
+
+/*
+ * gla_prefill_chunked -- outputs of every token of a known prompt and the final
+ * state, by the chunkwise block-parallel form ("Gated Linear Attention", Summary
+ * and Methodology; "Attention is recurrent", Prefill: the prefix states form a
+ * (weighted) scan).  Inside each chunk of `chunk` tokens the masked products run
+ * on the matrix cores; chunks are chained through the fp32 state.  The result
+ * equals the token recurrence above for any chunk size up to rounding.
+ *
+ *   q, k      in   [B][H][L][d_k], dtype (may be NULL when L == 0, as may v, o)
+ *   v         in   [B][H][L][d_v], dtype
+ *   g         in   fp32 log-gates, [B][H][L][d_k] (KEYDIM) / [B][H][L] (SCALAR);
+ *                  must be NULL for GLA_GATE_NONE; may be NULL when L == 0
+ *   s0        in   fp32 [B][H][d_k][d_v] initial state, or NULL for zero
+ *   o         out  [B][H][L][d_v], dtype
+ *   s_final   out  fp32 [B][H][d_k][d_v] state after the last token, or NULL;
+ *                  may equal s0 (update in place) but must not partially overlap it
+ *   workspace      device scratch of at least gla_prefill_workspace_bytes(...)
+ *                  bytes (NULL allowed when that is 0); contents are clobbered
+ *
+ * o must not overlap q, k, v, g, s0, s_final or the workspace; s_final must not
+ * overlap q, k, v, g or the workspace.  Errors: GLA_ERR_NULL, GLA_ERR_SHAPE,
+ * GLA_ERR_UNSUPPORTED, GLA_ERR_ALIGN, GLA_ERR_ALIAS, GLA_ERR_WORKSPACE, GLA_ERR_HIP.
+ */
+int gla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
+                        gla_gate_mode gate, const float *s0, void *o, float *s_final,
+                        int B, int H, int L, int d_k, int d_v, int chunk, gla_dtype dtype,
+                        gla_feature_map phi, void *workspace, size_t workspace_bytes,
+                        gla_stream_t stream);
+
+/*
+ * gla_decode_step -- one token of the recurrence on a resident state: for every
+ * (b, h), state <- Diag(alpha) state + phi(k) v^T in place, then
+ * o = state^T phi(q) ("Attention is recurrent", Linear attention and Gated linear
+ * attention; "Gated Linear Attention", Recurrent Form and its dataflow chart).
+ *
+ *   q, k      in      [B][H][d_k], dtype
+ *   v         in      [B][H][d_v], dtype
+ *   g         in      fp32 [B][H][d_k] (KEYDIM) / [B][H] (SCALAR) / NULL (NONE)
+ *   state     in/out  fp32 [B][H][d_k][d_v]
+ *   o         out     [B][H][d_v], dtype
+ *
+ * o must not overlap state, q, k, v or g; state must not overlap q, k, v or g.
+ * Errors: GLA_ERR_NULL, GLA_ERR_SHAPE, GLA_ERR_UNSUPPORTED, GLA_ERR_ALIGN,
+ * GLA_ERR_ALIAS, GLA_ERR_HIP.
+ */
+int gla_decode_step(const void *q, const void *k, const void *v, const float *g,
+                    gla_gate_mode gate, float *state, void *o, int B, int H, int d_k, int d_v,
+                    gla_dtype dtype, gla_feature_map phi, gla_stream_t stream);
+
+/* gla_strerror -- static text for a gla_status value (never NULL). */
+const char *gla_strerror(int status);
+
+/* gla_last_error_detail -- message for the last non-OK status returned on the
+ * calling thread ("" if none).  Valid until the next call on that thread. */
+const char *gla_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

@@ -1,0 +1,168 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point that
+include/gla.h declares, and its host-side validation rejects bad arguments with the
+documented status before touching the GPU (every case here is invalid, so no HIP
+call and no kernel launch happens)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_gated_linear_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from causal_gated_linear_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(["gla_state_alloc", "gla_state_free", "gla_prefill_workspace_bytes",
+                                  "gla_prefill_chunked", "gla_decode_step", "gla_strerror",
+                                  "gla_last_error_detail"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == _declared()
+
+
+def test_strerror_covers_every_status(lib):
+    for st in range(0, -9, -1):
+        s = lib.gla_strerror(st).decode()
+        assert s and s != "unknown status"
+    assert lib.gla_strerror(-99).decode() == "unknown status"
+
+
+# fake, 16-byte aligned device addresses: validation must reject every call below
+# before any of them is dereferenced or passed to HIP
+A = 0x10000000
+MB = 1 << 20
+
+
+def _prefill(lib, **kw):
+    args = dict(q=A, k=A + 16 * MB, v=A + 32 * MB, g=A + 48 * MB, gate=1, s0=None, o=A + 96 * MB,
+                s_final=A + 128 * MB, B=1, H=2, L=64, d_k=64, d_v=64, chunk=64, dtype=1, phi=0,
+                ws=None, ws_bytes=0)
+    args.update(kw)
+    P = ctypes.c_void_p
+    return lib.gla_prefill_chunked(P(args["q"]), P(args["k"]), P(args["v"]), P(args["g"]), args["gate"],
+                                   P(args["s0"]), P(args["o"]), P(args["s_final"]), args["B"],
+                                   args["H"], args["L"], args["d_k"], args["d_v"], args["chunk"],
+                                   args["dtype"], args["phi"], P(args["ws"]), args["ws_bytes"], None)
+
+
+PREFILL_BAD = {
+    "B_zero": (dict(B=0), _lib.GLA_ERR_SHAPE),
+    "H_negative": (dict(H=-3), _lib.GLA_ERR_SHAPE),
+    "L_negative": (dict(L=-1), _lib.GLA_ERR_SHAPE),
+    "d_k_48": (dict(d_k=48), _lib.GLA_ERR_UNSUPPORTED),
+    "d_v_256": (dict(d_v=256), _lib.GLA_ERR_UNSUPPORTED),
+    "chunk_128": (dict(chunk=128), _lib.GLA_ERR_UNSUPPORTED),
+    "chunk_8": (dict(chunk=8), _lib.GLA_ERR_UNSUPPORTED),
+    "dtype_7": (dict(dtype=7), _lib.GLA_ERR_UNSUPPORTED),
+    "gate_5": (dict(gate=5), _lib.GLA_ERR_UNSUPPORTED),
+    "phi_3": (dict(phi=3), _lib.GLA_ERR_UNSUPPORTED),
+    "gate_none_with_g": (dict(gate=0), _lib.GLA_ERR_UNSUPPORTED),
+    "keydim_without_g": (dict(g=None), _lib.GLA_ERR_NULL),
+    "q_null": (dict(q=None), _lib.GLA_ERR_NULL),
+    "o_null": (dict(o=None), _lib.GLA_ERR_NULL),
+    "q_misaligned": (dict(q=A + 8), _lib.GLA_ERR_ALIGN),
+    "s_final_misaligned": (dict(s_final=A + 128 * MB + 4), _lib.GLA_ERR_ALIGN),
+    "keydim_g_misaligned": (dict(g=A + 48 * MB + 4), _lib.GLA_ERR_ALIGN),
+    "scalar_g_misaligned": (dict(gate=2, g=A + 48 * MB + 2), _lib.GLA_ERR_ALIGN),
+    "o_overlaps_v": (dict(o=A + 32 * MB + 4096), _lib.GLA_ERR_ALIAS),
+    "o_overlaps_g": (dict(o=A + 48 * MB), _lib.GLA_ERR_ALIAS),
+    "o_overlaps_s_final": (dict(s_final=A + 96 * MB + 64), _lib.GLA_ERR_ALIAS),
+    "s_final_overlaps_q": (dict(s_final=A + 1024), _lib.GLA_ERR_ALIAS),
+    "s_final_partially_overlaps_s0": (dict(s0=A + 200 * MB, s_final=A + 200 * MB + 256), _lib.GLA_ERR_ALIAS),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PREFILL_BAD))
+def test_prefill_rejects(lib, case):
+    kw, want = PREFILL_BAD[case]
+    assert _prefill(lib, **kw) == want
+    assert lib.gla_last_error_detail().decode() != ""
+
+
+def _decode(lib, **kw):
+    args = dict(q=A, k=A + MB, v=A + 2 * MB, g=A + 3 * MB, gate=1, state=A + 16 * MB, o=A + 64 * MB,
+                B=2, H=4, d_k=128, d_v=128, dtype=1, phi=0)
+    args.update(kw)
+    P = ctypes.c_void_p
+    return lib.gla_decode_step(P(args["q"]), P(args["k"]), P(args["v"]), P(args["g"]), args["gate"],
+                               P(args["state"]), P(args["o"]), args["B"], args["H"], args["d_k"],
+                               args["d_v"], args["dtype"], args["phi"], None)
+
+
+DECODE_BAD = {
+    "state_null": (dict(state=None), _lib.GLA_ERR_NULL),
+    "v_null": (dict(v=None), _lib.GLA_ERR_NULL),
+    "B_zero": (dict(B=0), _lib.GLA_ERR_SHAPE),
+    "d_v_8": (dict(d_v=8), _lib.GLA_ERR_UNSUPPORTED),
+    "scalar_without_g": (dict(gate=2, g=None), _lib.GLA_ERR_NULL),
+    "o_overlaps_state": (dict(o=A + 16 * MB + 512), _lib.GLA_ERR_ALIAS),
+    "state_overlaps_k": (dict(state=A + MB), _lib.GLA_ERR_ALIAS),
+    "o_misaligned": (dict(o=A + 64 * MB + 2), _lib.GLA_ERR_ALIGN),
+    "scalar_g_misaligned": (dict(gate=2, g=A + 3 * MB + 1), _lib.GLA_ERR_ALIGN),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DECODE_BAD))
+def test_decode_rejects(lib, case):
+    kw, want = DECODE_BAD[case]
+    assert _decode(lib, **kw) == want
+
+
+def test_empty_prefill_may_omit_inputs(lib):
+    """With L == 0 the inputs (and g) may be NULL; the call is still validated (here it
+    fails on the chunk size, so nothing is launched)."""
+    assert _prefill(lib, L=0, q=None, k=None, v=None, o=None, g=None, chunk=8) == _lib.GLA_ERR_UNSUPPORTED
+    assert _prefill(lib, L=1, g=None) == _lib.GLA_ERR_NULL
+
+
+def test_state_alloc_rejects(lib):
+    assert lib.gla_state_alloc(1, 1, 16, 16, None, None) == _lib.GLA_ERR_NULL
+    p = ctypes.c_void_p(1234)
+    assert lib.gla_state_alloc(0, 1, 16, 16, ctypes.byref(p), None) == _lib.GLA_ERR_SHAPE
+    assert lib.gla_state_alloc(1, 1, 24, 16, ctypes.byref(p), None) == _lib.GLA_ERR_UNSUPPORTED
+    assert p.value == 1234                      # untouched on error
+    assert lib.gla_state_free(None, None) == _lib.GLA_OK
+
+
+def test_workspace_query_is_host_only(lib):
+    assert lib.gla_prefill_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) >= 0
+    assert lib.gla_prefill_workspace_bytes(-1, 16, 4096, 128, 128, 64, 1) == 0
+
+
+def test_python_binding_checks_shapes():
+    """The binding checks shapes and dtypes itself (the ABI cannot see buffer sizes)."""
+    import torch
+    from causal_gated_linear_amd import api
+    q = torch.zeros(1, 1, 16, 16)
+    with pytest.raises(ValueError):
+        api.prefill(q, q, q)                                   # host tensors
+    q = torch.zeros(1, 1, 16, 16, device="meta")
+    with pytest.raises(ValueError):
+        api.prefill(q, q, torch.zeros(1, 1, 8, 16))            # L mismatch
+    with pytest.raises(ValueError):
+        api.prefill(q, q.to(torch.bfloat16), q)                # dtype mismatch
+    with pytest.raises(ValueError):
+        api.prefill(q, q, q, log_gate=torch.zeros(1, 1, 16), gate="keydim")   # gate shape
+    with pytest.raises(ValueError):
+        api.prefill(q.transpose(2, 3), q, q)                   # non-contiguous

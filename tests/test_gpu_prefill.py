@@ -1,0 +1,175 @@
+"""GPU parity of gla_prefill_chunked (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs once and gives the same bits to both sides.  The
+metric is the normwise relative error per (batch, head), max|x - ref| / max|ref|,
+bounded by 2e-2 for bf16 inputs and 1e-4 for fp32 inputs; outputs and final states
+are both compared.  Small cases cover all heads at sizes that span several chunks
+and a ragged tail; the full workload sizes are checked on sampled heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+from causal_gated_linear_amd import api, inputs
+from oracle import oracle
+from tests import util
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+W = inputs.WORKLOADS
+
+
+def _to(d, dev):
+    return {k: (None if v is None else v.to(dev)) for k, v in d.items()}
+
+
+def _run_gpu(w, inp, s0=None, chunk=None, **kw):
+    o, s = api.prefill(inp["q"], inp["k"], inp["v"], log_gate=inp["g"], gate=w.gate,
+                       initial_state=s0, chunk=chunk or w.chunk, feature_map=w.feature_map, **kw)
+    torch.cuda.synchronize()
+    return o, s
+
+
+def _check_all_heads(w, B, H, L, seed, chunk=None, with_s0=False):
+    inp = inputs.draw(w, B=B, H=H, L=L, seed=seed)
+    s0 = inputs.draw_state(B, H, w.d_k, w.d_v, seed=seed + 1, scale=0.5) if with_s0 else None
+    o, s = _run_gpu(w, _to(inp, DEV), s0=None if s0 is None else s0.to(DEV), chunk=chunk)
+    ro, rs = oracle.forward(inp["q"], inp["k"], inp["v"], g=inp["g"], gate=w.gate,
+                            feature_map=w.feature_map, s0=s0)
+    tol = util.TOL[w.dtype]
+    eo = util.assert_close(o, ro, tol, "%s o" % w.name)
+    es = util.assert_close(s, rs, tol, "%s s_final" % w.name)
+    print("%s B=%d H=%d L=%d chunk=%s s0=%s: err o %.2e s %.2e" % (w.name, B, H, L, chunk or w.chunk,
+                                                                 with_s0, eo, es))
+    return o, s
+
+
+SMALL = {
+    # name: (workload, B, H, L)  -- several chunks plus a ragged tail
+    "fp32_single_head_full": ("fp32_single_head", 1, 1, 256),
+    "fp32_single_head_ragged": ("fp32_single_head", 2, 3, 250),
+    "linear_elu1_small": ("linear_elu1", 2, 3, 209),
+    "gla_prefill_small": ("gla_prefill", 2, 2, 300),
+    "scalar_long_small": ("scalar_long", 1, 3, 1000),
+    "decode_prefill_small": ("decode", 3, 2, 130),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_prefill_small(case, with_s0):
+    name, B, H, L = SMALL[case]
+    _check_all_heads(W[name], B, H, L, seed=100 + len(case), with_s0=with_s0)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("name", ["fp32_single_head", "gla_prefill", "scalar_long", "linear_elu1"])
+def test_prefill_chunk_sizes(name, chunk):
+    """Any chunk size gives the recurrence's result (chunking is a regrouping)."""
+    _check_all_heads(W[name], 1, 2, 3 * chunk + 7, seed=7 + chunk, chunk=chunk, with_s0=True)
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 63, 64, 65, 129])
+def test_prefill_lengths(L):
+    _check_all_heads(W["gla_prefill"], 1, 2, L, seed=300 + L, with_s0=True)
+    _check_all_heads(W["fp32_single_head"], 1, 2, L, seed=400 + L, with_s0=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 128), (128, 32), (16, 128), (128, 16)])
+@pytest.mark.parametrize("gate", ["keydim", "scalar", None])
+def test_prefill_dims(dtype, dk, dv, gate):
+    w = inputs.Workload("dims", dtype, 2, 2, 150, dk, dv, 64, gate, None, True, seed=0)
+    _check_all_heads(w, 2, 2, 150, seed=dk * 1000 + dv + (0 if gate is None else len(gate)), with_s0=True)
+
+
+def test_prefill_empty_sequence_copies_state():
+    w = W["gla_prefill"]
+    s0 = inputs.draw_state(2, 3, 128, 128, seed=5).to(DEV)
+    z = torch.empty(2, 3, 0, 128, dtype=torch.bfloat16, device=DEV)
+    g = torch.empty(2, 3, 0, 128, dtype=torch.float32, device=DEV)
+    o, s = api.prefill(z, z, z, log_gate=g, gate="keydim", initial_state=s0, chunk=w.chunk)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 128) and torch.equal(s, s0)
+    o, s = api.prefill(z, z, z, log_gate=g, gate="keydim", chunk=w.chunk)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(s).item() == 0
+
+
+def test_prefill_in_place_state():
+    """final_state may be the initial_state buffer (continue in place)."""
+    w = W["gla_prefill"]
+    inp = _to(inputs.draw(w, B=2, H=2, L=200, seed=11), DEV)
+    s0 = inputs.draw_state(2, 2, 128, 128, seed=12).to(DEV)
+    o_ref, s_ref = _run_gpu(w, inp, s0=s0.clone())
+    buf = s0.clone()
+    o, s = _run_gpu(w, inp, s0=buf, final_state=buf)
+    assert s.data_ptr() == buf.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(buf, s_ref)
+
+
+def test_prefill_gate_none_equals_zero_keydim_gate():
+    w = W["gla_prefill"]
+    inp = _to(inputs.draw(w, B=1, H=2, L=190, seed=13), DEV)
+    o1, s1 = api.prefill(inp["q"], inp["k"], inp["v"], chunk=64)
+    o2, s2 = api.prefill(inp["q"], inp["k"], inp["v"], log_gate=torch.zeros_like(inp["g"]), gate="keydim", chunk=64)
+    o3, s3 = api.prefill(inp["q"], inp["k"], inp["v"], log_gate=torch.zeros_like(inp["g"][..., 0]).contiguous(),
+                         gate="scalar", chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(o1, o3) and torch.equal(s1, s3)
+
+
+def test_prefill_scalar_equals_broadcast_keydim():
+    w = W["scalar_long"]
+    inp = _to(inputs.draw(w, B=1, H=2, L=333, seed=14), DEV)
+    o1, s1 = _run_gpu(w, inp)
+    gk = inp["g"][..., None].expand(-1, -1, -1, 128).contiguous()
+    o2, s2 = api.prefill(inp["q"], inp["k"], inp["v"], log_gate=gk, gate="keydim", chunk=64)
+    torch.cuda.synchronize()
+    assert util.head_errors(o1, o2.double().cpu().numpy()).max() < 2e-2
+    assert util.head_errors(s1, s2.double().cpu().numpy()).max() < 2e-2
+
+
+def test_prefill_deterministic():
+    w = W["gla_prefill"]
+    inp = _to(inputs.draw(w, B=2, H=4, L=500, seed=15), DEV)
+    o1, s1 = _run_gpu(w, inp)
+    o2, s2 = _run_gpu(w, inp)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_prefill_nan_stays_causal_and_in_its_head():
+    """A NaN in v at token t of one head reaches every later output of that head, and
+    never another head or an earlier chunk.  (Inside t's own chunk, earlier rows may
+    also turn NaN: the masked score 0 times NaN is NaN in the chunk product.)"""
+    w = W["gla_prefill"]
+    inp = _to(inputs.draw(w, B=1, H=2, L=256, seed=16), DEV)
+    t_bad = 150
+    inp["v"][0, 1, t_bad, 5] = float("nan")
+    o, s = _run_gpu(w, inp)
+    nan_rows = torch.isnan(o).any(dim=-1)[0]            # [H, L]
+    chunk_start = t_bad // w.chunk * w.chunk
+    assert not nan_rows[0].any()
+    assert not nan_rows[1, :chunk_start].any()
+    assert nan_rows[1, t_bad:].all()
+    assert torch.isfinite(s[0, 0]).all() and not torch.isfinite(s[0, 1]).all()
+
+
+# ---- full workload sizes, sampled heads ------------------------------------------------
+FULL = ["linear_elu1", "gla_prefill", "scalar_long", "decode"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_prefill_full_size_sampled_heads(name):
+    w = W[name]
+    torch.manual_seed(0)
+    inp = inputs.draw(w, device=DEV)                    # seeded on the device, all sizes as specified
+    o, s = _run_gpu(w, inp)
+    heads = util.sample_heads(w.B, w.H, 6 if w.L <= 4096 else 3, seed=len(name))
+    ro, rs = util.oracle_heads(inp, heads, w.gate, w.feature_map)
+    tol = util.TOL[w.dtype]
+    eo = util.assert_close(util.pick_heads(o, heads), ro, tol, "%s o" % name)
+    es = util.assert_close(util.pick_heads(s, heads), rs, tol, "%s s" % name)
+    assert torch.isfinite(o).all()
+    print("%s full size, heads %s: err o %.2e s %.2e" % (name, heads, eo, es))
