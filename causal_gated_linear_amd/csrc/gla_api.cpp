@@ -9,6 +9,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -17,41 +18,53 @@
 #include "gla_launch.hpp"
 
 namespace gla {
-hipError_t launch_prefill_0_16(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_0_32(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_0_64(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_0_128(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_1_16(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_1_32(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_1_64(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_1_128(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_0_16(const PrefillArgs &, int, int, int, hipStream_t);
+hipError_t launch_prefill_0_32(const PrefillArgs &, int, int, int, hipStream_t);
+hipError_t launch_prefill_0_64(const PrefillArgs &, int, int, int, hipStream_t);
+hipError_t launch_prefill_0_128(const PrefillArgs &, int, int, int, hipStream_t);
+hipError_t launch_prefill_1_16(const PrefillArgs &, int, int, int, hipStream_t);
+hipError_t launch_prefill_1_32(const PrefillArgs &, int, int, int, hipStream_t);
+hipError_t launch_prefill_1_64(const PrefillArgs &, int, int, int, hipStream_t);
+hipError_t launch_prefill_1_128(const PrefillArgs &, int, int, int, hipStream_t);
 
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, int nw,
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, PrefillTile tile,
                           hipStream_t stream)
 {
+    const int dvt = tile.dvt, nw = tile.nw;
     if (dtype == 1) {
         switch (d_k) {
-        case 16: return launch_prefill_1_16(a, chunk, nw, stream);
-        case 32: return launch_prefill_1_32(a, chunk, nw, stream);
-        case 64: return launch_prefill_1_64(a, chunk, nw, stream);
-        case 128: return launch_prefill_1_128(a, chunk, nw, stream);
+        case 16: return launch_prefill_1_16(a, chunk, dvt, nw, stream);
+        case 32: return launch_prefill_1_32(a, chunk, dvt, nw, stream);
+        case 64: return launch_prefill_1_64(a, chunk, dvt, nw, stream);
+        case 128: return launch_prefill_1_128(a, chunk, dvt, nw, stream);
         }
     } else {
         switch (d_k) {
-        case 16: return launch_prefill_0_16(a, chunk, nw, stream);
-        case 32: return launch_prefill_0_32(a, chunk, nw, stream);
-        case 64: return launch_prefill_0_64(a, chunk, nw, stream);
-        case 128: return launch_prefill_0_128(a, chunk, nw, stream);
+        case 16: return launch_prefill_0_16(a, chunk, dvt, nw, stream);
+        case 32: return launch_prefill_0_32(a, chunk, dvt, nw, stream);
+        case 64: return launch_prefill_0_64(a, chunk, dvt, nw, stream);
+        case 128: return launch_prefill_0_128(a, chunk, dvt, nw, stream);
         }
     }
     return hipErrorInvalidValue;
 }
 
-// Value-column tile width is 16 * waves: 4 waves (64 columns) when d_v allows.
-int prefill_waves(int d_v, int BH)
+// Launch shape.  The 256 compute units want at least 256 workgroups: 64 value columns
+// with 8 waves when that gives enough workgroups, else narrower tiles of 4 waves.
+// GLA_PREFILL_TILE="<columns>x<waves>" overrides the choice (a tuning knob).
+PrefillTile prefill_tile(int BH, int d_k, int d_v)
 {
-    (void)BH;
-    return d_v >= 64 ? 4 : d_v / 16;
+    static const char *env = getenv("GLA_PREFILL_TILE");
+    if (env) {
+        int dvt = 0, nw = 0;
+        if (sscanf(env, "%dx%d", &dvt, &nw) == 2 && (dvt == 16 || dvt == 32 || dvt == 64) &&
+            dvt <= d_v && d_v % dvt == 0 && (nw == 4 || (nw == 8 && dvt == 64 && d_k >= 32)))
+            return PrefillTile{dvt, nw};
+    }
+    const long bh = BH;
+    if (d_v >= 64 && d_k >= 32 && bh * (d_v / 64) >= 256) return PrefillTile{64, 8};
+    if (d_v >= 32 && bh * (d_v / 32) >= 256) return PrefillTile{32, 4};
+    return PrefillTile{16, 4};
 }
 }  // namespace gla
 
@@ -227,13 +240,13 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
     a.q = q; a.k = k; a.v = v; a.g = g; a.s0 = s0; a.o = o; a.s_final = s_final;
     a.BH = (int)BH; a.L = L; a.d_v = d_v;
     a.gate = (int)gate; a.elu1 = phi == GLA_PHI_ELU1;
-    const int nw = gla::prefill_waves(d_v, a.BH);
-    a.n_vt = d_v / (16 * nw);
+    const gla::PrefillTile tile = gla::prefill_tile(a.BH, d_k, d_v);
+    a.n_vt = d_v / tile.dvt;
     const long grid = (long)BH * a.n_vt;
     if (grid > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H too large");
     a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
     if (L == 0 && !s_final) return ok();
-    hipError_t e = gla::launch_prefill(a, dtype == GLA_BF16 ? 1 : 0, d_k, chunk, nw,
+    hipError_t e = gla::launch_prefill(a, dtype == GLA_BF16 ? 1 : 0, d_k, chunk, tile,
                                        (hipStream_t)stream);
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ok();

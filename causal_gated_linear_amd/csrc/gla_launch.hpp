@@ -30,11 +30,15 @@ struct DecodeArgs {
     int gate, elu1;
 };
 
-// Number of wavefronts per prefill workgroup (each wave owns 16 value columns).
-int prefill_waves(int d_v, int BH);
+// Prefill launch shape: value columns per workgroup (16, 32 or 64) and waves per
+// workgroup (4, or 8 with 64 columns and d_k >= 32).
+struct PrefillTile {
+    int dvt, nw;
+};
+PrefillTile prefill_tile(int BH, int d_k, int d_v);
 
 // Enqueue the prefill kernel.  dtype: 0 fp32, 1 bf16.  Sizes must already be valid.
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, int nw,
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, PrefillTile tile,
                           hipStream_t stream);
 
 // Enqueue one decode step.  Sizes must already be valid.

@@ -22,14 +22,17 @@ typedef float InstT;
 #endif
 
 hipError_t GLA_CAT3(launch_prefill_, GLA_INST_BF16, GLA_INST_DK)(const PrefillArgs &a, int chunk,
-                                                                 int nw, hipStream_t stream)
+                                                                 int dvt, int nw, hipStream_t stream)
 {
     constexpr int DK = GLA_INST_DK;
-#define GLA_CASE(C, NW) \
-    if (chunk == C && nw == NW) return launch_prefill_inst<InstT, DK, C, NW>(a, stream);
-    GLA_CASE(16, 1) GLA_CASE(16, 2) GLA_CASE(16, 4)
-    GLA_CASE(32, 1) GLA_CASE(32, 2) GLA_CASE(32, 4)
-    GLA_CASE(64, 1) GLA_CASE(64, 2) GLA_CASE(64, 4)
+#define GLA_CASE(C, DVT, NW) \
+    if (chunk == C && dvt == DVT && nw == NW) return launch_prefill_inst<InstT, DK, C, DVT, NW>(a, stream);
+#define GLA_CASES(C) GLA_CASE(C, 16, 4) GLA_CASE(C, 32, 4) GLA_CASE(C, 64, 4)
+    GLA_CASES(16) GLA_CASES(32) GLA_CASES(64)
+#if GLA_INST_DK >= 32
+    GLA_CASE(16, 64, 8) GLA_CASE(32, 64, 8) GLA_CASE(64, 64, 8)
+#endif
+#undef GLA_CASES
 #undef GLA_CASE
     return hipErrorInvalidValue;
 }
