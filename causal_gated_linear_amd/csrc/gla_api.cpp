@@ -18,53 +18,53 @@
 #include "gla_launch.hpp"
 
 namespace gla {
-hipError_t launch_prefill_0_16(const PrefillArgs &, int, int, int, hipStream_t);
-hipError_t launch_prefill_0_32(const PrefillArgs &, int, int, int, hipStream_t);
-hipError_t launch_prefill_0_64(const PrefillArgs &, int, int, int, hipStream_t);
-hipError_t launch_prefill_0_128(const PrefillArgs &, int, int, int, hipStream_t);
-hipError_t launch_prefill_1_16(const PrefillArgs &, int, int, int, hipStream_t);
-hipError_t launch_prefill_1_32(const PrefillArgs &, int, int, int, hipStream_t);
-hipError_t launch_prefill_1_64(const PrefillArgs &, int, int, int, hipStream_t);
-hipError_t launch_prefill_1_128(const PrefillArgs &, int, int, int, hipStream_t);
+hipError_t launch_prefill_0_16(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_0_32(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_0_64(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_0_128(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_1_16(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_1_32(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_1_64(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_1_128(const PrefillArgs &, int, int, hipStream_t);
 
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, PrefillTile tile,
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, int dvt,
                           hipStream_t stream)
 {
-    const int dvt = tile.dvt, nw = tile.nw;
     if (dtype == 1) {
         switch (d_k) {
-        case 16: return launch_prefill_1_16(a, chunk, dvt, nw, stream);
-        case 32: return launch_prefill_1_32(a, chunk, dvt, nw, stream);
-        case 64: return launch_prefill_1_64(a, chunk, dvt, nw, stream);
-        case 128: return launch_prefill_1_128(a, chunk, dvt, nw, stream);
+        case 16: return launch_prefill_1_16(a, chunk, dvt, stream);
+        case 32: return launch_prefill_1_32(a, chunk, dvt, stream);
+        case 64: return launch_prefill_1_64(a, chunk, dvt, stream);
+        case 128: return launch_prefill_1_128(a, chunk, dvt, stream);
         }
     } else {
         switch (d_k) {
-        case 16: return launch_prefill_0_16(a, chunk, dvt, nw, stream);
-        case 32: return launch_prefill_0_32(a, chunk, dvt, nw, stream);
-        case 64: return launch_prefill_0_64(a, chunk, dvt, nw, stream);
-        case 128: return launch_prefill_0_128(a, chunk, dvt, nw, stream);
+        case 16: return launch_prefill_0_16(a, chunk, dvt, stream);
+        case 32: return launch_prefill_0_32(a, chunk, dvt, stream);
+        case 64: return launch_prefill_0_64(a, chunk, dvt, stream);
+        case 128: return launch_prefill_0_128(a, chunk, dvt, stream);
         }
     }
     return hipErrorInvalidValue;
 }
 
-// Launch shape.  The 256 compute units want at least 256 workgroups: 64 value columns
-// with 8 waves when that gives enough workgroups, else narrower tiles of 4 waves.
-// GLA_PREFILL_TILE="<columns>x<waves>" overrides the choice (a tuning knob).
-PrefillTile prefill_tile(int BH, int d_k, int d_v)
+// Launch shape: the widest value tile (64, 32 or 16 columns) that fits in LDS and
+// still gives at least 256 workgroups for the 256 compute units.
+// GLA_PREFILL_TILE=<columns> overrides the choice (a tuning knob).
+int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes)
 {
+    auto usable = [&](int dvt) {
+        return dvt <= d_v && d_v % dvt == 0 && prefill_nbuf(elem_bytes, d_k, chunk, dvt) > 0;
+    };
     static const char *env = getenv("GLA_PREFILL_TILE");
     if (env) {
-        int dvt = 0, nw = 0;
-        if (sscanf(env, "%dx%d", &dvt, &nw) == 2 && (dvt == 16 || dvt == 32 || dvt == 64) &&
-            dvt <= d_v && d_v % dvt == 0 && (nw == 4 || (nw == 8 && dvt == 64 && d_k >= 32)))
-            return PrefillTile{dvt, nw};
+        const int dvt = atoi(env);
+        if ((dvt == 16 || dvt == 32 || dvt == 64) && usable(dvt)) return dvt;
     }
     const long bh = BH;
-    if (d_v >= 64 && d_k >= 32 && bh * (d_v / 64) >= 256) return PrefillTile{64, 8};
-    if (d_v >= 32 && bh * (d_v / 32) >= 256) return PrefillTile{32, 4};
-    return PrefillTile{16, 4};
+    if (usable(64) && bh * (d_v / 64) >= 256) return 64;
+    if (usable(32) && bh * (d_v / 32) >= 256) return 32;
+    return 16;
 }
 }  // namespace gla
 
@@ -240,13 +240,13 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
     a.q = q; a.k = k; a.v = v; a.g = g; a.s0 = s0; a.o = o; a.s_final = s_final;
     a.BH = (int)BH; a.L = L; a.d_v = d_v;
     a.gate = (int)gate; a.elu1 = phi == GLA_PHI_ELU1;
-    const gla::PrefillTile tile = gla::prefill_tile(a.BH, d_k, d_v);
-    a.n_vt = d_v / tile.dvt;
+    const int dvt = gla::prefill_tile(a.BH, d_k, d_v, chunk, (int)es);
+    a.n_vt = d_v / dvt;
     const long grid = (long)BH * a.n_vt;
     if (grid > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H too large");
     a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
     if (L == 0 && !s_final) return ok();
-    hipError_t e = gla::launch_prefill(a, dtype == GLA_BF16 ? 1 : 0, d_k, chunk, tile,
+    hipError_t e = gla::launch_prefill(a, dtype == GLA_BF16 ? 1 : 0, d_k, chunk, dvt,
                                        (hipStream_t)stream);
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ok();

@@ -30,15 +30,28 @@ struct DecodeArgs {
     int gate, elu1;
 };
 
-// Prefill launch shape: value columns per workgroup (16, 32 or 64) and waves per
-// workgroup (4, or 8 with 64 columns and d_k >= 32).
-struct PrefillTile {
-    int dvt, nw;
-};
-PrefillTile prefill_tile(int BH, int d_k, int d_v);
+// LDS bytes of a prefill workgroup: `nbuf` operand buffers (Q~ and K^ rows of
+// length d_k, K^T and V^T rows of length C, each padded by 16 bytes, plus exp(Gamma)
+// and the scalar-gate sums) and the two parity copies of the state operand.
+constexpr int kLdsBytes = 163840;                  // LDS per compute unit on gfx950
+constexpr int prefill_lds_bytes(int es, int dk, int c, int dvt, int nbuf)
+{
+    const int pad = 16 / es, ldk = dk + pad, ldc = c + pad;
+    const int buf = (2 * c * ldk + dk * ldc + dvt * ldc) * es + 4 * (dk + c);
+    return nbuf * buf + 2 * dvt * ldk * es;
+}
+// Operand buffers that fit (2: producer/consumer overlap, 1: alternating, 0: none).
+constexpr int prefill_nbuf(int es, int dk, int c, int dvt)
+{
+    return prefill_lds_bytes(es, dk, c, dvt, 2) <= kLdsBytes ? 2
+           : prefill_lds_bytes(es, dk, c, dvt, 1) <= kLdsBytes ? 1 : 0;
+}
+
+// Value columns per prefill workgroup (16, 32 or 64) for these sizes.
+int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes);
 
 // Enqueue the prefill kernel.  dtype: 0 fp32, 1 bf16.  Sizes must already be valid.
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, PrefillTile tile,
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, int dvt,
                           hipStream_t stream);
 
 // Enqueue one decode step.  Sizes must already be valid.

@@ -17,24 +17,27 @@
 // S <- exp(Gamma) S + (phi(K) * exp(Gamma - b))^T V.  The key-dim factorisation needs
 // exp(-B) finite: the in-chunk cumulative log-gate must stay above about -80.
 //
-// Decomposition: one workgroup of NW wavefronts per (batch*head, tile of DVT value
-// columns) walks the chunks of its head in order.  The fp32 state slice
-// S[d_k][DVT] lives in MFMA accumulator registers, split into 16x16 tiles dealt
-// round-robin to the waves.  Per chunk:
-//   A/B (all waves)  raw q, k, g rows prefetched into registers during the previous
-//       chunk are turned into LDS operands: each wave owns DK/NW key columns for all
-//       C rows, forms the cumulative gate sums with an in-register scan plus a
-//       cross-lane scan, and writes Q~, K^ (row-major) and K^ (or the scalar-gate
-//       K~) transposed; v is written transposed; each wave writes its state tiles
-//       as bf16 for the read-out.  Then the next chunk's raw rows are requested.
-//   D   (per wave)   for its 16-row blocks tb of the chunk: the score tiles
-//       P^T[s-block <= tb][tb] (kept in registers), then per 16-column value tile
-//       O^T = S^T Q~^T + V^T P^T, stored to global memory; then its state tiles
-//       S += K^^T V and the gate decay.
-// Two LDS barriers per chunk; the barrier waits only for LDS traffic, so the
-// prefetched global loads stay in flight across it.  bf16 inputs use bf16 MFMA
-// operands with fp32 accumulation; fp32 inputs use fp32 MFMA.
+// Decomposition: one workgroup per (batch*head, tile of DVT value columns) walks the
+// chunks of its head in order, with two kinds of wavefronts:
+//   producers (NP waves)  turn raw q, k, g, v rows into matrix-core operands in LDS:
+//       each owns DK/NP key columns of all C rows, forms the cumulative gate sums
+//       with an in-register scan plus a cross-lane scan, and writes Q~ and K^
+//       row-major and K^ (scalar gate: K~) and V transposed.  Raw rows are requested
+//       two chunks ahead into registers.
+//   consumers (NC waves)  hold the fp32 state slice S[d_k][DVT] in accumulator
+//       registers (16x16 tiles dealt round-robin) and, per 16-row block tb of the
+//       chunk they own, compute the score tiles P^T[s-block <= tb][tb] in registers
+//       and O^T = S^T Q~^T + V^T P^T per 16-column value tile, stored to global
+//       memory; then S += K^^T V and the gate decay.  The state is shared between
+//       consumers as a bf16 operand copy in LDS.
+// With two LDS operand buffers the producers prepare chunk n+1 while the consumers
+// compute chunk n (one barrier per chunk); where two buffers do not fit in LDS the
+// phases alternate on one buffer.  Barriers wait only for LDS traffic, so requested
+// global rows stay in flight.  bf16 inputs use bf16 MFMA operands with fp32
+// accumulation; fp32 inputs use fp32 MFMA.
 #pragma once
+
+#include <type_traits>
 
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
@@ -83,6 +86,11 @@ template <> struct Op<bf16> {
         const bf16x4 b = *(const bf16x4 *)(row + 32 * k + 16 + 4 * grp);
         return frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
+    static __device__ __forceinline__ frag split_lo(const bf16 *row, int k, int grp)
+    {
+        const bf16x4 a = *(const bf16x4 *)(row + 32 * k + 4 * grp);
+        return frag{a[0], a[1], a[2], a[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    }
     static __device__ __forceinline__ frag from_acc(f32x4 a, f32x4 b)
     {
         return frag{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
@@ -118,64 +126,72 @@ template <> struct Op<float> {
     }
 };
 
-template <typename T, int DK, int C, int DVT, int NW>
+template <typename T, int DK, int C, int DVT>
 struct PrefillShape {
     static constexpr bool BF = sizeof(T) == 2;
-    static constexpr int NT = 64 * NW;
+    static constexpr int NP = 4, NC = 4;           // producer / consumer waves
+    static constexpr int NT = 64 * (NP + NC);
     static constexpr int NTB = C / 16;             // 16-row blocks per chunk
     static constexpr int NKB = DK / 16;            // 16-blocks of the key dim
     static constexpr int NJT = DVT / 16;           // 16-column value tiles
     static constexpr int SW = Op<T>::W;            // contraction width per MFMA step
-    static constexpr int KSTEPS = (DK + SW - 1) / SW;   // steps over the key dim
+    static constexpr int KSTEPS = (DK + SW - 1) / SW;
+    static constexpr int CSTEPS = (C + SW - 1) / SW;
     static constexpr int PAD = 16 / sizeof(T);     // 16 bytes of row padding in LDS
     static constexpr int LDK = DK + PAD;           // rows of length d_k
     static constexpr int LDC = C + PAD;            // rows of length C
-    // gate stage: wave w owns key columns [w*CW, (w+1)*CW) for all C rows
-    static constexpr int CW = DK / NW;
-    static constexpr int CG = CW / 4;              // 4-column groups per wave
+    // producer gate mapping: producer p owns key columns [p*CW, (p+1)*CW)
+    static constexpr int CW = DK / NP;
+    static constexpr int CG = CW / 4;              // 4-column groups
     static constexpr int RSEG = (64 / CG) < C ? (64 / CG) : C;
     static constexpr int RPS = C / RSEG;           // rows per lane
-    // value stage: the whole workgroup covers C x DVT, a lane 4 columns x RV rows
+    // producer value mapping: 64*NP lanes cover C x DVT, a lane 4 columns x RV rows
     static constexpr int CGV = DVT / 4;
-    static constexpr int RGV = (NT / CGV) < C ? (NT / CGV) : C;
+    static constexpr int RGV = (64 * NP / CGV) < C ? (64 * NP / CGV) : C;
     static constexpr int RV = C / RGV;
-    // state tiles dealt round-robin to the waves
+    // consumer state tiles, dealt round-robin
     static constexpr int NU = NKB * NJT;
-    static constexpr int NSLOT = (NU + NW - 1) / NW;
-    static_assert(CW >= 4 && CW % 4 == 0 && 64 % CG == 0, "gate-stage mapping");
-    static_assert(NT % CGV == 0, "value-stage mapping");
+    static constexpr int NSLOT = (NU + NC - 1) / NC;
+    // LDS: operand buffers (Q~, K^, K^T, V^T, exp Gamma, B) and the state copies
+    static constexpr int NBUF = prefill_nbuf((int)sizeof(T), DK, C, DVT);
+    static_assert(NBUF >= 1, "LDS budget");
+    static_assert(CW >= 4 && CW % 4 == 0 && 64 % CG == 0, "producer gate mapping");
+    static_assert((64 * NP) % CGV == 0, "producer value mapping");
     static_assert(RPS >= 1 && RV >= 1, "rows per lane");
 };
 
-template <typename T, int DK, int C, int DVT, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a)
+template <typename T, int N> struct VecN { typedef T type __attribute__((ext_vector_type(N))); };
+template <typename T> struct VecN<T, 1> { typedef T type; };
+
+template <typename T, int DK, int C, int DVT, int GATE, bool ELU1>
+__global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 {
-    using SH = PrefillShape<T, DK, C, DVT, NW>;
+    using SH = PrefillShape<T, DK, C, DVT>;
     using O = Op<T>;
     using V4 = typename Vec4<T>::type;
+    constexpr int NP = SH::NP, NC = SH::NC, NBUF = SH::NBUF;
     constexpr int NTB = SH::NTB, NKB = SH::NKB, NJT = SH::NJT, LDK = SH::LDK, LDC = SH::LDC;
     constexpr int CW = SH::CW, CG = SH::CG, RSEG = SH::RSEG, RPS = SH::RPS;
     constexpr int CGV = SH::CGV, RGV = SH::RGV, RV = SH::RV, NSLOT = SH::NSLOT, NU = SH::NU;
 
-    __shared__ __attribute__((aligned(16))) T sQ[C * LDK];     // Q~ [t][i]
-    __shared__ __attribute__((aligned(16))) T sK[C * LDK];     // K^ [s][i]
-    __shared__ __attribute__((aligned(16))) T sKT[DK * LDC];   // K^ (scalar gate: K~) [i][s]
-    __shared__ __attribute__((aligned(16))) T sVT[DVT * LDC];  // V^T [j][s]
-    __shared__ __attribute__((aligned(16))) T sS[DVT * LDK];   // state^T [j][i] (operand copy)
-    __shared__ float sEG[DK];                                  // exp(Gamma_i)
-    __shared__ float sB[C];                                    // scalar gate: B_t (log2 units)
+    __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * LDK];     // Q~ [t][i]
+    __shared__ __attribute__((aligned(16))) T sK[NBUF][C * LDK];     // K^ [s][i]
+    __shared__ __attribute__((aligned(16))) T sKT[NBUF][DK * LDC];   // K^ (scalar: K~) [i][s]
+    __shared__ __attribute__((aligned(16))) T sVT[NBUF][DVT * LDC];  // V^T [j][s]
+    __shared__ __attribute__((aligned(16))) T sS[2][DVT * LDK];      // state^T [j][i], by parity
+    __shared__ float sEG[NBUF][DK];                                  // exp(Gamma_i)
+    __shared__ float sB[NBUF][C];                                    // scalar gate: B_t (log2)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int x = lane & 15, grp = lane >> 4;
+    const bool producer = w < NP;
 
     int wg = blockIdx.x;
     if (a.xcd_remap) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
     const int bh = wg / a.n_vt;
     const int vt = wg - bh * a.n_vt;
     const int L = a.L, DV = a.d_v;
-    const bool elu1 = a.elu1 != 0;
-    const int gate = a.gate;
 
     const T *__restrict__ qh = (const T *)a.q + (size_t)bh * L * DK;
     const T *__restrict__ kh = (const T *)a.k + (size_t)bh * L * DK;
@@ -183,15 +199,149 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a)
     T *__restrict__ oh = (T *)a.o + (size_t)bh * L * DV + vt * DVT;
     const float *__restrict__ gk = a.g + (size_t)bh * L * DK;   // key-dim gates
     const float *__restrict__ gs = a.g + (size_t)bh * L;        // scalar gates
+    const int nchunks = (L + C - 1) / C;
 
-    // ---- state tiles owned by this wave: tile u = slot*NW + w, (i-tile, j-tile) -----
+    // ---------------- producer state ------------------------------------------------
+    const int p = w;                               // producer index (when producer)
+    const int cg = lane % CG, rs = lane / CG;
+    const bool gate_lane = producer && rs < RSEG;
+    const int ic = p * CW + 4 * cg;                // first of this lane's 4 key columns
+    const int ptid = tid;                          // producer thread index (< 64*NP)
+    const int cgv = ptid % CGV, rgv = ptid / CGV;
+    const bool v_lane = producer && rgv < RGV;
+
+    struct Raw {
+        V4 q[RPS], k[RPS], v[RV];
+        f32x4 g[RPS];
+    };
+    Raw R[NBUF];
+
+    auto load_raw = [&](Raw &r_, int t0) __attribute__((always_inline)) {
+        if (gate_lane) {
+#pragma unroll
+            for (int r = 0; r < RPS; ++r) {
+                const int row = min(t0 + rs * RPS + r, L - 1);   // clamp: always in bounds
+                r_.q[r] = *(const V4 *)(qh + (size_t)row * DK + ic);
+                r_.k[r] = *(const V4 *)(kh + (size_t)row * DK + ic);
+                if constexpr (GATE == kGateKeydim) {
+                    r_.g[r] = *(const f32x4 *)(gk + (size_t)row * DK + ic);
+                } else if constexpr (GATE == kGateScalar) {
+                    const float gv = gs[row];
+                    r_.g[r] = f32x4{gv, gv, gv, gv};
+                }
+            }
+        }
+        if (v_lane) {
+#pragma unroll
+            for (int r = 0; r < RV; ++r) {
+                const int row = min(t0 + rgv * RV + r, L - 1);
+                r_.v[r] = *(const V4 *)(vh + (size_t)row * DV + 4 * cgv);
+            }
+        }
+    };
+
+    // Turn the raw rows of the chunk starting at t0 into the operands of buffer `buf`.
+    auto produce = [&](Raw &r_, int t0, int buf) __attribute__((always_inline)) {
+        const int nvalid = min(L - t0, C);
+        if (nvalid < C) {                          // ragged tail: rows past L carry no gate
+#pragma unroll                                     // and no value (their q, k are finite copies)
+            for (int r = 0; r < RPS; ++r)
+                if (rs * RPS + r >= nvalid) r_.g[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < RV; ++r)
+                if (rgv * RV + r >= nvalid) r_.v[r] = narrow4<T>(f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        if (gate_lane) {
+            f32x4 bc[RPS];
+            f32x4 incl = {0.f, 0.f, 0.f, 0.f}, excl = incl, tot = incl;
+            if constexpr (GATE != kGateNone) {
+                f32x4 run = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < RPS; ++r) {
+                    run += r_.g[r];
+                    bc[r] = run;
+                }
+                incl = run;
+#pragma unroll
+                for (int off = 1; off < RSEG; off <<= 1) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float up = __shfl_up(incl[e], off * CG, 64);
+                        if (rs >= off) incl[e] += up;
+                    }
+                }
+                excl = incl - run;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tot[e] = __shfl(incl[e], (RSEG - 1) * CG + cg, 64) * kLog2e;
+            }
+            typedef typename VecN<T, RPS>::type KTv;
+            KTv ktv[4];
+#pragma unroll
+            for (int r = 0; r < RPS; ++r) {
+                const int t = rs * RPS + r;
+                f32x4 q = widen(r_.q[r]), kk = widen(r_.k[r]);
+                if constexpr (ELU1) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        q[e] = feature(q[e], true);
+                        kk[e] = feature(kk[e], true);
+                    }
+                }
+                f32x4 qt = q, kt = kk, kT = kk;
+                if constexpr (GATE == kGateKeydim) {
+                    const f32x4 b = (excl + bc[r]) * kLog2e;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qt[e] = q[e] * exp2_fast(b[e]);
+                        kt[e] = kk[e] * exp2_fast(-b[e]);
+                    }
+                    kT = kt;
+                } else if constexpr (GATE == kGateScalar) {
+                    const float b = (excl[0] + bc[r][0]) * kLog2e;
+                    kT = kk * exp2_fast(tot[0] - b);
+                    if (p == 0 && cg == 0) sB[buf][t] = b;
+                }
+                *(V4 *)(sQ[buf] + t * LDK + ic) = narrow4<T>(qt);
+                *(V4 *)(sK[buf] + t * LDK + ic) = narrow4<T>(kt);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (RPS == 1) ktv[e] = from_f32<T>(kT[e]);
+                    else ktv[e][r] = from_f32<T>(kT[e]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *(KTv *)(sKT[buf] + (ic + e) * LDC + rs * RPS) = ktv[e];
+            if (rs == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sEG[buf][ic + e] = GATE == kGateNone ? 1.f : exp2_fast(tot[e]);
+            }
+        }
+        if (v_lane) {
+            typedef typename VecN<T, RV>::type Vv;
+            Vv vv[4];
+#pragma unroll
+            for (int r = 0; r < RV; ++r) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (RV == 1) vv[e] = r_.v[r][e];
+                    else vv[e][r] = r_.v[r][e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *(Vv *)(sVT[buf] + (4 * cgv + e) * LDC + rgv * RV) = vv[e];
+        }
+    };
+
+    // ---------------- consumer state ------------------------------------------------
+    const int c = w - NP;                          // consumer index (when consumer)
     f32x4 S[NSLOT];
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a.s0) {                                     // branch-free loads, issued together
+    if (!producer && a.s0) {                       // branch-free loads, issued together
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) {
-            const int u = k * NW + w;
+            const int u = k * NC + c;
             const int uc = u < NU ? u : NU - 1;
             const int it = uc % NKB, jt = uc / NKB;
 #pragma unroll
@@ -203,158 +353,32 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a)
         }
     }
 
-    // ---- gate-stage lane coordinates ------------------------------------------------
-    const int cg = lane % CG, rs = lane / CG;
-    const bool gate_lane = rs < RSEG;
-    const int ic = w * CW + 4 * cg;                 // first of this lane's 4 key columns
-    const int cgv = tid % CGV, rgv = tid / CGV;
-    const bool v_lane = rgv < RGV;
-
-    V4 qr[RPS], kr[RPS], vr[RV];
-    f32x4 gr[RPS];
-
-    auto load_raw = [&](int t0) {
-        if (gate_lane) {
+    auto write_state = [&](int par) __attribute__((always_inline)) {              // state tiles -> bf16 operand rows
 #pragma unroll
-            for (int r = 0; r < RPS; ++r) {
-                const int row = min(t0 + rs * RPS + r, L - 1);   // clamp: always in bounds
-                qr[r] = *(const V4 *)(qh + (size_t)row * DK + ic);
-                kr[r] = *(const V4 *)(kh + (size_t)row * DK + ic);
-            }
-            if (gate == kGateKeydim) {
-#pragma unroll
-                for (int r = 0; r < RPS; ++r) {
-                    const int row = min(t0 + rs * RPS + r, L - 1);
-                    gr[r] = *(const f32x4 *)(gk + (size_t)row * DK + ic);
-                }
-            } else if (gate == kGateScalar) {
-#pragma unroll
-                for (int r = 0; r < RPS; ++r) {
-                    const int row = min(t0 + rs * RPS + r, L - 1);
-                    const float gv = gs[row];
-                    gr[r] = f32x4{gv, gv, gv, gv};
-                }
-            }
-        }
-        if (v_lane) {
-#pragma unroll
-            for (int r = 0; r < RV; ++r) {
-                const int row = min(t0 + rgv * RV + r, L - 1);
-                vr[r] = *(const V4 *)(vh + (size_t)row * DV + 4 * cgv);
+        for (int k = 0; k < NSLOT; ++k) {
+            const int u = k * NC + c;
+            if (u < NU) {
+                const int it = u % NKB, jt = u / NKB;
+                *(V4 *)(sS[par] + (16 * jt + x) * LDK + 16 * it + 4 * grp) = narrow4<T>(S[k]);
             }
         }
     };
 
-    const int nchunks = (L + C - 1) / C;
-    if (nchunks > 0) load_raw(0);
-
-    for (int n = 0; n < nchunks; ++n) {
-        const int t0 = n * C;
+    // Outputs of chunk starting at t0 from operand buffer `buf`, then the state step.
+    auto consume = [&](int t0, int buf, int par) __attribute__((always_inline)) {
         const int nvalid = min(L - t0, C);
-
-        // ================= A/B: operands of chunk n into LDS ==========================
-        // state tiles as bf16 (or fp32) operand rows S^T[j][i]
-#pragma unroll
-        for (int k = 0; k < NSLOT; ++k) {
-            const int u = k * NW + w;
-            if (u < NU) {
-                const int it = u % NKB, jt = u / NKB;
-                *(V4 *)(sS + (16 * jt + x) * LDK + 16 * it + 4 * grp) = narrow4<T>(S[k]);
-            }
-        }
-        if (gate_lane) {
-            // cumulative log2-gates: serial within this lane's rows, then across lanes
-            f32x4 bc[RPS];
-            f32x4 run = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int r = 0; r < RPS; ++r) {
-                const bool valid = rs * RPS + r < nvalid;
-                const f32x4 gl = (gate != kGateNone && valid) ? gr[r] * kLog2e : f32x4{0.f, 0.f, 0.f, 0.f};
-                run += gl;
-                bc[r] = run;
-            }
-            f32x4 incl = run;
-#pragma unroll
-            for (int off = 1; off < RSEG; off <<= 1) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float up = __shfl_up(incl[e], off * CG, 64);
-                    if (rs >= off) incl[e] += up;
-                }
-            }
-            f32x4 excl = incl - run, tot;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tot[e] = __shfl(incl[e], (RSEG - 1) * CG + cg, 64);
-
-            typedef T KTvec __attribute__((ext_vector_type(RPS)));
-            KTvec ktv[4];
-#pragma unroll
-            for (int r = 0; r < RPS; ++r) {
-                const int t = rs * RPS + r;
-                const bool valid = t < nvalid;
-                const f32x4 b = excl + bc[r];
-                const f32x4 q = widen(qr[r]), kk = widen(kr[r]);
-                f32x4 qt, kt, kT;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float fq = valid ? feature(q[e], elu1) : 0.f;
-                    const float fk = valid ? feature(kk[e], elu1) : 0.f;
-                    if (gate == kGateKeydim) {
-                        qt[e] = fq * exp2_fast(b[e]);
-                        kt[e] = fk * exp2_fast(-b[e]);
-                        kT[e] = kt[e];
-                    } else if (gate == kGateScalar) {
-                        qt[e] = fq;
-                        kt[e] = fk;
-                        kT[e] = fk * exp2_fast(tot[e] - b[e]);
-                    } else {
-                        qt[e] = fq;
-                        kt[e] = fk;
-                        kT[e] = fk;
-                    }
-                    ktv[e][r] = from_f32<T>(kT[e]);
-                }
-                *(V4 *)(sQ + t * LDK + ic) = narrow4<T>(qt);
-                *(V4 *)(sK + t * LDK + ic) = narrow4<T>(kt);
-                if (gate == kGateScalar && w == 0 && cg == 0) sB[t] = b[0];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) *(KTvec *)(sKT + (ic + e) * LDC + rs * RPS) = ktv[e];
-            if (rs == 0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sEG[ic + e] = gate == kGateNone ? 1.f : exp2_fast(tot[e]);
-            }
-        }
-        if (v_lane) {
-            typedef T Vvec __attribute__((ext_vector_type(RV)));
-            Vvec vv[4];
-#pragma unroll
-            for (int r = 0; r < RV; ++r) {
-                const bool valid = rgv * RV + r < nvalid;
-                const f32x4 vf = widen(vr[r]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vv[e][r] = from_f32<T>(valid ? vf[e] : 0.f);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) *(Vvec *)(sVT + (4 * cgv + e) * LDC + rgv * RV) = vv[e];
-        }
-        // request the next chunk's rows; they arrive while this chunk is computed
-        if (n + 1 < nchunks) load_raw(t0 + C);
-        lds_barrier();
-
-        // ================= D: outputs and the state step ===============================
-        for (int tb = w; tb < NTB; tb += NW) {
+        const T *Q = sQ[buf], *K = sK[buf], *KT = sKT[buf], *VT = sVT[buf], *SS = sS[par];
+        for (int tb = c; tb < NTB; tb += NC) {
             const int t = 16 * tb + x;
             typename O::frag qf[SH::KSTEPS];
 #pragma unroll
             for (int k = 0; k < SH::KSTEPS; ++k) {
-                if constexpr (SH::BF) {
-                    qf[k] = (32 * k + 8 * grp < DK) ? O::contig(sQ + t * LDK, k, grp) : O::zero();
-                } else {
-                    qf[k] = O::contig(sQ + t * LDK, k, grp);
-                }
+                if constexpr (SH::BF && DK % 32 != 0)
+                    qf[k] = (32 * k + 8 * grp < DK) ? O::contig(Q + t * LDK, k, grp) : O::zero();
+                else
+                    qf[k] = O::contig(Q + t * LDK, k, grp);
             }
-            // score tiles P^T[s-block sb][t-block tb], lane holds P[t][16sb + 4grp + r]
+            // score tiles P^T[s-block sb][t-block tb]: lane holds P[t][16sb + 4grp + r]
             f32x4 pt[NTB];
 #pragma unroll
             for (int sb = 0; sb < NTB; ++sb) {
@@ -364,20 +388,26 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
                 for (int k = 0; k < SH::KSTEPS; ++k) {
                     typename O::frag af;
-                    if constexpr (SH::BF) af = (32 * k + 8 * grp < DK) ? O::contig(sK + srow * LDK, k, grp) : O::zero();
-                    else af = O::contig(sK + srow * LDK, k, grp);
+                    if constexpr (SH::BF && DK % 32 != 0)
+                        af = (32 * k + 8 * grp < DK) ? O::contig(K + srow * LDK, k, grp) : O::zero();
+                    else
+                        af = O::contig(K + srow * LDK, k, grp);
                     acc = O::mma(af, qf[k], acc);
                 }
+                if constexpr (GATE == kGateScalar) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * sb + 4 * grp + r;
-                    float p = s <= t ? acc[r] : 0.f;
-                    if (gate == kGateScalar && s <= t) p *= exp2_fast(sB[t] - sB[s]);
-                    acc[r] = p;
+                    for (int r = 0; r < 4; ++r) {
+                        const int s = 16 * sb + 4 * grp + r;
+                        acc[r] = s <= t ? acc[r] * exp2_fast(sB[buf][t] - sB[buf][s]) : 0.f;
+                    }
+                } else if (sb == tb) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] = 4 * grp + r <= x ? acc[r] : 0.f;
                 }
                 pt[sb] = acc;
             }
-            const float inter_scale = gate == kGateScalar ? exp2_fast(sB[t]) : 1.f;
+            float inter_scale = 1.f;
+            if constexpr (GATE == kGateScalar) inter_scale = exp2_fast(sB[buf][t]);
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt) {
                 const int jrow = 16 * jt + x;
@@ -386,34 +416,32 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
                 for (int k = 0; k < SH::KSTEPS; ++k) {
                     typename O::frag af;
-                    if constexpr (SH::BF) af = (32 * k + 8 * grp < DK) ? O::contig(sS + jrow * LDK, k, grp) : O::zero();
-                    else af = O::contig(sS + jrow * LDK, k, grp);
+                    if constexpr (SH::BF && DK % 32 != 0)
+                        af = (32 * k + 8 * grp < DK) ? O::contig(SS + jrow * LDK, k, grp) : O::zero();
+                    else
+                        af = O::contig(SS + jrow * LDK, k, grp);
                     acc = O::mma(af, qf[k], acc);
                 }
-                acc *= inter_scale;
+                if constexpr (GATE == kGateScalar) acc *= inter_scale;
                 // intra-chunk: O^T += V^T P^T over s-blocks 0..tb
                 if constexpr (SH::BF) {
 #pragma unroll
                     for (int sp = 0; sp < (NTB + 1) / 2; ++sp) {
                         if (2 * sp > tb) break;
-                        const bool hi = 2 * sp + 1 <= tb;
-                        typename O::frag af, bf;
-                        if (hi) {
-                            af = O::split(sVT + jrow * LDC, sp, grp);
-                            bf = O::from_acc(pt[2 * sp], pt[2 * sp + 1]);
-                        } else {    // only the first 16-block of this pair is in range
-                            const bf16x4 lo = *(const bf16x4 *)(sVT + jrow * LDC + 32 * sp + 4 * grp);
-                            af = typename O::frag{lo[0], lo[1], lo[2], lo[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+                        if (2 * sp + 1 <= tb) {
+                            acc = O::mma(O::split(VT + jrow * LDC, sp, grp),
+                                         O::from_acc(pt[2 * sp], pt[2 * sp + 1]), acc);
+                        } else {            // only the first 16-block of this pair is in range
                             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                            bf = O::from_acc(pt[2 * sp], z);
+                            acc = O::mma(O::split_lo(VT + jrow * LDC, sp, grp),
+                                         O::from_acc(pt[2 * sp], z), acc);
                         }
-                        acc = O::mma(af, bf, acc);
                     }
                 } else {
 #pragma unroll
                     for (int sb = 0; sb < NTB; ++sb) {
                         if (sb > tb) break;
-                        acc = O::mma(O::split(sVT + jrow * LDC, sb, grp), O::from_acc(pt[sb]), acc);
+                        acc = O::mma(O::split(VT + jrow * LDC, sb, grp), O::from_acc(pt[sb]), acc);
                     }
                 }
                 if (t < nvalid) store4(oh + (size_t)(t0 + t) * DV + 16 * jt + 4 * grp, acc);
@@ -422,58 +450,109 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a)
         // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) {
-            const int u = k * NW + w;
+            const int u = k * NC + c;
             if (u < NU) {
                 const int it = u % NKB, jt = u / NKB;
-                const T *arow = sKT + (16 * it + x) * LDC;
-                const T *brow = sVT + (16 * jt + x) * LDC;
+                const T *arow = KT + (16 * it + x) * LDC;
+                const T *brow = VT + (16 * jt + x) * LDC;
                 f32x4 acc = S[k];
-                if (gate == kGateScalar) acc *= sEG[0];
-                constexpr int CSTEPS = (C + SH::SW - 1) / SH::SW;
+                if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
-                for (int c = 0; c < CSTEPS; ++c) {
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) {
                     typename O::frag af, bfr;
-                    if constexpr (SH::BF) {
-                        const bool in = 32 * c + 8 * grp < C;
-                        af = in ? O::contig(arow, c, grp) : O::zero();
-                        bfr = in ? O::contig(brow, c, grp) : O::zero();
+                    if constexpr (SH::BF && C % 32 != 0) {
+                        const bool in = 32 * cs + 8 * grp < C;
+                        af = in ? O::contig(arow, cs, grp) : O::zero();
+                        bfr = in ? O::contig(brow, cs, grp) : O::zero();
                     } else {
-                        af = O::contig(arow, c, grp);
-                        bfr = O::contig(brow, c, grp);
+                        af = O::contig(arow, cs, grp);
+                        bfr = O::contig(brow, cs, grp);
                     }
                     acc = O::mma(af, bfr, acc);
                 }
-                if (gate == kGateKeydim) {
+                if constexpr (GATE == kGateKeydim) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] *= sEG[16 * it + 4 * grp + r];
+                    for (int r = 0; r < 4; ++r) acc[r] *= sEG[buf][16 * it + 4 * grp + r];
                 }
                 S[k] = acc;
             }
         }
-        lds_barrier();
-    }
+        write_state(par ^ 1);
+    };
 
-    if (a.s_final) {
+    // ---------------- pipeline ---------------------------------------------------------
+    // The two roles run separate loops (so their registers are not live at the same
+    // time) that meet at the same number of barriers: 1 + nchunks with two buffers,
+    // 2 * nchunks with one.
+    if (producer) {
+        if constexpr (NBUF == 2) {
+            // operands one chunk ahead of the consumers, raw rows two chunks ahead
+            if (nchunks > 0) {
+                load_raw(R[0], 0);
+                if (nchunks > 1) load_raw(R[1], C);
+                produce(R[0], 0, 0);
+                if (nchunks > 2) load_raw(R[0], 2 * C);
+            }
+            lds_barrier();
+            auto step = [&](auto pi, int n) __attribute__((always_inline)) {
+                constexpr int PI = decltype(pi)::value;        // n % 2
+                if (n + 1 < nchunks) {
+                    produce(R[1 - PI], (n + 1) * C, 1 - PI);
+                    if (n + 3 < nchunks) load_raw(R[1 - PI], (n + 3) * C);
+                }
+                lds_barrier();
+            };
+            for (int n = 0; n < nchunks; n += 2) {
+                step(std::integral_constant<int, 0>{}, n);
+                if (n + 1 < nchunks) step(std::integral_constant<int, 1>{}, n + 1);
+            }
+        } else {
+            if (nchunks > 0) load_raw(R[0], 0);
+            for (int n = 0; n < nchunks; ++n) {
+                produce(R[0], n * C, 0);
+                if (n + 1 < nchunks) load_raw(R[0], (n + 1) * C);
+                lds_barrier();
+                lds_barrier();
+            }
+        }
+    } else {
+        write_state(0);
+        if constexpr (NBUF == 2) {
+            lds_barrier();
+            for (int n = 0; n < nchunks; ++n) {
+                consume(n * C, n & 1, n & 1);
+                lds_barrier();
+            }
+        } else {
+            for (int n = 0; n < nchunks; ++n) {
+                lds_barrier();
+                consume(n * C, 0, n & 1);
+                lds_barrier();
+            }
+        }
+        if (a.s_final) {
 #pragma unroll
-        for (int k = 0; k < NSLOT; ++k) {
-            const int u = k * NW + w;
-            if (u < NU) {
-                const int it = u % NKB, jt = u / NKB;
+            for (int k = 0; k < NSLOT; ++k) {
+                const int u = k * NC + c;
+                if (u < NU) {
+                    const int it = u % NKB, jt = u / NKB;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * it + 4 * grp + r;
-                    a.s_final[((size_t)bh * DK + i) * DV + vt * DVT + 16 * jt + x] = S[k][r];
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * it + 4 * grp + r;
+                        a.s_final[((size_t)bh * DK + i) * DV + vt * DVT + 16 * jt + x] = S[k][r];
+                    }
                 }
             }
         }
     }
 }
 
-template <typename T, int DK, int C, int DVT, int NW>
+template <typename T, int DK, int C, int DVT, int GATE, bool ELU1>
 hipError_t launch_prefill_inst(const PrefillArgs &a, hipStream_t stream)
 {
     const int grid = a.BH * a.n_vt;
-    hipLaunchKernelGGL((prefill_kernel<T, DK, C, DVT, NW>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, DK, C, DVT, GATE, ELU1>), dim3(grid),
+                       dim3(PrefillShape<T, DK, C, DVT>::NT), 0, stream, a);
     return hipGetLastError();
 }
 

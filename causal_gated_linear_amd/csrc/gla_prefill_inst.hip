@@ -21,17 +21,31 @@ typedef bf16 InstT;
 typedef float InstT;
 #endif
 
-hipError_t GLA_CAT3(launch_prefill_, GLA_INST_BF16, GLA_INST_DK)(const PrefillArgs &a, int chunk,
-                                                                 int dvt, int nw, hipStream_t stream)
+template <int C, int DVT>
+static hipError_t dispatch_mode(const PrefillArgs &a, hipStream_t stream)
 {
     constexpr int DK = GLA_INST_DK;
-#define GLA_CASE(C, DVT, NW) \
-    if (chunk == C && dvt == DVT && nw == NW) return launch_prefill_inst<InstT, DK, C, DVT, NW>(a, stream);
-#define GLA_CASES(C) GLA_CASE(C, 16, 4) GLA_CASE(C, 32, 4) GLA_CASE(C, 64, 4)
+    if constexpr (prefill_nbuf((int)sizeof(InstT), DK, C, DVT) == 0) {
+        return hipErrorInvalidValue;               // does not fit in LDS; never chosen
+    } else {
+    if (a.gate == kGateKeydim)
+        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, true>(a, stream)
+                      : launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, false>(a, stream);
+    if (a.gate == kGateScalar)
+        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, true>(a, stream)
+                      : launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, false>(a, stream);
+    return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateNone, true>(a, stream)
+                  : launch_prefill_inst<InstT, DK, C, DVT, kGateNone, false>(a, stream);
+    }
+}
+
+hipError_t GLA_CAT3(launch_prefill_, GLA_INST_BF16, GLA_INST_DK)(const PrefillArgs &a, int chunk,
+                                                                 int dvt, hipStream_t stream)
+{
+#define GLA_CASE(C, DVT) \
+    if (chunk == C && dvt == DVT) return dispatch_mode<C, DVT>(a, stream);
+#define GLA_CASES(C) GLA_CASE(C, 16) GLA_CASE(C, 32) GLA_CASE(C, 64)
     GLA_CASES(16) GLA_CASES(32) GLA_CASES(64)
-#if GLA_INST_DK >= 32
-    GLA_CASE(16, 64, 8) GLA_CASE(32, 64, 8) GLA_CASE(64, 64, 8)
-#endif
 #undef GLA_CASES
 #undef GLA_CASE
     return hipErrorInvalidValue;
