@@ -31,14 +31,14 @@ struct DecodeArgs {
 };
 
 // LDS bytes of a prefill workgroup: `nbuf` operand buffers (Q~ and K^ rows of
-// length d_k, K^T and V^T rows of length C, each padded by 16 bytes, plus exp(Gamma)
-// and the scalar-gate sums) and the two parity copies of the state operand.
+// length d_k, K^T and V^T rows of length C, plus exp(Gamma) and the scalar-gate
+// sums), the two parity copies of the state operand, and the output staging rows of
+// the four consumer waves (16 rows each).
 constexpr int kLdsBytes = 163840;                  // LDS per compute unit on gfx950
 constexpr int prefill_lds_bytes(int es, int dk, int c, int dvt, int nbuf)
 {
-    const int pad = 16 / es, ldk = dk + pad, ldc = c + pad;
-    const int buf = (2 * c * ldk + dk * ldc + dvt * ldc) * es + 4 * (dk + c);
-    return nbuf * buf + 2 * dvt * ldk * es;
+    const int buf = (2 * c * dk + dk * c + dvt * c) * es + 4 * (dk + c);
+    return nbuf * buf + 2 * dvt * dk * es + 4 * 16 * dvt * es;
 }
 // Operand buffers that fit (2: producer/consumer overlap, 1: alternating, 0: none).
 constexpr int prefill_nbuf(int es, int dk, int c, int dvt)

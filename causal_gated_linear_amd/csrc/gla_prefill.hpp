@@ -20,24 +20,35 @@
 // Decomposition: one workgroup per (batch*head, tile of DVT value columns) walks the
 // chunks of its head in order, with two kinds of wavefronts:
 //   producers (NP waves)  turn raw q, k, g, v rows into matrix-core operands in LDS:
-//       each owns DK/NP key columns of all C rows, forms the cumulative gate sums
-//       with an in-register scan plus a cross-lane scan, and writes Q~ and K^
-//       row-major and K^ (scalar gate: K~) and V transposed.  Raw rows are requested
-//       two chunks ahead into registers.
+//       each owns DK/NP key columns of all C rows; a lane holds one 16-byte piece of
+//       q and k (8 bf16 columns) for RPS consecutive rows, so loads read whole row
+//       pieces; it sums the gates of its rows serially and finishes the cumulative
+//       sum with a cross-lane scan; Q~ and K^ are written row-major, K^ (scalar
+//       gate: K~) and V transposed.  Raw rows are requested two chunks ahead.
 //   consumers (NC waves)  hold the fp32 state slice S[d_k][DVT] in accumulator
-//       registers (16x16 tiles dealt round-robin) and, per 16-row block tb of the
-//       chunk they own, compute the score tiles P^T[s-block <= tb][tb] in registers
-//       and O^T = S^T Q~^T + V^T P^T per 16-column value tile, stored to global
-//       memory; then S += K^^T V and the gate decay.  The state is shared between
+//       registers (16x16 tiles) and, for the 16-row block of the chunk they own,
+//       compute the score tiles P^T[s-block <= tb][tb] in registers and
+//       O^T = S^T Q~^T + V^T P^T per 16-column value tile; the output block goes
+//       through a private LDS staging area so it is stored with 16-byte row-contiguous
+//       writes; then S += K^^T V and the gate decay.  The state is shared between
 //       consumers as a bf16 operand copy in LDS.
 // With two LDS operand buffers the producers prepare chunk n+1 while the consumers
 // compute chunk n (one barrier per chunk); where two buffers do not fit in LDS the
 // phases alternate on one buffer.  Barriers wait only for LDS traffic, so requested
 // global rows stay in flight.  bf16 inputs use bf16 MFMA operands with fp32
 // accumulation; fp32 inputs use fp32 MFMA.
+//
+// LDS layout: every operand fragment is one 16-byte read.  Rows are not padded;
+// instead the 16-byte chunks of a row are XOR-swizzled by (row mod 8), so the 8 rows
+// a fragment read touches per cycle, and the producers' writes, spread over all
+// banks.  Transposed arrays (K^T, V^T, rows of length C) also store the token index s
+// of each 32-token block permuted so the 8 values a lane feeds to one bf16 MFMA step
+// in the accumulator-compatible order (s = 4g..4g+3 and 16+4g..16+4g+3 of the block
+// for lane group g) are contiguous.
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
@@ -51,46 +62,31 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <typename T> struct Vec4;
-template <> struct Vec4<bf16> { typedef bf16x4 type; };
-template <> struct Vec4<float> { typedef f32x4 type; };
+template <typename T, int N> struct VecN { typedef T type __attribute__((ext_vector_type(N))); };
+template <typename T> struct VecN<T, 1> { typedef T type; };
+template <typename T> using Vec4 = VecN<T, 4>;
 
-__device__ __forceinline__ f32x4 widen(bf16x4 v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
-__device__ __forceinline__ f32x4 widen(f32x4 v) { return v; }
-
-template <typename E> __device__ __forceinline__ typename Vec4<E>::type narrow4(f32x4 v);
-template <> __device__ __forceinline__ bf16x4 narrow4<bf16>(f32x4 v)
+template <typename T, int N>
+__device__ __forceinline__ void widen(const typename VecN<T, N>::type &v, float (&f)[N])
 {
-    return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+#pragma unroll
+    for (int e = 0; e < N; ++e) f[e] = (float)v[e];
 }
-template <> __device__ __forceinline__ f32x4 narrow4<float>(f32x4 v) { return v; }
+
+template <typename E> __device__ __forceinline__ typename Vec4<E>::type narrow4(f32x4 v)
+{
+    return typename Vec4<E>::type{from_f32<E>(v[0]), from_f32<E>(v[1]), from_f32<E>(v[2]), from_f32<E>(v[3])};
+}
 
 // Operand fragment of one matrix-core step (see gla_device.hpp for the lane layout).
-// bf16: one 16x16x32 step covers a 32-wide slice of the contraction index; lane
-// group grp holds 8 values.  fp32: a 16-wide block is 4 steps of 16x16x4.
+// bf16: one 16x16x32 step covers a 32-wide slice of the contraction index (8 values
+// per lane); fp32: one 16-wide block, 4 steps of 16x16x4 (4 values per lane).  A
+// fragment is one 16-byte chunk of an LDS row.
 template <typename E> struct Op;
 
 template <> struct Op<bf16> {
-    typedef bf16x8 frag;                           // one step
+    typedef bf16x8 frag;
     static constexpr int W = 32;                   // contraction width of one step
-    // contiguous convention: elements [32k + 8grp, 32k + 8grp + 7] of an LDS row
-    static __device__ __forceinline__ frag contig(const bf16 *row, int k, int grp)
-    {
-        return *(const bf16x8 *)(row + 32 * k + 8 * grp);
-    }
-    // split convention (matches the accumulator layout): elements
-    // [32k + 4grp, +3] and [32k + 16 + 4grp, +3]
-    static __device__ __forceinline__ frag split(const bf16 *row, int k, int grp)
-    {
-        const bf16x4 a = *(const bf16x4 *)(row + 32 * k + 4 * grp);
-        const bf16x4 b = *(const bf16x4 *)(row + 32 * k + 16 + 4 * grp);
-        return frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    }
-    static __device__ __forceinline__ frag split_lo(const bf16 *row, int k, int grp)
-    {
-        const bf16x4 a = *(const bf16x4 *)(row + 32 * k + 4 * grp);
-        return frag{a[0], a[1], a[2], a[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-    }
     static __device__ __forceinline__ frag from_acc(f32x4 a, f32x4 b)
     {
         return frag{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
@@ -104,16 +100,8 @@ template <> struct Op<bf16> {
 };
 
 template <> struct Op<float> {
-    typedef f32x4 frag;                            // 4 steps of 16x16x4 (one 16-block)
+    typedef f32x4 frag;
     static constexpr int W = 16;
-    static __device__ __forceinline__ frag contig(const float *row, int k, int grp)
-    {
-        return *(const f32x4 *)(row + 16 * k + 4 * grp);
-    }
-    static __device__ __forceinline__ frag split(const float *row, int k, int grp)
-    {
-        return contig(row, k, grp);
-    }
     static __device__ __forceinline__ frag from_acc(f32x4 a) { return a; }
     static __device__ __forceinline__ frag zero() { return frag{0.f, 0.f, 0.f, 0.f}; }
     static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c)
@@ -126,10 +114,15 @@ template <> struct Op<float> {
     }
 };
 
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <typename T, int DK, int C, int DVT>
 struct PrefillShape {
     static constexpr bool BF = sizeof(T) == 2;
-    static constexpr int NP = 4, NC = 4;           // producer / consumer waves
+    static constexpr int CE = 16 / sizeof(T);      // elements per 16-byte chunk
+    static constexpr int NP = cmin(4, DK / CE);    // producer waves
+    static constexpr int NC = 4;                   // consumer waves
     static constexpr int NT = 64 * (NP + NC);
     static constexpr int NTB = C / 16;             // 16-row blocks per chunk
     static constexpr int NKB = DK / 16;            // 16-blocks of the key dim
@@ -137,31 +130,87 @@ struct PrefillShape {
     static constexpr int SW = Op<T>::W;            // contraction width per MFMA step
     static constexpr int KSTEPS = (DK + SW - 1) / SW;
     static constexpr int CSTEPS = (C + SW - 1) / SW;
-    static constexpr int PAD = 16 / sizeof(T);     // 16 bytes of row padding in LDS
-    static constexpr int LDK = DK + PAD;           // rows of length d_k
-    static constexpr int LDC = C + PAD;            // rows of length C
-    // producer gate mapping: producer p owns key columns [p*CW, (p+1)*CW)
+    static constexpr int KCH = DK / CE, TCH = C / CE, VCH = DVT / CE;   // chunks per row
+    static constexpr int SWK = cmin(KCH, 8) - 1, SWT = cmin(TCH, 8) - 1, SWV = cmin(VCH, 8) - 1;
+    static constexpr bool PERM = BF && C % 32 == 0;       // permuted token order
+    // producer gate mapping: producer p owns key columns [p*CW, (p+1)*CW); a lane
+    // has column group cg (one 16-byte chunk, CE columns) and row segment rs (RPS
+    // consecutive rows); column groups vary fastest across lanes
     static constexpr int CW = DK / NP;
-    static constexpr int CG = CW / 4;              // 4-column groups
-    static constexpr int RSEG = (64 / CG) < C ? (64 / CG) : C;
-    static constexpr int RPS = C / RSEG;           // rows per lane
+    static constexpr int CG = CW / CE;
+    static constexpr int RSEG = cmin(64 / CG, C);
+    static constexpr int RPS = C / RSEG;
     // producer value mapping: 64*NP lanes cover C x DVT, a lane 4 columns x RV rows
     static constexpr int CGV = DVT / 4;
-    static constexpr int RGV = (64 * NP / CGV) < C ? (64 * NP / CGV) : C;
+    static constexpr int RGV = cmin(64 * NP / CGV, C);
     static constexpr int RV = C / RGV;
-    // consumer state tiles, dealt round-robin
+    // consumer state tiles: with NKB % NC == 0 consumer c owns i-tiles c + NC*a
+    // (a < IPC) for every j-tile, so its fragments are shared across tiles;
+    // otherwise tiles are dealt round-robin
     static constexpr int NU = NKB * NJT;
-    static constexpr int NSLOT = (NU + NC - 1) / NC;
-    // LDS: operand buffers (Q~, K^, K^T, V^T, exp Gamma, B) and the state copies
+    static constexpr bool BLOCKED = NKB % NC == 0;
+    static constexpr int IPC = BLOCKED ? NKB / NC : 1;
+    static constexpr int NSLOT = BLOCKED ? IPC * NJT : (NU + NC - 1) / NC;
+    // output staging: 16 rows x DVT, stored by 64 lanes in 16-byte chunks
+    static constexpr int OCH = 16 * VCH;           // chunks per staged block
+    static constexpr int OCPL = cmax(1, OCH / 64); // chunks per lane
     static constexpr int NBUF = prefill_nbuf((int)sizeof(T), DK, C, DVT);
     static_assert(NBUF >= 1, "LDS budget");
-    static_assert(CW >= 4 && CW % 4 == 0 && 64 % CG == 0, "producer gate mapping");
+    static_assert(CW >= CE && CW % CE == 0 && 64 % CG == 0, "producer gate mapping");
     static_assert((64 * NP) % CGV == 0, "producer value mapping");
     static_assert(RPS >= 1 && RV >= 1, "rows per lane");
+
+    // element offset of (row, col) in a row-major array of rows of `len` elements
+    // whose 16-byte chunks are swizzled by (row & sw)
+    static __device__ __forceinline__ int sw_off(int row, int col, int len, int sw)
+    {
+        return row * len + (((col / CE) ^ (row & sw)) * CE) + col % CE;
+    }
+    static __device__ __forceinline__ int rk(int row, int col) { return sw_off(row, col, DK, SWK); }
+    static __device__ __forceinline__ int rt(int row, int pos) { return sw_off(row, pos, C, SWT); }
+    static __device__ __forceinline__ int rv(int row, int col) { return sw_off(row, col, DVT, SWV); }
+    // position of token s in a transposed row (length C) before the chunk swizzle
+    static __device__ __forceinline__ int tpos(int s)
+    {
+        if constexpr (!PERM) return s;
+        const int b = s & 31;
+        const int hi = b >> 4, q4 = (b >> 2) & 3;
+        return (s & ~31) + 8 * q4 + 4 * hi + (b & 3);
+    }
 };
 
-template <typename T, int N> struct VecN { typedef T type __attribute__((ext_vector_type(N))); };
-template <typename T> struct VecN<T, 1> { typedef T type; };
+// Calls fn(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <typename Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn &&fn, std::integer_sequence<int, I...>)
+{
+    (fn(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn &&fn)
+{
+    static_for_impl(fn, std::make_integer_sequence<int, N>{});
+}
+
+// Inclusive scan of v over the RSEG lanes of a segment group: the lanes
+// rs * STRIDE + cg (rs = 0 .. RSEG-1) for a fixed cg, in order of rs.
+template <int RSEG, int STRIDE, int OFF = 1>
+__device__ __forceinline__ float group_scan(float v, int rs)
+{
+    if constexpr (OFF >= RSEG) {
+        return v;
+    } else {
+        float up;
+        if constexpr (OFF * STRIDE < 16 && 16 % (RSEG * STRIDE) == 0) {
+            // the whole group lies in one 16-lane row: DPP row_shr stays inside it
+            up = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                               0, __builtin_bit_cast(int, v), 0x110 + OFF * STRIDE, 0xf, 0xf, false));
+        } else {
+            up = __shfl_up(v, OFF * STRIDE, 64);
+        }
+        v += rs >= OFF ? up : 0.f;
+        return group_scan<RSEG, STRIDE, 2 * OFF>(v, rs);
+    }
+}
 
 template <typename T, int DK, int C, int DVT, int GATE, bool ELU1>
 __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
@@ -169,18 +218,21 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     using SH = PrefillShape<T, DK, C, DVT>;
     using O = Op<T>;
     using V4 = typename Vec4<T>::type;
-    constexpr int NP = SH::NP, NC = SH::NC, NBUF = SH::NBUF;
-    constexpr int NTB = SH::NTB, NKB = SH::NKB, NJT = SH::NJT, LDK = SH::LDK, LDC = SH::LDC;
-    constexpr int CW = SH::CW, CG = SH::CG, RSEG = SH::RSEG, RPS = SH::RPS;
+    using VC = typename VecN<T, SH::CE>::type;       // one 16-byte chunk
+    using F = typename O::frag;
+    constexpr int NP = SH::NP, NC = SH::NC, NBUF = SH::NBUF, CE = SH::CE;
+    constexpr int NTB = SH::NTB, NKB = SH::NKB, NJT = SH::NJT;
+    constexpr int CW = SH::CW, RSEG = SH::RSEG, RPS = SH::RPS;
     constexpr int CGV = SH::CGV, RGV = SH::RGV, RV = SH::RV, NSLOT = SH::NSLOT, NU = SH::NU;
 
-    __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * LDK];     // Q~ [t][i]
-    __shared__ __attribute__((aligned(16))) T sK[NBUF][C * LDK];     // K^ [s][i]
-    __shared__ __attribute__((aligned(16))) T sKT[NBUF][DK * LDC];   // K^ (scalar: K~) [i][s]
-    __shared__ __attribute__((aligned(16))) T sVT[NBUF][DVT * LDC];  // V^T [j][s]
-    __shared__ __attribute__((aligned(16))) T sS[2][DVT * LDK];      // state^T [j][i], by parity
-    __shared__ float sEG[NBUF][DK];                                  // exp(Gamma_i)
-    __shared__ float sB[NBUF][C];                                    // scalar gate: B_t (log2)
+    __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * DK];      // Q~ [t][i]
+    __shared__ __attribute__((aligned(16))) T sK[NBUF][C * DK];      // K^ [s][i]
+    __shared__ __attribute__((aligned(16))) T sKT[NBUF][DK * C];     // K^ (scalar: K~) [i][pos(s)]
+    __shared__ __attribute__((aligned(16))) T sVT[NBUF][DVT * C];    // V^T [j][pos(s)]
+    __shared__ __attribute__((aligned(16))) T sS[2][DVT * DK];       // state^T [j][i], by parity
+    __shared__ __attribute__((aligned(16))) T sO[NC][16 * DVT];      // output staging, per consumer
+    __shared__ __attribute__((aligned(16))) float sEG[NBUF][DK];     // exp(Gamma_i)
+    __shared__ __attribute__((aligned(16))) float sB[NBUF][C];       // scalar gate: B_t (log2)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -201,36 +253,50 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     const float *__restrict__ gs = a.g + (size_t)bh * L;        // scalar gates
     const int nchunks = (L + C - 1) / C;
 
-    // ---------------- producer state ------------------------------------------------
-    const int p = w;                               // producer index (when producer)
-    const int cg = lane % CG, rs = lane / CG;
-    const bool gate_lane = producer && rs < RSEG;
-    const int ic = p * CW + 4 * cg;                // first of this lane's 4 key columns
-    const int ptid = tid;                          // producer thread index (< 64*NP)
-    const int cgv = ptid % CGV, rgv = ptid / CGV;
-    const bool v_lane = producer && rgv < RGV;
+    // ---------------- producers -------------------------------------------------------
+    const int p = w;
+    const int cg = lane % SH::CG, rs = lane / SH::CG;   // column group, row segment
+    // lanes with work in the gate / value mappings (all of them for the common shapes,
+    // known at compile time so that no branch surrounds the loads)
+    const bool gate_lane = (SH::CG * RSEG == 64) || rs < RSEG;
+    const int ic = p * CW + CE * cg;               // first of this lane's CE key columns
+    const int cgv = tid % CGV, rgv = tid / CGV;
+    const bool v_lane = (CGV * RGV == 64 * NP) || rgv < RGV;
 
     struct Raw {
-        V4 q[RPS], k[RPS], v[RV];
-        f32x4 g[RPS];
+        VC q[RPS], k[RPS];
+        f32x4 g[RPS][CE / 4];
+        V4 v[RV];
     };
     Raw R[NBUF];
 
-    auto load_raw = [&](Raw &r_, int t0) __attribute__((always_inline)) {
+    // Raw rows of the chunk starting at t0 (gates, q and k, v).
+    auto load_g = [&](Raw &r_, int t0) __attribute__((always_inline)) {
         if (gate_lane) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
                 const int row = min(t0 + rs * RPS + r, L - 1);   // clamp: always in bounds
-                r_.q[r] = *(const V4 *)(qh + (size_t)row * DK + ic);
-                r_.k[r] = *(const V4 *)(kh + (size_t)row * DK + ic);
                 if constexpr (GATE == kGateKeydim) {
-                    r_.g[r] = *(const f32x4 *)(gk + (size_t)row * DK + ic);
+#pragma unroll
+                    for (int h = 0; h < CE / 4; ++h) r_.g[r][h] = *(const f32x4 *)(gk + (size_t)row * DK + ic + 4 * h);
                 } else if constexpr (GATE == kGateScalar) {
                     const float gv = gs[row];
-                    r_.g[r] = f32x4{gv, gv, gv, gv};
+                    r_.g[r][0] = f32x4{gv, gv, gv, gv};
                 }
             }
         }
+    };
+    auto load_qk = [&](Raw &r_, int t0) __attribute__((always_inline)) {
+        if (gate_lane) {
+#pragma unroll
+            for (int r = 0; r < RPS; ++r) {
+                const int row = min(t0 + rs * RPS + r, L - 1);
+                r_.q[r] = *(const VC *)(qh + (size_t)row * DK + ic);
+                r_.k[r] = *(const VC *)(kh + (size_t)row * DK + ic);
+            }
+        }
+    };
+    auto load_v = [&](Raw &r_, int t0) __attribute__((always_inline)) {
         if (v_lane) {
 #pragma unroll
             for (int r = 0; r < RV; ++r) {
@@ -239,127 +305,256 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
             }
         }
     };
+    auto load_raw = [&](Raw &r_, int t0) __attribute__((always_inline)) {
+        load_g(r_, t0);
+        load_qk(r_, t0);
+        load_v(r_, t0);
+    };
+
+    // Store N consecutive transposed values (tokens s0..s0+N-1, s0 % N == 0) of row `row`.
+    auto write_t = [&](T *base, int row, int s0, const auto &vals) __attribute__((always_inline)) {
+        constexpr int N = sizeof(vals) / sizeof(vals[0]);
+        if constexpr (SH::PERM && N % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < N; j += 4)         // runs of 4 tokens stay in one chunk
+                *(bf16x4 *)(base + SH::rt(row, SH::tpos(s0 + j))) = bf16x4{vals[j], vals[j + 1], vals[j + 2], vals[j + 3]};
+        } else {
+#pragma unroll
+            for (int j = 0; j < N; ++j) base[SH::rt(row, SH::tpos(s0 + j))] = vals[j];
+        }
+    };
 
     // Turn the raw rows of the chunk starting at t0 into the operands of buffer `buf`.
     auto produce = [&](Raw &r_, int t0, int buf) __attribute__((always_inline)) {
+        // Rows past L (ragged tail) carry no gate and no value; their q, k are finite
+        // copies of the last row.  Masked arithmetically, not by a branch, so the wait
+        // for this chunk's loads does not also wait for the rows requested after it.
         const int nvalid = min(L - t0, C);
-        if (nvalid < C) {                          // ragged tail: rows past L carry no gate
-#pragma unroll                                     // and no value (their q, k are finite copies)
-            for (int r = 0; r < RPS; ++r)
-                if (rs * RPS + r >= nvalid) r_.g[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < RV; ++r)
-                if (rgv * RV + r >= nvalid) r_.v[r] = narrow4<T>(f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int r = 0; r < RV; ++r) {
+            const float keep = rgv * RV + r < nvalid ? 1.f : 0.f;            // v is finite
+            const V4 v = r_.v[r];
+            r_.v[r] = V4{from_f32<T>((float)v[0] * keep), from_f32<T>((float)v[1] * keep),
+                         from_f32<T>((float)v[2] * keep), from_f32<T>((float)v[3] * keep)};
         }
         if (gate_lane) {
-            f32x4 bc[RPS];
-            f32x4 incl = {0.f, 0.f, 0.f, 0.f}, excl = incl, tot = incl;
+            float bc[RPS][CE];
+            float excl[CE], tot[CE];
+#pragma unroll
+            for (int e = 0; e < CE; ++e) excl[e] = tot[e] = 0.f;
             if constexpr (GATE != kGateNone) {
-                f32x4 run = {0.f, 0.f, 0.f, 0.f};
+                constexpr int NE = GATE == kGateScalar ? 1 : CE;
+                float run[NE];
+#pragma unroll
+                for (int e = 0; e < NE; ++e) run[e] = 0.f;
 #pragma unroll
                 for (int r = 0; r < RPS; ++r) {
-                    run += r_.g[r];
-                    bc[r] = run;
-                }
-                incl = run;
+                    const float keep = rs * RPS + r < nvalid ? 1.f : 0.f;   // g is finite
 #pragma unroll
-                for (int off = 1; off < RSEG; off <<= 1) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float up = __shfl_up(incl[e], off * CG, 64);
-                        if (rs >= off) incl[e] += up;
+                    for (int e = 0; e < NE; ++e) {
+                        run[e] += r_.g[r][e / 4][e % 4] * keep;
+                        bc[r][e] = run[e];
                     }
                 }
-                excl = incl - run;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) tot[e] = __shfl(incl[e], (RSEG - 1) * CG + cg, 64) * kLog2e;
+                for (int e = 0; e < NE; ++e) {
+                    const float incl = group_scan<RSEG, SH::CG>(run[e], rs);
+                    excl[e] = incl - run[e];
+                    tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64) * kLog2e;
+                }
+                if constexpr (GATE == kGateScalar) {
+#pragma unroll
+                    for (int e = 1; e < CE; ++e) { excl[e] = excl[0]; tot[e] = tot[0]; }
+#pragma unroll
+                    for (int r = 0; r < RPS; ++r)
+#pragma unroll
+                        for (int e = 1; e < CE; ++e) bc[r][e] = bc[r][0];
+                }
             }
-            typedef typename VecN<T, RPS>::type KTv;
-            KTv ktv[4];
+            T ktv[CE][RPS];
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
                 const int t = rs * RPS + r;
-                f32x4 q = widen(r_.q[r]), kk = widen(r_.k[r]);
-                if constexpr (ELU1) {
+                float q[CE], kk[CE], qt[CE], kt[CE];
+                widen<T, CE>(r_.q[r], q);
+                widen<T, CE>(r_.k[r], kk);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < CE; ++e) {
+                    if constexpr (ELU1) {
                         q[e] = feature(q[e], true);
                         kk[e] = feature(kk[e], true);
                     }
-                }
-                f32x4 qt = q, kt = kk, kT = kk;
-                if constexpr (GATE == kGateKeydim) {
-                    const f32x4 b = (excl + bc[r]) * kLog2e;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        qt[e] = q[e] * exp2_fast(b[e]);
-                        kt[e] = kk[e] * exp2_fast(-b[e]);
+                    float kT = kk[e];
+                    qt[e] = q[e];
+                    kt[e] = kk[e];
+                    if constexpr (GATE == kGateKeydim) {
+                        const float b = (excl[e] + bc[r][e]) * kLog2e;
+                        qt[e] = q[e] * exp2_fast(b);
+                        kt[e] = kk[e] * exp2_fast(-b);
+                        kT = kt[e];
+                    } else if constexpr (GATE == kGateScalar) {
+                        const float b = (excl[0] + bc[r][0]) * kLog2e;
+                        kT = kk[e] * exp2_fast(tot[0] - b);
+                        if (e == 0 && p == 0 && cg == 0) sB[buf][t] = b;
                     }
-                    kT = kt;
-                } else if constexpr (GATE == kGateScalar) {
-                    const float b = (excl[0] + bc[r][0]) * kLog2e;
-                    kT = kk * exp2_fast(tot[0] - b);
-                    if (p == 0 && cg == 0) sB[buf][t] = b;
+                    ktv[e][r] = from_f32<T>(kT);
                 }
-                *(V4 *)(sQ[buf] + t * LDK + ic) = narrow4<T>(qt);
-                *(V4 *)(sK[buf] + t * LDK + ic) = narrow4<T>(kt);
+                VC qv, kv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (RPS == 1) ktv[e] = from_f32<T>(kT[e]);
-                    else ktv[e][r] = from_f32<T>(kT[e]);
+                for (int e = 0; e < CE; ++e) {
+                    qv[e] = from_f32<T>(qt[e]);
+                    kv[e] = from_f32<T>(kt[e]);
                 }
+                *(VC *)(sQ[buf] + SH::rk(t, ic)) = qv;
+                *(VC *)(sK[buf] + SH::rk(t, ic)) = kv;
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) *(KTv *)(sKT[buf] + (ic + e) * LDC + rs * RPS) = ktv[e];
+            for (int e = 0; e < CE; ++e) write_t(sKT[buf], ic + e, rs * RPS, ktv[e]);
             if (rs == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < CE; ++e)
                     sEG[buf][ic + e] = GATE == kGateNone ? 1.f : exp2_fast(tot[e]);
             }
         }
         if (v_lane) {
-            typedef typename VecN<T, RV>::type Vv;
-            Vv vv[4];
+            T vv[4][RV];
 #pragma unroll
             for (int r = 0; r < RV; ++r) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (RV == 1) vv[e] = r_.v[r][e];
-                    else vv[e][r] = r_.v[r][e];
-                }
+                for (int e = 0; e < 4; ++e) vv[e][r] = r_.v[r][e];
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) *(Vv *)(sVT[buf] + (4 * cgv + e) * LDC + rgv * RV) = vv[e];
+            for (int e = 0; e < 4; ++e) write_t(sVT[buf], 4 * cgv + e, rgv * RV, vv[e]);
         }
     };
 
-    // ---------------- consumer state ------------------------------------------------
-    const int c = w - NP;                          // consumer index (when consumer)
+    // ---------------- consumers -------------------------------------------------------
+    const int c = w - NP;
+    auto tile_i = [&](int k) __attribute__((always_inline)) -> int {
+        if constexpr (SH::BLOCKED) return c + NC * (k % SH::IPC);
+        else return (k * NC + c) % NKB;
+    };
+    auto tile_j = [&](int k) __attribute__((always_inline)) -> int {
+        if constexpr (SH::BLOCKED) return k / SH::IPC;
+        else return (k * NC + c) / NKB;
+    };
+    auto tile_ok = [&](int k) __attribute__((always_inline)) -> bool {
+        if constexpr (SH::BLOCKED) return true;
+        else return k * NC + c < NU;
+    };
+
     f32x4 S[NSLOT];
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (!producer && a.s0) {                       // branch-free loads, issued together
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) {
-            const int u = k * NC + c;
-            const int uc = u < NU ? u : NU - 1;
-            const int it = uc % NKB, jt = uc / NKB;
+            const bool ok = tile_ok(k);
+            const int it = ok ? tile_i(k) : 0, jt = ok ? tile_j(k) : 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * it + 4 * grp + r;
                 const float v = a.s0[((size_t)bh * DK + i) * DV + vt * DVT + 16 * jt + x];
-                S[k][r] = u < NU ? v : 0.f;
+                S[k][r] = ok ? v : 0.f;
             }
         }
     }
 
-    auto write_state = [&](int par) __attribute__((always_inline)) {              // state tiles -> bf16 operand rows
+    auto write_state = [&](int par) __attribute__((always_inline)) {   // -> bf16 operand rows
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) {
-            const int u = k * NC + c;
-            if (u < NU) {
-                const int it = u % NKB, jt = u / NKB;
-                *(V4 *)(sS[par] + (16 * jt + x) * LDK + 16 * it + 4 * grp) = narrow4<T>(S[k]);
+            if (tile_ok(k)) {
+                const int it = tile_i(k), jt = tile_j(k);
+                *(V4 *)(sS[par] + SH::rk(16 * jt + x, 16 * it + 4 * grp)) = narrow4<T>(S[k]);
+            }
+        }
+    };
+
+    // fragment k-step `ks` of a row of length d_k (contraction over d_k)
+    auto frag_k = [&](const T *base, int row, int ks) __attribute__((always_inline)) -> F {
+        const int col = SH::SW * ks + CE * grp;
+        if constexpr (SH::BF && DK % 32 != 0) {
+            if (col >= DK) return O::zero();
+        }
+        return *(const F *)(base + SH::rk(row, col));
+    };
+    // fragment k-step `ks` of a transposed row of length C (contraction over tokens)
+    auto frag_t = [&](const T *base, int row, int ks) __attribute__((always_inline)) -> F {
+        const int pos = SH::SW * ks + CE * grp;
+        if constexpr (SH::BF && C % 32 != 0) {
+            if (pos >= C) return O::zero();
+        }
+        return *(const F *)(base + SH::rt(row, pos));
+    };
+
+    // Outputs of the 16-row block TB of the chunk starting at t0 (straight-line code:
+    // TB is a compile-time constant, so every tile loop below is unrolled).
+    auto out_block = [&](auto tbc, int t0, int nvalid, int buf, const T *Q, const T *K,
+                         const T *VT, const T *SS) __attribute__((always_inline)) {
+        constexpr int TB = decltype(tbc)::value;
+        const int t = 16 * TB + x;
+        F qf[SH::KSTEPS];
+#pragma unroll
+        for (int k = 0; k < SH::KSTEPS; ++k) qf[k] = frag_k(Q, t, k);
+        // score tiles P^T[s-block sb][t-block TB]: lane holds P[t][16sb + 4grp + r]
+        f32x4 pt[TB + 2];
+#pragma unroll
+        for (int sb = 0; sb <= TB; ++sb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < SH::KSTEPS; ++k) acc = O::mma(frag_k(K, 16 * sb + x, k), qf[k], acc);
+            if constexpr (GATE == kGateScalar) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * sb + 4 * grp + r;
+                    acc[r] = s <= t ? acc[r] * exp2_fast(sB[buf][t] - sB[buf][s]) : 0.f;
+                }
+            } else if (sb == TB) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = 4 * grp + r <= x ? acc[r] : 0.f;
+            }
+            pt[sb] = acc;
+        }
+        pt[TB + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float inter_scale = 1.f;
+        if constexpr (GATE == kGateScalar) inter_scale = exp2_fast(sB[buf][t]);
+        T *stage = sO[c];
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+            const int jrow = 16 * jt + x;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < SH::KSTEPS; ++k) acc = O::mma(frag_k(SS, jrow, k), qf[k], acc);
+            if constexpr (GATE == kGateScalar) acc *= inter_scale;
+            // intra-chunk: O^T += V^T P^T over s-blocks 0..TB
+            if constexpr (SH::BF) {
+#pragma unroll
+                for (int sp = 0; 2 * sp <= TB; ++sp) {
+                    F af;
+                    if constexpr (SH::PERM) {
+                        af = frag_t(VT, jrow, sp);
+                    } else {                       // C == 16: one 16-block, natural order
+                        const bf16x4 lo = *(const bf16x4 *)(VT + SH::rt(jrow, 4 * grp));
+                        af = F{lo[0], lo[1], lo[2], lo[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+                    }
+                    acc = O::mma(af, O::from_acc(pt[2 * sp], pt[2 * sp + 1]), acc);
+                }
+            } else {
+#pragma unroll
+                for (int sb = 0; sb <= TB; ++sb) acc = O::mma(frag_t(VT, jrow, sb), O::from_acc(pt[sb]), acc);
+            }
+            // lane holds O[t][16jt + 4grp + r]: stage it row-major
+            *(V4 *)(stage + SH::rv(x, 16 * jt + 4 * grp)) = narrow4<T>(acc);
+        }
+        // read the block back row-contiguous and store 16-byte chunks (wave-local:
+        // LDS operations of one wave complete in order)
+#pragma unroll
+        for (int h = 0; h < SH::OCPL; ++h) {
+            const int chunk = lane * SH::OCPL + h;
+            if (chunk < SH::OCH) {
+                const int row = chunk / SH::VCH, col = (chunk % SH::VCH) * CE;
+                const VC val = *(const VC *)(stage + SH::rv(row, col));
+                if (16 * TB + row < nvalid) *(VC *)(oh + (size_t)(t0 + 16 * TB + row) * DV + col) = val;
             }
         }
     };
@@ -368,113 +563,46 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     auto consume = [&](int t0, int buf, int par) __attribute__((always_inline)) {
         const int nvalid = min(L - t0, C);
         const T *Q = sQ[buf], *K = sK[buf], *KT = sKT[buf], *VT = sVT[buf], *SS = sS[par];
-        for (int tb = c; tb < NTB; tb += NC) {
-            const int t = 16 * tb + x;
-            typename O::frag qf[SH::KSTEPS];
+        // consumer c owns the 16-row blocks tb with tb % NC == c
+        static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
+            if (decltype(tbc)::value % NC == c) out_block(tbc, t0, nvalid, buf, Q, K, VT, SS);
+        });
+        // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
+        if constexpr (SH::BLOCKED) {
+            F af[SH::IPC][SH::CSTEPS];
 #pragma unroll
-            for (int k = 0; k < SH::KSTEPS; ++k) {
-                if constexpr (SH::BF && DK % 32 != 0)
-                    qf[k] = (32 * k + 8 * grp < DK) ? O::contig(Q + t * LDK, k, grp) : O::zero();
-                else
-                    qf[k] = O::contig(Q + t * LDK, k, grp);
-            }
-            // score tiles P^T[s-block sb][t-block tb]: lane holds P[t][16sb + 4grp + r]
-            f32x4 pt[NTB];
+            for (int ia = 0; ia < SH::IPC; ++ia)
 #pragma unroll
-            for (int sb = 0; sb < NTB; ++sb) {
-                if (sb > tb) break;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const int srow = 16 * sb + x;
-#pragma unroll
-                for (int k = 0; k < SH::KSTEPS; ++k) {
-                    typename O::frag af;
-                    if constexpr (SH::BF && DK % 32 != 0)
-                        af = (32 * k + 8 * grp < DK) ? O::contig(K + srow * LDK, k, grp) : O::zero();
-                    else
-                        af = O::contig(K + srow * LDK, k, grp);
-                    acc = O::mma(af, qf[k], acc);
-                }
-                if constexpr (GATE == kGateScalar) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int s = 16 * sb + 4 * grp + r;
-                        acc[r] = s <= t ? acc[r] * exp2_fast(sB[buf][t] - sB[buf][s]) : 0.f;
-                    }
-                } else if (sb == tb) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] = 4 * grp + r <= x ? acc[r] : 0.f;
-                }
-                pt[sb] = acc;
-            }
-            float inter_scale = 1.f;
-            if constexpr (GATE == kGateScalar) inter_scale = exp2_fast(sB[buf][t]);
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_t(KT, 16 * (c + NC * ia) + x, cs);
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt) {
-                const int jrow = 16 * jt + x;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                // inter-chunk: O^T += S^T Q~^T
+                F bfr[SH::CSTEPS];
 #pragma unroll
-                for (int k = 0; k < SH::KSTEPS; ++k) {
-                    typename O::frag af;
-                    if constexpr (SH::BF && DK % 32 != 0)
-                        af = (32 * k + 8 * grp < DK) ? O::contig(SS + jrow * LDK, k, grp) : O::zero();
-                    else
-                        af = O::contig(SS + jrow * LDK, k, grp);
-                    acc = O::mma(af, qf[k], acc);
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) bfr[cs] = frag_t(VT, 16 * jt + x, cs);
+#pragma unroll
+                for (int ia = 0; ia < SH::IPC; ++ia) {
+                    const int k = jt * SH::IPC + ia;
+                    f32x4 acc = S[k];
+                    if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
+#pragma unroll
+                    for (int cs = 0; cs < SH::CSTEPS; ++cs) acc = O::mma(af[ia][cs], bfr[cs], acc);
+                    if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * (c + NC * ia) + 4 * grp);
+                    S[k] = acc;
                 }
-                if constexpr (GATE == kGateScalar) acc *= inter_scale;
-                // intra-chunk: O^T += V^T P^T over s-blocks 0..tb
-                if constexpr (SH::BF) {
-#pragma unroll
-                    for (int sp = 0; sp < (NTB + 1) / 2; ++sp) {
-                        if (2 * sp > tb) break;
-                        if (2 * sp + 1 <= tb) {
-                            acc = O::mma(O::split(VT + jrow * LDC, sp, grp),
-                                         O::from_acc(pt[2 * sp], pt[2 * sp + 1]), acc);
-                        } else {            // only the first 16-block of this pair is in range
-                            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                            acc = O::mma(O::split_lo(VT + jrow * LDC, sp, grp),
-                                         O::from_acc(pt[2 * sp], z), acc);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int sb = 0; sb < NTB; ++sb) {
-                        if (sb > tb) break;
-                        acc = O::mma(O::split(VT + jrow * LDC, sb, grp), O::from_acc(pt[sb]), acc);
-                    }
-                }
-                if (t < nvalid) store4(oh + (size_t)(t0 + t) * DV + 16 * jt + 4 * grp, acc);
             }
-        }
-        // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
+        } else {
 #pragma unroll
-        for (int k = 0; k < NSLOT; ++k) {
-            const int u = k * NC + c;
-            if (u < NU) {
-                const int it = u % NKB, jt = u / NKB;
-                const T *arow = KT + (16 * it + x) * LDC;
-                const T *brow = VT + (16 * jt + x) * LDC;
-                f32x4 acc = S[k];
-                if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
+            for (int k = 0; k < NSLOT; ++k) {
+                if (tile_ok(k)) {
+                    const int it = tile_i(k), jt = tile_j(k);
+                    f32x4 acc = S[k];
+                    if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
-                for (int cs = 0; cs < SH::CSTEPS; ++cs) {
-                    typename O::frag af, bfr;
-                    if constexpr (SH::BF && C % 32 != 0) {
-                        const bool in = 32 * cs + 8 * grp < C;
-                        af = in ? O::contig(arow, cs, grp) : O::zero();
-                        bfr = in ? O::contig(brow, cs, grp) : O::zero();
-                    } else {
-                        af = O::contig(arow, cs, grp);
-                        bfr = O::contig(brow, cs, grp);
-                    }
-                    acc = O::mma(af, bfr, acc);
+                    for (int cs = 0; cs < SH::CSTEPS; ++cs)
+                        acc = O::mma(frag_t(KT, 16 * it + x, cs), frag_t(VT, 16 * jt + x, cs), acc);
+                    if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
+                    S[k] = acc;
                 }
-                if constexpr (GATE == kGateKeydim) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] *= sEG[buf][16 * it + 4 * grp + r];
-                }
-                S[k] = acc;
             }
         }
         write_state(par ^ 1);
@@ -482,35 +610,34 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 
     // ---------------- pipeline ---------------------------------------------------------
     // The two roles run separate loops (so their registers are not live at the same
-    // time) that meet at the same number of barriers: 1 + nchunks with two buffers,
-    // 2 * nchunks with one.
+    // time) that meet at the same number of barriers.  With two buffers both run
+    // 1 + 2*npairs barriers over chunk pairs; producers always request and prepare
+    // (rows are clamped into range, surplus operands are never read), so the loop has
+    // no branch around its global loads.  With one buffer: 2 * nchunks barriers.
     if (producer) {
         if constexpr (NBUF == 2) {
+            const int npairs = (nchunks + 1) / 2;
             // operands one chunk ahead of the consumers, raw rows two chunks ahead
             if (nchunks > 0) {
                 load_raw(R[0], 0);
-                if (nchunks > 1) load_raw(R[1], C);
+                load_raw(R[1], C);
                 produce(R[0], 0, 0);
-                if (nchunks > 2) load_raw(R[0], 2 * C);
+                load_raw(R[0], 2 * C);
             }
             lds_barrier();
-            auto step = [&](auto pi, int n) __attribute__((always_inline)) {
-                constexpr int PI = decltype(pi)::value;        // n % 2
-                if (n + 1 < nchunks) {
-                    produce(R[1 - PI], (n + 1) * C, 1 - PI);
-                    if (n + 3 < nchunks) load_raw(R[1 - PI], (n + 3) * C);
-                }
+            for (int n = 0; n < 2 * npairs; n += 2) {
+                produce(R[1], (n + 1) * C, 1);
+                load_raw(R[1], (n + 3) * C);
                 lds_barrier();
-            };
-            for (int n = 0; n < nchunks; n += 2) {
-                step(std::integral_constant<int, 0>{}, n);
-                if (n + 1 < nchunks) step(std::integral_constant<int, 1>{}, n + 1);
+                produce(R[0], (n + 2) * C, 0);
+                load_raw(R[0], (n + 4) * C);
+                lds_barrier();
             }
         } else {
             if (nchunks > 0) load_raw(R[0], 0);
             for (int n = 0; n < nchunks; ++n) {
                 produce(R[0], n * C, 0);
-                if (n + 1 < nchunks) load_raw(R[0], (n + 1) * C);
+                load_raw(R[0], (n + 1) * C);
                 lds_barrier();
                 lds_barrier();
             }
@@ -518,9 +645,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     } else {
         write_state(0);
         if constexpr (NBUF == 2) {
+            const int npairs = (nchunks + 1) / 2;
             lds_barrier();
-            for (int n = 0; n < nchunks; ++n) {
-                consume(n * C, n & 1, n & 1);
+            for (int n = 0; n < 2 * npairs; ++n) {
+                if (n < nchunks) consume(n * C, n & 1, n & 1);
                 lds_barrier();
             }
         } else {
@@ -533,9 +661,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         if (a.s_final) {
 #pragma unroll
             for (int k = 0; k < NSLOT; ++k) {
-                const int u = k * NC + c;
-                if (u < NU) {
-                    const int it = u % NKB, jt = u / NKB;
+                if (tile_ok(k)) {
+                    const int it = tile_i(k), jt = tile_j(k);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = 16 * it + 4 * grp + r;
