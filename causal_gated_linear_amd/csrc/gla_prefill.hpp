@@ -24,7 +24,9 @@
 //       q and k (8 bf16 columns) for RPS consecutive rows, so loads read whole row
 //       pieces; it sums the gates of its rows serially and finishes the cumulative
 //       sum with a cross-lane scan; Q~ and K^ are written row-major, K^ (scalar
-//       gate: K~) and V transposed.  Raw rows are requested two chunks ahead.
+//       gate: K~) and V transposed.  Raw rows are requested two chunks ahead, and
+//       each part of a lane's raw registers (gates, q and k, v) is requested again
+//       as soon as it has been consumed, so the loads overlap the arithmetic.
 //   consumers (NC waves)  hold the fp32 state slice S[d_k][DVT] in accumulator
 //       registers (16x16 tiles) and, for the 16-row block of the chunk they own,
 //       compute the score tiles P^T[s-block <= tb][tb] in registers and
@@ -270,7 +272,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     };
     Raw R[NBUF];
 
-    // Raw rows of the chunk starting at t0 (gates, q and k, v).
+    // Raw rows of the chunk starting at t0, requested in three parts so that each
+    // part of a register set can be refilled as soon as it has been consumed.
     auto load_g = [&](Raw &r_, int t0) __attribute__((always_inline)) {
         if (gate_lane) {
 #pragma unroll
@@ -324,8 +327,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         }
     };
 
-    // Turn the raw rows of the chunk starting at t0 into the operands of buffer `buf`.
-    auto produce = [&](Raw &r_, int t0, int buf) __attribute__((always_inline)) {
+    // Turn the raw rows of the chunk starting at t0 into the operands of buffer `buf`,
+    // refilling each part of the register set with the rows of the chunk at t_next
+    // as soon as that part has been consumed.
+    auto produce = [&](Raw &r_, int t0, int buf, int t_next) __attribute__((always_inline)) {
         // Rows past L (ragged tail) carry no gate and no value; their q, k are finite
         // copies of the last row.  Masked arithmetically, not by a branch, so the wait
         // for this chunk's loads does not also wait for the rows requested after it.
@@ -356,6 +361,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                         bc[r][e] = run[e];
                     }
                 }
+                load_g(r_, t_next);                // gates consumed: refill them now
 #pragma unroll
                 for (int e = 0; e < NE; ++e) {
                     const float incl = group_scan<RSEG, SH::CG>(run[e], rs);
@@ -408,6 +414,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                 *(VC *)(sQ[buf] + SH::rk(t, ic)) = qv;
                 *(VC *)(sK[buf] + SH::rk(t, ic)) = kv;
             }
+            load_qk(r_, t_next);                   // q, k consumed: refill them now
 #pragma unroll
             for (int e = 0; e < CE; ++e) write_t(sKT[buf], ic + e, rs * RPS, ktv[e]);
             if (rs == 0) {
@@ -423,6 +430,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vv[e][r] = r_.v[r][e];
             }
+            load_v(r_, t_next);                    // v consumed: refill it now
 #pragma unroll
             for (int e = 0; e < 4; ++e) write_t(sVT[buf], 4 * cgv + e, rgv * RV, vv[e]);
         }
@@ -621,23 +629,19 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
             if (nchunks > 0) {
                 load_raw(R[0], 0);
                 load_raw(R[1], C);
-                produce(R[0], 0, 0);
-                load_raw(R[0], 2 * C);
+                produce(R[0], 0, 0, 2 * C);
             }
             lds_barrier();
             for (int n = 0; n < 2 * npairs; n += 2) {
-                produce(R[1], (n + 1) * C, 1);
-                load_raw(R[1], (n + 3) * C);
+                produce(R[1], (n + 1) * C, 1, (n + 3) * C);
                 lds_barrier();
-                produce(R[0], (n + 2) * C, 0);
-                load_raw(R[0], (n + 4) * C);
+                produce(R[0], (n + 2) * C, 0, (n + 4) * C);
                 lds_barrier();
             }
         } else {
             if (nchunks > 0) load_raw(R[0], 0);
             for (int n = 0; n < nchunks; ++n) {
-                produce(R[0], n * C, 0);
-                load_raw(R[0], (n + 1) * C);
+                produce(R[0], n * C, 0, (n + 1) * C);
                 lds_barrier();
                 lds_barrier();
             }
