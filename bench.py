@@ -9,12 +9,23 @@ gla_decode_step calls), and the fp64 CPU oracle on a bounded sample of the prefi
 workload.
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Profiling helpers (same file, so every profile command runs committed code only):
+  --copy-kernel                 run only a plain device copy of known size (the
+                                calibration kernel for the HBM byte counters)
+  --summarize-stats DIR         turn a rocprofv3 --kernel-trace --stats run into a text
+                                summary under profiles/
+  --summarize-traffic F W CF CW turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE
+                                of the prefill, then of the copy kernel) into the traffic
+                                summary that the JSON line's roofline.traffic reads
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -26,6 +37,14 @@ if ROOT not in sys.path:
 METRIC = "GLA prefill tokens/s + % MFMA peak (L=4096,d=128); decode tok/s + HBM GB/s"
 HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E, GB/s (datasheet)
 BF16_MFMA_PEAK_TFLOPS = 2516.6        # dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_KERNEL = "prefill_kernel"
+PREFILL_SOURCES = ("gla_prefill.hpp", "gla_prefill_inst.hip", "gla_device.hpp", "gla_launch.hpp")
+TRAFFIC_FILE = os.path.join(PROFILES, "prefill_kernel_bf16_dk128_L4096_traffic.txt")
+STATS_FILE = os.path.join(PROFILES, "prefill_decode_kernels_L4096_kernel_stats.txt")
+COPY_MIB = 512                        # calibration copy: reads and writes this many MiB
 
 
 def prefill_bytes(B, H, L, dk, dv, es=2, gate="keydim"):
@@ -114,6 +133,160 @@ def run_decode(args, torch, api, inputs):
     return dict(w=w, steps=T, ms_per_step=per, bytes=nbytes)
 
 
+def kernel_source_hash():
+    """sha256 over the prefill kernel's sources: a traffic figure taken from counters
+    applies only while this is unchanged."""
+    h = hashlib.sha256()
+    for name in PREFILL_SOURCES:
+        with open(os.path.join(ROOT, "causal_gated_linear_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def run_copy_kernel(args, torch):
+    """A plain device copy of known size (one elementwise kernel: read n bytes, write n
+    bytes) for calibrating FETCH_SIZE / WRITE_SIZE against known traffic."""
+    n = COPY_MIB * 2**20 // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup + args.steps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "mul(src, 1.0, out=dst) fp32", "read_bytes": n * 4, "write_bytes": n * 4,
+                      "launches": args.warmup + args.steps}))
+
+
+def _counter_rows(d):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        sys.exit("no counter_collection.csv under %s" % d)
+    return rows
+
+
+def _per_dispatch(rows, kernel_substr, counter):
+    """Mean over dispatches of `counter` (KiB) for kernels whose name contains the
+    substring; values of one dispatch (one row per counter instance) are summed."""
+    per = {}
+    for r in rows:
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        sys.exit("no %s rows for kernels matching %r" % (counter, kernel_substr))
+    vals = list(per.values())
+    return sum(vals) / len(vals), len(vals), per
+
+
+def summarize_traffic(dirs, command):
+    """Traffic summary of the prefill kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by bytes / counter of the calibration copy kernel."""
+    fdir, wdir, cfdir, cwdir = dirs
+    copy_bytes = COPY_MIB * 2**20
+    cf, ncf, _ = _per_dispatch(_counter_rows(cfdir), "MulFunctor", "FETCH_SIZE")
+    cw, ncw, _ = _per_dispatch(_counter_rows(cwdir), "MulFunctor", "WRITE_SIZE")
+    ff, nf, _ = _per_dispatch(_counter_rows(fdir), PREFILL_KERNEL, "FETCH_SIZE")
+    fw, nw, _ = _per_dispatch(_counter_rows(wdir), PREFILL_KERNEL, "WRITE_SIZE")
+    kf, kw = copy_bytes / cf, copy_bytes / cw          # bytes per counter unit
+    fetch_b, write_b = ff * kf, fw * kw
+    from causal_gated_linear_amd import inputs
+    w = inputs.WORKLOADS["gla_prefill"]
+    alg = prefill_bytes(w.B, w.H, w.L, w.d_k, w.d_v)
+    lines = [
+        "# HBM traffic of the prefill kernel, bf16 d_k=d_v=128, B=8 H=16 L=4096 chunk 64, key-dim gates",
+        "# commands (run from the repository root, each a rocprofv3 --pmc pass of its own):",
+    ] + ["#   " + c for c in command.split(" ;; ")] + [
+        "# calibration: copy kernel reads and writes %d bytes per launch" % copy_bytes,
+        "copy_FETCH_SIZE_KiB_per_dispatch: %.1f  (%d dispatches)" % (cf, ncf),
+        "copy_WRITE_SIZE_KiB_per_dispatch: %.1f  (%d dispatches)" % (cw, ncw),
+        "fetch_scale_bytes_per_unit: %.2f" % kf,
+        "write_scale_bytes_per_unit: %.2f" % kw,
+        "prefill_FETCH_SIZE_KiB_per_dispatch: %.1f  (%d dispatches)" % (ff, nf),
+        "prefill_WRITE_SIZE_KiB_per_dispatch: %.1f  (%d dispatches)" % (fw, nw),
+        "fetch_bytes_per_launch: %.0f" % fetch_b,
+        "write_bytes_per_launch: %.0f" % write_b,
+        "traffic_bytes_per_launch: %.0f" % (fetch_b + write_b),
+        "algorithmic_bytes_per_launch: %d" % alg,
+        "traffic_over_algorithmic: %.3f" % ((fetch_b + write_b) / alg),
+        "kernel_source_sha256: %s" % kernel_source_hash(),
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _demangle(name):
+    import subprocess
+    try:
+        out = subprocess.run(["c++filt"], input=name, capture_output=True, text=True, timeout=10).stdout.strip()
+        return out or name
+    except (OSError, subprocess.SubprocessError):
+        return name
+
+
+def summarize_stats(d, command):
+    """Text summary of a rocprofv3 --kernel-trace --stats run: rocprofv3's own per-kernel
+    statistics for the GLA kernels, then the kernel trace grouped by (kernel, grid size),
+    i.e. by workload, with the mean over all dispatches and over all but the first."""
+    def find(pattern):
+        files = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+        if not files:
+            sys.exit("no %s under %s" % (pattern, d))
+        with open(files[0]) as fh:
+            return list(csv.DictReader(fh))
+    stats, trace = find("*kernel_stats.csv"), find("*kernel_trace.csv")
+    lines = ["# rocprofv3 kernel statistics of the GLA kernels (kernel trace) for the bench.py workloads",
+             "#   prefill: B=8 H=16 L=4096 d_k=d_v=128 chunk 64, bf16, key-dim gates (grid 256)",
+             "#   decode:  B=256 H=32 d=128 bf16, fp32 state; its state comes from a 512-token prefill "
+             "(prefill grid 16384)",
+             "# kernel names are mangled: prefill_kernel<T, d_k, chunk, value-column tile, gate, elu1>,",
+             "#   DF16b = bf16, gate 1 = key-dim; decode_kernel<T, d_k, d_v>",
+             "# command (from the repository root, REPO = its absolute path):", "#   " + command, "",
+             "## rocprofv3 stats (all dispatches, warm-up included)",
+             "%-8s %14s %12s %12s %12s  %s" % ("calls", "total_ns", "avg_ns", "min_ns", "max_ns", "kernel")]
+    for r in stats:
+        if "gla::" in _demangle(r["Name"]) or r["Name"].startswith("_ZN3gla"):
+            lines.append("%-8s %14.0f %12.0f %12.0f %12.0f  %s" % (
+                r["Calls"], float(r["TotalDurationNs"]), float(r["AverageNs"]), float(r["MinNs"]),
+                float(r["MaxNs"]), _demangle(r["Name"])))
+    groups = {}
+    for r in trace:
+        if not r["Kernel_Name"].startswith("_ZN3gla") and "gla::" not in r["Kernel_Name"]:
+            continue
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines += ["", "## kernel trace by workload (duration per dispatch, ns)",
+              "%-8s %-8s %12s %12s %12s  %s" % ("grid", "calls", "mean", "mean_2nd+", "median", "kernel")]
+    for (name, grid), ds in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+        rest = ds[1:] or ds
+        med = sorted(ds)[len(ds) // 2]
+        lines.append("%-8d %-8d %12.0f %12.0f %12.0f  %s" % (grid, len(ds), sum(ds) / len(ds),
+                                                          sum(rest) / len(rest), med, _demangle(name)))
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(STATS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(pf, budget_s):
     """The fp64 oracle, unchanged, on a sample of the prefill workload's heads (same
     input bits), sized to roughly ``budget_s`` seconds on this host's cores."""
@@ -134,12 +307,15 @@ def cpu_baseline(pf, budget_s):
     n = int(min(len(heads_all), max(len(probe), len(probe) * budget_s / max(t_probe, 1e-3))))
     n = max(threads, n // threads * threads) if n >= threads else n
     heads = heads_all[:n]
-    t = run(heads)
-    tok_s = n * w.L / w.H / t                            # full-workload tokens (B*L) per second
+    reps, t = 0, 0.0
+    while reps == 0 or t < 0.5 * budget_s:               # repeat a sample that is quick
+        t += run(heads)
+        reps += 1
+    tok_s = reps * n * w.L / w.H / t                     # full-workload tokens (B*L) per second
     return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d heads of the prefill workload (L=%d, d=%d, key-dim gates), fp64 "
+            "sample": "%d of %d heads of the prefill workload (L=%d, d=%d, key-dim gates) x %d runs, fp64 "
                       "token recurrence, %.1f s; tokens/s scaled as heads/H" % (n, len(heads_all), w.L,
-                                                                               w.d_k, t)}
+                                                                               w.d_k, reps, t)}
 
 
 def main():
@@ -151,7 +327,15 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-kernel", action="store_true")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--command", default="", help="profile command recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(args.summarize_stats, args.command)
+    if args.summarize_traffic:
+        return summarize_traffic(args.summarize_traffic, args.command)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the GLA kernels here are single-GPU "
               "(heads and batch shard across GPUs with no communication; see the design "
@@ -162,6 +346,8 @@ def main():
     from causal_gated_linear_amd import api, inputs
 
     torch.cuda.set_device(0)
+    if args.copy_kernel:
+        return run_copy_kernel(args, torch)
     pf = run_prefill(args, torch, api, inputs)
     w = pf["w"]
     per_s = pf["ms_per_step"] / 1e3
@@ -186,8 +372,8 @@ def main():
                    "B": w.B, "H": w.H, "L": w.L, "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk,
                    "gate": "keydim"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gla::prefill_kernel<bf16,128,64,4>",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": stored_traffic(),
+                     "kernel": "gla::prefill_kernel (bf16, d_k 128, chunk 64, key-dim gate)",
                      "bytes_per_launch": pf["bytes"]},
         "mfma": {"tflops": tflops, "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
                  "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": pf["flops"],
