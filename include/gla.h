@@ -34,7 +34,13 @@
  *    key-dim gates g: [B][H][L][d_k]; scalar gates g: [B][H][L]; states s0,
  *    s_final, state: [B][H][d_k][d_v], always fp32; gates always fp32 natural-log
  *    values g = log(alpha), finite and <= 0 (outside that domain results are
- *    undefined; the library does not scan device data to check it).
+ *    undefined; the library does not scan device data to check it).  Key-dim
+ *    gates in gla_prefill_chunked: the chunkwise form scales keys by
+ *    exp(-(sum of the chunk's log-gates up to that token)), so results are exact up
+ *    to rounding while, in every key dimension, the log-gates summed over any one
+ *    chunk stay above about -80 (chunk 64: a mean log-gate above -1.25); stronger
+ *    gates need a smaller chunk.  Scalar gates and gla_decode_step have no such
+ *    limit.
  *  - q, k, v and o share one dtype (GLA_F32 or GLA_BF16); bf16 results are rounded
  *    to nearest even.  Arithmetic: fp32 accumulation and fp32 state; with bf16
  *    inputs the matrix-core operands are bf16.
