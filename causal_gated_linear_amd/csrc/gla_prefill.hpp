@@ -23,30 +23,29 @@
 //       each owns DK/NP key columns of all C rows; a lane holds one 16-byte piece of
 //       q and k (8 bf16 columns) for RPS consecutive rows, so loads read whole row
 //       pieces; it sums the gates of its rows serially and finishes the cumulative
-//       sum with a cross-lane scan; Q~ and K^ are written row-major, K^ (scalar
-//       gate: K~) and V transposed.  Raw rows are requested two chunks ahead, and
-//       each part of a lane's raw registers (gates, q and k, v) is requested again
-//       as soon as it has been consumed, so the loads overlap the arithmetic.
+//       sum with a cross-lane scan; Q~ and K^ (scalar gate: also K~) are written
+//       row-major, and V rows are copied as they are.  Raw rows are requested two
+//       chunks ahead, and each part of a lane's raw registers (gates, q and k, v) is
+//       requested again as soon as it has been consumed, so the loads overlap the
+//       arithmetic.
 //   consumers (NC waves)  hold the fp32 state slice S[d_k][DVT] in accumulator
 //       registers (16x16 tiles) and, for the 16-row block of the chunk they own,
 //       compute the score tiles P^T[s-block <= tb][tb] in registers and
 //       O^T = S^T Q~^T + V^T P^T per 16-column value tile; the output block goes
 //       through a private LDS staging area so it is stored with 16-byte row-contiguous
-//       writes; then S += K^^T V and the gate decay.  The state is shared between
-//       consumers as a bf16 operand copy in LDS.
+//       writes; then S += K^^T V and the gate decay.  The products that contract over
+//       tokens (V^T P^T, K^^T V) read their operands from the row-major arrays with
+//       transposing LDS reads.  The state is shared between consumers as a bf16
+//       operand copy in LDS.
 // With two LDS operand buffers the producers prepare chunk n+1 while the consumers
 // compute chunk n (one barrier per chunk); where two buffers do not fit in LDS the
 // phases alternate on one buffer.  Barriers wait only for LDS traffic, so requested
 // global rows stay in flight.  bf16 inputs use bf16 MFMA operands with fp32
 // accumulation; fp32 inputs use fp32 MFMA.
 //
-// LDS layout: every operand fragment is one 16-byte read.  Rows are not padded;
-// instead the 16-byte chunks of a row are XOR-swizzled by (row mod 8), so the 8 rows
-// a fragment read touches per cycle, and the producers' writes, spread over all
-// banks.  Transposed arrays (K^T, V^T, rows of length C) also store the token index s
-// of each 32-token block permuted so the 8 values a lane feeds to one bf16 MFMA step
-// in the accumulator-compatible order (s = 4g..4g+3 and 16+4g..16+4g+3 of the block
-// for lane group g) are contiguous.
+// LDS layout: operand rows are not padded; the 16-byte chunks of a row are
+// XOR-swizzled by (row mod 8), so the rows that one fragment read touches, and the
+// producers' writes, spread over all banks.
 #pragma once
 
 #include <type_traits>
@@ -132,9 +131,8 @@ struct PrefillShape {
     static constexpr int SW = Op<T>::W;            // contraction width per MFMA step
     static constexpr int KSTEPS = (DK + SW - 1) / SW;
     static constexpr int CSTEPS = (C + SW - 1) / SW;
-    static constexpr int KCH = DK / CE, TCH = C / CE, VCH = DVT / CE;   // chunks per row
-    static constexpr int SWK = cmin(KCH, 8) - 1, SWT = cmin(TCH, 8) - 1, SWV = cmin(VCH, 8) - 1;
-    static constexpr bool PERM = BF && C % 32 == 0;       // permuted token order
+    static constexpr int KCH = DK / CE, VCH = DVT / CE;   // 16-byte chunks per row
+    static constexpr int SWK = cmin(KCH, 8) - 1, SWV = cmin(VCH, 8) - 1;
     // producer gate mapping: producer p owns key columns [p*CW, (p+1)*CW); a lane
     // has column group cg (one 16-byte chunk, CE columns) and row segment rs (RPS
     // consecutive rows); column groups vary fastest across lanes
@@ -142,10 +140,10 @@ struct PrefillShape {
     static constexpr int CG = CW / CE;
     static constexpr int RSEG = cmin(64 / CG, C);
     static constexpr int RPS = C / RSEG;
-    // producer value mapping: 64*NP lanes cover C x DVT, a lane 4 columns x RV rows
-    static constexpr int CGV = DVT / 4;
-    static constexpr int RGV = cmin(64 * NP / CGV, C);
-    static constexpr int RV = C / RGV;
+    // producer value mapping: the C x VCH 16-byte pieces of a chunk's value tile are
+    // dealt to the 64*NP producer lanes in order, NVL per lane
+    static constexpr int NVP = C * VCH;
+    static constexpr int NVL = NVP >= 64 * NP ? NVP / (64 * NP) : 1;
     // consumer state tiles: with NKB % NC == 0 consumer c owns i-tiles c + NC*a
     // (a < IPC) for every j-tile, so its fragments are shared across tiles;
     // otherwise tiles are dealt round-robin
@@ -159,8 +157,9 @@ struct PrefillShape {
     static constexpr int NBUF = prefill_nbuf((int)sizeof(T), DK, C, DVT);
     static_assert(NBUF >= 1, "LDS budget");
     static_assert(CW >= CE && CW % CE == 0 && 64 % CG == 0, "producer gate mapping");
-    static_assert((64 * NP) % CGV == 0, "producer value mapping");
-    static_assert(RPS >= 1 && RV >= 1, "rows per lane");
+    static_assert(NVP < 64 * NP || NVP % (64 * NP) == 0, "producer value mapping");
+    static_assert(RPS >= 1, "rows per lane");
+    static_assert(16 % CG == 0, "gate scan: column groups per 16-lane row");
 
     // element offset of (row, col) in a row-major array of rows of `len` elements
     // whose 16-byte chunks are swizzled by (row & sw)
@@ -169,16 +168,7 @@ struct PrefillShape {
         return row * len + (((col / CE) ^ (row & sw)) * CE) + col % CE;
     }
     static __device__ __forceinline__ int rk(int row, int col) { return sw_off(row, col, DK, SWK); }
-    static __device__ __forceinline__ int rt(int row, int pos) { return sw_off(row, pos, C, SWT); }
     static __device__ __forceinline__ int rv(int row, int col) { return sw_off(row, col, DVT, SWV); }
-    // position of token s in a transposed row (length C) before the chunk swizzle
-    static __device__ __forceinline__ int tpos(int s)
-    {
-        if constexpr (!PERM) return s;
-        const int b = s & 31;
-        const int hi = b >> 4, q4 = (b >> 2) & 3;
-        return (s & ~31) + 8 * q4 + 4 * hi + (b & 3);
-    }
 };
 
 // Calls fn(std::integral_constant<int, I>) for I = 0 .. N-1.
@@ -194,24 +184,46 @@ __device__ __forceinline__ void static_for(Fn &&fn)
 }
 
 // Inclusive scan of v over the RSEG lanes of a segment group: the lanes
-// rs * STRIDE + cg (rs = 0 .. RSEG-1) for a fixed cg, in order of rs.
-template <int RSEG, int STRIDE, int OFF = 1>
-__device__ __forceinline__ float group_scan(float v, int rs)
+// rs * STRIDE + cg (rs = 0 .. RSEG-1, STRIDE divides 16) for a fixed cg, in order of
+// rs.  Inside each 16-lane row the segments are scanned with DPP row shifts (a
+// source outside the row reads 0, which is exactly the row-local scan); the rows are
+// then combined by adding the running total at the last segment of earlier rows.
+template <int DPPSHIFT>
+__device__ __forceinline__ float row_shr(float v)
 {
-    if constexpr (OFF >= RSEG) {
-        return v;
-    } else {
-        float up;
-        if constexpr (OFF * STRIDE < 16 && 16 % (RSEG * STRIDE) == 0) {
-            // the whole group lies in one 16-lane row: DPP row_shr stays inside it
-            up = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                               0, __builtin_bit_cast(int, v), 0x110 + OFF * STRIDE, 0xf, 0xf, false));
-        } else {
-            up = __shfl_up(v, OFF * STRIDE, 64);
-        }
-        v += rs >= OFF ? up : 0.f;
-        return group_scan<RSEG, STRIDE, 2 * OFF>(v, rs);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                  0x110 + DPPSHIFT, 0xf, 0xf, true));
+}
+template <int RSEG, int STRIDE>
+__device__ __forceinline__ float group_scan(float v, int lane)
+{
+    constexpr int SPR = 16 / STRIDE;                   // segments per 16-lane row
+    constexpr int NR = (RSEG * STRIDE + 15) / 16;      // rows of the group
+    if constexpr (SPR > 1) v += row_shr<STRIDE>(v);
+    if constexpr (SPR > 2) v += row_shr<2 * STRIDE>(v);
+    if constexpr (SPR > 4) v += row_shr<4 * STRIDE>(v);
+    if constexpr (SPR > 8) v += row_shr<8 * STRIDE>(v);
+    const int row = lane >> 4, last = 16 - STRIDE + (lane & (STRIDE - 1));
+    if constexpr (NR > 1) {
+        const float up = __shfl(v, 16 * (row - 1) + last, 64);
+        v += row >= 1 ? up : 0.f;
     }
+    if constexpr (NR > 2) {
+        const float up = __shfl(v, 16 * (row - 2) + last, 64);
+        v += row >= 2 ? up : 0.f;
+    }
+    return v;
+}
+
+// Transposed operand reads from row-major LDS arrays (rows = tokens s, columns =
+// i or j), for the products that contract over tokens.  One ds_read_b64_tr_b16
+// serves a 16-lane group: lane l of the group gives the address of row s0 + l/4,
+// columns n0 + 4(l%4) .. +3, and receives column n0 + l of rows s0 .. s0+3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16 *p)
+{
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)(p));
+    return __builtin_bit_cast(bf16x4, r);
 }
 
 template <typename T, int DK, int C, int DVT, int GATE, bool ELU1>
@@ -225,12 +237,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     constexpr int NP = SH::NP, NC = SH::NC, NBUF = SH::NBUF, CE = SH::CE;
     constexpr int NTB = SH::NTB, NKB = SH::NKB, NJT = SH::NJT;
     constexpr int CW = SH::CW, RSEG = SH::RSEG, RPS = SH::RPS;
-    constexpr int CGV = SH::CGV, RGV = SH::RGV, RV = SH::RV, NSLOT = SH::NSLOT, NU = SH::NU;
+    constexpr int NVL = SH::NVL, NSLOT = SH::NSLOT, NU = SH::NU;
+    constexpr bool KU = GATE == kGateScalar;        // separate K~ operand for the state
 
     __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * DK];      // Q~ [t][i]
     __shared__ __attribute__((aligned(16))) T sK[NBUF][C * DK];      // K^ [s][i]
-    __shared__ __attribute__((aligned(16))) T sKT[NBUF][DK * C];     // K^ (scalar: K~) [i][pos(s)]
-    __shared__ __attribute__((aligned(16))) T sVT[NBUF][DVT * C];    // V^T [j][pos(s)]
+    __shared__ __attribute__((aligned(16))) T sKU[KU ? NBUF : 1][KU ? C * DK : CE];  // scalar: K~ [s][i]
+    __shared__ __attribute__((aligned(16))) T sV[NBUF][C * DVT];     // V [s][j]
     __shared__ __attribute__((aligned(16))) T sS[2][DVT * DK];       // state^T [j][i], by parity
     __shared__ __attribute__((aligned(16))) T sO[NC][16 * DVT];      // output staging, per consumer
     __shared__ __attribute__((aligned(16))) float sEG[NBUF][DK];     // exp(Gamma_i)
@@ -262,23 +275,23 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     // known at compile time so that no branch surrounds the loads)
     const bool gate_lane = (SH::CG * RSEG == 64) || rs < RSEG;
     const int ic = p * CW + CE * cg;               // first of this lane's CE key columns
-    const int cgv = tid % CGV, rgv = tid / CGV;
-    const bool v_lane = (CGV * RGV == 64 * NP) || rgv < RGV;
+    const bool v_lane = SH::NVP >= 64 * NP || tid < SH::NVP;
 
     struct Raw {
         VC q[RPS], k[RPS];
         f32x4 g[RPS][CE / 4];
-        V4 v[RV];
+        VC v[NVL];
     };
     Raw R[NBUF];
 
     // Raw rows of the chunk starting at t0, requested in three parts so that each
-    // part of a register set can be refilled as soon as it has been consumed.
+    // part of a register set can be refilled as soon as it has been consumed.  Rows
+    // past L are clamped to row L-1, so every load is in bounds.
     auto load_g = [&](Raw &r_, int t0) __attribute__((always_inline)) {
         if (gate_lane) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
-                const int row = min(t0 + rs * RPS + r, L - 1);   // clamp: always in bounds
+                const int row = min(t0 + rs * RPS + r, L - 1);
                 if constexpr (GATE == kGateKeydim) {
 #pragma unroll
                     for (int h = 0; h < CE / 4; ++h) r_.g[r][h] = *(const f32x4 *)(gk + (size_t)row * DK + ic + 4 * h);
@@ -302,9 +315,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     auto load_v = [&](Raw &r_, int t0) __attribute__((always_inline)) {
         if (v_lane) {
 #pragma unroll
-            for (int r = 0; r < RV; ++r) {
-                const int row = min(t0 + rgv * RV + r, L - 1);
-                r_.v[r] = *(const V4 *)(vh + (size_t)row * DV + 4 * cgv);
+            for (int h = 0; h < NVL; ++h) {
+                const int id = tid + 64 * NP * h;
+                const int row = min(t0 + id / SH::VCH, L - 1);
+                r_.v[h] = *(const VC *)(vh + (size_t)row * DV + (id % SH::VCH) * CE);
             }
         }
     };
@@ -314,35 +328,26 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         load_v(r_, t0);
     };
 
-    // Store N consecutive transposed values (tokens s0..s0+N-1, s0 % N == 0) of row `row`.
-    auto write_t = [&](T *base, int row, int s0, const auto &vals) __attribute__((always_inline)) {
-        constexpr int N = sizeof(vals) / sizeof(vals[0]);
-        if constexpr (SH::PERM && N % 4 == 0) {
-#pragma unroll
-            for (int j = 0; j < N; j += 4)         // runs of 4 tokens stay in one chunk
-                *(bf16x4 *)(base + SH::rt(row, SH::tpos(s0 + j))) = bf16x4{vals[j], vals[j + 1], vals[j + 2], vals[j + 3]};
-        } else {
-#pragma unroll
-            for (int j = 0; j < N; ++j) base[SH::rt(row, SH::tpos(s0 + j))] = vals[j];
-        }
-    };
-
     // Turn the raw rows of the chunk starting at t0 into the operands of buffer `buf`,
     // refilling each part of the register set with the rows of the chunk at t_next
     // as soon as that part has been consumed.
     auto produce = [&](Raw &r_, int t0, int buf, int t_next) __attribute__((always_inline)) {
-        // Rows past L (ragged tail) carry no gate and no value; their q, k are finite
-        // copies of the last row.  Masked arithmetically, not by a branch, so the wait
-        // for this chunk's loads does not also wait for the rows requested after it.
+        // Rows past L (ragged tail, wave-uniform test) carry no gate, and their keys are
+        // zeroed in LDS below, so they add nothing to the state; their q, k, v are
+        // finite copies of row L-1 and their outputs are never stored.
         const int nvalid = min(L - t0, C);
-#pragma unroll
-        for (int r = 0; r < RV; ++r) {
-            const float keep = rgv * RV + r < nvalid ? 1.f : 0.f;            // v is finite
-            const V4 v = r_.v[r];
-            r_.v[r] = V4{from_f32<T>((float)v[0] * keep), from_f32<T>((float)v[1] * keep),
-                         from_f32<T>((float)v[2] * keep), from_f32<T>((float)v[3] * keep)};
-        }
         if (gate_lane) {
+            if constexpr (GATE != kGateNone) {
+                if (nvalid < C) {
+#pragma unroll
+                    for (int r = 0; r < RPS; ++r) {
+                        if (rs * RPS + r >= nvalid) {
+#pragma unroll
+                            for (int h = 0; h < CE / 4; ++h) r_.g[r][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
+                }
+            }
             float bc[RPS][CE];
             float excl[CE], tot[CE];
 #pragma unroll
@@ -354,17 +359,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                 for (int e = 0; e < NE; ++e) run[e] = 0.f;
 #pragma unroll
                 for (int r = 0; r < RPS; ++r) {
-                    const float keep = rs * RPS + r < nvalid ? 1.f : 0.f;   // g is finite
 #pragma unroll
                     for (int e = 0; e < NE; ++e) {
-                        run[e] += r_.g[r][e / 4][e % 4] * keep;
+                        run[e] += r_.g[r][e / 4][e % 4];
                         bc[r][e] = run[e];
                     }
                 }
                 load_g(r_, t_next);                // gates consumed: refill them now
 #pragma unroll
                 for (int e = 0; e < NE; ++e) {
-                    const float incl = group_scan<RSEG, SH::CG>(run[e], rs);
+                    const float incl = group_scan<RSEG, SH::CG>(run[e], lane);
                     excl[e] = incl - run[e];
                     tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64) * kLog2e;
                 }
@@ -377,11 +381,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                         for (int e = 1; e < CE; ++e) bc[r][e] = bc[r][0];
                 }
             }
-            T ktv[CE][RPS];
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
                 const int t = rs * RPS + r;
-                float q[CE], kk[CE], qt[CE], kt[CE];
+                float q[CE], kk[CE], qt[CE], kt[CE], ku[CE];
                 widen<T, CE>(r_.q[r], q);
                 widen<T, CE>(r_.k[r], kk);
 #pragma unroll
@@ -390,20 +393,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                         q[e] = feature(q[e], true);
                         kk[e] = feature(kk[e], true);
                     }
-                    float kT = kk[e];
                     qt[e] = q[e];
                     kt[e] = kk[e];
                     if constexpr (GATE == kGateKeydim) {
                         const float b = (excl[e] + bc[r][e]) * kLog2e;
                         qt[e] = q[e] * exp2_fast(b);
                         kt[e] = kk[e] * exp2_fast(-b);
-                        kT = kt[e];
                     } else if constexpr (GATE == kGateScalar) {
                         const float b = (excl[0] + bc[r][0]) * kLog2e;
-                        kT = kk[e] * exp2_fast(tot[0] - b);
+                        ku[e] = kk[e] * exp2_fast(tot[0] - b);
                         if (e == 0 && p == 0 && cg == 0) sB[buf][t] = b;
                     }
-                    ktv[e][r] = from_f32<T>(kT);
                 }
                 VC qv, kv;
 #pragma unroll
@@ -413,10 +413,23 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                 }
                 *(VC *)(sQ[buf] + SH::rk(t, ic)) = qv;
                 *(VC *)(sK[buf] + SH::rk(t, ic)) = kv;
+                if constexpr (KU) {
+                    VC uv;
+#pragma unroll
+                    for (int e = 0; e < CE; ++e) uv[e] = from_f32<T>(ku[e]);
+                    *(VC *)(sKU[buf] + SH::rk(t, ic)) = uv;
+                }
             }
             load_qk(r_, t_next);                   // q, k consumed: refill them now
+            if (nvalid < C) {                      // keys of rows past L enter no state
 #pragma unroll
-            for (int e = 0; e < CE; ++e) write_t(sKT[buf], ic + e, rs * RPS, ktv[e]);
+                for (int r = 0; r < RPS; ++r) {
+                    const int t = rs * RPS + r;
+                    T *kz = sK[buf];
+                    if constexpr (KU) kz = sKU[buf];
+                    if (t >= nvalid) *(VC *)(kz + SH::rk(t, ic)) = VC{};
+                }
+            }
             if (rs == 0) {
 #pragma unroll
                 for (int e = 0; e < CE; ++e)
@@ -424,15 +437,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
             }
         }
         if (v_lane) {
-            T vv[4][RV];
+            VC vv[NVL];
 #pragma unroll
-            for (int r = 0; r < RV; ++r) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vv[e][r] = r_.v[r][e];
-            }
+            for (int h = 0; h < NVL; ++h) vv[h] = r_.v[h];
             load_v(r_, t_next);                    // v consumed: refill it now
 #pragma unroll
-            for (int e = 0; e < 4; ++e) write_t(sVT[buf], 4 * cgv + e, rgv * RV, vv[e]);
+            for (int h = 0; h < NVL; ++h) {
+                const int id = tid + 64 * NP * h;
+                *(VC *)(sV[buf] + SH::rv(id / SH::VCH, (id % SH::VCH) * CE)) = vv[h];
+            }
         }
     };
 
@@ -486,19 +499,30 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         }
         return *(const F *)(base + SH::rk(row, col));
     };
-    // fragment k-step `ks` of a transposed row of length C (contraction over tokens)
-    auto frag_t = [&](const T *base, int row, int ks) __attribute__((always_inline)) -> F {
-        const int pos = SH::SW * ks + CE * grp;
-        if constexpr (SH::BF && C % 32 != 0) {
-            if (pos >= C) return O::zero();
+    // fragment k-step `ks` of column n0 + x of a row-major array [C][len] (swizzle sw),
+    // contracting over tokens.  bf16: a lane of group grp holds tokens 32ks + 4grp + 0..3
+    // and 32ks + 16 + 4grp + 0..3, the order in which a score accumulator tile pair
+    // feeds the next product (Op::from_acc); fp32: tokens 16ks + 4grp + 0..3.
+    auto frag_tr = [&](const T *base, int len, int sw, int n0, int ks) __attribute__((always_inline)) -> F {
+        if constexpr (SH::BF) {
+            const int col = n0 + 4 * (x & 3);
+            const int r0 = 32 * ks + 4 * grp + (x >> 2);
+            const bf16x4 lo = lds_read_tr16(base + SH::sw_off(r0, col, len, sw));
+            bf16x4 hi = {};
+            if constexpr (C % 32 == 0) hi = lds_read_tr16(base + SH::sw_off(r0 + 16, col, len, sw));
+            return F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+            F f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = base[SH::sw_off(16 * ks + 4 * grp + r, n0 + x, len, sw)];
+            return f;
         }
-        return *(const F *)(base + SH::rt(row, pos));
     };
 
     // Outputs of the 16-row block TB of the chunk starting at t0 (straight-line code:
     // TB is a compile-time constant, so every tile loop below is unrolled).
     auto out_block = [&](auto tbc, int t0, int nvalid, int buf, const T *Q, const T *K,
-                         const T *VT, const T *SS) __attribute__((always_inline)) {
+                         const T *V, const T *SS) __attribute__((always_inline)) {
         constexpr int TB = decltype(tbc)::value;
         const int t = 16 * TB + x;
         F qf[SH::KSTEPS];
@@ -537,19 +561,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
             // intra-chunk: O^T += V^T P^T over s-blocks 0..TB
             if constexpr (SH::BF) {
 #pragma unroll
-                for (int sp = 0; 2 * sp <= TB; ++sp) {
-                    F af;
-                    if constexpr (SH::PERM) {
-                        af = frag_t(VT, jrow, sp);
-                    } else {                       // C == 16: one 16-block, natural order
-                        const bf16x4 lo = *(const bf16x4 *)(VT + SH::rt(jrow, 4 * grp));
-                        af = F{lo[0], lo[1], lo[2], lo[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-                    }
-                    acc = O::mma(af, O::from_acc(pt[2 * sp], pt[2 * sp + 1]), acc);
-                }
+                for (int sp = 0; 2 * sp <= TB; ++sp)
+                    acc = O::mma(frag_tr(V, DVT, SH::SWV, 16 * jt, sp), O::from_acc(pt[2 * sp], pt[2 * sp + 1]), acc);
             } else {
 #pragma unroll
-                for (int sb = 0; sb <= TB; ++sb) acc = O::mma(frag_t(VT, jrow, sb), O::from_acc(pt[sb]), acc);
+                for (int sb = 0; sb <= TB; ++sb) acc = O::mma(frag_tr(V, DVT, SH::SWV, 16 * jt, sb), O::from_acc(pt[sb]), acc);
             }
             // lane holds O[t][16jt + 4grp + r]: stage it row-major
             *(V4 *)(stage + SH::rv(x, 16 * jt + 4 * grp)) = narrow4<T>(acc);
@@ -570,10 +586,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     // Outputs of chunk starting at t0 from operand buffer `buf`, then the state step.
     auto consume = [&](int t0, int buf, int par) __attribute__((always_inline)) {
         const int nvalid = min(L - t0, C);
-        const T *Q = sQ[buf], *K = sK[buf], *KT = sKT[buf], *VT = sVT[buf], *SS = sS[par];
+        const T *Q = sQ[buf], *K = sK[buf], *V = sV[buf], *SS = sS[par];
+        const T *KU_ = K;                          // keys of the state update
+        if constexpr (KU) KU_ = sKU[buf];
         // consumer c owns the 16-row blocks tb with tb % NC == c
         static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
-            if (decltype(tbc)::value % NC == c) out_block(tbc, t0, nvalid, buf, Q, K, VT, SS);
+            if (decltype(tbc)::value % NC == c) out_block(tbc, t0, nvalid, buf, Q, K, V, SS);
         });
         // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
         if constexpr (SH::BLOCKED) {
@@ -581,12 +599,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
             for (int ia = 0; ia < SH::IPC; ++ia)
 #pragma unroll
-                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_t(KT, 16 * (c + NC * ia) + x, cs);
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_tr(KU_, DK, SH::SWK, 16 * (c + NC * ia), cs);
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt) {
                 F bfr[SH::CSTEPS];
 #pragma unroll
-                for (int cs = 0; cs < SH::CSTEPS; ++cs) bfr[cs] = frag_t(VT, 16 * jt + x, cs);
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) bfr[cs] = frag_tr(V, DVT, SH::SWV, 16 * jt, cs);
 #pragma unroll
                 for (int ia = 0; ia < SH::IPC; ++ia) {
                     const int k = jt * SH::IPC + ia;
@@ -607,7 +625,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                     if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs)
-                        acc = O::mma(frag_t(KT, 16 * it + x, cs), frag_t(VT, 16 * jt + x, cs), acc);
+                        acc = O::mma(frag_tr(KU_, DK, SH::SWK, 16 * it, cs), frag_tr(V, DVT, SH::SWV, 16 * jt, cs), acc);
                     if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
                     S[k] = acc;
                 }
