@@ -208,6 +208,10 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
     if (st != GLA_OK) return st;
     if (!chunk_supported(chunk))
         return fail(GLA_ERR_UNSUPPORTED, "chunk=%d: must be 16, 32 or 64", chunk);
+    // the kernel addresses one head's rows (and the rows of its last chunk past L)
+    // with 32-bit byte offsets: (L + chunk) * max(d_k, d_v) * 4 must stay below 2^31
+    if ((long long)(L + chunk) * (d_k > d_v ? d_k : d_v) * 4 > 0x7fffffffLL)
+        return fail(GLA_ERR_SHAPE, "L=%d too long for one head (limit (L + chunk) * max(d_k, d_v) * 4 < 2^31)", L);
     if (L > 0 && (!q || !k || !v || !o))
         return fail(GLA_ERR_NULL, "q, k, v and o are required when L > 0");
     const void *ptrs[] = {q, k, v, s0, o, s_final, workspace};

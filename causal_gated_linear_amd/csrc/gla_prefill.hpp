@@ -44,8 +44,8 @@
 // accumulation; fp32 inputs use fp32 MFMA.
 //
 // LDS layout: operand rows are not padded; the 16-byte chunks of a row are
-// XOR-swizzled by (row mod 8), so the rows that one fragment read touches, and the
-// producers' writes, spread over all banks.
+// XOR-swizzled by a permutation of (row mod 8), so the rows that one fragment read or
+// one transposing read touches, and the producers' writes, spread over all banks.
 #pragma once
 
 #include <type_traits>
@@ -162,10 +162,18 @@ struct PrefillShape {
     static_assert(16 % CG == 0, "gate scan: column groups per 16-lane row");
 
     // element offset of (row, col) in a row-major array of rows of `len` elements
-    // whose 16-byte chunks are swizzled by (row & sw)
+    // whose 16-byte chunks are XOR-swizzled by a function of the row.  Rows of at
+    // least 8 chunks use the row bits rotated, (row & 3) << 1 | (row >> 2) & 1: any 8
+    // consecutive rows still get 8 distinct values (16-byte fragment reads of 8 rows
+    // hit all banks), and any 4 rows 4k..4k+3 get distinct 32-byte pairs (transposing
+    // reads of 4 rows x 32 bytes hit all banks).
+    static __device__ __forceinline__ int swz(int row, int sw)
+    {
+        return sw == 7 ? (((row & 3) << 1) | ((row >> 2) & 1)) : (row & sw);
+    }
     static __device__ __forceinline__ int sw_off(int row, int col, int len, int sw)
     {
-        return row * len + (((col / CE) ^ (row & sw)) * CE) + col % CE;
+        return row * len + (((col / CE) ^ swz(row, sw)) * CE) + col % CE;
     }
     static __device__ __forceinline__ int rk(int row, int col) { return sw_off(row, col, DK, SWK); }
     static __device__ __forceinline__ int rv(int row, int col) { return sw_off(row, col, DVT, SWV); }
@@ -226,6 +234,25 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16 *p)
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// Raw buffer access over `bytes` bytes from p: a load at a byte offset at or past
+// `bytes` returns zeros and touches no memory.  Rows past the end of a sequence
+// therefore read as zero q, k, v and zero log-gates.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *p, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ V buf_load16(Rsrc r, int off)
+{
+    static_assert(sizeof(V) == 16, "16-byte load");
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(Rsrc r, int off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 template <typename T, int DK, int C, int DVT, int GATE, bool ELU1>
 __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 {
@@ -260,12 +287,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     const int vt = wg - bh * a.n_vt;
     const int L = a.L, DV = a.d_v;
 
-    const T *__restrict__ qh = (const T *)a.q + (size_t)bh * L * DK;
-    const T *__restrict__ kh = (const T *)a.k + (size_t)bh * L * DK;
-    const T *__restrict__ vh = (const T *)a.v + (size_t)bh * L * DV + vt * DVT;
+    // per-head buffer views (host code guarantees each head's bytes fit in 31 bits)
+    constexpr int ES = sizeof(T);
+    const Rsrc rq = make_rsrc((const T *)a.q + (size_t)bh * L * DK, (unsigned)(L * DK * ES));
+    const Rsrc rk = make_rsrc((const T *)a.k + (size_t)bh * L * DK, (unsigned)(L * DK * ES));
+    const Rsrc rvv = make_rsrc((const T *)a.v + (size_t)bh * L * DV, (unsigned)(L * DV * ES));
     T *__restrict__ oh = (T *)a.o + (size_t)bh * L * DV + vt * DVT;
-    const float *__restrict__ gk = a.g + (size_t)bh * L * DK;   // key-dim gates
-    const float *__restrict__ gs = a.g + (size_t)bh * L;        // scalar gates
+    Rsrc rg = make_rsrc(a.g, 0u);                  // no gates: never read
+    if constexpr (GATE == kGateKeydim) rg = make_rsrc(a.g + (size_t)bh * L * DK, (unsigned)(L * DK * 4));
+    if constexpr (GATE == kGateScalar) rg = make_rsrc(a.g + (size_t)bh * L, (unsigned)(L * 4));
     const int nchunks = (L + C - 1) / C;
 
     // ---------------- producers -------------------------------------------------------
@@ -286,17 +316,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 
     // Raw rows of the chunk starting at t0, requested in three parts so that each
     // part of a register set can be refilled as soon as it has been consumed.  Rows
-    // past L are clamped to row L-1, so every load is in bounds.
+    // past L read as zeros (buffer range check), which is exactly the masking the
+    // tail chunk needs: zero log-gates leave the cumulative gate flat, zero keys and
+    // values add nothing to the state, and those rows' outputs are never stored.
+    const int qk_off = (rs * RPS) * DK * ES + ic * ES;
     auto load_g = [&](Raw &r_, int t0) __attribute__((always_inline)) {
         if (gate_lane) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
-                const int row = min(t0 + rs * RPS + r, L - 1);
                 if constexpr (GATE == kGateKeydim) {
 #pragma unroll
-                    for (int h = 0; h < CE / 4; ++h) r_.g[r][h] = *(const f32x4 *)(gk + (size_t)row * DK + ic + 4 * h);
+                    for (int h = 0; h < CE / 4; ++h)
+                        r_.g[r][h] = buf_load16<f32x4>(rg, (t0 + rs * RPS + r) * DK * 4 + (ic + 4 * h) * 4);
                 } else if constexpr (GATE == kGateScalar) {
-                    const float gv = gs[row];
+                    const float gv = buf_load4(rg, (t0 + rs * RPS + r) * 4);
                     r_.g[r][0] = f32x4{gv, gv, gv, gv};
                 }
             }
@@ -306,9 +339,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         if (gate_lane) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
-                const int row = min(t0 + rs * RPS + r, L - 1);
-                r_.q[r] = *(const VC *)(qh + (size_t)row * DK + ic);
-                r_.k[r] = *(const VC *)(kh + (size_t)row * DK + ic);
+                r_.q[r] = buf_load16<VC>(rq, qk_off + (t0 + r) * DK * ES);
+                r_.k[r] = buf_load16<VC>(rk, qk_off + (t0 + r) * DK * ES);
             }
         }
     };
@@ -317,8 +349,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
             for (int h = 0; h < NVL; ++h) {
                 const int id = tid + 64 * NP * h;
-                const int row = min(t0 + id / SH::VCH, L - 1);
-                r_.v[h] = *(const VC *)(vh + (size_t)row * DV + (id % SH::VCH) * CE);
+                r_.v[h] = buf_load16<VC>(rvv, (t0 + id / SH::VCH) * DV * ES + (vt * DVT + (id % SH::VCH) * CE) * ES);
             }
         }
     };
@@ -332,22 +363,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     // refilling each part of the register set with the rows of the chunk at t_next
     // as soon as that part has been consumed.
     auto produce = [&](Raw &r_, int t0, int buf, int t_next) __attribute__((always_inline)) {
-        // Rows past L (ragged tail, wave-uniform test) carry no gate, and their keys are
-        // zeroed in LDS below, so they add nothing to the state; their q, k, v are
-        // finite copies of row L-1 and their outputs are never stored.
-        const int nvalid = min(L - t0, C);
+        // No branch here depends on a pending load: a branch would make the compiler's
+        // wait analysis wait for every outstanding load at the join.
         if (gate_lane) {
-            if constexpr (GATE != kGateNone) {
-                if (nvalid < C) {
-#pragma unroll
-                    for (int r = 0; r < RPS; ++r) {
-                        if (rs * RPS + r >= nvalid) {
-#pragma unroll
-                            for (int h = 0; h < CE / 4; ++h) r_.g[r][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        }
-                    }
-                }
-            }
             float bc[RPS][CE];
             float excl[CE], tot[CE];
 #pragma unroll
@@ -360,8 +378,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
                 for (int r = 0; r < RPS; ++r) {
 #pragma unroll
-                    for (int e = 0; e < NE; ++e) {
-                        run[e] += r_.g[r][e / 4][e % 4];
+                    for (int e = 0; e < NE; ++e) {             // cumulative sums in log2 units
+                        run[e] += r_.g[r][e / 4][e % 4] * kLog2e;
                         bc[r][e] = run[e];
                     }
                 }
@@ -370,7 +388,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                 for (int e = 0; e < NE; ++e) {
                     const float incl = group_scan<RSEG, SH::CG>(run[e], lane);
                     excl[e] = incl - run[e];
-                    tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64) * kLog2e;
+                    tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64);
                 }
                 if constexpr (GATE == kGateScalar) {
 #pragma unroll
@@ -396,11 +414,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                     qt[e] = q[e];
                     kt[e] = kk[e];
                     if constexpr (GATE == kGateKeydim) {
-                        const float b = (excl[e] + bc[r][e]) * kLog2e;
+                        const float b = excl[e] + bc[r][e];
                         qt[e] = q[e] * exp2_fast(b);
                         kt[e] = kk[e] * exp2_fast(-b);
                     } else if constexpr (GATE == kGateScalar) {
-                        const float b = (excl[0] + bc[r][0]) * kLog2e;
+                        const float b = excl[0] + bc[r][0];
                         ku[e] = kk[e] * exp2_fast(tot[0] - b);
                         if (e == 0 && p == 0 && cg == 0) sB[buf][t] = b;
                     }
@@ -421,15 +439,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                 }
             }
             load_qk(r_, t_next);                   // q, k consumed: refill them now
-            if (nvalid < C) {                      // keys of rows past L enter no state
-#pragma unroll
-                for (int r = 0; r < RPS; ++r) {
-                    const int t = rs * RPS + r;
-                    T *kz = sK[buf];
-                    if constexpr (KU) kz = sKU[buf];
-                    if (t >= nvalid) *(VC *)(kz + SH::rk(t, ic)) = VC{};
-                }
-            }
             if (rs == 0) {
 #pragma unroll
                 for (int e = 0; e < CE; ++e)
@@ -437,15 +446,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
             }
         }
         if (v_lane) {
-            VC vv[NVL];
-#pragma unroll
-            for (int h = 0; h < NVL; ++h) vv[h] = r_.v[h];
-            load_v(r_, t_next);                    // v consumed: refill it now
+            // store first, then refill the same registers (a load issued while the old
+            // values are still live would land in other registers and need a copy,
+            // and the copy a wait for the load)
 #pragma unroll
             for (int h = 0; h < NVL; ++h) {
                 const int id = tid + 64 * NP * h;
-                *(VC *)(sV[buf] + SH::rv(id / SH::VCH, (id % SH::VCH) * CE)) = vv[h];
+                *(VC *)(sV[buf] + SH::rv(id / SH::VCH, (id % SH::VCH) * CE)) = r_.v[h];
             }
+            load_v(r_, t_next);                    // v consumed: refill it now
         }
     };
 
@@ -467,19 +476,23 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     f32x4 S[NSLOT];
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!producer && a.s0) {                       // branch-free loads, issued together
+    // initial state (consumers, inside their own branch below, so that these loads
+    // are never pending on the producers' path)
+    auto load_s0 = [&]() __attribute__((always_inline)) {
+        if (a.s0) {
 #pragma unroll
-        for (int k = 0; k < NSLOT; ++k) {
-            const bool ok = tile_ok(k);
-            const int it = ok ? tile_i(k) : 0, jt = ok ? tile_j(k) : 0;
+            for (int k = 0; k < NSLOT; ++k) {
+                const bool ok = tile_ok(k);
+                const int it = ok ? tile_i(k) : 0, jt = ok ? tile_j(k) : 0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * it + 4 * grp + r;
-                const float v = a.s0[((size_t)bh * DK + i) * DV + vt * DVT + 16 * jt + x];
-                S[k][r] = ok ? v : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * it + 4 * grp + r;
+                    const float v = a.s0[((size_t)bh * DK + i) * DV + vt * DVT + 16 * jt + x];
+                    S[k][r] = ok ? v : 0.f;
+                }
             }
         }
-    }
+    };
 
     auto write_state = [&](int par) __attribute__((always_inline)) {   // -> bf16 operand rows
 #pragma unroll
@@ -574,7 +587,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         // LDS operations of one wave complete in order)
 #pragma unroll
         for (int h = 0; h < SH::OCPL; ++h) {
-            const int chunk = lane * SH::OCPL + h;
+            const int chunk = lane + 64 * h;       // 8 lanes read one 128-byte row
             if (chunk < SH::OCH) {
                 const int row = chunk / SH::VCH, col = (chunk % SH::VCH) * CE;
                 const VC val = *(const VC *)(stage + SH::rv(row, col));
@@ -665,6 +678,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
             }
         }
     } else {
+        load_s0();
         write_state(0);
         if constexpr (NBUF == 2) {
             const int npairs = (nchunks + 1) / 2;

@@ -46,7 +46,8 @@
  *    inputs the matrix-core operands are bf16.
  *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}; chunk in {16, 32, 64};
  *    B, H >= 1; L >= 0 (L need not be a multiple of chunk; L == 0 only copies the
- *    initial state to s_final).
+ *    initial state to s_final); per head (L + chunk) * max(d_k, d_v) * 4 < 2^31
+ *    bytes (L up to about 4.19 million tokens at d = 128), else GLA_ERR_SHAPE.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
  *    stream).  Argument validation is host-only and runs before any HIP call: on
  *    any error nothing is launched and nothing is written.  Faults during

@@ -74,6 +74,7 @@ PREFILL_BAD = {
     "d_v_256": (dict(d_v=256), _lib.GLA_ERR_UNSUPPORTED),
     "chunk_128": (dict(chunk=128), _lib.GLA_ERR_UNSUPPORTED),
     "chunk_8": (dict(chunk=8), _lib.GLA_ERR_UNSUPPORTED),
+    "L_past_32bit_head_offsets": (dict(L=4194304, d_k=128, d_v=128), _lib.GLA_ERR_SHAPE),
     "dtype_7": (dict(dtype=7), _lib.GLA_ERR_UNSUPPORTED),
     "gate_5": (dict(gate=5), _lib.GLA_ERR_UNSUPPORTED),
     "phi_3": (dict(phi=3), _lib.GLA_ERR_UNSUPPORTED),
