@@ -105,6 +105,38 @@ def run_prefill(args, torch, api, inputs):
     return dict(w=w, inp=inp, ms_per_step=per, wall_s=wall, bytes=nbytes, flops=flops)
 
 
+def run_other_prefills(args, torch, api, inputs):
+    """The other prefill workloads, timed the same way (reported beside the headline;
+    fewer steps).  Bytes follow the same convention as the headline workload."""
+    out = {}
+    for name in ("linear_elu1", "scalar_long", "fp32_single_head"):
+        w = inputs.WORKLOADS[name]
+        inp = inputs.draw(w, device="cuda")
+        o = torch.empty(w.B, w.H, w.L, w.d_v, dtype=w.dtype, device="cuda")
+        s = torch.empty(w.B, w.H, w.d_k, w.d_v, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def step():
+            api.prefill(inp["q"], inp["k"], inp["v"], log_gate=inp["g"], gate=w.gate, chunk=w.chunk,
+                        feature_map=w.feature_map, out=o, final_state=s, stream=stream)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        n = max(5, args.steps // 2)
+        per = _events_ms(step, n, stream) / n
+        es = 2 if w.dtype == torch.bfloat16 else 4
+        nbytes = prefill_bytes(w.B, w.H, w.L, w.d_k, w.d_v, es=es, gate=w.gate or "none")
+        gbs = nbytes / (per / 1e3) / 1e9
+        out[name] = {"ms_per_step": per, "tokens_per_s": w.B * w.L / (per / 1e3), "GB_per_s": gbs,
+                     "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes,
+                     "shape": "B=%d H=%d L=%d d_k=%d d_v=%d chunk=%d %s gate=%s phi=%s" % (
+                         w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, str(w.dtype).replace("torch.", ""), w.gate,
+                         w.feature_map or "identity")}
+        del inp, o, s
+    return out
+
+
 def run_decode(args, torch, api, inputs):
     w = inputs.WORKLOADS["decode"]
     pre = inputs.draw(w, device="cuda")
@@ -326,6 +358,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-kernel", action="store_true")
     ap.add_argument("--summarize-stats", metavar="DIR")
@@ -388,6 +421,8 @@ def main():
                           "tokens_per_s": dc["w"].B / dper, "ms_per_step": dc["ms_per_step"],
                           "GB_per_s": dgbs, "hbm_frac": dgbs / HBM_PEAK_GBS,
                           "bytes_per_step": dc["bytes"]}
+    if not args.no_others:
+        line["other_prefill"] = run_other_prefills(args, torch, api, inputs)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget_s)
     print(json.dumps(line))
