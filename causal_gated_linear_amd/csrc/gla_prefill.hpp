@@ -123,11 +123,18 @@ struct PrefillShape {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int CE = 16 / sizeof(T);      // elements per 16-byte chunk
     static constexpr int NP = cmin(4, DK / CE);    // producer waves
-    static constexpr int NC = 4;                   // consumer waves
-    static constexpr int NT = 64 * (NP + NC);
     static constexpr int NTB = C / 16;             // 16-row blocks per chunk
     static constexpr int NKB = DK / 16;            // 16-blocks of the key dim
     static constexpr int NJT = DVT / 16;           // 16-column value tiles
+    static constexpr int NC = 4;                   // consumer waves
+    static constexpr int NT = 64 * (NP + NC);
+    // output blocks: consumer c computes t-block c % NTB for value tiles
+    // [(c / NTB) * NJC, +NJC); with more consumers than t-blocks, JS consumers share a
+    // t-block (each recomputes its score tiles) and split its value tiles
+    static constexpr int JS = (NC > NTB && NJT % (NC / NTB) == 0) ? NC / NTB : 1;
+    static constexpr int NJC = NJT / JS;
+    static constexpr int DVS = DVT / JS;           // staged output columns per consumer
+    static_assert(NC * DVS <= 4 * DVT, "output staging within the LDS budget");
     static constexpr int SW = Op<T>::W;            // contraction width per MFMA step
     static constexpr int KSTEPS = (DK + SW - 1) / SW;
     static constexpr int CSTEPS = (C + SW - 1) / SW;
@@ -151,8 +158,9 @@ struct PrefillShape {
     static constexpr bool BLOCKED = NKB % NC == 0;
     static constexpr int IPC = BLOCKED ? NKB / NC : 1;
     static constexpr int NSLOT = BLOCKED ? IPC * NJT : (NU + NC - 1) / NC;
-    // output staging: 16 rows x DVT, stored by 64 lanes in 16-byte chunks
-    static constexpr int OCH = 16 * VCH;           // chunks per staged block
+    // output staging: 16 rows x DVS, stored by 64 lanes in 16-byte chunks
+    static constexpr int SCH = DVS / CE, SWS = cmin(SCH, 8) - 1;
+    static constexpr int OCH = 16 * SCH;           // chunks per staged block
     static constexpr int OCPL = cmax(1, OCH / 64); // chunks per lane
     static constexpr int NBUF = prefill_nbuf((int)sizeof(T), DK, C, DVT);
     static_assert(NBUF >= 1, "LDS budget");
@@ -177,6 +185,7 @@ struct PrefillShape {
     }
     static __device__ __forceinline__ int rk(int row, int col) { return sw_off(row, col, DK, SWK); }
     static __device__ __forceinline__ int rv(int row, int col) { return sw_off(row, col, DVT, SWV); }
+    static __device__ __forceinline__ int ro(int row, int col) { return sw_off(row, col, DVS, SWS); }
 };
 
 // Calls fn(std::integral_constant<int, I>) for I = 0 .. N-1.
@@ -254,7 +263,7 @@ __device__ __forceinline__ float buf_load4(Rsrc r, int off)
 }
 
 template <typename T, int DK, int C, int DVT, int GATE, bool ELU1>
-__global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
+__global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_kernel(const PrefillArgs a)
 {
     using SH = PrefillShape<T, DK, C, DVT>;
     using O = Op<T>;
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
     __shared__ __attribute__((aligned(16))) T sKU[KU ? NBUF : 1][KU ? C * DK : CE];  // scalar: K~ [s][i]
     __shared__ __attribute__((aligned(16))) T sV[NBUF][C * DVT];     // V [s][j]
     __shared__ __attribute__((aligned(16))) T sS[2][DVT * DK];       // state^T [j][i], by parity
-    __shared__ __attribute__((aligned(16))) T sO[NC][16 * DVT];      // output staging, per consumer
+    __shared__ __attribute__((aligned(16))) T sO[NC][16 * SH::DVS];  // output staging, per consumer
     __shared__ __attribute__((aligned(16))) float sEG[NBUF][DK];     // exp(Gamma_i)
     __shared__ __attribute__((aligned(16))) float sB[NBUF][C];       // scalar gate: B_t (log2)
 
@@ -312,7 +321,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         f32x4 g[RPS][CE / 4];
         VC v[NVL];
     };
-    Raw R[NBUF];
+    // raw register sets: rows are requested two chunks ahead with two operand buffers
+    constexpr int NRAW = NBUF == 2 ? 2 : 1;
+    Raw R[NRAW];
 
     // Raw rows of the chunk starting at t0, requested in three parts so that each
     // part of a register set can be refilled as soon as it has been consumed.  Rows
@@ -534,7 +545,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
 
     // Outputs of the 16-row block TB of the chunk starting at t0 (straight-line code:
     // TB is a compile-time constant, so every tile loop below is unrolled).
-    auto out_block = [&](auto tbc, int t0, int nvalid, int buf, const T *Q, const T *K,
+    auto out_block = [&](auto tbc, int j0, int t0, int nvalid, int buf, const T *Q, const T *K,
                          const T *V, const T *SS) __attribute__((always_inline)) {
         constexpr int TB = decltype(tbc)::value;
         const int t = 16 * TB + x;
@@ -565,7 +576,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         if constexpr (GATE == kGateScalar) inter_scale = exp2_fast(sB[buf][t]);
         T *stage = sO[c];
 #pragma unroll
-        for (int jt = 0; jt < NJT; ++jt) {
+        for (int jj = 0; jj < SH::NJC; ++jj) {
+            const int jt = j0 + jj;
             const int jrow = 16 * jt + x;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -581,7 +593,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
                 for (int sb = 0; sb <= TB; ++sb) acc = O::mma(frag_tr(V, DVT, SH::SWV, 16 * jt, sb), O::from_acc(pt[sb]), acc);
             }
             // lane holds O[t][16jt + 4grp + r]: stage it row-major
-            *(V4 *)(stage + SH::rv(x, 16 * jt + 4 * grp)) = narrow4<T>(acc);
+            *(V4 *)(stage + SH::ro(x, 16 * jj + 4 * grp)) = narrow4<T>(acc);
         }
         // read the block back row-contiguous and store 16-byte chunks (wave-local:
         // LDS operations of one wave complete in order)
@@ -589,9 +601,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         for (int h = 0; h < SH::OCPL; ++h) {
             const int chunk = lane + 64 * h;       // 8 lanes read one 128-byte row
             if (chunk < SH::OCH) {
-                const int row = chunk / SH::VCH, col = (chunk % SH::VCH) * CE;
-                const VC val = *(const VC *)(stage + SH::rv(row, col));
-                if (16 * TB + row < nvalid) *(VC *)(oh + (size_t)(t0 + 16 * TB + row) * DV + col) = val;
+                const int row = chunk / SH::SCH, col = (chunk % SH::SCH) * CE;
+                const VC val = *(const VC *)(stage + SH::ro(row, col));
+                if (16 * TB + row < nvalid)
+                    *(VC *)(oh + (size_t)(t0 + 16 * TB + row) * DV + 16 * j0 + col) = val;
             }
         }
     };
@@ -602,9 +615,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(const PrefillArgs a)
         const T *Q = sQ[buf], *K = sK[buf], *V = sV[buf], *SS = sS[par];
         const T *KU_ = K;                          // keys of the state update
         if constexpr (KU) KU_ = sKU[buf];
-        // consumer c owns the 16-row blocks tb with tb % NC == c
+        // consumer c owns t-block c % NTB (value tiles from (c / NTB) * NJC), or the
+        // t-blocks tb with tb % NC == c when there are more t-blocks than consumers
         static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
-            if (decltype(tbc)::value % NC == c) out_block(tbc, t0, nvalid, buf, Q, K, V, SS);
+            constexpr int TB = decltype(tbc)::value;
+            if constexpr (NTB <= NC) {
+                if (c < NTB * SH::JS && TB == c % NTB) out_block(tbc, (c / NTB) * SH::NJC, t0, nvalid, buf, Q, K, V, SS);
+            } else {
+                if (TB % NC == c) out_block(tbc, 0, t0, nvalid, buf, Q, K, V, SS);
+            }
         });
         // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
         if constexpr (SH::BLOCKED) {
