@@ -30,15 +30,15 @@ struct DecodeArgs {
     int gate, elu1;
 };
 
-// LDS bytes of a prefill workgroup: `nbuf` operand buffers (Q~ and K^ rows of
-// length d_k, K^T and V^T rows of length C, plus exp(Gamma) and the scalar-gate
-// sums), the two parity copies of the state operand, and the output staging rows of
-// the four consumer waves (16 rows each).
+// LDS bytes of a prefill workgroup (an upper bound, alignment included): `nbuf`
+// operand buffers (Q~ and K^ rows of length d_k, V rows of length dvt, exp(Gamma)
+// and the scalar-gate sums), the two parity copies of the state operand, and the
+// output staging rows of the consumer waves (at most 4 x 16 x dvt).
 constexpr int kLdsBytes = 163840;                  // LDS per compute unit on gfx950
 constexpr int prefill_lds_bytes(int es, int dk, int c, int dvt, int nbuf)
 {
-    const int buf = (2 * c * dk + dk * c + dvt * c) * es + 4 * (dk + c);
-    return nbuf * buf + 2 * dvt * dk * es + 4 * 16 * dvt * es;
+    const int buf = (2 * c * dk + dvt * c) * es + 4 * (dk + c + 4);
+    return nbuf * buf + 2 * dvt * dk * es + 4 * 16 * dvt * es + 128;
 }
 // Operand buffers that fit (2: producer/consumer overlap, 1: alternating, 0: none).
 constexpr int prefill_nbuf(int es, int dk, int c, int dvt)

@@ -274,16 +274,14 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     constexpr int NTB = SH::NTB, NKB = SH::NKB, NJT = SH::NJT;
     constexpr int CW = SH::CW, RSEG = SH::RSEG, RPS = SH::RPS;
     constexpr int NVL = SH::NVL, NSLOT = SH::NSLOT, NU = SH::NU;
-    constexpr bool KU = GATE == kGateScalar;        // separate K~ operand for the state
 
     __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * DK];      // Q~ [t][i]
     __shared__ __attribute__((aligned(16))) T sK[NBUF][C * DK];      // K^ [s][i]
-    __shared__ __attribute__((aligned(16))) T sKU[KU ? NBUF : 1][KU ? C * DK : CE];  // scalar: K~ [s][i]
     __shared__ __attribute__((aligned(16))) T sV[NBUF][C * DVT];     // V [s][j]
     __shared__ __attribute__((aligned(16))) T sS[2][DVT * DK];       // state^T [j][i], by parity
     __shared__ __attribute__((aligned(16))) T sO[NC][16 * SH::DVS];  // output staging, per consumer
     __shared__ __attribute__((aligned(16))) float sEG[NBUF][DK];     // exp(Gamma_i)
-    __shared__ __attribute__((aligned(16))) float sB[NBUF][C];       // scalar gate: B_t (log2)
+    __shared__ __attribute__((aligned(16))) float sB[NBUF][C + 1];   // scalar gate: B_t, then Gamma (log2)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -413,40 +411,38 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
                 const int t = rs * RPS + r;
-                float q[CE], kk[CE], qt[CE], kt[CE], ku[CE];
-                widen<T, CE>(r_.q[r], q);
-                widen<T, CE>(r_.k[r], kk);
-#pragma unroll
-                for (int e = 0; e < CE; ++e) {
-                    if constexpr (ELU1) {
-                        q[e] = feature(q[e], true);
-                        kk[e] = feature(kk[e], true);
-                    }
-                    qt[e] = q[e];
-                    kt[e] = kk[e];
-                    if constexpr (GATE == kGateKeydim) {
-                        const float b = excl[e] + bc[r][e];
-                        qt[e] = q[e] * exp2_fast(b);
-                        kt[e] = kk[e] * exp2_fast(-b);
-                    } else if constexpr (GATE == kGateScalar) {
-                        const float b = excl[0] + bc[r][0];
-                        ku[e] = kk[e] * exp2_fast(tot[0] - b);
-                        if (e == 0 && p == 0 && cg == 0) sB[buf][t] = b;
-                    }
+                if constexpr (GATE == kGateScalar) {
+                    // scalar gate: the row factors are applied by the consumers
+                    if (p == 0 && cg == 0) sB[buf][t] = excl[0] + bc[r][0];
                 }
-                VC qv, kv;
+                if constexpr (GATE != kGateKeydim && !ELU1) {
+                    // q and k enter the products as they are
+                    *(VC *)(sQ[buf] + SH::rk(t, ic)) = r_.q[r];
+                    *(VC *)(sK[buf] + SH::rk(t, ic)) = r_.k[r];
+                } else {
+                    float q[CE], kk[CE];
+                    widen<T, CE>(r_.q[r], q);
+                    widen<T, CE>(r_.k[r], kk);
 #pragma unroll
-                for (int e = 0; e < CE; ++e) {
-                    qv[e] = from_f32<T>(qt[e]);
-                    kv[e] = from_f32<T>(kt[e]);
-                }
-                *(VC *)(sQ[buf] + SH::rk(t, ic)) = qv;
-                *(VC *)(sK[buf] + SH::rk(t, ic)) = kv;
-                if constexpr (KU) {
-                    VC uv;
+                    for (int e = 0; e < CE; ++e) {
+                        if constexpr (ELU1) {
+                            q[e] = feature(q[e], true);
+                            kk[e] = feature(kk[e], true);
+                        }
+                        if constexpr (GATE == kGateKeydim) {
+                            const float b = excl[e] + bc[r][e];
+                            q[e] *= exp2_fast(b);
+                            kk[e] *= exp2_fast(-b);
+                        }
+                    }
+                    VC qv, kv;
 #pragma unroll
-                    for (int e = 0; e < CE; ++e) uv[e] = from_f32<T>(ku[e]);
-                    *(VC *)(sKU[buf] + SH::rk(t, ic)) = uv;
+                    for (int e = 0; e < CE; ++e) {
+                        qv[e] = from_f32<T>(q[e]);
+                        kv[e] = from_f32<T>(kk[e]);
+                    }
+                    *(VC *)(sQ[buf] + SH::rk(t, ic)) = qv;
+                    *(VC *)(sK[buf] + SH::rk(t, ic)) = kv;
                 }
             }
             load_qk(r_, t_next);                   // q, k consumed: refill them now
@@ -454,6 +450,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
                 for (int e = 0; e < CE; ++e)
                     sEG[buf][ic + e] = GATE == kGateNone ? 1.f : exp2_fast(tot[e]);
+                if constexpr (GATE == kGateScalar) {
+                    if (p == 0 && cg == 0) sB[buf][C] = tot[0];
+                }
             }
         }
         if (v_lane) {
@@ -613,8 +612,21 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     auto consume = [&](int t0, int buf, int par) __attribute__((always_inline)) {
         const int nvalid = min(L - t0, C);
         const T *Q = sQ[buf], *K = sK[buf], *V = sV[buf], *SS = sS[par];
-        const T *KU_ = K;                          // keys of the state update
-        if constexpr (KU) KU_ = sKU[buf];
+        // scalar gate: the state update weights token s by exp(Gamma - b_s), applied
+        // to the value fragments (tokens are the contraction index)
+        auto vfrag = [&](int jt, int cs) __attribute__((always_inline)) -> F {
+            F f = frag_tr(V, DVT, SH::SWV, 16 * jt, cs);
+            if constexpr (GATE == kGateScalar) {
+                const float gam = sB[buf][C];
+                constexpr int NE = SH::BF ? (C % 32 == 0 ? 8 : 4) : 4;
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    const int s = SH::BF ? 32 * cs + 4 * grp + (e & 3) + 16 * (e >> 2) : 16 * cs + 4 * grp + e;
+                    f[e] = from_f32<T>(to_f32(f[e]) * exp2_fast(gam - sB[buf][s]));
+                }
+            }
+            return f;
+        };
         // consumer c owns t-block c % NTB (value tiles from (c / NTB) * NJC), or the
         // t-blocks tb with tb % NC == c when there are more t-blocks than consumers
         static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
@@ -625,18 +637,19 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 if (TB % NC == c) out_block(tbc, 0, t0, nvalid, buf, Q, K, V, SS);
             }
         });
-        // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
+        // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V
+        // with K~ = K exp(Gamma - b), the factor moved onto V's rows)
         if constexpr (SH::BLOCKED) {
             F af[SH::IPC][SH::CSTEPS];
 #pragma unroll
             for (int ia = 0; ia < SH::IPC; ++ia)
 #pragma unroll
-                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_tr(KU_, DK, SH::SWK, 16 * (c + NC * ia), cs);
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_tr(K, DK, SH::SWK, 16 * (c + NC * ia), cs);
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt) {
                 F bfr[SH::CSTEPS];
 #pragma unroll
-                for (int cs = 0; cs < SH::CSTEPS; ++cs) bfr[cs] = frag_tr(V, DVT, SH::SWV, 16 * jt, cs);
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) bfr[cs] = vfrag(jt, cs);
 #pragma unroll
                 for (int ia = 0; ia < SH::IPC; ++ia) {
                     const int k = jt * SH::IPC + ia;
@@ -657,7 +670,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs)
-                        acc = O::mma(frag_tr(KU_, DK, SH::SWK, 16 * it, cs), frag_tr(V, DVT, SH::SWV, 16 * jt, cs), acc);
+                        acc = O::mma(frag_tr(K, DK, SH::SWK, 16 * it, cs), vfrag(jt, cs), acc);
                     if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
                     S[k] = acc;
                 }
