@@ -33,6 +33,7 @@ def _units():
             units.append(("gla_prefill_inst.hip", "prefill_%d_%d.o" % (bf, dk),
                           ["-DGLA_INST_BF16=%d" % bf, "-DGLA_INST_DK=%d" % dk]))
     units.append(("gla_decode.hip", "decode.o", []))
+    units.append(("gla_scan.hip", "scan.o", []))
     units.append(("gla_api.cpp", "api.o", ["-x", "hip"]))
     return units
 

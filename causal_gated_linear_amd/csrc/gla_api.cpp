@@ -18,31 +18,31 @@
 #include "gla_launch.hpp"
 
 namespace gla {
-hipError_t launch_prefill_0_16(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_0_32(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_0_64(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_0_128(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_1_16(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_1_32(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_1_64(const PrefillArgs &, int, int, hipStream_t);
-hipError_t launch_prefill_1_128(const PrefillArgs &, int, int, hipStream_t);
+hipError_t launch_prefill_0_16(const PrefillArgs &, int, int, bool, hipStream_t);
+hipError_t launch_prefill_0_32(const PrefillArgs &, int, int, bool, hipStream_t);
+hipError_t launch_prefill_0_64(const PrefillArgs &, int, int, bool, hipStream_t);
+hipError_t launch_prefill_0_128(const PrefillArgs &, int, int, bool, hipStream_t);
+hipError_t launch_prefill_1_16(const PrefillArgs &, int, int, bool, hipStream_t);
+hipError_t launch_prefill_1_32(const PrefillArgs &, int, int, bool, hipStream_t);
+hipError_t launch_prefill_1_64(const PrefillArgs &, int, int, bool, hipStream_t);
+hipError_t launch_prefill_1_128(const PrefillArgs &, int, int, bool, hipStream_t);
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, int dvt,
-                          hipStream_t stream)
+                          bool state_only, hipStream_t stream)
 {
     if (dtype == 1) {
         switch (d_k) {
-        case 16: return launch_prefill_1_16(a, chunk, dvt, stream);
-        case 32: return launch_prefill_1_32(a, chunk, dvt, stream);
-        case 64: return launch_prefill_1_64(a, chunk, dvt, stream);
-        case 128: return launch_prefill_1_128(a, chunk, dvt, stream);
+        case 16: return launch_prefill_1_16(a, chunk, dvt, state_only, stream);
+        case 32: return launch_prefill_1_32(a, chunk, dvt, state_only, stream);
+        case 64: return launch_prefill_1_64(a, chunk, dvt, state_only, stream);
+        case 128: return launch_prefill_1_128(a, chunk, dvt, state_only, stream);
         }
     } else {
         switch (d_k) {
-        case 16: return launch_prefill_0_16(a, chunk, dvt, stream);
-        case 32: return launch_prefill_0_32(a, chunk, dvt, stream);
-        case 64: return launch_prefill_0_64(a, chunk, dvt, stream);
-        case 128: return launch_prefill_0_128(a, chunk, dvt, stream);
+        case 16: return launch_prefill_0_16(a, chunk, dvt, state_only, stream);
+        case 32: return launch_prefill_0_32(a, chunk, dvt, state_only, stream);
+        case 64: return launch_prefill_0_64(a, chunk, dvt, state_only, stream);
+        case 128: return launch_prefill_0_128(a, chunk, dvt, state_only, stream);
         }
     }
     return hipErrorInvalidValue;
@@ -51,20 +51,62 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, i
 // Launch shape: the widest value tile (64, 32 or 16 columns) that fits in LDS and
 // still gives at least 256 workgroups for the 256 compute units.
 // GLA_PREFILL_TILE=<columns> overrides the choice (a tuning knob).
+static bool tile_usable(int dvt, int d_k, int d_v, int chunk, int elem_bytes)
+{
+    return dvt <= d_v && d_v % dvt == 0 && prefill_nbuf(elem_bytes, d_k, chunk, dvt) > 0;
+}
+
 int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes)
 {
-    auto usable = [&](int dvt) {
-        return dvt <= d_v && d_v % dvt == 0 && prefill_nbuf(elem_bytes, d_k, chunk, dvt) > 0;
-    };
-    static const char *env = getenv("GLA_PREFILL_TILE");
+    const char *env = getenv("GLA_PREFILL_TILE");
     if (env) {
         const int dvt = atoi(env);
-        if ((dvt == 16 || dvt == 32 || dvt == 64) && usable(dvt)) return dvt;
+        if ((dvt == 16 || dvt == 32 || dvt == 64) && tile_usable(dvt, d_k, d_v, chunk, elem_bytes)) return dvt;
     }
     const long bh = BH;
-    if (usable(64) && bh * (d_v / 64) >= 256) return 64;
-    if (usable(32) && bh * (d_v / 32) >= 256) return 32;
+    if (tile_usable(64, d_k, d_v, chunk, elem_bytes) && bh * (d_v / 64) >= 256) return 64;
+    if (tile_usable(32, d_k, d_v, chunk, elem_bytes) && bh * (d_v / 32) >= 256) return 32;
     return 16;
+}
+
+// Few long sequences: rather than narrowing the value tile (which repeats the per-
+// token gate and score work in every tile of a head), split each sequence into
+// segments at the widest tile.  A state-only pass computes every segment's state
+// from zero, a scan over segments turns those into each segment's initial state,
+// and the full pass then runs all segments in parallel.  Used when the widest tile
+// gives fewer than 256 workgroups and the sequences have at least 64 chunks;
+// segments keep at least 16 chunks.  GLA_PREFILL_SEGMENTS=<n> overrides the count.
+constexpr int kSegMinChunks = 16, kSegMinSeqChunks = 64;
+
+PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes)
+{
+    PrefillPlan p{prefill_tile(BH, d_k, d_v, chunk, elem_bytes), 1, L};
+    const int nchunks = (L + chunk - 1) / chunk;
+    int dvt = 16;
+    for (int t : {64, 32})
+        if (dvt == 16 && tile_usable(t, d_k, d_v, chunk, elem_bytes)) dvt = t;
+    const long wgs = (long)BH * (d_v / dvt);
+    int nseg = 1;
+    if (nchunks >= kSegMinSeqChunks)
+        while (wgs * nseg < 256 && nchunks / (2 * nseg) >= kSegMinChunks) nseg *= 2;
+    const char *env = getenv("GLA_PREFILL_SEGMENTS");
+    if (env && atoi(env) >= 1) nseg = atoi(env) < nchunks ? atoi(env) : (nchunks > 0 ? nchunks : 1);
+    if (nseg > 1) {
+        const int cps = (nchunks + nseg - 1) / nseg;   // chunks per segment
+        p.nseg = (nchunks + cps - 1) / cps;
+        p.seg_len = cps * chunk;
+        p.dvt = dvt;
+    }
+    return p;
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v)
+{
+    if (p.nseg <= 1) return 0;
+    const size_t states = (size_t)BH * p.nseg * d_k * d_v * 4;
+    return 2 * round256(states) + round256((size_t)BH * p.nseg * d_k * 4);
 }
 }  // namespace gla
 
@@ -193,8 +235,12 @@ int gla_state_free(float *state, gla_stream_t stream)
 size_t gla_prefill_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chunk,
                                    gla_dtype dtype)
 {
-    (void)B; (void)H; (void)L; (void)d_k; (void)d_v; (void)chunk; (void)dtype;
-    return 0;
+    if (B <= 0 || H <= 0 || L < 0 || !dim_supported(d_k) || !dim_supported(d_v) || !chunk_supported(chunk) ||
+        (dtype != GLA_F32 && dtype != GLA_BF16) || (long long)B * H > 0x7fffffffLL)
+        return 0;
+    const int BH = B * H;
+    const gla::PrefillPlan p = gla::prefill_plan(BH, L, d_k, d_v, chunk, (int)elem_size(dtype));
+    return gla::prefill_workspace(p, BH, d_k, d_v);
 }
 
 int gla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
@@ -240,18 +286,38 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
     if (overlap(ssf, ss0) && s_final != s0)
         return fail(GLA_ERR_ALIAS, "s_final partially overlaps s0");
 
+    const gla::PrefillPlan plan = gla::prefill_plan((int)BH, L, d_k, d_v, chunk, (int)es);
     gla::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s0 = s0; a.o = o; a.s_final = s_final;
     a.BH = (int)BH; a.L = L; a.d_v = d_v;
     a.gate = (int)gate; a.elu1 = phi == GLA_PHI_ELU1;
-    const int dvt = gla::prefill_tile(a.BH, d_k, d_v, chunk, (int)es);
-    a.n_vt = d_v / dvt;
-    const long grid = (long)BH * a.n_vt;
+    a.n_vt = d_v / plan.dvt;
+    a.nseg = plan.nseg; a.seg_len = plan.seg_len; a.gam = nullptr;
+    const long grid = (long)BH * a.nseg * a.n_vt;
     if (grid > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H too large");
     a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
     if (L == 0 && !s_final) return ok();
-    hipError_t e = gla::launch_prefill(a, dtype == GLA_BF16 ? 1 : 0, d_k, chunk, dvt,
-                                       (hipStream_t)stream);
+    const int dt = dtype == GLA_BF16 ? 1 : 0;
+    const hipStream_t hs = (hipStream_t)stream;
+    hipError_t e;
+    if (plan.nseg == 1) {
+        e = gla::launch_prefill(a, dt, d_k, chunk, plan.dvt, false, hs);
+    } else {
+        // workspace: segment states from zero, segment initial states, gate totals
+        const size_t states = (size_t)BH * plan.nseg * d_k * d_v * 4;
+        char *w = (char *)workspace;
+        float *ds = (float *)w, *sin = (float *)(w + gla::round256(states));
+        float *gam = (float *)(w + 2 * gla::round256(states));
+        gla::PrefillArgs a1 = a;                   // pass 1: segment states from zero
+        a1.s0 = nullptr; a1.s_final = ds; a1.o = nullptr; a1.gam = gam;
+        e = gla::launch_prefill(a1, dt, d_k, chunk, plan.dvt, true, hs);
+        if (e == hipSuccess)                       // scan over segments
+            e = gla::launch_segment_scan(ds, gate == GLA_GATE_NONE ? nullptr : gam, s0, sin, s_final,
+                                         (int)BH, plan.nseg, d_k, d_v, hs);
+        gla::PrefillArgs a2 = a;                   // pass 2: outputs of every segment
+        a2.s0 = sin; a2.s_final = nullptr;
+        if (e == hipSuccess) e = gla::launch_prefill(a2, dt, d_k, chunk, plan.dvt, false, hs);
+    }
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -19,6 +19,11 @@ struct PrefillArgs {
     int gate, elu1;
     int n_vt;                // value-column tiles per head (d_v / tile width)
     int xcd_remap;           // 1: map workgroups so a head's tiles share one XCD
+    // sequence segments: workgroup (head, segment, tile) covers rows
+    // [seg * seg_len, min(L, (seg + 1) * seg_len)) of its head; s0 and s_final are
+    // then indexed [BH][nseg][d_k][d_v].  nseg = 1, seg_len = L: whole sequences.
+    int nseg, seg_len;
+    float *gam;              // state-only pass: segment totals of the log2-gates [BH][nseg][d_k]
 };
 
 struct DecodeArgs {
@@ -31,13 +36,14 @@ struct DecodeArgs {
 };
 
 // LDS bytes of a prefill workgroup (an upper bound, alignment included): `nbuf`
-// operand buffers (Q~ and K^ rows of length d_k, V rows of length dvt, exp(Gamma)
-// and the scalar-gate sums), the two parity copies of the state operand, and the
-// output staging rows of the consumer waves (at most 4 x 16 x dvt).
+// operand buffers (Q~ and K^ rows of length d_k, the scalar gate's K~ rows, V rows
+// of length dvt, exp(Gamma) and the scalar-gate sums), the two parity copies of the
+// state operand, and the output staging rows of the consumer waves (at most
+// 4 x 16 x dvt).
 constexpr int kLdsBytes = 163840;                  // LDS per compute unit on gfx950
 constexpr int prefill_lds_bytes(int es, int dk, int c, int dvt, int nbuf)
 {
-    const int buf = (2 * c * dk + dvt * c) * es + 4 * (dk + c + 4);
+    const int buf = (3 * c * dk + dvt * c) * es + 4 * (dk + c + 4);
     return nbuf * buf + 2 * dvt * dk * es + 4 * 16 * dvt * es + 128;
 }
 // Operand buffers that fit (2: producer/consumer overlap, 1: alternating, 0: none).
@@ -47,12 +53,30 @@ constexpr int prefill_nbuf(int es, int dk, int c, int dvt)
            : prefill_lds_bytes(es, dk, c, dvt, 1) <= kLdsBytes ? 1 : 0;
 }
 
-// Value columns per prefill workgroup (16, 32 or 64) for these sizes.
-int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes);
+// Launch plan of a prefill: value columns per workgroup (16, 32 or 64) and, for
+// few long sequences, the number of sequence segments and their length in rows.
+struct PrefillPlan {
+    int dvt, nseg, seg_len;
+};
+PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes);
 
-// Enqueue the prefill kernel.  dtype: 0 fp32, 1 bf16.  Sizes must already be valid.
+// Device workspace of a segmented prefill: segment states from zero, segment
+// initial states (both fp32 [BH][nseg][d_k][d_v]) and segment gate totals
+// (fp32 [BH][nseg][d_k]); 0 when nseg == 1.
+size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v);
+
+// Enqueue the prefill kernel.  dtype: 0 fp32, 1 bf16.  state_only: compute only
+// each segment's final state from a zero start and its gate totals (a.gam), with no
+// outputs.  Sizes must already be valid.
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, int dvt,
-                          hipStream_t stream);
+                          bool state_only, hipStream_t stream);
+
+// Enqueue the scan over segments: for every head and state element, in segment
+// order, sin[seg] = S; S = exp2(gam[seg]) * S + ds[seg], from S = s0 (or 0); then
+// s_final = S (if not null).  gam may be null (no gate).
+hipError_t launch_segment_scan(const float *ds, const float *gam, const float *s0, float *sin,
+                               float *s_final, int BH, int nseg, int d_k, int d_v,
+                               hipStream_t stream);
 
 // Enqueue one decode step.  Sizes must already be valid.
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int d_k, int d_v, hipStream_t stream);

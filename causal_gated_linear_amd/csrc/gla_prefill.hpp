@@ -262,7 +262,10 @@ __device__ __forceinline__ float buf_load4(Rsrc r, int off)
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-template <typename T, int DK, int C, int DVT, int GATE, bool ELU1>
+// SO (state only): the first pass of a segmented prefill.  Each workgroup runs the
+// state recurrence over its segment from a zero state and stores that state and the
+// segment's gate totals; no outputs, no Q~.
+template <typename T, int DK, int C, int DVT, int GATE, bool ELU1, bool SO>
 __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_kernel(const PrefillArgs a)
 {
     using SH = PrefillShape<T, DK, C, DVT>;
@@ -277,6 +280,8 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 
     __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * DK];      // Q~ [t][i]
     __shared__ __attribute__((aligned(16))) T sK[NBUF][C * DK];      // K^ [s][i]
+    constexpr bool KU = GATE == kGateScalar;        // separate K~ operand for the state
+    __shared__ __attribute__((aligned(16))) T sKU[KU ? NBUF : 1][KU ? C * DK : CE];  // scalar: K~ [s][i]
     __shared__ __attribute__((aligned(16))) T sV[NBUF][C * DVT];     // V [s][j]
     __shared__ __attribute__((aligned(16))) T sS[2][DVT * DK];       // state^T [j][i], by parity
     __shared__ __attribute__((aligned(16))) T sO[NC][16 * SH::DVS];  // output staging, per consumer
@@ -290,19 +295,24 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 
     int wg = blockIdx.x;
     if (a.xcd_remap) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
-    const int bh = wg / a.n_vt;
-    const int vt = wg - bh * a.n_vt;
-    const int L = a.L, DV = a.d_v;
+    const int bhs = wg / a.n_vt;                   // (head, segment)
+    const int vt = wg - bhs * a.n_vt;
+    const int bh = bhs / a.nseg, seg = bhs - bh * a.nseg;
+    const int DV = a.d_v;
+    // this workgroup's rows: [row0, row0 + L) of its head
+    const int row0 = seg * a.seg_len;
+    const int L = max(0, min(a.L - row0, a.seg_len));
+    const size_t hrow = (size_t)bh * a.L + row0;   // first row, counted over all heads
 
-    // per-head buffer views (host code guarantees each head's bytes fit in 31 bits)
+    // per-segment buffer views (host code guarantees each head's bytes fit in 31 bits)
     constexpr int ES = sizeof(T);
-    const Rsrc rq = make_rsrc((const T *)a.q + (size_t)bh * L * DK, (unsigned)(L * DK * ES));
-    const Rsrc rk = make_rsrc((const T *)a.k + (size_t)bh * L * DK, (unsigned)(L * DK * ES));
-    const Rsrc rvv = make_rsrc((const T *)a.v + (size_t)bh * L * DV, (unsigned)(L * DV * ES));
-    T *__restrict__ oh = (T *)a.o + (size_t)bh * L * DV + vt * DVT;
+    const Rsrc rq = make_rsrc((const T *)a.q + hrow * DK, (unsigned)(L * DK * ES));
+    const Rsrc rk = make_rsrc((const T *)a.k + hrow * DK, (unsigned)(L * DK * ES));
+    const Rsrc rvv = make_rsrc((const T *)a.v + hrow * DV, (unsigned)(L * DV * ES));
+    T *__restrict__ oh = SO ? nullptr : (T *)a.o + hrow * DV + vt * DVT;
     Rsrc rg = make_rsrc(a.g, 0u);                  // no gates: never read
-    if constexpr (GATE == kGateKeydim) rg = make_rsrc(a.g + (size_t)bh * L * DK, (unsigned)(L * DK * 4));
-    if constexpr (GATE == kGateScalar) rg = make_rsrc(a.g + (size_t)bh * L, (unsigned)(L * 4));
+    if constexpr (GATE == kGateKeydim) rg = make_rsrc(a.g + hrow * DK, (unsigned)(L * DK * 4));
+    if constexpr (GATE == kGateScalar) rg = make_rsrc(a.g + hrow, (unsigned)(L * 4));
     const int nchunks = (L + C - 1) / C;
 
     // ---------------- producers -------------------------------------------------------
@@ -319,6 +329,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         f32x4 g[RPS][CE / 4];
         VC v[NVL];
     };
+    float gsum[CE];                                // state-only pass: gate totals so far
+#pragma unroll
+    for (int e = 0; e < CE; ++e) gsum[e] = 0.f;
     // raw register sets: rows are requested two chunks ahead with two operand buffers
     constexpr int NRAW = NBUF == 2 ? 2 : 1;
     Raw R[NRAW];
@@ -348,7 +361,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         if (gate_lane) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
-                r_.q[r] = buf_load16<VC>(rq, qk_off + (t0 + r) * DK * ES);
+                if constexpr (!SO) r_.q[r] = buf_load16<VC>(rq, qk_off + (t0 + r) * DK * ES);
                 r_.k[r] = buf_load16<VC>(rk, qk_off + (t0 + r) * DK * ES);
             }
         }
@@ -415,37 +428,51 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     // scalar gate: the row factors are applied by the consumers
                     if (p == 0 && cg == 0) sB[buf][t] = excl[0] + bc[r][0];
                 }
+                if constexpr (KU) {
+                    // scalar gate: K~ = phi(k) exp(Gamma - b_t) for the state update
+                    const float f = exp2_fast(tot[0] - (excl[0] + bc[r][0]));
+                    float kk[CE];
+                    widen<T, CE>(r_.k[r], kk);
+                    VC uv;
+#pragma unroll
+                    for (int e = 0; e < CE; ++e) uv[e] = from_f32<T>((ELU1 ? feature(kk[e], true) : kk[e]) * f);
+                    *(VC *)(sKU[buf] + SH::rk(t, ic)) = uv;
+                }
                 if constexpr (GATE != kGateKeydim && !ELU1) {
                     // q and k enter the products as they are
-                    *(VC *)(sQ[buf] + SH::rk(t, ic)) = r_.q[r];
-                    *(VC *)(sK[buf] + SH::rk(t, ic)) = r_.k[r];
+                    if constexpr (!SO) *(VC *)(sQ[buf] + SH::rk(t, ic)) = r_.q[r];
+                    if constexpr (!(SO && KU)) *(VC *)(sK[buf] + SH::rk(t, ic)) = r_.k[r];
                 } else {
                     float q[CE], kk[CE];
-                    widen<T, CE>(r_.q[r], q);
+                    if constexpr (!SO) widen<T, CE>(r_.q[r], q);
                     widen<T, CE>(r_.k[r], kk);
 #pragma unroll
                     for (int e = 0; e < CE; ++e) {
                         if constexpr (ELU1) {
-                            q[e] = feature(q[e], true);
+                            if constexpr (!SO) q[e] = feature(q[e], true);
                             kk[e] = feature(kk[e], true);
                         }
                         if constexpr (GATE == kGateKeydim) {
                             const float b = excl[e] + bc[r][e];
-                            q[e] *= exp2_fast(b);
+                            if constexpr (!SO) q[e] *= exp2_fast(b);
                             kk[e] *= exp2_fast(-b);
                         }
                     }
                     VC qv, kv;
 #pragma unroll
                     for (int e = 0; e < CE; ++e) {
-                        qv[e] = from_f32<T>(q[e]);
+                        if constexpr (!SO) qv[e] = from_f32<T>(q[e]);
                         kv[e] = from_f32<T>(kk[e]);
                     }
-                    *(VC *)(sQ[buf] + SH::rk(t, ic)) = qv;
+                    if constexpr (!SO) *(VC *)(sQ[buf] + SH::rk(t, ic)) = qv;
                     *(VC *)(sK[buf] + SH::rk(t, ic)) = kv;
                 }
             }
             load_qk(r_, t_next);                   // q, k consumed: refill them now
+            if constexpr (SO) {
+#pragma unroll
+                for (int e = 0; e < CE; ++e) gsum[e] += tot[e];
+            }
             if (rs == 0) {
 #pragma unroll
                 for (int e = 0; e < CE; ++e)
@@ -497,7 +524,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * it + 4 * grp + r;
-                    const float v = a.s0[((size_t)bh * DK + i) * DV + vt * DVT + 16 * jt + x];
+                    const float v = a.s0[((size_t)bhs * DK + i) * DV + vt * DVT + 16 * jt + x];
                     S[k][r] = ok ? v : 0.f;
                 }
             }
@@ -612,24 +639,14 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     auto consume = [&](int t0, int buf, int par) __attribute__((always_inline)) {
         const int nvalid = min(L - t0, C);
         const T *Q = sQ[buf], *K = sK[buf], *V = sV[buf], *SS = sS[par];
-        // scalar gate: the state update weights token s by exp(Gamma - b_s), applied
-        // to the value fragments (tokens are the contraction index)
+        const T *KS = K;                           // keys of the state update
+        if constexpr (KU) KS = sKU[buf];
         auto vfrag = [&](int jt, int cs) __attribute__((always_inline)) -> F {
-            F f = frag_tr(V, DVT, SH::SWV, 16 * jt, cs);
-            if constexpr (GATE == kGateScalar) {
-                const float gam = sB[buf][C];
-                constexpr int NE = SH::BF ? (C % 32 == 0 ? 8 : 4) : 4;
-#pragma unroll
-                for (int e = 0; e < NE; ++e) {
-                    const int s = SH::BF ? 32 * cs + 4 * grp + (e & 3) + 16 * (e >> 2) : 16 * cs + 4 * grp + e;
-                    f[e] = from_f32<T>(to_f32(f[e]) * exp2_fast(gam - sB[buf][s]));
-                }
-            }
-            return f;
+            return frag_tr(V, DVT, SH::SWV, 16 * jt, cs);
         };
         // consumer c owns t-block c % NTB (value tiles from (c / NTB) * NJC), or the
         // t-blocks tb with tb % NC == c when there are more t-blocks than consumers
-        static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
+        if constexpr (!SO) static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
             constexpr int TB = decltype(tbc)::value;
             if constexpr (NTB <= NC) {
                 if (c < NTB * SH::JS && TB == c % NTB) out_block(tbc, (c / NTB) * SH::NJC, t0, nvalid, buf, Q, K, V, SS);
@@ -637,14 +654,13 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 if (TB % NC == c) out_block(tbc, 0, t0, nvalid, buf, Q, K, V, SS);
             }
         });
-        // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V
-        // with K~ = K exp(Gamma - b), the factor moved onto V's rows)
+        // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
         if constexpr (SH::BLOCKED) {
             F af[SH::IPC][SH::CSTEPS];
 #pragma unroll
             for (int ia = 0; ia < SH::IPC; ++ia)
 #pragma unroll
-                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_tr(K, DK, SH::SWK, 16 * (c + NC * ia), cs);
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_tr(KS, DK, SH::SWK, 16 * (c + NC * ia), cs);
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt) {
                 F bfr[SH::CSTEPS];
@@ -670,13 +686,13 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs)
-                        acc = O::mma(frag_tr(K, DK, SH::SWK, 16 * it, cs), vfrag(jt, cs), acc);
+                        acc = O::mma(frag_tr(KS, DK, SH::SWK, 16 * it, cs), vfrag(jt, cs), acc);
                     if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
                     S[k] = acc;
                 }
             }
         }
-        write_state(par ^ 1);
+        if constexpr (!SO) write_state(par ^ 1);
     };
 
     // ---------------- pipeline ---------------------------------------------------------
@@ -709,9 +725,15 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 lds_barrier();
             }
         }
+        if constexpr (SO && GATE != kGateNone) {   // segment gate totals (log2 units)
+            if (vt == 0 && gate_lane && rs == 0) {
+#pragma unroll
+                for (int e = 0; e < CE; ++e) a.gam[(size_t)bhs * DK + ic + e] = gsum[e];
+            }
+        }
     } else {
         load_s0();
-        write_state(0);
+        if constexpr (!SO) write_state(0);
         if constexpr (NBUF == 2) {
             const int npairs = (nchunks + 1) / 2;
             lds_barrier();
@@ -734,7 +756,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = 16 * it + 4 * grp + r;
-                        a.s_final[((size_t)bh * DK + i) * DV + vt * DVT + 16 * jt + x] = S[k][r];
+                        a.s_final[((size_t)bhs * DK + i) * DV + vt * DVT + 16 * jt + x] = S[k][r];
                     }
                 }
             }
@@ -742,11 +764,11 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     }
 }
 
-template <typename T, int DK, int C, int DVT, int GATE, bool ELU1>
+template <typename T, int DK, int C, int DVT, int GATE, bool ELU1, bool SO>
 hipError_t launch_prefill_inst(const PrefillArgs &a, hipStream_t stream)
 {
-    const int grid = a.BH * a.n_vt;
-    hipLaunchKernelGGL((prefill_kernel<T, DK, C, DVT, GATE, ELU1>), dim3(grid),
+    const int grid = a.BH * a.nseg * a.n_vt;
+    hipLaunchKernelGGL((prefill_kernel<T, DK, C, DVT, GATE, ELU1, SO>), dim3(grid),
                        dim3(PrefillShape<T, DK, C, DVT>::NT), 0, stream, a);
     return hipGetLastError();
 }

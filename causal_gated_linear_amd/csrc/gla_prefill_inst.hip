@@ -21,29 +21,36 @@ typedef bf16 InstT;
 typedef float InstT;
 #endif
 
-template <int C, int DVT>
-static hipError_t dispatch_mode(const PrefillArgs &a, hipStream_t stream)
+template <int C, int DVT, bool SO>
+static hipError_t dispatch_gate(const PrefillArgs &a, hipStream_t stream)
 {
     constexpr int DK = GLA_INST_DK;
-    if constexpr (prefill_nbuf((int)sizeof(InstT), DK, C, DVT) == 0) {
+    if (a.gate == kGateKeydim)
+        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, true, SO>(a, stream)
+                      : launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, false, SO>(a, stream);
+    if (a.gate == kGateScalar)
+        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, true, SO>(a, stream)
+                      : launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, false, SO>(a, stream);
+    return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateNone, true, SO>(a, stream)
+                  : launch_prefill_inst<InstT, DK, C, DVT, kGateNone, false, SO>(a, stream);
+}
+
+template <int C, int DVT>
+static hipError_t dispatch_mode(const PrefillArgs &a, bool state_only, hipStream_t stream)
+{
+    if constexpr (prefill_nbuf((int)sizeof(InstT), GLA_INST_DK, C, DVT) == 0) {
         return hipErrorInvalidValue;               // does not fit in LDS; never chosen
     } else {
-    if (a.gate == kGateKeydim)
-        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, true>(a, stream)
-                      : launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, false>(a, stream);
-    if (a.gate == kGateScalar)
-        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, true>(a, stream)
-                      : launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, false>(a, stream);
-    return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateNone, true>(a, stream)
-                  : launch_prefill_inst<InstT, DK, C, DVT, kGateNone, false>(a, stream);
+        return state_only ? dispatch_gate<C, DVT, true>(a, stream) : dispatch_gate<C, DVT, false>(a, stream);
     }
 }
 
 hipError_t GLA_CAT3(launch_prefill_, GLA_INST_BF16, GLA_INST_DK)(const PrefillArgs &a, int chunk,
-                                                                 int dvt, hipStream_t stream)
+                                                                 int dvt, bool state_only,
+                                                                 hipStream_t stream)
 {
 #define GLA_CASE(C, DVT) \
-    if (chunk == C && dvt == DVT) return dispatch_mode<C, DVT>(a, stream);
+    if (chunk == C && dvt == DVT) return dispatch_mode<C, DVT>(a, state_only, stream);
 #define GLA_CASES(C) GLA_CASE(C, 16) GLA_CASE(C, 32) GLA_CASE(C, 64)
     GLA_CASES(16) GLA_CASES(32) GLA_CASES(64)
 #undef GLA_CASES

@@ -75,6 +75,8 @@ PREFILL_BAD = {
     "chunk_128": (dict(chunk=128), _lib.GLA_ERR_UNSUPPORTED),
     "chunk_8": (dict(chunk=8), _lib.GLA_ERR_UNSUPPORTED),
     "L_past_32bit_head_offsets": (dict(L=4194304, d_k=128, d_v=128), _lib.GLA_ERR_SHAPE),
+    "segmented_without_workspace": (dict(B=1, H=2, L=64 * 65), _lib.GLA_ERR_WORKSPACE),
+    "segmented_short_workspace": (dict(B=1, H=2, L=64 * 65, ws=A + 400 * MB, ws_bytes=4096), _lib.GLA_ERR_WORKSPACE),
     "dtype_7": (dict(dtype=7), _lib.GLA_ERR_UNSUPPORTED),
     "gate_5": (dict(gate=5), _lib.GLA_ERR_UNSUPPORTED),
     "phi_3": (dict(phi=3), _lib.GLA_ERR_UNSUPPORTED),
@@ -144,6 +146,16 @@ def test_state_alloc_rejects(lib):
     assert lib.gla_state_alloc(1, 1, 24, 16, ctypes.byref(p), None) == _lib.GLA_ERR_UNSUPPORTED
     assert p.value == 1234                      # untouched on error
     assert lib.gla_state_free(None, None) == _lib.GLA_OK
+
+
+def test_workspace_for_few_long_sequences(lib):
+    """Few long sequences are split into segments, which need a workspace: two fp32
+    state arrays [B*H][segments][d_k][d_v] and the segment gate totals."""
+    n = lib.gla_prefill_workspace_bytes(1, 32, 32768, 128, 128, 64, 1)
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert n == 2 * rnd(32 * 4 * 128 * 128 * 4) + rnd(32 * 4 * 128 * 4)   # 4 segments of 8192 tokens
+    assert lib.gla_prefill_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 0   # enough heads
+    assert lib.gla_prefill_workspace_bytes(1, 2, 64 * 63, 64, 64, 64, 1) == 0   # too short
 
 
 def test_workspace_query_is_host_only(lib):

@@ -173,3 +173,53 @@ def test_prefill_full_size_sampled_heads(name):
     es = util.assert_close(util.pick_heads(s, heads), rs, tol, "%s s" % name)
     assert torch.isfinite(o).all()
     print("%s full size, heads %s: err o %.2e s %.2e" % (name, heads, eo, es))
+
+
+# Few long sequences run as segments: a state-only pass per segment, a scan over the
+# segments, then all segments in parallel ("Attention is recurrent", Prefill: the
+# prefix states form a (weighted) scan).  These sizes trigger it: B*H = 2 heads with
+# at least 64 chunks; the ragged lengths leave a short last segment.
+SEGMENTED = {
+    # name: (workload, B, H, L)
+    "gla_prefill_seg": ("gla_prefill", 1, 2, 64 * 65 + 37),
+    "scalar_seg": ("scalar_long", 1, 2, 64 * 80 + 5),
+    "linear_elu1_seg": ("linear_elu1", 2, 1, 64 * 70),
+    "fp32_seg": ("fp32_single_head", 1, 2, 16 * 70 + 9),
+}
+
+
+def test_segmented_sizes_use_a_workspace():
+    for case, (name, B, H, L) in SEGMENTED.items():
+        w = W[name]
+        assert api.workspace_bytes(B, H, L, w.d_k, w.d_v, w.chunk, w.dtype) > 0, case
+    w = W["gla_prefill"]
+    assert api.workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, w.dtype) == 0
+
+
+@pytest.mark.parametrize("case", sorted(SEGMENTED))
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_prefill_segmented(case, with_s0):
+    name, B, H, L = SEGMENTED[case]
+    _check_all_heads(W[name], B, H, L, seed=500 + len(case), with_s0=with_s0)
+
+
+@pytest.mark.parametrize("nseg", [1, 2, 3, 7])
+def test_prefill_segment_counts(monkeypatch, nseg):
+    """Any segmentation gives the recurrence's result (the scan is a regrouping)."""
+    monkeypatch.setenv("GLA_PREFILL_SEGMENTS", str(nseg))
+    _check_all_heads(W["gla_prefill"], 1, 2, 64 * 20 + 3, seed=600 + nseg, with_s0=True)
+    _check_all_heads(W["scalar_long"], 1, 2, 64 * 20 + 3, seed=700 + nseg, with_s0=True)
+
+
+def test_prefill_segmented_in_place_state():
+    """s_final may be s0 on the segmented path too (the scan reads s0 before it writes)."""
+    w = W["gla_prefill"]
+    B, H, L = 1, 2, 64 * 66
+    inp = inputs.draw(w, B=B, H=H, L=L, seed=801)
+    s0 = inputs.draw_state(B, H, w.d_k, w.d_v, seed=802, scale=0.5)
+    st = s0.to(DEV)
+    o, s = _run_gpu(w, _to(inp, DEV), s0=st, final_state=st)
+    assert s.data_ptr() == st.data_ptr()
+    ro, rs = oracle.forward(inp["q"], inp["k"], inp["v"], g=inp["g"], gate=w.gate, s0=s0)
+    util.assert_close(o, ro, util.TOL[w.dtype], "o")
+    util.assert_close(s, rs, util.TOL[w.dtype], "s_final in place")
