@@ -580,11 +580,21 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         for (int k = 0; k < SH::KSTEPS; ++k) qf[k] = frag_k(Q, t, k);
         // score tiles P^T[s-block sb][t-block TB]: lane holds P[t][16sb + 4grp + r]
         f32x4 pt[TB + 2];
+        // the next s-block's key fragments are requested before the current block's
+        // products
+        F kf[2][SH::KSTEPS];
+#pragma unroll
+        for (int k = 0; k < SH::KSTEPS; ++k) kf[0][k] = frag_k(K, x, k);
 #pragma unroll
         for (int sb = 0; sb <= TB; ++sb) {
+            if (sb < TB) {
+#pragma unroll
+                for (int k = 0; k < SH::KSTEPS; ++k) kf[(sb + 1) & 1][k] = frag_k(K, 16 * (sb + 1) + x, k);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < SH::KSTEPS; ++k) acc = O::mma(frag_k(K, 16 * sb + x, k), qf[k], acc);
+            for (int k = 0; k < SH::KSTEPS; ++k) acc = O::mma(kf[sb & 1][k], qf[k], acc);
             if constexpr (GATE == kGateScalar) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -601,24 +611,36 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         float inter_scale = 1.f;
         if constexpr (GATE == kGateScalar) inter_scale = exp2_fast(sB[buf][t]);
         T *stage = sO[c];
+        // value tiles in order; the next tile's state and value fragments are requested
+        // before the current tile's products (two register slots), so LDS latency
+        // overlaps the matrix cores
+        constexpr int NSP = SH::BF ? TB / 2 + 1 : TB + 1;
+        F sf[2][SH::KSTEPS], vf[2][NSP];
+        auto load_j = [&](int jj, int slot) __attribute__((always_inline)) {
+            const int jt = j0 + jj;
+#pragma unroll
+            for (int k = 0; k < SH::KSTEPS; ++k) sf[slot][k] = frag_k(SS, 16 * jt + x, k);
+#pragma unroll
+            for (int sp = 0; sp < NSP; ++sp) vf[slot][sp] = frag_tr(V, DVT, SH::SWV, 16 * jt, sp);
+        };
+        load_j(0, 0);
 #pragma unroll
         for (int jj = 0; jj < SH::NJC; ++jj) {
-            const int jt = j0 + jj;
-            const int jrow = 16 * jt + x;
+            if (jj + 1 < SH::NJC) load_j(jj + 1, (jj + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int sl = jj & 1;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < SH::KSTEPS; ++k) acc = O::mma(frag_k(SS, jrow, k), qf[k], acc);
+            for (int k = 0; k < SH::KSTEPS; ++k) acc = O::mma(sf[sl][k], qf[k], acc);
             if constexpr (GATE == kGateScalar) acc *= inter_scale;
-            // intra-chunk: O^T += V^T P^T over s-blocks 0..TB
             if constexpr (SH::BF) {
 #pragma unroll
                 for (int sp = 0; 2 * sp <= TB; ++sp)
-                    acc = O::mma(frag_tr(V, DVT, SH::SWV, 16 * jt, sp), O::from_acc(pt[2 * sp], pt[2 * sp + 1]), acc);
+                    acc = O::mma(vf[sl][sp], O::from_acc(pt[2 * sp], pt[2 * sp + 1]), acc);
             } else {
 #pragma unroll
-                for (int sb = 0; sb <= TB; ++sb) acc = O::mma(frag_tr(V, DVT, SH::SWV, 16 * jt, sb), O::from_acc(pt[sb]), acc);
+                for (int sb = 0; sb <= TB; ++sb) acc = O::mma(vf[sl][sb], O::from_acc(pt[sb]), acc);
             }
-            // lane holds O[t][16jt + 4grp + r]: stage it row-major
             *(V4 *)(stage + SH::ro(x, 16 * jj + 4 * grp)) = narrow4<T>(acc);
         }
         // read the block back row-contiguous and store 16-byte chunks (wave-local:
