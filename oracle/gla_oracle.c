@@ -39,6 +39,18 @@
  *
  * Layouts: contiguous [B][H][L][d] for q, k, v, o; g is [B][H][L][d_k] (key-dim
  * mode) or [B][H][L] (scalar mode) or unused; s0 / s_out are [B][H][d_k][d_v].
+ *
+ * Normalised form (gla_oracle_forward_norm): the "Transformers are RNNs" notes
+ * divide the kernel-weighted sum of values by the sum of the same weights, both
+ * written with the feature map, numerator over denominator.  Carried as a second,
+ * vector-valued state:
+ *
+ *       z_t = a (*) z_{t-1} + k~                          d_k vector, z_{-1} = z0 (or 0)
+ *       o_t[j] = (sum_i q~_i S_t[i][j]) / (sum_i q~_i z_t[i])
+ *
+ * Reading taken: with a gate, z decays with the same gate as S (it is the state of
+ * a value that is 1 in every token); the notes have no gate.  No epsilon is added
+ * to the denominator.  z0 / z_out are [B][H][d_k].
  */
 #include <math.h>
 #include <pthread.h>
@@ -56,15 +68,17 @@ static double feature(double x, int phi)
 }
 
 typedef struct {
-    const double *q, *k, *v, *g, *s0;
-    double *o, *s_out;
+    const double *q, *k, *v, *g, *s0, *z0;
+    double *o, *s_out, *z_out;
+    int norm;
     long B, H, L, dk, dv;
     int gate_mode, phi;
     long next_head;          /* shared work counter, guarded by lock */
     pthread_mutex_t lock;
 } job_t;
 
-static void run_head(const job_t *jb, long head, double *S, double *qf, double *kf, double *a)
+static void run_head(const job_t *jb, long head, double *S, double *qf, double *kf, double *a,
+                     double *z)
 {
     const long L = jb->L, dk = jb->dk, dv = jb->dv;
     const double *q = jb->q + head * L * dk;
@@ -74,6 +88,8 @@ static void run_head(const job_t *jb, long head, double *S, double *qf, double *
 
     if (jb->s0) memcpy(S, jb->s0 + head * dk * dv, sizeof(double) * dk * dv);
     else memset(S, 0, sizeof(double) * dk * dv);
+    if (jb->z0) memcpy(z, jb->z0 + head * dk, sizeof(double) * dk);
+    else memset(z, 0, sizeof(double) * dk);
 
     for (long t = 0; t < L; ++t) {
         for (long i = 0; i < dk; ++i) {
@@ -89,14 +105,24 @@ static void run_head(const job_t *jb, long head, double *S, double *qf, double *
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];
-        /* read-out from the updated state: o_t = S_t^T q~ */
+        /* normaliser state: the same decay, the feature-mapped key added */
+        double den = 1.0;
+        if (jb->norm) {
+            den = 0.0;
+            for (long i = 0; i < dk; ++i) {
+                z[i] = a[i] * z[i] + kf[i];
+                den += qf[i] * z[i];
+            }
+        }
+        /* read-out from the updated state: o_t = S_t^T q~ (normalised: / q~ . z_t) */
         for (long j = 0; j < dv; ++j) {
             double acc = 0.0;
             for (long i = 0; i < dk; ++i) acc += qf[i] * S[i * dv + j];
-            o[t * dv + j] = acc;
+            o[t * dv + j] = jb->norm ? acc / den : acc;
         }
     }
     if (jb->s_out) memcpy(jb->s_out + head * dk * dv, S, sizeof(double) * dk * dv);
+    if (jb->z_out) memcpy(jb->z_out + head * dk, z, sizeof(double) * dk);
 }
 
 static void *worker(void *arg)
@@ -106,26 +132,24 @@ static void *worker(void *arg)
     double *qf = (double *)malloc(sizeof(double) * jb->dk);
     double *kf = (double *)malloc(sizeof(double) * jb->dk);
     double *a = (double *)malloc(sizeof(double) * jb->dk);
-    if (S && qf && kf && a) {          /* on allocation failure take no head */
+    double *z = (double *)malloc(sizeof(double) * jb->dk);
+    if (S && qf && kf && a && z) {     /* on allocation failure take no head */
         for (;;) {
             pthread_mutex_lock(&jb->lock);
             long head = jb->next_head++;
             pthread_mutex_unlock(&jb->lock);
             if (head >= jb->B * jb->H) break;
-            run_head(jb, head, S, qf, kf, a);
+            run_head(jb, head, S, qf, kf, a, z);
         }
     }
-    free(S); free(qf); free(kf); free(a);
+    free(S); free(qf); free(kf); free(a); free(z);
     return NULL;
 }
 
-/*
- * Forward pass over all (b, h).  Returns 0 on success, -1 on bad arguments,
- * -2 if scratch memory could not be allocated.  nthreads <= 0 means 1.
- */
-int gla_oracle_forward(const double *q, const double *k, const double *v, const double *g,
-                       int gate_mode, int phi, const double *s0, double *o, double *s_out,
-                       long B, long H, long L, long dk, long dv, int nthreads)
+static int forward(const double *q, const double *k, const double *v, const double *g,
+                   int gate_mode, int phi, const double *s0, const double *z0, double *o,
+                   double *s_out, double *z_out, int norm, long B, long H, long L, long dk,
+                   long dv, int nthreads)
 {
     if (!q || !k || !v || !o || B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0) return -1;
     if (gate_mode != ORACLE_GATE_NONE && gate_mode != ORACLE_GATE_KEYDIM &&
@@ -135,6 +159,7 @@ int gla_oracle_forward(const double *q, const double *k, const double *v, const 
 
     job_t jb;
     jb.q = q; jb.k = k; jb.v = v; jb.g = g; jb.s0 = s0; jb.o = o; jb.s_out = s_out;
+    jb.z0 = z0; jb.z_out = z_out; jb.norm = norm;
     jb.B = B; jb.H = H; jb.L = L; jb.dk = dk; jb.dv = dv;
     jb.gate_mode = gate_mode; jb.phi = phi; jb.next_head = 0;
     pthread_mutex_init(&jb.lock, NULL);
@@ -157,4 +182,27 @@ int gla_oracle_forward(const double *q, const double *k, const double *v, const 
     /* a worker that failed took no head: if none succeeded, heads are left over */
     if (jb.next_head < B * H) return -2;
     return 0;
+}
+
+/*
+ * Forward pass over all (b, h).  Returns 0 on success, -1 on bad arguments,
+ * -2 if scratch memory could not be allocated.  nthreads <= 0 means 1.
+ */
+int gla_oracle_forward(const double *q, const double *k, const double *v, const double *g,
+                       int gate_mode, int phi, const double *s0, double *o, double *s_out,
+                       long B, long H, long L, long dk, long dv, int nthreads)
+{
+    return forward(q, k, v, g, gate_mode, phi, s0, NULL, o, s_out, NULL, 0, B, H, L, dk, dv,
+                   nthreads);
+}
+
+/* The normalised form (see the header): as gla_oracle_forward, plus the normaliser
+ * state z0 (nullable: zero) and z_out (nullable). */
+int gla_oracle_forward_norm(const double *q, const double *k, const double *v, const double *g,
+                            int gate_mode, int phi, const double *s0, const double *z0,
+                            double *o, double *s_out, double *z_out, long B, long H, long L,
+                            long dk, long dv, int nthreads)
+{
+    return forward(q, k, v, g, gate_mode, phi, s0, z0, o, s_out, z_out, 1, B, H, L, dk, dv,
+                   nthreads);
 }

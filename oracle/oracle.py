@@ -59,6 +59,10 @@ def _load(lib_path=None):
                                            ctypes.c_long, ctypes.c_long, ctypes.c_long,
                                            ctypes.c_long, ctypes.c_long, ctypes.c_int]
         lib.gla_oracle_forward.restype = ctypes.c_int
+        lib.gla_oracle_forward_norm.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, dp, dp, dp,
+                                                dp, dp, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                                ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        lib.gla_oracle_forward_norm.restype = ctypes.c_int
         _libs[lib_path] = lib
     return _libs[lib_path]
 
@@ -85,15 +89,7 @@ def default_threads() -> int:
         return max(1, os.cpu_count() or 1)
 
 
-def forward(q, k, v, g=None, gate=None, feature_map=None, s0=None, nthreads=None, lib_path=None):
-    """Run the recurrence over every (b, h).
-
-    q, k: [B, H, L, d_k]; v: [B, H, L, d_v]; g: [B, H, L, d_k] for gate="keydim",
-    [B, H, L] for gate="scalar", None for no gate; s0: [B, H, d_k, d_v] or None.
-    Returns (o [B, H, L, d_v], s_final [B, H, d_k, d_v]) as float64 arrays.
-    ``lib_path`` selects another build of the oracle source (the pin tests use it to
-    check that planted mistakes are caught); by default the committed source is used.
-    """
+def _prepare(q, k, v, g, gate, s0):
     q, k, v, g, s0 = _f64(q), _f64(k), _f64(v), _f64(g), _f64(s0)
     if q.ndim != 4 or k.shape != q.shape or v.ndim != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("oracle: q, k must be [B,H,L,d_k] and v [B,H,L,d_v]")
@@ -108,6 +104,19 @@ def forward(q, k, v, g=None, gate=None, feature_map=None, s0=None, nthreads=None
         g = None
     if s0 is not None and s0.shape != (B, H, dk, dv):
         raise ValueError("oracle: s0 must be [B,H,d_k,d_v]")
+    return q, k, v, g, s0, mode, (B, H, L, dk, dv)
+
+
+def forward(q, k, v, g=None, gate=None, feature_map=None, s0=None, nthreads=None, lib_path=None):
+    """Run the recurrence over every (b, h).
+
+    q, k: [B, H, L, d_k]; v: [B, H, L, d_v]; g: [B, H, L, d_k] for gate="keydim",
+    [B, H, L] for gate="scalar", None for no gate; s0: [B, H, d_k, d_v] or None.
+    Returns (o [B, H, L, d_v], s_final [B, H, d_k, d_v]) as float64 arrays.
+    ``lib_path`` selects another build of the oracle source (the pin tests use it to
+    check that planted mistakes are caught); by default the committed source is used.
+    """
+    q, k, v, g, s0, mode, (B, H, L, dk, dv) = _prepare(q, k, v, g, gate, s0)
     o = np.zeros((B, H, L, dv), dtype=np.float64)
     s = np.zeros((B, H, dk, dv), dtype=np.float64)
     nthreads = default_threads() if nthreads is None else int(nthreads)
@@ -117,3 +126,25 @@ def forward(q, k, v, g=None, gate=None, feature_map=None, s0=None, nthreads=None
     if rc != 0:
         raise RuntimeError("gla_oracle_forward failed with code %d" % rc)
     return o, s
+
+
+def forward_norm(q, k, v, g=None, gate=None, feature_map=None, s0=None, z0=None, nthreads=None,
+                 lib_path=None):
+    """The normalised form ("Transformers are RNNs" notes: weighted sum of values over
+    the sum of the weights): as ``forward``, with the normaliser state z carried
+    beside S (z_t = alpha_t * z_{t-1} + phi(k_t), o_t = S_t^T phi(q_t) / phi(q_t).z_t).
+    z0: [B, H, d_k] or None.  Returns (o, s_final, z_final) as float64 arrays."""
+    q, k, v, g, s0, mode, (B, H, L, dk, dv) = _prepare(q, k, v, g, gate, s0)
+    z0 = _f64(z0)
+    if z0 is not None and z0.shape != (B, H, dk):
+        raise ValueError("oracle: z0 must be [B,H,d_k]")
+    o = np.zeros((B, H, L, dv), dtype=np.float64)
+    s = np.zeros((B, H, dk, dv), dtype=np.float64)
+    z = np.zeros((B, H, dk), dtype=np.float64)
+    nthreads = default_threads() if nthreads is None else int(nthreads)
+    rc = _load(lib_path).gla_oracle_forward_norm(_ptr(q), _ptr(k), _ptr(v), _ptr(g), mode,
+                                         FEATURE_MAPS[feature_map], _ptr(s0), _ptr(z0), _ptr(o),
+                                         _ptr(s), _ptr(z), B, H, L, dk, dv, nthreads)
+    if rc != 0:
+        raise RuntimeError("gla_oracle_forward_norm failed with code %d" % rc)
+    return o, s, z

@@ -256,6 +256,97 @@ def pin_positive_monotone(fwd, seed=8, L=40, dk=4, dv=3):
     return float(np.min(np.diff(o[0, 0], axis=0)))
 
 
+# ---- the normalised form ("Transformers are RNNs" notes: numerator over denominator,
+# both with the feature map; with gates the denominator state decays like S) ----
+
+def pin_norm_quadratic(fwd_norm, seed=20, fm="elu1", B=2, H=2, L=29, dk=5, dv=4):
+    """alpha = 1: o_t = (W V)_t / (W 1)_t with W = (phi(Q) phi(K)^T) (.) L, L_ts = [s <= t]."""
+    q, k, v, _, _ = rng_inputs(seed, B, H, L, dk, dv)
+    o, _, _ = fwd_norm(q, k, v, feature_map=fm)
+    Lm = np.tril(np.ones((L, L)))
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            W = (_phi(q[b, h], fm) @ _phi(k[b, h], fm).T) * Lm
+            worst = max(worst, rel_err(o[b, h], (W @ v[b, h]) / W.sum(axis=1, keepdims=True)))
+    return worst
+
+
+def pin_norm_unrolled(fwd_norm, seed=21, gate="keydim", B=2, H=2, L=19, dk=4, dv=3):
+    """Gated, with initial states: numerator and denominator each in the unrolled form
+    (the denominator is the numerator of a value that is 1 in every token, its
+    initial state the column z0), and the final z as the explicit sum
+    z_L = sum_s phi(k_s) (.) prod_{m>s} alpha_m + prod_m alpha_m (.) z0."""
+    q, k, v, g, S0 = rng_inputs(seed, B, H, L, dk, dv, gate=gate, s0=True)
+    r = np.random.default_rng(seed + 1000)
+    z0 = r.random((B, H, dk)) + 0.5
+    qf, kf = _phi(q, "elu1"), _phi(k, "elu1")
+    o, _, z = fwd_norm(q, k, v, g=g, gate=gate, feature_map="elu1", s0=S0, z0=z0)
+    num = unrolled_reference(qf, kf, v, g, gate, S0)
+    den = unrolled_reference(qf, kf, np.ones((B, H, L, 1)), g, gate, z0[..., None])
+    worst = rel_err(o, num / den)
+    for b in range(B):
+        for h in range(H):
+            if gate == "keydim":
+                alpha = np.exp(g[b, h])
+            elif gate == "scalar":
+                alpha = np.repeat(np.exp(g[b, h])[:, None], dk, axis=1)
+            else:
+                alpha = np.ones((L, dk))
+            zz = np.prod(alpha, axis=0) * z0[b, h]
+            for s_ in range(L):
+                zz = zz + kf[b, h, s_] * np.prod(alpha[s_ + 1:], axis=0)
+            worst = max(worst, rel_err(z[b, h], zz))
+    return worst
+
+
+def pin_norm_constant_value(fwd_norm, seed=22, B=2, H=2, L=17, dk=3, dv=4):
+    """Every value equal to one vector c, zero initial states: every output is c (a
+    weighted average of copies of c), with any gate and positive features."""
+    q, k, _, g, _ = rng_inputs(seed, B, H, L, dk, dv, gate="keydim")
+    c = np.array([0.5, -2.0, 3.25, 1.0])[:dv]
+    v = np.broadcast_to(c, (B, H, L, dv)).copy()
+    o, _, _ = fwd_norm(q, k, v, g=g, gate="keydim", feature_map="elu1")
+    return rel_err(o, np.broadcast_to(c, o.shape))
+
+
+def pin_norm_chaining(fwd_norm, seed=23, B=2, H=2, L1=13, L2=9, dk=4, dv=3):
+    """run(L1 + L2) equals run(L1) followed by run(L2) from its (S, z): the same
+    operations in the same order, so bit for bit."""
+    q, k, v, g, S0 = rng_inputs(seed, B, H, L1 + L2, dk, dv, gate="scalar", s0=True)
+    o, s, z = fwd_norm(q, k, v, g=g, gate="scalar", feature_map="elu1", s0=S0)
+    o1, s1, z1 = fwd_norm(q[:, :, :L1], k[:, :, :L1], v[:, :, :L1], g=g[:, :, :L1], gate="scalar",
+                          feature_map="elu1", s0=S0)
+    o2, s2, z2 = fwd_norm(q[:, :, L1:], k[:, :, L1:], v[:, :, L1:], g=g[:, :, L1:], gate="scalar",
+                          feature_map="elu1", s0=s1, z0=z1)
+    with np.errstate(invalid="ignore"):            # a broken oracle may give NaN: reported as NaN
+        return float(max(np.abs(o - np.concatenate([o1, o2], axis=2)).max(), np.abs(s - s2).max(),
+                         np.abs(z - z2).max()))
+
+
+def norm_convexity_violation(fwd_norm, seed=24, B=2, H=2, L=31, dk=4, dv=5):
+    """Positive features and gates in (0, 1]: each output coordinate is a convex
+    combination of that coordinate over the values so far.  Returns the largest
+    amount by which an output leaves [min_{s<=t} v_s, max_{s<=t} v_s] (0 when none)."""
+    q, k, v, g, _ = rng_inputs(seed, B, H, L, dk, dv, gate="keydim")
+    o, _, _ = fwd_norm(q, k, v, g=g, gate="keydim", feature_map="elu1")
+    lo = np.minimum.accumulate(v, axis=2)
+    hi = np.maximum.accumulate(v, axis=2)
+    return float(max(0.0, (lo - o).max(), (o - hi).max()))
+
+
+NORM_ERROR_PINS = {
+    # name: (callable on forward_norm, tolerance)
+    "norm_quadratic_elu1": (pin_norm_quadratic, 1e-12),
+    "norm_unrolled_keydim": (pin_norm_unrolled, 1e-12),
+    "norm_unrolled_scalar": (lambda f: pin_norm_unrolled(f, seed=25, gate="scalar"), 1e-12),
+    "norm_unrolled_none": (lambda f: pin_norm_unrolled(f, seed=26, gate=None), 1e-12),
+    "norm_constant_value": (pin_norm_constant_value, 1e-14),
+    "norm_chaining": (pin_norm_chaining, 0.0),
+    "norm_convexity": (norm_convexity_violation, 1e-12),
+}
+
+
 ALL_ERROR_PINS = {
     # name: (callable, tolerance); each returns an error that must stay below tolerance
     "feature_map_points": (pin_feature_map_points, 1e-15),

@@ -35,26 +35,36 @@ MUTANTS = {
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];
-        /* read-out from the updated state: o_t = S_t^T q~ */
-        for (long j = 0; j < dv; ++j) {
-            double acc = 0.0;
-            for (long i = 0; i < dk; ++i) acc += qf[i] * S[i * dv + j];
-            o[t * dv + j] = acc;
-        }""",
-         """        for (long j = 0; j < dv; ++j) {
-            double acc = 0.0;
-            for (long i = 0; i < dk; ++i) acc += qf[i] * S[i * dv + j];
-            o[t * dv + j] = acc;
+""", ""),
+        ("""            o[t * dv + j] = jb->norm ? acc / den : acc;
+        }""", """            o[t * dv + j] = jb->norm ? acc / den : acc;
         }
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];""")],
     "off_by_one_value_row": [(UPDATE, "S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[(t > 0 ? t - 1 : 0) * dv + j];")],
+    # the normalised form
+    "norm_z_no_decay": [("z[i] = a[i] * z[i] + kf[i];", "z[i] = z[i] + kf[i];")],
+    "norm_den_uses_key": [("den += qf[i] * z[i];", "den += kf[i] * z[i];")],
+    "norm_exclusive_den": [("""                z[i] = a[i] * z[i] + kf[i];
+                den += qf[i] * z[i];""", """                den += qf[i] * z[i];
+                z[i] = a[i] * z[i] + kf[i];""")],
+    "norm_z0_ignored": [("if (jb->z0) memcpy", "if (0) memcpy")],
+    "norm_not_divided": [("o[t * dv + j] = jb->norm ? acc / den : acc;", "o[t * dv + j] = acc;")],
+    "norm_z_value_weighted": [("z[i] = a[i] * z[i] + kf[i];", "z[i] = a[i] * z[i] + kf[i] * v[t * dv];")],
 }
 
 
-def _pin_results(fwd):
+def _pin_results(fwd, fwd_norm):
     failed = []
+    for name, (fn, tol) in pins.NORM_ERROR_PINS.items():
+        try:
+            err = fn(fwd_norm)
+        except AssertionError:
+            failed.append(name)
+            continue
+        if not err <= tol:
+            failed.append(name)
     for name, (fn, tol) in pins.ALL_ERROR_PINS.items():
         try:
             err = fn(fwd)
@@ -81,5 +91,6 @@ def test_pins_reject_planted_mistake(mutant, tmp_path):
     c_path.write_text(src)
     lib = oracle.compile_source(str(c_path), str(tmp_path / ("libmutant_%s.so" % mutant)))
     fwd = functools.partial(oracle.forward, lib_path=lib)
-    failed = _pin_results(fwd)
+    fwd_norm = functools.partial(oracle.forward_norm, lib_path=lib)
+    failed = _pin_results(fwd, fwd_norm)
     assert failed, "planted mistake %r passed every pin" % mutant

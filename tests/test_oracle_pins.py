@@ -20,6 +20,21 @@ def test_oracle_pin(name):
     assert err <= tol, "%s: error %.3e above %.1e" % (name, err, tol)
 
 
+@pytest.mark.parametrize("name", sorted(pins.NORM_ERROR_PINS))
+def test_oracle_norm_pin(name):
+    fn, tol = pins.NORM_ERROR_PINS[name]
+    err = fn(oracle.forward_norm)
+    assert err <= tol, "%s: error %.3e above %.1e" % (name, err, tol)
+
+
+def test_oracle_norm_matches_unnormalised_state():
+    """The normalised entry carries S exactly as the plain one does."""
+    q, k, v, g, S0 = pins.rng_inputs(27, 2, 3, 21, 5, 4, gate="keydim", s0=True)
+    _, s1 = oracle.forward(q, k, v, g=g, gate="keydim", feature_map="elu1", s0=S0)
+    _, s2, _ = oracle.forward_norm(q, k, v, g=g, gate="keydim", feature_map="elu1", s0=S0)
+    assert np.array_equal(s1, s2)
+
+
 def test_oracle_positive_monotone():
     assert pins.pin_positive_monotone(oracle.forward) > 0.0
 
