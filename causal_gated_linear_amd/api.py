@@ -46,16 +46,7 @@ def workspace_bytes(B, H, L, d_k, d_v, chunk, dtype=torch.bfloat16) -> int:
     return int(_lib.load().gla_prefill_workspace_bytes(B, H, L, d_k, d_v, chunk, _DTYPES[dtype]))
 
 
-def prefill(q, k, v, log_gate=None, gate=None, initial_state=None, chunk=64, feature_map=None,
-            out=None, final_state=None, workspace=None, stream=None):
-    """Chunkwise GLA prefill (gla_prefill_chunked).
-
-    q, k: [B, H, L, d_k]; v: [B, H, L, d_v] (fp32 or bf16, same dtype, CUDA);
-    log_gate: fp32 [B, H, L, d_k] (gate="keydim") or [B, H, L] (gate="scalar");
-    initial_state: fp32 [B, H, d_k, d_v] or None.  Returns (o, s_final).
-    ``final_state`` may be ``initial_state`` to update it in place.
-    """
-    lib = _lib.load()
+def _check_prefill(q, k, v, log_gate, gate, initial_state):
     _need(q.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D [B, H, L, d]")
     B, H, L, dk = q.shape
     dv = v.shape[3]
@@ -75,6 +66,20 @@ def prefill(q, k, v, log_gate=None, gate=None, initial_state=None, chunk=64, fea
     if initial_state is not None:
         _check_tensor(initial_state, "initial_state", (B, H, dk, dv), torch.float32, dev)
     _need(dev.type == "cuda", "tensors must be on a GPU device")
+    return B, H, L, dk, dv, dev, dt, gate
+
+
+def prefill(q, k, v, log_gate=None, gate=None, initial_state=None, chunk=64, feature_map=None,
+            out=None, final_state=None, workspace=None, stream=None):
+    """Chunkwise GLA prefill (gla_prefill_chunked).
+
+    q, k: [B, H, L, d_k]; v: [B, H, L, d_v] (fp32 or bf16, same dtype, CUDA);
+    log_gate: fp32 [B, H, L, d_k] (gate="keydim") or [B, H, L] (gate="scalar");
+    initial_state: fp32 [B, H, d_k, d_v] or None.  Returns (o, s_final).
+    ``final_state`` may be ``initial_state`` to update it in place.
+    """
+    lib = _lib.load()
+    B, H, L, dk, dv, dev, dt, gate = _check_prefill(q, k, v, log_gate, gate, initial_state)
     if out is None:
         out = torch.empty((B, H, L, dv), dtype=dt, device=dev)
     else:
@@ -98,12 +103,36 @@ def prefill(q, k, v, log_gate=None, gate=None, initial_state=None, chunk=64, fea
     return out, final_state
 
 
-def decode_step(q, k, v, log_gate=None, state=None, gate=None, feature_map=None, out=None,
-                stream=None):
-    """One recurrent step (gla_decode_step); ``state`` [B, H, d_k, d_v] fp32 is updated
-    in place.  q, k: [B, H, d_k]; v: [B, H, d_v]; log_gate: fp32 [B, H, d_k] (keydim)
-    or [B, H] (scalar).  Returns o [B, H, d_v]."""
+def prefill_norm(q, k, v, log_gate=None, gate=None, initial_state=None, initial_norm=None, chunk=64,
+                 feature_map=None, out=None, final_state=None, final_norm=None, stream=None):
+    """Normalised chunkwise prefill (gla_prefill_chunked_norm): as ``prefill``, with the
+    normaliser state z (fp32 [B, H, d_k]); o_t = S_t^T phi(q_t) / phi(q_t) . z_t.
+    Returns (o, s_final, z_final); ``final_norm`` may be ``initial_norm`` (in place)."""
     lib = _lib.load()
+    B, H, L, dk, dv, dev, dt, gate = _check_prefill(q, k, v, log_gate, gate, initial_state)
+    if initial_norm is not None:
+        _check_tensor(initial_norm, "initial_norm", (B, H, dk), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor(out, "out", (B, H, L, dv), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
+    if final_norm is None:
+        final_norm = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor(final_norm, "final_norm", (B, H, dk), torch.float32, dev)
+    st = lib.gla_prefill_chunked_norm(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _lib.GATES[gate],
+                                      _ptr(initial_state), _ptr(initial_norm), _ptr(out),
+                                      _ptr(final_state), _ptr(final_norm), B, H, L, dk, dv, int(chunk),
+                                      _DTYPES[dt], _lib.FEATURE_MAPS[feature_map], _stream_handle(stream))
+    _lib.check(st, "gla_prefill_chunked_norm")
+    return out, final_state, final_norm
+
+
+def _check_decode(q, k, v, log_gate, gate, state, out):
     _need(q.dim() == 3 and v.dim() == 3, "q, k, v must be 3-D [B, H, d]")
     B, H, dk = q.shape
     dv = v.shape[2]
@@ -127,10 +156,35 @@ def decode_step(q, k, v, log_gate=None, state=None, gate=None, feature_map=None,
         out = torch.empty((B, H, dv), dtype=dt, device=dev)
     else:
         _check_tensor(out, "out", (B, H, dv), dt, dev)
+    return B, H, dk, dv, dev, dt, gate, out
+
+
+def decode_step(q, k, v, log_gate=None, state=None, gate=None, feature_map=None, out=None,
+                stream=None):
+    """One recurrent step (gla_decode_step); ``state`` [B, H, d_k, d_v] fp32 is updated
+    in place.  q, k: [B, H, d_k]; v: [B, H, d_v]; log_gate: fp32 [B, H, d_k] (keydim)
+    or [B, H] (scalar).  Returns o [B, H, d_v]."""
+    lib = _lib.load()
+    B, H, dk, dv, dev, dt, gate, out = _check_decode(q, k, v, log_gate, gate, state, out)
     st = lib.gla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _lib.GATES[gate],
                              _ptr(state), _ptr(out), B, H, dk, dv, _DTYPES[dt],
                              _lib.FEATURE_MAPS[feature_map], _stream_handle(stream))
     _lib.check(st, "gla_decode_step")
+    return out
+
+
+def decode_step_norm(q, k, v, log_gate=None, state=None, norm=None, gate=None, feature_map=None,
+                     out=None, stream=None):
+    """One step of the normalised recurrence (gla_decode_step_norm); ``state`` and the
+    normaliser state ``norm`` (fp32 [B, H, d_k]) are updated in place.  Returns o."""
+    lib = _lib.load()
+    B, H, dk, dv, dev, dt, gate, out = _check_decode(q, k, v, log_gate, gate, state, out)
+    _need(norm is not None, "norm (the normaliser state) is required")
+    _check_tensor(norm, "norm", (B, H, dk), torch.float32, dev)
+    st = lib.gla_decode_step_norm(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _lib.GATES[gate],
+                                  _ptr(state), _ptr(norm), _ptr(out), B, H, dk, dv, _DTYPES[dt],
+                                  _lib.FEATURE_MAPS[feature_map], _stream_handle(stream))
+    _lib.check(st, "gla_decode_step_norm")
     return out
 
 

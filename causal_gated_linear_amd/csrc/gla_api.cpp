@@ -243,11 +243,13 @@ size_t gla_prefill_workspace_bytes(int B, int H, int L, int d_k, int d_v, int ch
     return gla::prefill_workspace(p, BH, d_k, d_v);
 }
 
-int gla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
-                        gla_gate_mode gate, const float *s0, void *o, float *s_final,
-                        int B, int H, int L, int d_k, int d_v, int chunk, gla_dtype dtype,
-                        gla_feature_map phi, void *workspace, size_t workspace_bytes,
-                        gla_stream_t stream)
+// Both prefill entry points.  norm: the normalised form, with the normaliser state
+// z0 (nullable) / z_final (nullable); it runs unsegmented and needs no workspace.
+static int prefill_impl(const void *q, const void *k, const void *v, const float *g,
+                        gla_gate_mode gate, const float *s0, const float *z0, void *o, float *s_final,
+                        float *z_final, int B, int H, int L, int d_k, int d_v, int chunk,
+                        gla_dtype dtype, gla_feature_map phi, void *workspace,
+                        size_t workspace_bytes, gla_stream_t stream, bool norm)
 {
     if (L < 0) return fail(GLA_ERR_SHAPE, "L=%d must be >= 0", L);
     int st = check_common(B, H, d_k, d_v, dtype, gate, phi, g, L > 0);
@@ -260,12 +262,12 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
         return fail(GLA_ERR_SHAPE, "L=%d too long for one head (limit (L + chunk) * max(d_k, d_v) * 4 < 2^31)", L);
     if (L > 0 && (!q || !k || !v || !o))
         return fail(GLA_ERR_NULL, "q, k, v and o are required when L > 0");
-    const void *ptrs[] = {q, k, v, s0, o, s_final, workspace};
-    const char *names[] = {"q", "k", "v", "s0", "o", "s_final", "workspace"};
-    for (int i = 0; i < 7; ++i)
+    const void *ptrs[] = {q, k, v, s0, o, s_final, workspace, z0, z_final};
+    const char *names[] = {"q", "k", "v", "s0", "o", "s_final", "workspace", "z0", "z_final"};
+    for (int i = 0; i < 9; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
-    const size_t need = gla_prefill_workspace_bytes(B, H, L, d_k, d_v, chunk, dtype);
+    const size_t need = norm ? 0 : gla_prefill_workspace_bytes(B, H, L, d_k, d_v, chunk, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -277,26 +279,35 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
     const Span sv = span(v, BH * L * d_v * es, "v"), sg = span(g, g ? gbytes : 0, "g");
     const Span ss0 = span(s0, sbytes, "s0"), so = span(o, BH * L * d_v * es, "o");
     const Span ssf = span(s_final, sbytes, "s_final"), sw = span(workspace, need, "workspace");
-    const Span o_forbidden[] = {sq, sk, sv, sg, ss0, ssf, sw};
+    const size_t zbytes = BH * d_k * 4;
+    const Span sz0 = span(z0, zbytes, "z0"), szf = span(z_final, zbytes, "z_final");
+    const Span o_forbidden[] = {sq, sk, sv, sg, ss0, ssf, sw, sz0, szf};
     for (const Span &x : o_forbidden)
         if (overlap(so, x)) return fail(GLA_ERR_ALIAS, "o overlaps %s", x.name);
-    const Span sf_forbidden[] = {sq, sk, sv, sg, sw};
+    const Span sf_forbidden[] = {sq, sk, sv, sg, sw, sz0, szf};
     for (const Span &x : sf_forbidden)
         if (overlap(ssf, x)) return fail(GLA_ERR_ALIAS, "s_final overlaps %s", x.name);
     if (overlap(ssf, ss0) && s_final != s0)
         return fail(GLA_ERR_ALIAS, "s_final partially overlaps s0");
+    const Span zf_forbidden[] = {sq, sk, sv, sg, sw, ss0};
+    for (const Span &x : zf_forbidden)
+        if (overlap(szf, x)) return fail(GLA_ERR_ALIAS, "z_final overlaps %s", x.name);
+    if (overlap(szf, sz0) && z_final != z0)
+        return fail(GLA_ERR_ALIAS, "z_final partially overlaps z0");
 
-    const gla::PrefillPlan plan = gla::prefill_plan((int)BH, L, d_k, d_v, chunk, (int)es);
+    gla::PrefillPlan plan = gla::prefill_plan((int)BH, L, d_k, d_v, chunk, (int)es);
+    if (norm) plan = {gla::prefill_tile((int)BH, d_k, d_v, chunk, (int)es), 1, L};
     gla::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s0 = s0; a.o = o; a.s_final = s_final;
     a.BH = (int)BH; a.L = L; a.d_v = d_v;
     a.gate = (int)gate; a.elu1 = phi == GLA_PHI_ELU1;
     a.n_vt = d_v / plan.dvt;
     a.nseg = plan.nseg; a.seg_len = plan.seg_len; a.gam = nullptr;
+    a.norm = norm ? 1 : 0; a.z0 = z0; a.z_final = z_final;
     const long grid = (long)BH * a.nseg * a.n_vt;
     if (grid > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H too large");
     a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
-    if (L == 0 && !s_final) return ok();
+    if (L == 0 && !s_final && !z_final) return ok();
     const int dt = dtype == GLA_BF16 ? 1 : 0;
     const hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
@@ -322,17 +333,38 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
     return ok();
 }
 
-int gla_decode_step(const void *q, const void *k, const void *v, const float *g,
-                    gla_gate_mode gate, float *state, void *o, int B, int H, int d_k, int d_v,
-                    gla_dtype dtype, gla_feature_map phi, gla_stream_t stream)
+int gla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
+                        gla_gate_mode gate, const float *s0, void *o, float *s_final,
+                        int B, int H, int L, int d_k, int d_v, int chunk, gla_dtype dtype,
+                        gla_feature_map phi, void *workspace, size_t workspace_bytes,
+                        gla_stream_t stream)
+{
+    return prefill_impl(q, k, v, g, gate, s0, nullptr, o, s_final, nullptr, B, H, L, d_k, d_v, chunk,
+                        dtype, phi, workspace, workspace_bytes, stream, false);
+}
+
+int gla_prefill_chunked_norm(const void *q, const void *k, const void *v, const float *g,
+                             gla_gate_mode gate, const float *s0, const float *z0, void *o,
+                             float *s_final, float *z_final, int B, int H, int L, int d_k,
+                             int d_v, int chunk, gla_dtype dtype, gla_feature_map phi,
+                             gla_stream_t stream)
+{
+    return prefill_impl(q, k, v, g, gate, s0, z0, o, s_final, z_final, B, H, L, d_k, d_v, chunk, dtype,
+                        phi, nullptr, 0, stream, true);
+}
+
+// Both decode entry points; z non-null selects the normalised form.
+static int decode_impl(const void *q, const void *k, const void *v, const float *g,
+                       gla_gate_mode gate, float *state, float *z, void *o, int B, int H, int d_k,
+                       int d_v, gla_dtype dtype, gla_feature_map phi, gla_stream_t stream)
 {
     int st = check_common(B, H, d_k, d_v, dtype, gate, phi, g, true);
     if (st != GLA_OK) return st;
     if (!q || !k || !v || !state || !o)
         return fail(GLA_ERR_NULL, "q, k, v, state and o are required");
-    const void *ptrs[] = {q, k, v, state, o};
-    const char *names[] = {"q", "k", "v", "state", "o"};
-    for (int i = 0; i < 5; ++i)
+    const void *ptrs[] = {q, k, v, state, o, z};
+    const char *names[] = {"q", "k", "v", "state", "o", "z"};
+    for (int i = 0; i < 6; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
     const size_t BH = (size_t)B * H, es = elem_size(dtype);
@@ -340,20 +372,39 @@ int gla_decode_step(const void *q, const void *k, const void *v, const float *g,
     const Span sq = span(q, BH * d_k * es, "q"), sk = span(k, BH * d_k * es, "k");
     const Span sv = span(v, BH * d_v * es, "v"), sg = span(g, g ? gbytes : 0, "g");
     const Span sst = span(state, BH * d_k * d_v * 4, "state"), so = span(o, BH * d_v * es, "o");
-    const Span o_forbidden[] = {sq, sk, sv, sg, sst};
+    const Span sz = span(z, BH * d_k * 4, "z");
+    const Span o_forbidden[] = {sq, sk, sv, sg, sst, sz};
     for (const Span &x : o_forbidden)
         if (overlap(so, x)) return fail(GLA_ERR_ALIAS, "o overlaps %s", x.name);
-    const Span st_forbidden[] = {sq, sk, sv, sg};
+    const Span st_forbidden[] = {sq, sk, sv, sg, sz};
     for (const Span &x : st_forbidden)
         if (overlap(sst, x)) return fail(GLA_ERR_ALIAS, "state overlaps %s", x.name);
+    const Span z_forbidden[] = {sq, sk, sv, sg};
+    for (const Span &x : z_forbidden)
+        if (overlap(sz, x)) return fail(GLA_ERR_ALIAS, "z overlaps %s", x.name);
     if (BH > 0x7fffffffUL) return fail(GLA_ERR_SHAPE, "B*H too large");
 
     gla::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.state = state; a.o = o;
-    a.BH = (int)BH; a.gate = (int)gate; a.elu1 = phi == GLA_PHI_ELU1;
+    a.BH = (int)BH; a.gate = (int)gate; a.elu1 = phi == GLA_PHI_ELU1; a.z = z;
     hipError_t e = gla::launch_decode(a, dtype == GLA_BF16 ? 1 : 0, d_k, d_v, (hipStream_t)stream);
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+int gla_decode_step(const void *q, const void *k, const void *v, const float *g,
+                    gla_gate_mode gate, float *state, void *o, int B, int H, int d_k, int d_v,
+                    gla_dtype dtype, gla_feature_map phi, gla_stream_t stream)
+{
+    return decode_impl(q, k, v, g, gate, state, nullptr, o, B, H, d_k, d_v, dtype, phi, stream);
+}
+
+int gla_decode_step_norm(const void *q, const void *k, const void *v, const float *g,
+                         gla_gate_mode gate, float *state, float *z, void *o, int B, int H, int d_k,
+                         int d_v, gla_dtype dtype, gla_feature_map phi, gla_stream_t stream)
+{
+    if (!z) return fail(GLA_ERR_NULL, "z (the normaliser state) is required");
+    return decode_impl(q, k, v, g, gate, state, z, o, B, H, d_k, d_v, dtype, phi, stream);
 }
 
 }  // extern "C"

@@ -12,12 +12,16 @@
 // group and every RS-th row, issues all of its state loads before using any
 // (the row loop is fully unrolled), and the column partial sums of o are reduced
 // across rows through LDS.  Row accesses are contiguous 16-byte vectors.
+//
+// Normalised form ("Transformers are RNNs" notes, numerator over denominator): the
+// normaliser state z, the state of a value that is 1 in every token, is updated in
+// place beside S, z_i <- alpha_i z_i + phi(k)_i, and o is divided by phi(q) . z.
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
 
 namespace gla {
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool NM>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a)
 {
     constexpr int CQ = DV / 4;                               // float4 groups per row
@@ -28,6 +32,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a)
 
     __shared__ float sq[DK], sk[DK], sa[DK];
     __shared__ f32x4 sred[RS][CQ];
+    __shared__ float sden[NM ? DK : 1];
 
     const int tid = threadIdx.x;
     const size_t bh = blockIdx.x;
@@ -42,6 +47,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a)
         if (a.gate == kGateKeydim) al = exp2_fast(a.g[bh * DK + tid] * kLog2e);
         else if (a.gate == kGateScalar) al = exp2_fast(a.g[bh] * kLog2e);
         sa[tid] = al;
+        if constexpr (NM) {                        // z_i <- alpha_i z_i + phi(k)_i; q~_i z_i
+            float *zp = a.z + bh * DK + tid;
+            const float z = al * *zp + sk[tid];
+            *zp = z;
+            sden[tid] = sq[tid] * z;
+        }
     }
 
     const int c = tid % CQ, r0 = tid / CQ;
@@ -68,6 +79,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a)
         f32x4 acc = sred[0][tid];
 #pragma unroll
         for (int r = 1; r < RS; ++r) acc += sred[r][tid];
+        if constexpr (NM) {
+            float den = 0.f;
+            for (int i = 0; i < DK; ++i) den += sden[i];
+            acc *= 1.f / den;
+        }
         store4((T *)a.o + bh * DV + 4 * tid, acc);
     }
 }
@@ -77,7 +93,8 @@ static hipError_t launch_decode_inst(const DecodeArgs &a, hipStream_t stream)
 {
     constexpr int CQ = DV / 4;
     constexpr int NT = (DK * CQ) < 256 ? (DK * CQ) : 256;
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(a.BH), dim3(NT), 0, stream, a);
+    if (a.z) hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3(a.BH), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3(a.BH), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -24,6 +24,10 @@ struct PrefillArgs {
     // then indexed [BH][nseg][d_k][d_v].  nseg = 1, seg_len = L: whole sequences.
     int nseg, seg_len;
     float *gam;              // state-only pass: segment totals of the log2-gates [BH][nseg][d_k]
+    // normalised form: outputs divided by phi(q) . z, z the normaliser state
+    int norm;
+    const float *z0;         // [B][H][d_k] or null
+    float *z_final;          // [B][H][d_k] or null
 };
 
 struct DecodeArgs {
@@ -33,6 +37,7 @@ struct DecodeArgs {
     void *o;                 // [B][H][d_v], T
     int BH;
     int gate, elu1;
+    float *z;                // normalised form: [B][H][d_k], in/out; null otherwise
 };
 
 // LDS bytes of a prefill workgroup (an upper bound, alignment included): `nbuf`

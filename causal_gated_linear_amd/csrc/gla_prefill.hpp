@@ -265,7 +265,12 @@ __device__ __forceinline__ float buf_load4(Rsrc r, int off)
 // SO (state only): the first pass of a segmented prefill.  Each workgroup runs the
 // state recurrence over its segment from a zero state and stores that state and the
 // segment's gate totals; no outputs, no Q~.
-template <typename T, int DK, int C, int DVT, int GATE, bool ELU1, bool SO>
+// NM (normalised, "Transformers are RNNs" notes: the weighted sum of values over the
+// sum of the same weights): the consumers also carry the normaliser state z, the
+// state of a value that is 1 in every token, z <- Diag(e^Gamma)(z + K^^T 1), with the
+// matrix cores (a fragment of ones as the value operand); each output row is divided
+// by its denominator Q~_t . z + sum_{s<=t} P_ts.
+template <typename T, int DK, int C, int DVT, int GATE, bool ELU1, bool SO, bool NM>
 __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_kernel(const PrefillArgs a)
 {
     using SH = PrefillShape<T, DK, C, DVT>;
@@ -287,6 +292,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     __shared__ __attribute__((aligned(16))) T sO[NC][16 * SH::DVS];  // output staging, per consumer
     __shared__ __attribute__((aligned(16))) float sEG[NBUF][DK];     // exp(Gamma_i)
     __shared__ __attribute__((aligned(16))) float sB[NBUF][C + 1];   // scalar gate: B_t, then Gamma (log2)
+    __shared__ __attribute__((aligned(16))) float sZ[NM ? 2 : 1][NM ? DK : 4];   // normaliser z, by parity
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -513,6 +519,12 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     f32x4 S[NSLOT];
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // normaliser tiles: consumer c holds z rows 16 it + 4 grp + r for it = c + NC m
+    constexpr int NZ = NM ? (NKB + NC - 1) / NC : 0;
+    f32x4 Z[NZ > 0 ? NZ : 1];
+#pragma unroll
+    for (int m = 0; m < NZ; ++m) Z[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto z_ok = [&](int m) __attribute__((always_inline)) -> bool { return c + NC * m < NKB; };
     // initial state (consumers, inside their own branch below, so that these loads
     // are never pending on the producers' path)
     auto load_s0 = [&]() __attribute__((always_inline)) {
@@ -528,6 +540,29 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     S[k][r] = ok ? v : 0.f;
                 }
             }
+        }
+    };
+
+    auto load_z0 = [&]() __attribute__((always_inline)) {
+        if constexpr (NM) {
+            if (a.z0) {
+#pragma unroll
+                for (int m = 0; m < NZ; ++m) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * (z_ok(m) ? c + NC * m : 0) + 4 * grp + r;
+                        const float v = a.z0[(size_t)bhs * DK + i];
+                        Z[m][r] = z_ok(m) ? v : 0.f;
+                    }
+                }
+            }
+        }
+    };
+    auto write_z = [&](int par) __attribute__((always_inline)) {     // -> fp32 rows for the denominators
+        if constexpr (NM) {
+#pragma unroll
+            for (int m = 0; m < NZ; ++m)
+                if (z_ok(m) && x == 0) *(f32x4 *)(sZ[par] + 16 * (c + NC * m) + 4 * grp) = Z[m];
         }
     };
 
@@ -571,7 +606,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 
     // Outputs of the 16-row block TB of the chunk starting at t0 (straight-line code:
     // TB is a compile-time constant, so every tile loop below is unrolled).
-    auto out_block = [&](auto tbc, int j0, int t0, int nvalid, int buf, const T *Q, const T *K,
+    auto out_block = [&](auto tbc, int j0, int t0, int nvalid, int buf, int par, const T *Q, const T *K,
                          const T *V, const T *SS) __attribute__((always_inline)) {
         constexpr int TB = decltype(tbc)::value;
         const int t = 16 * TB + x;
@@ -610,6 +645,26 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         pt[TB + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
         float inter_scale = 1.f;
         if constexpr (GATE == kGateScalar) inter_scale = exp2_fast(sB[buf][t]);
+        // normalised: denominator of row t = Q~_t . z + sum_{s <= t} P_ts; a lane sums
+        // its share, the four lane groups of column x are then added
+        float rden = 1.f;
+        if constexpr (NM) {
+            float dz = 0.f, dp = 0.f;
+#pragma unroll
+            for (int k = 0; k < SH::KSTEPS; ++k) {
+                constexpr int NE = sizeof(F) / sizeof(T);
+                const int i0 = SH::SW * k + (SH::BF ? 8 : 4) * grp;
+#pragma unroll
+                for (int e = 0; e < NE; ++e)
+                    if (!SH::BF || DK % 32 == 0 || i0 + e < DK) dz += to_f32(qf[k][e]) * sZ[par][i0 + e];
+            }
+#pragma unroll
+            for (int sb = 0; sb <= TB; ++sb) dp += pt[sb][0] + pt[sb][1] + pt[sb][2] + pt[sb][3];
+            float den = dz * inter_scale + dp;
+            den += __shfl_xor(den, 16, 64);
+            den += __shfl_xor(den, 32, 64);
+            rden = 1.f / den;
+        }
         T *stage = sO[c];
         // value tiles in order; the next tile's state and value fragments are requested
         // before the current tile's products (two register slots), so LDS latency
@@ -641,6 +696,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
                 for (int sb = 0; sb <= TB; ++sb) acc = O::mma(vf[sl][sb], O::from_acc(pt[sb]), acc);
             }
+            if constexpr (NM) acc *= rden;
             *(V4 *)(stage + SH::ro(x, 16 * jj + 4 * grp)) = narrow4<T>(acc);
         }
         // read the block back row-contiguous and store 16-byte chunks (wave-local:
@@ -671,9 +727,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         if constexpr (!SO) static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
             constexpr int TB = decltype(tbc)::value;
             if constexpr (NTB <= NC) {
-                if (c < NTB * SH::JS && TB == c % NTB) out_block(tbc, (c / NTB) * SH::NJC, t0, nvalid, buf, Q, K, V, SS);
+                if (c < NTB * SH::JS && TB == c % NTB) out_block(tbc, (c / NTB) * SH::NJC, t0, nvalid, buf, par, Q, K, V, SS);
             } else {
-                if (TB % NC == c) out_block(tbc, 0, t0, nvalid, buf, Q, K, V, SS);
+                if (TB % NC == c) out_block(tbc, 0, t0, nvalid, buf, par, Q, K, V, SS);
             }
         });
         // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
@@ -713,6 +769,32 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     S[k] = acc;
                 }
             }
+        }
+        if constexpr (NM) {                        // z <- Diag(e^Gamma)(z + K^^T 1)
+            // the value-1 operand, 0 for rows past L (their keys are phi(0), not 0,
+            // under elu+1)
+            F ones[SH::CSTEPS];
+#pragma unroll
+            for (int cs = 0; cs < SH::CSTEPS; ++cs) {
+#pragma unroll
+                for (int e = 0; e < (int)(sizeof(F) / sizeof(T)); ++e) {
+                    const int s = SH::BF ? 32 * cs + 4 * grp + (e & 3) + 16 * (e >> 2) : 16 * cs + 4 * grp + e;
+                    ones[cs][e] = from_f32<T>(s < nvalid ? 1.f : 0.f);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NZ; ++m) {
+                if (z_ok(m)) {
+                    const int it = c + NC * m;
+                    f32x4 acc = Z[m];
+                    if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
+#pragma unroll
+                    for (int cs = 0; cs < SH::CSTEPS; ++cs) acc = O::mma(frag_tr(KS, DK, SH::SWK, 16 * it, cs), ones[cs], acc);
+                    if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
+                    Z[m] = acc;
+                }
+            }
+            write_z(par ^ 1);
         }
         if constexpr (!SO) write_state(par ^ 1);
     };
@@ -755,7 +837,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         }
     } else {
         load_s0();
+        load_z0();
         if constexpr (!SO) write_state(0);
+        write_z(0);
         if constexpr (NBUF == 2) {
             const int npairs = (nchunks + 1) / 2;
             lds_barrier();
@@ -783,14 +867,21 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 }
             }
         }
+        if constexpr (NM) {
+            if (a.z_final && vt == 0 && x == 0) {
+#pragma unroll
+                for (int m = 0; m < NZ; ++m)
+                    if (z_ok(m)) *(f32x4 *)(a.z_final + (size_t)bhs * DK + 16 * (c + NC * m) + 4 * grp) = Z[m];
+            }
+        }
     }
 }
 
-template <typename T, int DK, int C, int DVT, int GATE, bool ELU1, bool SO>
+template <typename T, int DK, int C, int DVT, int GATE, bool ELU1, bool SO, bool NM>
 hipError_t launch_prefill_inst(const PrefillArgs &a, hipStream_t stream)
 {
     const int grid = a.BH * a.nseg * a.n_vt;
-    hipLaunchKernelGGL((prefill_kernel<T, DK, C, DVT, GATE, ELU1, SO>), dim3(grid),
+    hipLaunchKernelGGL((prefill_kernel<T, DK, C, DVT, GATE, ELU1, SO, NM>), dim3(grid),
                        dim3(PrefillShape<T, DK, C, DVT>::NT), 0, stream, a);
     return hipGetLastError();
 }

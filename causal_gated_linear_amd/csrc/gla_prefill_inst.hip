@@ -21,18 +21,18 @@ typedef bf16 InstT;
 typedef float InstT;
 #endif
 
-template <int C, int DVT, bool SO>
+template <int C, int DVT, bool SO, bool NM>
 static hipError_t dispatch_gate(const PrefillArgs &a, hipStream_t stream)
 {
     constexpr int DK = GLA_INST_DK;
     if (a.gate == kGateKeydim)
-        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, true, SO>(a, stream)
-                      : launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, false, SO>(a, stream);
+        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, true, SO, NM>(a, stream)
+                      : launch_prefill_inst<InstT, DK, C, DVT, kGateKeydim, false, SO, NM>(a, stream);
     if (a.gate == kGateScalar)
-        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, true, SO>(a, stream)
-                      : launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, false, SO>(a, stream);
-    return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateNone, true, SO>(a, stream)
-                  : launch_prefill_inst<InstT, DK, C, DVT, kGateNone, false, SO>(a, stream);
+        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, true, SO, NM>(a, stream)
+                      : launch_prefill_inst<InstT, DK, C, DVT, kGateScalar, false, SO, NM>(a, stream);
+    return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateNone, true, SO, NM>(a, stream)
+                  : launch_prefill_inst<InstT, DK, C, DVT, kGateNone, false, SO, NM>(a, stream);
 }
 
 template <int C, int DVT>
@@ -41,7 +41,9 @@ static hipError_t dispatch_mode(const PrefillArgs &a, bool state_only, hipStream
     if constexpr (prefill_nbuf((int)sizeof(InstT), GLA_INST_DK, C, DVT) == 0) {
         return hipErrorInvalidValue;               // does not fit in LDS; never chosen
     } else {
-        return state_only ? dispatch_gate<C, DVT, true>(a, stream) : dispatch_gate<C, DVT, false>(a, stream);
+        // the normalised form is never segmented: no state-only normalised variant
+        if (state_only) return a.norm ? hipErrorInvalidValue : dispatch_gate<C, DVT, true, false>(a, stream);
+        return a.norm ? dispatch_gate<C, DVT, false, true>(a, stream) : dispatch_gate<C, DVT, false, false>(a, stream);
     }
 }
 

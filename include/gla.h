@@ -166,6 +166,43 @@ int gla_decode_step(const void *q, const void *k, const void *v, const float *g,
                     gla_gate_mode gate, float *state, void *o, int B, int H, int d_k, int d_v,
                     gla_dtype dtype, gla_feature_map phi, gla_stream_t stream);
 
+/*
+ * gla_prefill_chunked_norm -- the normalised form of gla_prefill_chunked ("Transformers
+ * are RNNs" notes: the kernel-weighted sum of values divided by the sum of the same
+ * weights, numerator and denominator both through the feature map).  Beside S the
+ * recurrence carries the normaliser state z, the state of a value that is 1 in every
+ * token, with the same gate:
+ *
+ *     z_t = alpha_t (*) z_{t-1} + phi(k_t)        z is d_k, fp32; z_{-1} = z0 (or 0)
+ *     o_t = (S_t^T phi(q_t)) / (phi(q_t) . z_t)
+ *
+ * Arguments as gla_prefill_chunked, plus
+ *   z0        in   fp32 [B][H][d_k] initial normaliser state, or NULL for zero
+ *   z_final   out  fp32 [B][H][d_k] normaliser state after the last token, or NULL;
+ *                  may equal z0 but must not partially overlap it
+ * No workspace is used.  The denominator must not vanish: no epsilon is added.  With
+ * phi = elu+1 (positive features) and z0 = 0 it is positive for every token; with
+ * the identity map it can be zero or negative, and such outputs are undefined.  o
+ * must not overlap any other argument; s_final and z_final must not overlap any
+ * input.  Errors as gla_prefill_chunked (no GLA_ERR_WORKSPACE).
+ */
+int gla_prefill_chunked_norm(const void *q, const void *k, const void *v, const float *g,
+                             gla_gate_mode gate, const float *s0, const float *z0, void *o,
+                             float *s_final, float *z_final, int B, int H, int L, int d_k,
+                             int d_v, int chunk, gla_dtype dtype, gla_feature_map phi,
+                             gla_stream_t stream);
+
+/*
+ * gla_decode_step_norm -- one token of the normalised recurrence on resident states:
+ * state <- Diag(alpha) state + phi(k) v^T and z <- alpha (*) z + phi(k) in place, then
+ * o = state^T phi(q) / (phi(q) . z).  Arguments as gla_decode_step, plus
+ *   z         in/out  fp32 [B][H][d_k] normaliser state (required)
+ * z must not overlap q, k, v, g, state or o.  Errors as gla_decode_step.
+ */
+int gla_decode_step_norm(const void *q, const void *k, const void *v, const float *g,
+                         gla_gate_mode gate, float *state, float *z, void *o, int B, int H, int d_k,
+                         int d_v, gla_dtype dtype, gla_feature_map phi, gla_stream_t stream);
+
 /* gla_strerror -- static text for a gla_status value (never NULL). */
 const char *gla_strerror(int status);
 

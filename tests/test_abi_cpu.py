@@ -31,7 +31,8 @@ def _declared():
 def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["gla_state_alloc", "gla_state_free", "gla_prefill_workspace_bytes",
                                   "gla_prefill_chunked", "gla_decode_step", "gla_strerror",
-                                  "gla_last_error_detail"])
+                                  "gla_last_error_detail", "gla_prefill_chunked_norm",
+                                  "gla_decode_step_norm"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -179,3 +180,56 @@ def test_python_binding_checks_shapes():
         api.prefill(q, q, q, log_gate=torch.zeros(1, 1, 16), gate="keydim")   # gate shape
     with pytest.raises(ValueError):
         api.prefill(q.transpose(2, 3), q, q)                   # non-contiguous
+
+
+# the normalised entry points share the validation above and add the z arguments
+def _prefill_norm(lib, **kw):
+    args = dict(q=A, k=A + 16 * MB, v=A + 32 * MB, g=A + 48 * MB, gate=1, s0=None, z0=None, o=A + 96 * MB,
+                s_final=A + 128 * MB, z_final=A + 160 * MB, B=1, H=2, L=64, d_k=64, d_v=64, chunk=64,
+                dtype=1, phi=0)
+    args.update(kw)
+    P = ctypes.c_void_p
+    return lib.gla_prefill_chunked_norm(P(args["q"]), P(args["k"]), P(args["v"]), P(args["g"]), args["gate"],
+                                        P(args["s0"]), P(args["z0"]), P(args["o"]), P(args["s_final"]),
+                                        P(args["z_final"]), args["B"], args["H"], args["L"], args["d_k"],
+                                        args["d_v"], args["chunk"], args["dtype"], args["phi"], None)
+
+
+PREFILL_NORM_BAD = {
+    "d_k_48": (dict(d_k=48), _lib.GLA_ERR_UNSUPPORTED),
+    "z0_misaligned": (dict(z0=A + 200 * MB + 4), _lib.GLA_ERR_ALIGN),
+    "z_final_misaligned": (dict(z_final=A + 160 * MB + 8), _lib.GLA_ERR_ALIGN),
+    "o_overlaps_z_final": (dict(z_final=A + 96 * MB + 256), _lib.GLA_ERR_ALIAS),
+    "z_final_overlaps_k": (dict(z_final=A + 16 * MB + 64), _lib.GLA_ERR_ALIAS),
+    "z_final_partially_overlaps_z0": (dict(z0=A + 200 * MB, z_final=A + 200 * MB + 16), _lib.GLA_ERR_ALIAS),
+    "s_final_overlaps_z0": (dict(z0=A + 128 * MB + 32), _lib.GLA_ERR_ALIAS),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PREFILL_NORM_BAD))
+def test_prefill_norm_rejects(lib, case):
+    kw, want = PREFILL_NORM_BAD[case]
+    assert _prefill_norm(lib, **kw) == want
+    assert lib.gla_last_error_detail().decode() != ""
+
+
+def test_prefill_norm_needs_no_workspace_even_when_segmentable(lib):
+    """Sizes that the plain prefill would split into segments (and so need a
+    workspace) run unsegmented in the normalised form; validation must pass that
+    point and fail only on the deliberately bad alignment below."""
+    assert lib.gla_prefill_workspace_bytes(1, 2, 64 * 65, 64, 64, 64, 1) > 0
+    assert _prefill_norm(lib, L=64 * 65, o=A + 96 * MB + 2) == _lib.GLA_ERR_ALIGN
+
+
+def test_decode_norm_requires_z(lib):
+    P = ctypes.c_void_p
+    st = lib.gla_decode_step_norm(P(A), P(A + MB), P(A + 2 * MB), P(A + 3 * MB), 1, P(A + 16 * MB), None,
+                                  P(A + 64 * MB), 2, 4, 128, 128, 1, 0, None)
+    assert st == _lib.GLA_ERR_NULL
+
+
+def test_decode_norm_rejects_z_overlapping_state(lib):
+    P = ctypes.c_void_p
+    st = lib.gla_decode_step_norm(P(A), P(A + MB), P(A + 2 * MB), P(A + 3 * MB), 1, P(A + 16 * MB),
+                                  P(A + 16 * MB + 1024), P(A + 64 * MB), 2, 4, 128, 128, 1, 0, None)
+    assert st == _lib.GLA_ERR_ALIAS
