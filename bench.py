@@ -134,6 +134,30 @@ def run_other_prefills(args, torch, api, inputs):
                          w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, str(w.dtype).replace("torch.", ""), w.gate,
                          w.feature_map or "identity")}
         del inp, o, s
+    # the normalised form (normaliser state z beside S) at the headline shape, elu+1
+    w = inputs.WORKLOADS["gla_prefill"]
+    inp = inputs.draw(w, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, w.d_v, dtype=w.dtype, device="cuda")
+    s = torch.empty(w.B, w.H, w.d_k, w.d_v, dtype=torch.float32, device="cuda")
+    z = torch.empty(w.B, w.H, w.d_k, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step_norm():
+        api.prefill_norm(inp["q"], inp["k"], inp["v"], log_gate=inp["g"], gate="keydim", chunk=w.chunk,
+                         feature_map="elu1", out=o, final_state=s, final_norm=z, stream=stream)
+
+    for _ in range(3):
+        step_norm()
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 2)
+    per = _events_ms(step_norm, n, stream) / n
+    nbytes = prefill_bytes(w.B, w.H, w.L, w.d_k, w.d_v) + w.B * w.H * w.d_k * 4
+    gbs = nbytes / (per / 1e3) / 1e9
+    out["gla_prefill_norm_elu1"] = {
+        "ms_per_step": per, "tokens_per_s": w.B * w.L / (per / 1e3), "GB_per_s": gbs,
+        "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes,
+        "shape": "B=%d H=%d L=%d d_k=%d d_v=%d chunk=%d bfloat16 gate=keydim phi=elu1, normalised" % (
+            w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)}
     return out
 
 
@@ -162,7 +186,20 @@ def run_decode(args, torch, api, inputs):
     ms = _events_ms(step, T, stream)
     per = ms / T
     nbytes = decode_step_bytes(w.B, w.H, w.d_k, w.d_v)
-    return dict(w=w, steps=T, ms_per_step=per, bytes=nbytes)
+    # the normalised step (elu+1, normaliser state z updated beside S), fewer steps
+    z = torch.ones(w.B, w.H, w.d_k, dtype=torch.float32, device="cuda")
+    Tn = min(T, 256)
+    it = iter(range(Tn))
+
+    def step_norm():
+        t = next(it)
+        api.decode_step_norm(d["q"][t], d["k"][t], d["v"][t], log_gate=d["g"][t], state=state, norm=z,
+                             gate="keydim", feature_map="elu1", out=o, stream=stream)
+
+    per_n = _events_ms(step_norm, Tn, stream) / Tn
+    nbytes_n = nbytes + w.B * w.H * w.d_k * 8
+    return dict(w=w, steps=T, ms_per_step=per, bytes=nbytes, norm_steps=Tn, norm_ms_per_step=per_n,
+                norm_bytes=nbytes_n)
 
 
 def kernel_source_hash():
@@ -421,6 +458,12 @@ def main():
                           "tokens_per_s": dc["w"].B / dper, "ms_per_step": dc["ms_per_step"],
                           "GB_per_s": dgbs, "hbm_frac": dgbs / HBM_PEAK_GBS,
                           "bytes_per_step": dc["bytes"]}
+        nper = dc["norm_ms_per_step"] / 1e3
+        line["decode_norm"] = {"workload": "normalised decode, same shape, elu+1, %d steps" % dc["norm_steps"],
+                               "tokens_per_s": dc["w"].B / nper, "ms_per_step": dc["norm_ms_per_step"],
+                               "GB_per_s": dc["norm_bytes"] / nper / 1e9,
+                               "hbm_frac": dc["norm_bytes"] / nper / 1e9 / HBM_PEAK_GBS,
+                               "bytes_per_step": dc["norm_bytes"]}
     if not args.no_others:
         line["other_prefill"] = run_other_prefills(args, torch, api, inputs)
     if not args.no_cpu_baseline:
