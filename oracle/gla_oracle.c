@@ -51,6 +51,18 @@
  * Reading taken: with a gate, z decays with the same gate as S (it is the state of
  * a value that is 1 in every token); the notes have no gate.  No epsilon is added
  * to the denominator.  z0 / z_out are [B][H][d_k].
+ *
+ * Delta rule (gla_oracle_delta): "Attention is recurrent", section "Delta attention".
+ * Before writing, the state is asked what it already predicts for the key, and only
+ * the error is written, scaled by the write strength beta_n:
+ *
+ *       u_t = beta_t (v_t - S_{t-1}^T k_t)                d_v
+ *       S_t = S_{t-1} + k_t u_t^T,     o_t = S_t^T q_t
+ *
+ * Readings taken: the read-out is inclusive as above; beta is one scalar per token
+ * and head, passed as is; no gate, no feature map and no key normalisation inside
+ * (callers scale keys); S_{-1} = s0 or zero (the page assumes zero).  beta is
+ * [B][H][L].
  */
 #include <math.h>
 #include <pthread.h>
@@ -68,9 +80,9 @@ static double feature(double x, int phi)
 }
 
 typedef struct {
-    const double *q, *k, *v, *g, *s0, *z0;
+    const double *q, *k, *v, *g, *s0, *z0, *beta;
     double *o, *s_out, *z_out;
-    int norm;
+    int norm, delta;
     long B, H, L, dk, dv;
     int gate_mode, phi;
     long next_head;          /* shared work counter, guarded by lock */
@@ -91,7 +103,23 @@ static void run_head(const job_t *jb, long head, double *S, double *qf, double *
     if (jb->z0) memcpy(z, jb->z0 + head * dk, sizeof(double) * dk);
     else memset(z, 0, sizeof(double) * dk);
 
-    for (long t = 0; t < L; ++t) {
+    for (long t = 0; jb->delta && t < L; ++t) {
+        /* delta rule: write the prediction error of the key, scaled by beta */
+        const double bt = jb->beta[head * L + t];
+        for (long j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (long i = 0; i < dk; ++i) pred += k[t * dk + i] * S[i * dv + j];
+            z[j] = bt * (v[t * dv + j] - pred);     /* z holds u_t here (d_v <= its size) */
+        }
+        for (long i = 0; i < dk; ++i)
+            for (long j = 0; j < dv; ++j) S[i * dv + j] += k[t * dk + i] * z[j];
+        for (long j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk; ++i) acc += q[t * dk + i] * S[i * dv + j];
+            o[t * dv + j] = acc;
+        }
+    }
+    for (long t = 0; !jb->delta && t < L; ++t) {
         for (long i = 0; i < dk; ++i) {
             qf[i] = feature(q[t * dk + i], jb->phi);
             kf[i] = feature(k[t * dk + i], jb->phi);
@@ -132,7 +160,7 @@ static void *worker(void *arg)
     double *qf = (double *)malloc(sizeof(double) * jb->dk);
     double *kf = (double *)malloc(sizeof(double) * jb->dk);
     double *a = (double *)malloc(sizeof(double) * jb->dk);
-    double *z = (double *)malloc(sizeof(double) * jb->dk);
+    double *z = (double *)malloc(sizeof(double) * (jb->dk > jb->dv ? jb->dk : jb->dv));
     if (S && qf && kf && a && z) {     /* on allocation failure take no head */
         for (;;) {
             pthread_mutex_lock(&jb->lock);
@@ -148,8 +176,8 @@ static void *worker(void *arg)
 
 static int forward(const double *q, const double *k, const double *v, const double *g,
                    int gate_mode, int phi, const double *s0, const double *z0, double *o,
-                   double *s_out, double *z_out, int norm, long B, long H, long L, long dk,
-                   long dv, int nthreads)
+                   double *s_out, double *z_out, int norm, const double *beta, long B, long H,
+                   long L, long dk, long dv, int nthreads)
 {
     if (!q || !k || !v || !o || B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0) return -1;
     if (gate_mode != ORACLE_GATE_NONE && gate_mode != ORACLE_GATE_KEYDIM &&
@@ -160,6 +188,7 @@ static int forward(const double *q, const double *k, const double *v, const doub
     job_t jb;
     jb.q = q; jb.k = k; jb.v = v; jb.g = g; jb.s0 = s0; jb.o = o; jb.s_out = s_out;
     jb.z0 = z0; jb.z_out = z_out; jb.norm = norm;
+    jb.beta = beta; jb.delta = beta != NULL;
     jb.B = B; jb.H = H; jb.L = L; jb.dk = dk; jb.dv = dv;
     jb.gate_mode = gate_mode; jb.phi = phi; jb.next_head = 0;
     pthread_mutex_init(&jb.lock, NULL);
@@ -192,7 +221,7 @@ int gla_oracle_forward(const double *q, const double *k, const double *v, const 
                        int gate_mode, int phi, const double *s0, double *o, double *s_out,
                        long B, long H, long L, long dk, long dv, int nthreads)
 {
-    return forward(q, k, v, g, gate_mode, phi, s0, NULL, o, s_out, NULL, 0, B, H, L, dk, dv,
+    return forward(q, k, v, g, gate_mode, phi, s0, NULL, o, s_out, NULL, 0, NULL, B, H, L, dk, dv,
                    nthreads);
 }
 
@@ -203,6 +232,16 @@ int gla_oracle_forward_norm(const double *q, const double *k, const double *v, c
                             double *o, double *s_out, double *z_out, long B, long H, long L,
                             long dk, long dv, int nthreads)
 {
-    return forward(q, k, v, g, gate_mode, phi, s0, z0, o, s_out, z_out, 1, B, H, L, dk, dv,
+    return forward(q, k, v, g, gate_mode, phi, s0, z0, o, s_out, z_out, 1, NULL, B, H, L, dk, dv,
                    nthreads);
+}
+
+/* The delta rule (see the header): beta [B][H][L] required; s0 nullable (zero). */
+int gla_oracle_delta(const double *q, const double *k, const double *v, const double *beta,
+                     const double *s0, double *o, double *s_out, long B, long H, long L, long dk,
+                     long dv, int nthreads)
+{
+    if (!beta) return -1;
+    return forward(q, k, v, NULL, ORACLE_GATE_NONE, ORACLE_PHI_IDENTITY, s0, NULL, o, s_out, NULL, 0,
+                   beta, B, H, L, dk, dv, nthreads);
 }

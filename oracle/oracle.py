@@ -63,6 +63,9 @@ def _load(lib_path=None):
                                                 dp, dp, ctypes.c_long, ctypes.c_long, ctypes.c_long,
                                                 ctypes.c_long, ctypes.c_long, ctypes.c_int]
         lib.gla_oracle_forward_norm.restype = ctypes.c_int
+        lib.gla_oracle_delta.argtypes = [dp, dp, dp, dp, dp, dp, dp, ctypes.c_long, ctypes.c_long,
+                                         ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        lib.gla_oracle_delta.restype = ctypes.c_int
         _libs[lib_path] = lib
     return _libs[lib_path]
 
@@ -148,3 +151,21 @@ def forward_norm(q, k, v, g=None, gate=None, feature_map=None, s0=None, z0=None,
     if rc != 0:
         raise RuntimeError("gla_oracle_forward_norm failed with code %d" % rc)
     return o, s, z
+
+
+def forward_delta(q, k, v, beta, s0=None, nthreads=None, lib_path=None):
+    """The delta rule ("Attention is recurrent", Delta attention): u_t = beta_t (v_t -
+    S_{t-1}^T k_t), S_t = S_{t-1} + k_t u_t^T, o_t = S_t^T q_t.  beta: [B, H, L];
+    s0: [B, H, d_k, d_v] or None.  Returns (o, s_final) as float64 arrays."""
+    q, k, v, _, s0, _, (B, H, L, dk, dv) = _prepare(q, k, v, None, None, s0)
+    beta = _f64(beta)
+    if beta is None or beta.shape != (B, H, L):
+        raise ValueError("oracle: beta must be [B,H,L]")
+    o = np.zeros((B, H, L, dv), dtype=np.float64)
+    s = np.zeros((B, H, dk, dv), dtype=np.float64)
+    nthreads = default_threads() if nthreads is None else int(nthreads)
+    rc = _load(lib_path).gla_oracle_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o), _ptr(s),
+                                          B, H, L, dk, dv, nthreads)
+    if rc != 0:
+        raise RuntimeError("gla_oracle_delta failed with code %d" % rc)
+    return o, s

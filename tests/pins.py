@@ -363,3 +363,109 @@ ALL_ERROR_PINS = {
     "geometric_closed_form": (pin_geometric_closed_form, 1e-14),
     "chaining": (pin_chaining, 0.0),
 }
+
+
+# ---- the delta rule ("Attention is recurrent", Delta attention and its Prefill):
+# the write is the prediction error scaled by beta; prefill is one triangular system ----
+
+def delta_inputs(seed, B, H, L, dk, dv, s0=False):
+    """Unit-norm keys and queries (the usual normalisation for the delta rule, which
+    keeps every I - beta k k^T a contraction for beta in [0, 1]) and beta in (0, 1)."""
+    r = np.random.default_rng(seed)
+    unit = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)
+    q = unit(r.standard_normal((B, H, L, dk)))
+    k = unit(r.standard_normal((B, H, L, dk)))
+    v = r.standard_normal((B, H, L, dv))
+    beta = r.uniform(0.05, 0.95, size=(B, H, L))
+    S0 = r.standard_normal((B, H, dk, dv)) if s0 else None
+    return q, k, v, beta, S0
+
+
+def pin_delta_triangular(fwd_delta, seed=30, with_s0=True, B=2, H=2, L=23, dk=5, dv=4):
+    """The whole prompt as one lower-triangular system: with T = I + tril(diag(beta) K K^T, -1),
+    the writes are U = T^{-1} diag(beta) (V - K S0), the outputs O = Q S0 + tril(Q K^T) U
+    (the read-out includes the token's own write) and the final state S0 + K^T U.
+    Solved with numpy's dense solver, not by substitution."""
+    q, k, v, beta, S0 = delta_inputs(seed, B, H, L, dk, dv, s0=with_s0)
+    o, s = fwd_delta(q, k, v, beta, s0=S0)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            K, Q, V, be = k[b, h], q[b, h], v[b, h], beta[b, h]
+            s0 = S0[b, h] if S0 is not None else np.zeros((dk, dv))
+            T = np.eye(L) + np.tril(be[:, None] * (K @ K.T), -1)
+            U = np.linalg.solve(T, be[:, None] * (V - K @ s0))
+            worst = max(worst, rel_err(o[b, h], Q @ s0 + np.tril(Q @ K.T) @ U),
+                        rel_err(s[b, h], s0 + K.T @ U))
+    return worst
+
+
+def pin_delta_zero_strength(fwd_delta, seed=31, B=2, H=2, L=11, dk=4, dv=3):
+    """beta = 0 writes nothing: S stays S0 and o_t = S0^T q_t."""
+    q, k, v, _, S0 = delta_inputs(seed, B, H, L, dk, dv, s0=True)
+    o, s = fwd_delta(q, k, v, np.zeros((B, H, L)), s0=S0)
+    return max(float(np.abs(s - S0).max()),
+               rel_err(o, np.einsum("bhli,bhij->bhlj", q, S0)))
+
+
+def pin_delta_overwrite(fwd_delta, seed=32, B=1, H=2, L=20, dk=6, dv=3):
+    """beta = 1 with keys drawn from an orthonormal basis: each write replaces the
+    value stored under its key exactly.  Reading with q_t = k_t returns v_t; at the
+    end S^T e = the last value written to basis key e, and S is unchanged along
+    basis keys never written."""
+    r = np.random.default_rng(seed)
+    basis, _ = np.linalg.qr(r.standard_normal((dk, dk)))
+    idx = r.integers(0, dk - 1, size=(B, H, L))          # the last basis key is never written
+    k = basis.T[idx]                                      # rows are basis vectors
+    v = r.standard_normal((B, H, L, dv))
+    S0 = r.standard_normal((B, H, dk, dv))
+    o, s = fwd_delta(k.copy(), k, v, np.ones((B, H, L)), s0=S0)
+    worst = rel_err(o, v)
+    for b in range(B):
+        for h in range(H):
+            for e in range(dk):
+                hits = np.nonzero(idx[b, h] == e)[0]
+                want = v[b, h, hits[-1]] if hits.size else S0[b, h].T @ basis[:, e]
+                worst = max(worst, float(np.abs(s[b, h].T @ basis[:, e] - want).max()))
+    return worst
+
+
+def pin_delta_moving_average(fwd_delta, seed=33, L=30, dv=3):
+    """d_k = 1, every key and query 1: the delta rule is the exponential moving average
+    s_n = (1 - beta_n) s_{n-1} + beta_n v_n, here in its explicit product form
+    s_n = prod_{m<=n} (1 - beta_m) s0 + sum_{i<=n} beta_i v_i prod_{i<m<=n} (1 - beta_m)."""
+    r = np.random.default_rng(seed)
+    beta = r.uniform(0.0, 1.0, size=(1, 1, L))
+    v = r.standard_normal((1, 1, L, dv))
+    S0 = r.standard_normal((1, 1, 1, dv))
+    ones = np.ones((1, 1, L, 1))
+    o, s = fwd_delta(ones, ones, v, beta, s0=S0)
+    keep = 1.0 - beta[0, 0]
+    want = np.zeros((L, dv))
+    for n in range(L):
+        acc = np.prod(keep[:n + 1]) * S0[0, 0, 0]
+        for i in range(n + 1):
+            acc = acc + beta[0, 0, i] * v[0, 0, i] * np.prod(keep[i + 1:n + 1])
+        want[n] = acc
+    return max(rel_err(o[0, 0], want), rel_err(s[0, 0, 0], want[-1]))
+
+
+def pin_delta_chaining(fwd_delta, seed=34, B=2, H=2, L1=12, L2=9, dk=4, dv=3):
+    """run(L1 + L2) equals run(L1) followed by run(L2) from its final state, bit for bit."""
+    q, k, v, beta, S0 = delta_inputs(seed, B, H, L1 + L2, dk, dv, s0=True)
+    o, s = fwd_delta(q, k, v, beta, s0=S0)
+    o1, s1 = fwd_delta(q[:, :, :L1], k[:, :, :L1], v[:, :, :L1], beta[:, :, :L1], s0=S0)
+    o2, s2 = fwd_delta(q[:, :, L1:], k[:, :, L1:], v[:, :, L1:], beta[:, :, L1:], s0=s1)
+    with np.errstate(invalid="ignore"):
+        return float(max(np.abs(o - np.concatenate([o1, o2], axis=2)).max(), np.abs(s - s2).max()))
+
+
+DELTA_ERROR_PINS = {
+    # name: (callable on forward_delta, tolerance)
+    "delta_triangular": (pin_delta_triangular, 1e-12),
+    "delta_triangular_zero_init": (lambda f: pin_delta_triangular(f, seed=35, with_s0=False), 1e-12),
+    "delta_zero_strength": (pin_delta_zero_strength, 1e-15),
+    "delta_overwrite": (pin_delta_overwrite, 1e-13),
+    "delta_moving_average": (pin_delta_moving_average, 1e-13),
+    "delta_chaining": (pin_delta_chaining, 0.0),
+}

@@ -16,6 +16,7 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 UPDATE = "S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];"
 READ = "acc += qf[i] * S[i * dv + j];"
+DELTA_ERR = "z[j] = bt * (v[t * dv + j] - pred);"
 
 MUTANTS = {
     "no_decay": [(UPDATE, "S[i * dv + j] = S[i * dv + j] + kf[i] * v[t * dv + j];")],
@@ -52,11 +53,37 @@ MUTANTS = {
     "norm_z0_ignored": [("if (jb->z0) memcpy", "if (0) memcpy")],
     "norm_not_divided": [("o[t * dv + j] = jb->norm ? acc / den : acc;", "o[t * dv + j] = acc;")],
     "norm_z_value_weighted": [("z[i] = a[i] * z[i] + kf[i];", "z[i] = a[i] * z[i] + kf[i] * v[t * dv];")],
+    # the delta rule
+    "delta_no_strength": [(DELTA_ERR, "z[j] = (v[t * dv + j] - pred);")],
+    "delta_error_sign": [(DELTA_ERR, "z[j] = bt * (v[t * dv + j] + pred);")],
+    "delta_no_prediction": [(DELTA_ERR, "z[j] = bt * v[t * dv + j];")],
+    "delta_predicts_with_query": [("pred += k[t * dk + i] * S[i * dv + j];", "pred += q[t * dk + i] * S[i * dv + j];")],
+    "delta_strength_head_offset": [("const double bt = jb->beta[head * L + t];", "const double bt = jb->beta[t];")],
+    "delta_write_unscaled_key": [("S[i * dv + j] += k[t * dk + i] * z[j];", "S[i * dv + j] += z[j];")],
+    "delta_exclusive_readout": [
+        ("""        for (long i = 0; i < dk; ++i)
+            for (long j = 0; j < dv; ++j) S[i * dv + j] += k[t * dk + i] * z[j];
+""", ""),
+        ("""            o[t * dv + j] = acc;
+        }
+    }""", """            o[t * dv + j] = acc;
+        }
+        for (long i = 0; i < dk; ++i)
+            for (long j = 0; j < dv; ++j) S[i * dv + j] += k[t * dk + i] * z[j];
+    }""")],
 }
 
 
-def _pin_results(fwd, fwd_norm):
+def _pin_results(fwd, fwd_norm, fwd_delta):
     failed = []
+    for name, (fn, tol) in pins.DELTA_ERROR_PINS.items():
+        try:
+            err = fn(fwd_delta)
+        except AssertionError:
+            failed.append(name)
+            continue
+        if not err <= tol:
+            failed.append(name)
     for name, (fn, tol) in pins.NORM_ERROR_PINS.items():
         try:
             err = fn(fwd_norm)
@@ -92,5 +119,6 @@ def test_pins_reject_planted_mistake(mutant, tmp_path):
     lib = oracle.compile_source(str(c_path), str(tmp_path / ("libmutant_%s.so" % mutant)))
     fwd = functools.partial(oracle.forward, lib_path=lib)
     fwd_norm = functools.partial(oracle.forward_norm, lib_path=lib)
-    failed = _pin_results(fwd, fwd_norm)
+    fwd_delta = functools.partial(oracle.forward_delta, lib_path=lib)
+    failed = _pin_results(fwd, fwd_norm, fwd_delta)
     assert failed, "planted mistake %r passed every pin" % mutant

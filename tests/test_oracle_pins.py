@@ -27,6 +27,31 @@ def test_oracle_norm_pin(name):
     assert err <= tol, "%s: error %.3e above %.1e" % (name, err, tol)
 
 
+@pytest.mark.parametrize("name", sorted(pins.DELTA_ERROR_PINS))
+def test_oracle_delta_pin(name):
+    fn, tol = pins.DELTA_ERROR_PINS[name]
+    err = fn(oracle.forward_delta)
+    assert err <= tol, "%s: error %.3e above %.1e" % (name, err, tol)
+
+
+def test_oracle_delta_empty_and_bad_strength():
+    q, k, v, beta, S0 = pins.delta_inputs(36, 2, 2, 0, 4, 3, s0=True)
+    o, s = oracle.forward_delta(q, k, v, beta, s0=S0)
+    assert o.shape == (2, 2, 0, 3) and np.array_equal(s, S0)
+    q, k, v, beta, _ = pins.delta_inputs(37, 1, 2, 5, 4, 3)
+    with pytest.raises(ValueError):
+        oracle.forward_delta(q, k, v, beta[..., :4])
+    with pytest.raises(ValueError):
+        oracle.forward_delta(q, k, v, None)
+
+
+def test_oracle_delta_threads_agree_bitwise():
+    q, k, v, beta, S0 = pins.delta_inputs(38, 3, 5, 17, 6, 7, s0=True)
+    o1, s1 = oracle.forward_delta(q, k, v, beta, s0=S0, nthreads=1)
+    o8, s8 = oracle.forward_delta(q, k, v, beta, s0=S0, nthreads=8)
+    assert np.array_equal(o1, o8) and np.array_equal(s1, s8)
+
+
 def test_oracle_norm_matches_unnormalised_state():
     """The normalised entry carries S exactly as the plain one does."""
     q, k, v, g, S0 = pins.rng_inputs(27, 2, 3, 21, 5, 4, gate="keydim", s0=True)
