@@ -4,6 +4,7 @@ The computation lives in hand-written HIP kernels behind the C ABI of
 ``include/gla.h`` (``libgla.so``, built in-tree); this package is its thin Python
 binding.  ``inputs`` holds the seeded synthetic workloads.
 """
-from .api import (DeviceState, decode_step, decode_step_norm, prefill, prefill_norm,  # noqa: F401
-                  state_alloc, workspace_bytes)
+from .api import (DeviceState, decode_step, decode_step_delta, decode_step_norm,  # noqa: F401
+                  delta_workspace_bytes, prefill, prefill_delta, prefill_norm, state_alloc,
+                  workspace_bytes)
 from ._lib import GLAError  # noqa: F401

@@ -26,6 +26,9 @@ SIGNATURES = [
     ("gla_prefill_chunked_norm", _I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                       _I, _I, _I, _P]),
     ("gla_decode_step_norm", _I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    ("gla_delta_workspace_bytes", _SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    ("gla_prefill_delta", _I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    ("gla_decode_step_delta", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     ("gla_strerror", ctypes.c_char_p, [_I]),
     ("gla_last_error_detail", ctypes.c_char_p, []),
 ]

@@ -188,6 +188,55 @@ def decode_step_norm(q, k, v, log_gate=None, state=None, norm=None, gate=None, f
     return out
 
 
+def delta_workspace_bytes(B, H, L, d_k, d_v, chunk, dtype=torch.bfloat16) -> int:
+    """Bytes of device workspace gla_prefill_delta needs for these sizes."""
+    return int(_lib.load().gla_delta_workspace_bytes(B, H, L, d_k, d_v, chunk, _DTYPES[dtype]))
+
+
+def prefill_delta(q, k, v, beta, initial_state=None, chunk=64, out=None, final_state=None,
+                  workspace=None, stream=None):
+    """Chunkwise delta-rule prefill (gla_prefill_delta).
+
+    q, k: [B, H, L, d_k]; v: [B, H, L, d_v] (fp32 or bf16, same dtype, CUDA);
+    beta: fp32 [B, H, L] write strengths; initial_state: fp32 [B, H, d_k, d_v] or None.
+    Returns (o, s_final); ``final_state`` may be ``initial_state`` to update it in place.
+    """
+    lib = _lib.load()
+    B, H, L, dk, dv, dev, dt, _ = _check_prefill(q, k, v, None, None, initial_state)
+    _check_tensor(beta, "beta", (B, H, L), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor(out, "out", (B, H, L, dv), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
+    need = delta_workspace_bytes(B, H, L, dk, dv, chunk, dt)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace.is_contiguous() and workspace.device == dev, "workspace must be contiguous on %s" % dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gla_prefill_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(initial_state), _ptr(out),
+                               _ptr(final_state), B, H, L, dk, dv, int(chunk), _DTYPES[dt],
+                               _ptr(workspace), ws_bytes, _stream_handle(stream))
+    _lib.check(st, "gla_prefill_delta")
+    return out, final_state
+
+
+def decode_step_delta(q, k, v, beta, state=None, out=None, stream=None):
+    """One delta-rule step (gla_decode_step_delta); ``state`` [B, H, d_k, d_v] fp32 is
+    updated in place.  q, k: [B, H, d_k]; v: [B, H, d_v]; beta: fp32 [B, H].  Returns o."""
+    lib = _lib.load()
+    B, H, dk, dv, dev, dt, _, out = _check_decode(q, k, v, None, None, state, out)
+    _check_tensor(beta, "beta", (B, H), torch.float32, dev)
+    st = lib.gla_decode_step_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(state), _ptr(out),
+                                   B, H, dk, dv, _DTYPES[dt], _stream_handle(stream))
+    _lib.check(st, "gla_decode_step_delta")
+    return out
+
+
 class DeviceState:
     """A zeroed fp32 state [B, H, d_k, d_v] from gla_state_alloc, owned by this object
     (freed with gla_state_free).  ``tensor()`` views it as a torch tensor (no copy)

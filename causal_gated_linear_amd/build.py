@@ -34,6 +34,7 @@ def _units():
                           ["-DGLA_INST_BF16=%d" % bf, "-DGLA_INST_DK=%d" % dk]))
     units.append(("gla_decode.hip", "decode.o", []))
     units.append(("gla_scan.hip", "scan.o", []))
+    units.append(("gla_delta.hip", "delta.o", []))
     units.append(("gla_api.cpp", "api.o", ["-x", "hip"]))
     return units
 

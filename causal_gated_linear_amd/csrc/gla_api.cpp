@@ -407,4 +407,107 @@ int gla_decode_step_norm(const void *q, const void *k, const void *v, const floa
     return decode_impl(q, k, v, g, gate, state, z, o, B, H, d_k, d_v, dtype, phi, stream);
 }
 
+// ---- the delta rule ----------------------------------------------------------------
+
+size_t gla_delta_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chunk, gla_dtype dtype)
+{
+    if (B <= 0 || H <= 0 || L < 0 || !dim_supported(d_k) || !dim_supported(d_v) || !chunk_supported(chunk) ||
+        (dtype != GLA_F32 && dtype != GLA_BF16) || (long long)B * H > 0x7fffffffLL)
+        return 0;
+    return gla::delta_workspace(B * H, L, d_k, d_v, chunk, (int)elem_size(dtype));
+}
+
+int gla_prefill_delta(const void *q, const void *k, const void *v, const float *beta, const float *s0,
+                      void *o, float *s_final, int B, int H, int L, int d_k, int d_v, int chunk,
+                      gla_dtype dtype, void *workspace, size_t workspace_bytes, gla_stream_t stream)
+{
+    if (L < 0) return fail(GLA_ERR_SHAPE, "L=%d must be >= 0", L);
+    int st = check_common(B, H, d_k, d_v, dtype, GLA_GATE_NONE, GLA_PHI_IDENTITY, nullptr, false);
+    if (st != GLA_OK) return st;
+    if (!chunk_supported(chunk))
+        return fail(GLA_ERR_UNSUPPORTED, "chunk=%d: must be 16, 32 or 64", chunk);
+    if ((long long)(L + chunk) * (d_k > d_v ? d_k : d_v) * 4 > 0x7fffffffLL)
+        return fail(GLA_ERR_SHAPE, "L=%d too long for one head (limit (L + chunk) * max(d_k, d_v) * 4 < 2^31)", L);
+    if (L > 0 && (!q || !k || !v || !beta || !o))
+        return fail(GLA_ERR_NULL, "q, k, v, beta and o are required when L > 0");
+    const void *ptrs[] = {q, k, v, s0, o, s_final, workspace};
+    const char *names[] = {"q", "k", "v", "s0", "o", "s_final", "workspace"};
+    for (int i = 0; i < 7; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    if (beta && ((uintptr_t)beta & 3u)) return fail(GLA_ERR_ALIGN, "beta=%p is not 4-byte aligned", (const void *)beta);
+    const size_t need = gla_delta_workspace_bytes(B, H, L, d_k, d_v, chunk, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    const size_t BH = (size_t)B * H, es = elem_size(dtype);
+    const size_t sbytes = BH * d_k * d_v * 4;
+    const Span sq = span(q, BH * L * d_k * es, "q"), sk = span(k, BH * L * d_k * es, "k");
+    const Span sv = span(v, BH * L * d_v * es, "v"), sb = span(beta, BH * L * 4, "beta");
+    const Span ss0 = span(s0, sbytes, "s0"), so = span(o, BH * L * d_v * es, "o");
+    const Span ssf = span(s_final, sbytes, "s_final"), sw = span(workspace, need, "workspace");
+    const Span o_forbidden[] = {sq, sk, sv, sb, ss0, ssf, sw};
+    for (const Span &x : o_forbidden)
+        if (overlap(so, x)) return fail(GLA_ERR_ALIAS, "o overlaps %s", x.name);
+    const Span sf_forbidden[] = {sq, sk, sv, sb, sw};
+    for (const Span &x : sf_forbidden)
+        if (overlap(ssf, x)) return fail(GLA_ERR_ALIAS, "s_final overlaps %s", x.name);
+    if (overlap(ssf, ss0) && s_final != s0)
+        return fail(GLA_ERR_ALIAS, "s_final partially overlaps s0");
+    const Span w_forbidden[] = {sq, sk, sv, sb, ss0};
+    for (const Span &x : w_forbidden)
+        if (overlap(sw, x)) return fail(GLA_ERR_ALIAS, "workspace overlaps %s", x.name);
+
+    const long nch = (L + chunk - 1) / chunk;
+    if ((long)BH * (nch > 1 ? nch : 1) > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H*chunks too large");
+    gla::DeltaArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.s0 = s0; a.o = o; a.s_final = s_final;
+    const size_t lp = (size_t)nch * chunk;
+    a.ws_w = workspace;
+    a.ws_u = workspace ? (char *)workspace + BH * lp * d_k * es : nullptr;
+    a.BH = (int)BH; a.L = L; a.d_k = d_k; a.d_v = d_v;
+    a.dvt = d_v < 64 ? d_v : 64;
+    const char *env = getenv("GLA_DELTA_TILE");
+    if (env && (atoi(env) == 16 || atoi(env) == 32 || atoi(env) == 64) && atoi(env) <= d_v) a.dvt = atoi(env);
+    a.n_vt = d_v / a.dvt;
+    const long grid = (long)BH * a.n_vt;
+    a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
+    if (L == 0 && !s_final) return ok();
+    const hipError_t e = gla::launch_delta_prefill(a, dtype == GLA_BF16 ? 1 : 0, chunk, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "delta prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int gla_decode_step_delta(const void *q, const void *k, const void *v, const float *beta, float *state,
+                          void *o, int B, int H, int d_k, int d_v, gla_dtype dtype, gla_stream_t stream)
+{
+    int st = check_common(B, H, d_k, d_v, dtype, GLA_GATE_NONE, GLA_PHI_IDENTITY, nullptr, false);
+    if (st != GLA_OK) return st;
+    if (!q || !k || !v || !beta || !state || !o)
+        return fail(GLA_ERR_NULL, "q, k, v, beta, state and o are required");
+    const void *ptrs[] = {q, k, v, state, o};
+    const char *names[] = {"q", "k", "v", "state", "o"};
+    for (int i = 0; i < 5; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    if ((uintptr_t)beta & 3u) return fail(GLA_ERR_ALIGN, "beta=%p is not 4-byte aligned", (const void *)beta);
+    const size_t BH = (size_t)B * H, es = elem_size(dtype);
+    const Span sq = span(q, BH * d_k * es, "q"), sk = span(k, BH * d_k * es, "k");
+    const Span sv = span(v, BH * d_v * es, "v"), sb = span(beta, BH * 4, "beta");
+    const Span sst = span(state, BH * d_k * d_v * 4, "state"), so = span(o, BH * d_v * es, "o");
+    const Span o_forbidden[] = {sq, sk, sv, sb, sst};
+    for (const Span &x : o_forbidden)
+        if (overlap(so, x)) return fail(GLA_ERR_ALIAS, "o overlaps %s", x.name);
+    const Span st_forbidden[] = {sq, sk, sv, sb};
+    for (const Span &x : st_forbidden)
+        if (overlap(sst, x)) return fail(GLA_ERR_ALIAS, "state overlaps %s", x.name);
+    if (BH > 0x7fffffffUL) return fail(GLA_ERR_SHAPE, "B*H too large");
+    gla::DeltaArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.s0 = state; a.s_final = state; a.o = o;
+    a.BH = (int)BH; a.d_k = d_k; a.d_v = d_v;
+    const hipError_t e = gla::launch_delta_decode(a, dtype == GLA_BF16 ? 1 : 0, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "delta decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -143,4 +143,41 @@ __device__ __forceinline__ f32x4 contract_regs_rows(const f32x4 (&atiles)[NBLK],
     return acc;
 }
 
+// Barrier for LDS communication only: waits for this wave's LDS operations, not
+// for its outstanding global loads.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Transposed operand reads from row-major LDS arrays (rows = tokens s, columns =
+// i or j), for the products that contract over tokens.  One ds_read_b64_tr_b16
+// serves a 16-lane group: lane l of the group gives the address of row s0 + l/4,
+// columns n0 + 4(l%4) .. +3, and receives column n0 + l of rows s0 .. s0+3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16 *p)
+{
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Raw buffer access over `bytes` bytes from p: a load at a byte offset at or past
+// `bytes` returns zeros and touches no memory.  Rows past the end of a sequence
+// therefore read as zero q, k, v and zero log-gates.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *p, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ V buf_load16(Rsrc r, int off)
+{
+    static_assert(sizeof(V) == 16, "16-byte load");
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(Rsrc r, int off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 }  // namespace gla

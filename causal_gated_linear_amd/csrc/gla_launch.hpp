@@ -86,4 +86,23 @@ hipError_t launch_segment_scan(const float *ds, const float *gam, const float *s
 // Enqueue one decode step.  Sizes must already be valid.
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int d_k, int d_v, hipStream_t stream);
 
+// The delta rule (gla_delta.hip).  Workspace per head, element type T: the negated
+// write weights -W = -X diag(beta) K as rows [lp][d_k] (lp = chunks * chunk), then the
+// state-free writes U~ = X diag(beta) V transposed per chunk, [chunks][d_v][chunk];
+// X is the inverse of the chunk's unit lower-triangular system.
+struct DeltaArgs {
+    const void *q, *k, *v;   // [B][H][L][d_k] / [B][H][L][d_v], element type T
+    const float *beta;       // [B][H][L] write strengths
+    const float *s0;         // [B][H][d_k][d_v] or null
+    void *o;                 // [B][H][L][d_v], T
+    float *s_final;          // [B][H][d_k][d_v] or null
+    void *ws_w, *ws_u;       // workspace parts (see above)
+    int BH, L, d_k, d_v;
+    int dvt, n_vt;           // value columns per scan workgroup (16, 32 or 64), tiles per head
+    int xcd_remap;
+};
+size_t delta_workspace(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes);
+hipError_t launch_delta_prefill(const DeltaArgs &a, int dtype, int chunk, hipStream_t stream);
+hipError_t launch_delta_decode(const DeltaArgs &a, int dtype, hipStream_t stream);
+
 }  // namespace gla

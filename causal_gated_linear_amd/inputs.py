@@ -24,6 +24,14 @@ Attention", section "Motivation"):
 Draw order for one call: q, k, v, z, each standard normal in fp32 on the chosen
 device from ``torch.Generator(device).manual_seed(seed)``, then scaled and cast
 (bf16 casts round to nearest even).
+
+The delta rule ("Attention is recurrent", Delta attention) has its own recipe,
+drawn by ``draw_delta`` / ``draw_delta_decode`` in the same order (q, k, v, z):
+
+  delta_prefill      bf16, B=8 H=16 L=4096 d=128 (the gla_prefill shape), q and k
+                     ~ N(0,1) rescaled to unit length per token (in fp32, before the
+                     cast), v ~ N(0,1), write strength beta = sigmoid(z) in fp32 per
+                     head and token, chunk 64
 """
 from __future__ import annotations
 
@@ -62,6 +70,8 @@ WORKLOADS = {
                             "scalar", None, True, seed=4),
     "decode": Workload("decode", torch.bfloat16, 256, 32, 512, 128, 128, 64,
                        "keydim", None, True, decode_steps=1024, seed=5),
+    "delta_prefill": Workload("delta_prefill", torch.bfloat16, 8, 16, 4096, 128, 128, 64,
+                              None, None, False, seed=6),
 }
 
 
@@ -131,3 +141,38 @@ def draw_state(B, H, d_k, d_v, *, seed, scale=1.0, device="cpu"):
     """A random fp32 initial state [B, H, d_k, d_v] ~ scale * N(0,1)."""
     gen = _gen(device, seed)
     return torch.randn(B, H, d_k, d_v, dtype=torch.float32, device=device, generator=gen) * scale
+
+
+def _unit_rows(x):
+    """Rescale the last axis to unit length (an input distribution, as the gates' recipe)."""
+    return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+
+
+def draw_delta(w: Workload, *, B=None, H=None, L=None, seed=None, device="cpu"):
+    """Draw q, k (unit rows), v and beta [B, H, L] for a delta-rule prefill."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    L = w.L if L is None else L
+    seed = w.seed if seed is None else seed
+    gen = _gen(device, seed)
+    f32 = dict(dtype=torch.float32, device=device, generator=gen)
+    q = _unit_rows(torch.randn(B, H, L, w.d_k, **f32))
+    k = _unit_rows(torch.randn(B, H, L, w.d_k, **f32))
+    v = torch.randn(B, H, L, w.d_v, **f32)
+    beta = torch.sigmoid(torch.randn(B, H, L, **f32))
+    return dict(q=q.to(w.dtype), k=k.to(w.dtype), v=v.to(w.dtype), beta=beta.contiguous())
+
+
+def draw_delta_decode(w: Workload, *, steps, B=None, H=None, seed=None, device="cpu"):
+    """Step-major delta-rule decode inputs: q, k [T, B, H, d_k], v [T, B, H, d_v],
+    beta [T, B, H].  Seeded apart from ``draw_delta``."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    seed = (w.seed if seed is None else seed) + 7919
+    gen = _gen(device, seed)
+    f32 = dict(dtype=torch.float32, device=device, generator=gen)
+    q = _unit_rows(torch.randn(steps, B, H, w.d_k, **f32))
+    k = _unit_rows(torch.randn(steps, B, H, w.d_k, **f32))
+    v = torch.randn(steps, B, H, w.d_v, **f32)
+    beta = torch.sigmoid(torch.randn(steps, B, H, **f32))
+    return dict(q=q.to(w.dtype), k=k.to(w.dtype), v=v.to(w.dtype), beta=beta.contiguous())

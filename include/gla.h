@@ -203,6 +203,66 @@ int gla_decode_step_norm(const void *q, const void *k, const void *v, const floa
                          gla_gate_mode gate, float *state, float *z, void *o, int B, int H, int d_k,
                          int d_v, gla_dtype dtype, gla_feature_map phi, gla_stream_t stream);
 
+/*
+ * The delta rule ("Attention is recurrent", sections "Delta attention" and the
+ * "Prefill" section after it).  Before each write the state is asked what it already
+ * predicts for the key, and only the prediction error is written, scaled by the write
+ * strength beta_t:
+ *
+ *     u_t = beta_t (v_t - S_{t-1}^T k_t)                u_t is d_v
+ *     S_t = S_{t-1} + k_t u_t^T,     o_t = S_t^T q_t     (reads the updated state)
+ *
+ * with S_{-1} = s0 (zero when NULL).  No gate, no feature map and no key
+ * normalisation are applied: callers scale keys (unit-norm keys and beta in [0, 1]
+ * keep every step I - beta k k^T a contraction) and queries themselves.
+ *
+ * gla_delta_workspace_bytes -- bytes of device workspace gla_prefill_delta needs:
+ * B*H*ceil(L/chunk)*chunk*(d_k + d_v) elements of the input dtype.  0 for L == 0
+ * or invalid sizes (gla_prefill_delta reports those).
+ */
+size_t gla_delta_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chunk,
+                                 gla_dtype dtype);
+
+/*
+ * gla_prefill_delta -- all outputs of a prompt under the delta rule.  Within a chunk
+ * of `chunk` tokens the writes solve one unit lower-triangular system (the page's
+ * prefill argument applied to a chunk that starts from a nonzero state); the
+ * chunk's state-free parts are computed for all chunks in parallel into the
+ * workspace, then a pass over each head's chunks in order carries the state.
+ *   q, k      in   [B][H][L][d_k], dtype
+ *   v         in   [B][H][L][d_v], dtype
+ *   beta      in   fp32 [B][H][L] write strengths (4-byte aligned)
+ *   s0        in   fp32 [B][H][d_k][d_v] initial state, or NULL for zero
+ *   o         out  [B][H][L][d_v], dtype
+ *   s_final   out  fp32 [B][H][d_k][d_v] state after the last token, or NULL; may
+ *                  equal s0 (in-place update) but must not partially overlap it
+ *   chunk     16, 32 or 64
+ *   workspace device scratch of at least gla_delta_workspace_bytes(...) bytes,
+ *             16-byte aligned; contents are clobbered
+ * Sizes and dtypes as for gla_prefill_chunked.  o must not overlap any other
+ * argument; s_final and the workspace must not overlap any input.  Errors:
+ * GLA_ERR_NULL, GLA_ERR_SHAPE, GLA_ERR_UNSUPPORTED, GLA_ERR_ALIGN, GLA_ERR_ALIAS,
+ * GLA_ERR_WORKSPACE, GLA_ERR_HIP.
+ */
+int gla_prefill_delta(const void *q, const void *k, const void *v, const float *beta,
+                      const float *s0, void *o, float *s_final, int B, int H, int L, int d_k,
+                      int d_v, int chunk, gla_dtype dtype, void *workspace,
+                      size_t workspace_bytes, gla_stream_t stream);
+
+/*
+ * gla_decode_step_delta -- one token of the delta rule on a resident state, in place:
+ * u = beta (v - state^T k), state <- state + k u^T, o = state^T q.
+ *   q, k      in      [B][H][d_k], dtype
+ *   v         in      [B][H][d_v], dtype
+ *   beta      in      fp32 [B][H] (4-byte aligned)
+ *   state     in/out  fp32 [B][H][d_k][d_v]
+ *   o         out     [B][H][d_v], dtype
+ * state and o must not overlap the inputs or each other.  Errors as gla_decode_step.
+ */
+int gla_decode_step_delta(const void *q, const void *k, const void *v, const float *beta,
+                          float *state, void *o, int B, int H, int d_k, int d_v, gla_dtype dtype,
+                          gla_stream_t stream);
+
 /* gla_strerror -- static text for a gla_status value (never NULL). */
 const char *gla_strerror(int status);
 

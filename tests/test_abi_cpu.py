@@ -32,7 +32,8 @@ def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["gla_state_alloc", "gla_state_free", "gla_prefill_workspace_bytes",
                                   "gla_prefill_chunked", "gla_decode_step", "gla_strerror",
                                   "gla_last_error_detail", "gla_prefill_chunked_norm",
-                                  "gla_decode_step_norm"])
+                                  "gla_decode_step_norm", "gla_delta_workspace_bytes",
+                                  "gla_prefill_delta", "gla_decode_step_delta"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -233,3 +234,79 @@ def test_decode_norm_rejects_z_overlapping_state(lib):
     st = lib.gla_decode_step_norm(P(A), P(A + MB), P(A + 2 * MB), P(A + 3 * MB), 1, P(A + 16 * MB),
                                   P(A + 16 * MB + 1024), P(A + 64 * MB), 2, 4, 128, 128, 1, 0, None)
     assert st == _lib.GLA_ERR_ALIAS
+
+
+# the delta rule: no gate or feature map; beta and a workspace always
+def _prefill_delta(lib, **kw):
+    args = dict(q=A, k=A + 16 * MB, v=A + 32 * MB, beta=A + 48 * MB, s0=None, o=A + 96 * MB,
+                s_final=A + 128 * MB, B=1, H=2, L=64, d_k=64, d_v=64, chunk=64, dtype=1,
+                ws=A + 256 * MB, ws_bytes=1 * MB)
+    args.update(kw)
+    P = ctypes.c_void_p
+    return lib.gla_prefill_delta(P(args["q"]), P(args["k"]), P(args["v"]), P(args["beta"]), P(args["s0"]),
+                                 P(args["o"]), P(args["s_final"]), args["B"], args["H"], args["L"],
+                                 args["d_k"], args["d_v"], args["chunk"], args["dtype"], P(args["ws"]),
+                                 args["ws_bytes"], None)
+
+
+PREFILL_DELTA_BAD = {
+    "B_zero": (dict(B=0), _lib.GLA_ERR_SHAPE),
+    "L_negative": (dict(L=-5), _lib.GLA_ERR_SHAPE),
+    "d_k_48": (dict(d_k=48), _lib.GLA_ERR_UNSUPPORTED),
+    "chunk_128": (dict(chunk=128), _lib.GLA_ERR_UNSUPPORTED),
+    "dtype_2": (dict(dtype=2), _lib.GLA_ERR_UNSUPPORTED),
+    "beta_null": (dict(beta=None), _lib.GLA_ERR_NULL),
+    "o_null": (dict(o=None), _lib.GLA_ERR_NULL),
+    "beta_misaligned": (dict(beta=A + 48 * MB + 2), _lib.GLA_ERR_ALIGN),
+    "q_misaligned": (dict(q=A + 8), _lib.GLA_ERR_ALIGN),
+    "workspace_missing": (dict(ws=None, ws_bytes=0), _lib.GLA_ERR_WORKSPACE),
+    "workspace_short": (dict(ws_bytes=64 * 128 * 2 * 2 - 2), _lib.GLA_ERR_WORKSPACE),
+    "L_past_32bit_head_offsets": (dict(L=4194304, d_k=128, d_v=128), _lib.GLA_ERR_SHAPE),
+    "o_overlaps_beta": (dict(o=A + 48 * MB + 64), _lib.GLA_ERR_ALIAS),
+    "o_overlaps_workspace": (dict(o=A + 256 * MB + 4096), _lib.GLA_ERR_ALIAS),
+    "workspace_overlaps_k": (dict(ws=A + 16 * MB + 1024), _lib.GLA_ERR_ALIAS),
+    "s_final_overlaps_v": (dict(s_final=A + 32 * MB + 16), _lib.GLA_ERR_ALIAS),
+    "s_final_partially_overlaps_s0": (dict(s0=A + 200 * MB, s_final=A + 200 * MB + 256), _lib.GLA_ERR_ALIAS),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PREFILL_DELTA_BAD))
+def test_prefill_delta_rejects(lib, case):
+    kw, want = PREFILL_DELTA_BAD[case]
+    assert _prefill_delta(lib, **kw) == want
+    assert lib.gla_last_error_detail().decode() != ""
+
+
+def test_delta_workspace_bytes(lib):
+    """-W rows [B*H][padded L][d_k] and U~ [B*H][padded L][d_v], in the input dtype."""
+    assert lib.gla_delta_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 8 * 16 * 4096 * 256 * 2
+    assert lib.gla_delta_workspace_bytes(1, 2, 100, 64, 32, 32, 0) == 2 * 128 * 96 * 4
+    assert lib.gla_delta_workspace_bytes(1, 2, 0, 64, 32, 32, 0) == 0
+    assert lib.gla_delta_workspace_bytes(1, 2, 100, 48, 32, 32, 0) == 0
+
+
+def _decode_delta(lib, **kw):
+    args = dict(q=A, k=A + MB, v=A + 2 * MB, beta=A + 3 * MB, state=A + 16 * MB, o=A + 64 * MB,
+                B=2, H=4, d_k=128, d_v=128, dtype=1)
+    args.update(kw)
+    P = ctypes.c_void_p
+    return lib.gla_decode_step_delta(P(args["q"]), P(args["k"]), P(args["v"]), P(args["beta"]),
+                                     P(args["state"]), P(args["o"]), args["B"], args["H"], args["d_k"],
+                                     args["d_v"], args["dtype"], None)
+
+
+DECODE_DELTA_BAD = {
+    "beta_null": (dict(beta=None), _lib.GLA_ERR_NULL),
+    "state_null": (dict(state=None), _lib.GLA_ERR_NULL),
+    "H_zero": (dict(H=0), _lib.GLA_ERR_SHAPE),
+    "d_k_8": (dict(d_k=8), _lib.GLA_ERR_UNSUPPORTED),
+    "beta_misaligned": (dict(beta=A + 3 * MB + 1), _lib.GLA_ERR_ALIGN),
+    "o_overlaps_state": (dict(o=A + 16 * MB + 512), _lib.GLA_ERR_ALIAS),
+    "state_overlaps_beta": (dict(state=A + 3 * MB), _lib.GLA_ERR_ALIAS),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DECODE_DELTA_BAD))
+def test_decode_delta_rejects(lib, case):
+    kw, want = DECODE_DELTA_BAD[case]
+    assert _decode_delta(lib, **kw) == want
