@@ -62,6 +62,23 @@ def prefill_flops(B, H, L, dk, dv, C):
     return B * H * (n_full * per(C) + (per(tail) if tail else 0))
 
 
+def delta_bytes(B, H, L, dk, dv, es=2):
+    """Algorithmic HBM bytes of one delta-rule prefill: read q, k, v and beta once, write
+    o and the final state once (the workspace between its two kernels not counted)."""
+    return B * H * (L * (2 * dk * es + dv * es + 4 + dv * es) + dk * dv * 4)
+
+
+def delta_flops(B, H, L, dk, dv, C):
+    """Flops of the chunkwise delta rule, causal count: per chunk of c tokens the
+    strictly lower K K^T (c(c-1) d_k), the triangular inverse (c^3 / 3), W and U~ from
+    the lower-triangular inverse (c(c+1)(d_k + d_v)), the masked scores and their
+    product with U (c(c+1)(d_k + d_v)), and the three state products U~ - W S, Q S and
+    S += K^T U (6 c d_k d_v)."""
+    n_full, tail = divmod(L, C)
+    per = lambda c: c * (c - 1) * dk + c ** 3 // 3 + 2 * c * (c + 1) * (dk + dv) + 6 * c * dk * dv
+    return B * H * (n_full * per(C) + (per(tail) if tail else 0))
+
+
 def decode_step_bytes(B, H, dk, dv, es=2):
     """Per step: read + write the fp32 state, read q, k, v, g, write o."""
     return B * H * (2 * dk * dv * 4 + (2 * dk + dv) * es + 4 * dk + dv * es)
@@ -200,6 +217,66 @@ def run_decode(args, torch, api, inputs):
     nbytes_n = nbytes + w.B * w.H * w.d_k * 8
     return dict(w=w, steps=T, ms_per_step=per, bytes=nbytes, norm_steps=Tn, norm_ms_per_step=per_n,
                 norm_bytes=nbytes_n)
+
+
+def run_delta(args, torch, api, inputs):
+    """The delta rule ("Attention is recurrent", Delta attention): the chunkwise prefill
+    at the gla_prefill shape and, at the decode shape, single-token steps."""
+    w = inputs.WORKLOADS["delta_prefill"]
+    inp = inputs.draw_delta(w, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, w.d_v, dtype=w.dtype, device="cuda")
+    s = torch.empty(w.B, w.H, w.d_k, w.d_v, dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.delta_workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, w.dtype),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.prefill_delta(inp["q"], inp["k"], inp["v"], inp["beta"], chunk=w.chunk, out=o, final_state=s,
+                          workspace=ws, stream=stream)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 2)
+    per = _events_ms(step, n, stream) / n
+    nbytes = delta_bytes(w.B, w.H, w.L, w.d_k, w.d_v)
+    flops = delta_flops(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)
+    gbs = nbytes / (per / 1e3) / 1e9
+    tfl = flops / (per / 1e3) / 1e12
+    out = {"prefill": {
+        "workload": "delta_prefill: B=8 H=16 L=4096 d_k=d_v=128 chunk=64, bf16 q/k/v (unit-length q, k), "
+                    "fp32 beta = sigmoid(N(0,1)), fp32 final state",
+        "ms_per_step": per, "tokens_per_s": w.B * w.L / (per / 1e3), "GB_per_s": gbs,
+        "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes, "tflops": tfl,
+        "mfma_frac": tfl / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": flops,
+        "workspace_bytes": int(ws.numel()),
+        "kernels": "delta_prep_kernel (all chunks in parallel) then delta_scan_kernel (chunks in order)"}}
+    del inp, o, s, ws
+    wd = inputs.WORKLOADS["decode"]
+    T = min(256, args.decode_steps)
+    d = inputs.draw_delta_decode(dataclass_replace(w, d_k=wd.d_k, d_v=wd.d_v), steps=T, B=wd.B, H=wd.H,
+                                 device="cuda")
+    state = inputs.draw_state(wd.B, wd.H, wd.d_k, wd.d_v, seed=17, scale=0.1, device="cuda")
+    od = torch.empty(wd.B, wd.H, wd.d_v, dtype=torch.bfloat16, device="cuda")
+    it = iter(range(T))
+
+    def dstep():
+        t = next(it)
+        api.decode_step_delta(d["q"][t], d["k"][t], d["v"][t], d["beta"][t], state=state, out=od, stream=stream)
+
+    torch.cuda.synchronize()
+    dper = _events_ms(dstep, T, stream) / T
+    dbytes = decode_step_bytes(wd.B, wd.H, wd.d_k, wd.d_v) - wd.B * wd.H * 4 * wd.d_k + wd.B * wd.H * 4
+    out["decode"] = {"workload": "delta decode: B=256 H=32 d=128 bf16 q/k/v, fp32 beta, fp32 state, %d steps" % T,
+                     "ms_per_step": dper, "tokens_per_s": wd.B / (dper / 1e3),
+                     "GB_per_s": dbytes / (dper / 1e3) / 1e9,
+                     "hbm_frac": dbytes / (dper / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": dbytes}
+    return out
+
+
+def dataclass_replace(w, **kw):
+    import dataclasses
+    return dataclasses.replace(w, **kw)
 
 
 def kernel_source_hash():
@@ -466,6 +543,7 @@ def main():
                                "bytes_per_step": dc["norm_bytes"]}
     if not args.no_others:
         line["other_prefill"] = run_other_prefills(args, torch, api, inputs)
+        line["delta"] = run_delta(args, torch, api, inputs)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget_s)
     print(json.dumps(line))
