@@ -469,3 +469,90 @@ DELTA_ERROR_PINS = {
     "delta_moving_average": (pin_delta_moving_average, 1e-13),
     "delta_chaining": (pin_delta_chaining, 0.0),
 }
+
+
+# ---- the input-side gate producer ("Gated Linear Attention", Recurrent Form:
+# alpha_t = sigmoid(W_up W_down x_t); log-gates in the prefill layout) ----
+
+def _gate_inputs(seed, B, L, dm, r, H, dk, scale=1.0):
+    rr = np.random.default_rng(seed)
+    x = rr.standard_normal((B, L, dm))
+    wd = rr.standard_normal((r, dm)) * scale / math.sqrt(dm)
+    wu = rr.standard_normal((H * dk, r)) * scale / math.sqrt(r)
+    return x, wd, wu
+
+
+def pin_gate_brute_force(gate, seed=40, B=2, L=3, dm=5, r=2, H=2, dk=3, tau=1.0):
+    """Explicit sums over d_model and r in Python floats, and the textbook
+    log(1 / (1 + e^-z)) (the values here stay well inside its safe range)."""
+    x, wd, wu = _gate_inputs(seed, B, L, dm, r, H, dk)
+    g = gate(x, wd, wu, H, dk, tau)
+    worst = 0.0
+    for b in range(B):
+        for t in range(L):
+            zd = [sum(wd[j][m] * x[b][t][m] for m in range(dm)) for j in range(r)]
+            for h in range(H):
+                for i in range(dk):
+                    z = sum(wu[h * dk + i][j] * zd[j] for j in range(r))
+                    want = math.log(1.0 / (1.0 + math.exp(-z))) / tau
+                    worst = max(worst, abs(g[b, h, t, i] - want) / max(abs(want), 1e-300))
+    return worst
+
+
+def pin_gate_zero_input(gate, seed=41, B=1, L=4, dm=8, r=4, H=2, dk=4, tau=16.0):
+    """x = 0 (or zero weights) gives z = 0: every gate is sigmoid(0) = 1/2, g = -ln 2 / tau."""
+    _, wd, wu = _gate_inputs(seed, B, L, dm, r, H, dk)
+    g1 = gate(np.zeros((B, L, dm)), wd, wu, H, dk, tau)
+    g2 = gate(np.ones((B, L, dm)), np.zeros_like(wd), wu, H, dk, tau)
+    want = -math.log(2.0) / tau
+    return float(max(np.abs(g1 - want).max(), np.abs(g2 - want).max()) / abs(want))
+
+
+def pin_gate_rank_one_select(gate, seed=42, B=2, L=5, dm=6, r=3, H=2, dk=4):
+    """W_down picks input coordinate c into rank slot 0, W_up copies slot 0 to output
+    n scaled by s_n: z_t[n] = s_n x_t[c], so g[b, h, t, i] = log sigmoid(s_{h d_k+i} x[b, t, c])."""
+    rr = np.random.default_rng(seed)
+    x = rr.standard_normal((B, L, dm)) * 3.0
+    c = 2
+    wd = np.zeros((r, dm))
+    wd[0, c] = 1.0
+    s = rr.standard_normal(H * dk)
+    wu = np.zeros((H * dk, r))
+    wu[:, 0] = s
+    g = gate(x, wd, wu, H, dk, 1.0)
+    z = x[:, :, c][:, None, :, None] * s.reshape(H, dk)[None, :, None, :]
+    want = np.log(1.0 / (1.0 + np.exp(-z)))
+    return rel_err(g, want)
+
+
+def pin_gate_extremes(gate):
+    """Large |z|: log sigmoid(z) -> z for z -> -inf and -> -e^-z for z -> +inf; each
+    checked to relative accuracy (a naive log(sigmoid) would give -inf / 0)."""
+    zs = np.array([-800.0, -60.0, -30.0, 30.0, 60.0, 700.0])
+    x = zs.reshape(1, len(zs), 1)
+    g = gate(x, np.ones((1, 1)), np.ones((1, 1)), 1, 1, 1.0)[0, 0, :, 0]
+    neg, pos = np.minimum(zs, 0.0), np.maximum(zs, 0.0)
+    want = np.where(zs < 0, neg - np.exp(neg), -np.exp(-pos) + np.exp(-2 * pos) / 2)   # series
+    return float(np.max(np.abs(g - want) / np.abs(want)))
+
+
+def pin_gate_sigmoid_identity(gate, seed=43, B=2, L=7, dm=16, r=4, H=3, dk=4, tau=4.0):
+    """exp(tau g) is the logistic function of z, here via scipy.special.expit, and lies
+    in (0, 1)."""
+    from scipy.special import expit
+    x, wd, wu = _gate_inputs(seed, B, L, dm, r, H, dk, scale=2.0)
+    g = gate(x, wd, wu, H, dk, tau)
+    z = (x @ wd.T @ wu.T).reshape(B, L, H, dk).transpose(0, 2, 1, 3)
+    a = np.exp(tau * g)
+    return max(rel_err(a, expit(z)), float(max(0.0, a.max() - 1.0, -a.min())))
+
+
+GATE_ERROR_PINS = {
+    # name: (callable on the gate producer, tolerance)
+    "gate_brute_force": (pin_gate_brute_force, 1e-12),
+    "gate_brute_force_tau": (lambda f: pin_gate_brute_force(f, seed=44, tau=16.0), 1e-12),
+    "gate_zero_input": (pin_gate_zero_input, 1e-14),
+    "gate_rank_one_select": (pin_gate_rank_one_select, 1e-12),
+    "gate_extremes": (pin_gate_extremes, 1e-14),
+    "gate_sigmoid_identity": (pin_gate_sigmoid_identity, 1e-13),
+}
