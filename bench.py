@@ -274,6 +274,36 @@ def run_delta(args, torch, api, inputs):
     return out
 
 
+def run_gate(args, torch, api, inputs):
+    """The input-side gate producer ("Gated Linear Attention", Recurrent Form:
+    alpha_t = sigmoid(W_up W_down x_t)) at the gla_prefill shape: the log-gates that the
+    headline prefill reads, produced from a d_model = 2048 input with rank-16 weights."""
+    w = inputs.GATE_WORKLOAD
+    d = inputs.draw_gate(device="cuda")
+    g = torch.empty(w["B"], w["H"], w["L"], w["d_k"], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.gate_project(d["x"], d["w_down"], d["w_up"], w["H"], w["d_k"], tau=w["tau"], out=g, stream=stream)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 2)
+    per = _events_ms(step, n, stream) / n
+    es = 2
+    ntok = w["B"] * w["L"]
+    nbytes = ntok * w["d_model"] * es + (w["rank"] * w["d_model"] + w["H"] * w["d_k"] * w["rank"]) * es \
+        + ntok * w["H"] * w["d_k"] * 4
+    flops = 2 * ntok * w["rank"] * (w["d_model"] + w["H"] * w["d_k"])
+    gbs = nbytes / (per / 1e3) / 1e9
+    return {"workload": "gate_project: B=8 L=4096 d_model=2048 rank 16 -> H=16 x d_k=128 fp32 log-gates, "
+                        "bf16 x and weights, tau 16",
+            "ms_per_step": per, "tokens_per_s": ntok / (per / 1e3), "GB_per_s": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes, "flops_per_launch": flops,
+            "tflops": flops / (per / 1e3) / 1e12}
+
+
 def dataclass_replace(w, **kw):
     import dataclasses
     return dataclasses.replace(w, **kw)
@@ -544,6 +574,7 @@ def main():
     if not args.no_others:
         line["other_prefill"] = run_other_prefills(args, torch, api, inputs)
         line["delta"] = run_delta(args, torch, api, inputs)
+        line["gate_producer"] = run_gate(args, torch, api, inputs)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget_s)
     print(json.dumps(line))

@@ -237,6 +237,32 @@ def decode_step_delta(q, k, v, beta, state=None, out=None, stream=None):
     return out
 
 
+def gate_project(x, w_down, w_up, H, d_k, tau=1.0, out=None, stream=None):
+    """Input-side gate producer (gla_gate_project): fp32 log-gates
+    g [B, H, L, d_k] = log(sigmoid(W_up W_down x)) / tau for the key-dim prefill.
+    x: [B, L, d_model]; w_down: [rank, d_model]; w_up: [H*d_k, rank] (fp32 or bf16,
+    same dtype, CUDA)."""
+    lib = _lib.load()
+    _need(x.dim() == 3, "x must be 3-D [B, L, d_model]")
+    B, L, dm = x.shape
+    dev, dt = x.device, x.dtype
+    _need(dt in _DTYPES, "dtype must be float32 or bfloat16")
+    _need(w_down.dim() == 2, "w_down must be 2-D [rank, d_model]")
+    r = w_down.shape[0]
+    _check_tensor(x, "x", (B, L, dm), dt, dev)
+    _check_tensor(w_down, "w_down", (r, dm), dt, dev)
+    _check_tensor(w_up, "w_up", (H * d_k, r), dt, dev)
+    _need(dev.type == "cuda", "tensors must be on a GPU device")
+    if out is None:
+        out = torch.empty((B, H, L, d_k), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor(out, "out", (B, H, L, d_k), torch.float32, dev)
+    st = lib.gla_gate_project(_ptr(x), _ptr(w_down), _ptr(w_up), _ptr(out), B, L, dm, r, H, d_k, float(tau),
+                              _DTYPES[dt], _stream_handle(stream))
+    _lib.check(st, "gla_gate_project")
+    return out
+
+
 class DeviceState:
     """A zeroed fp32 state [B, H, d_k, d_v] from gla_state_alloc, owned by this object
     (freed with gla_state_free).  ``tensor()`` views it as a torch tensor (no copy)

@@ -510,4 +510,47 @@ int gla_decode_step_delta(const void *q, const void *k, const void *v, const flo
     return ok();
 }
 
+// ---- the input-side gate producer ------------------------------------------------
+
+int gla_gate_project(const void *x, const void *w_down, const void *w_up, float *g, int B, int L,
+                     int d_model, int rank, int H, int d_k, float tau, gla_dtype dtype,
+                     gla_stream_t stream)
+{
+    if (B <= 0 || H <= 0 || L < 0) return fail(GLA_ERR_SHAPE, "B=%d, H=%d must be positive and L=%d >= 0", B, H, L);
+    if (d_model <= 0) return fail(GLA_ERR_SHAPE, "d_model=%d must be positive", d_model);
+    if (d_model % 32 != 0 || d_model > 65536)
+        return fail(GLA_ERR_UNSUPPORTED, "d_model=%d: must be a multiple of 32, at most 65536", d_model);
+    if (rank != 16 && rank != 32) return fail(GLA_ERR_UNSUPPORTED, "rank=%d: must be 16 or 32", rank);
+    if (!dim_supported(d_k)) return fail(GLA_ERR_UNSUPPORTED, "d_k=%d: must be 16, 32, 64 or 128", d_k);
+    if (dtype != GLA_F32 && dtype != GLA_BF16)
+        return fail(GLA_ERR_UNSUPPORTED, "dtype %d is not GLA_F32 or GLA_BF16", (int)dtype);
+    if (!(tau > 0.f) || tau > 3.0e38f) return fail(GLA_ERR_SHAPE, "tau=%g must be positive and finite", (double)tau);
+    if ((long long)H * d_k > (1LL << 20)) return fail(GLA_ERR_SHAPE, "H*d_k=%lld too large", (long long)H * d_k);
+    if ((long long)B * L > (1LL << 40)) return fail(GLA_ERR_SHAPE, "B*L too large");
+    if (L > 0 && (!x || !w_down || !w_up || !g))
+        return fail(GLA_ERR_NULL, "x, w_down, w_up and g are required when L > 0");
+    const void *ptrs[] = {x, w_down, w_up, g};
+    const char *names[] = {"x", "w_down", "w_up", "g"};
+    for (int i = 0; i < 4; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    const size_t es = elem_size(dtype), ntok = (size_t)B * L;
+    const Span sx = span(x, ntok * d_model * es, "x"), swd = span(w_down, (size_t)rank * d_model * es, "w_down");
+    const Span swu = span(w_up, (size_t)H * d_k * rank * es, "w_up"), sg = span(g, ntok * H * d_k * 4, "g");
+    const Span g_forbidden[] = {sx, swd, swu};
+    for (const Span &s : g_forbidden)
+        if (overlap(sg, s)) return fail(GLA_ERR_ALIAS, "g overlaps %s", s.name);
+    if (L == 0) return ok();
+    if ((ntok + 63) / 64 > 0x7fffffffUL) return fail(GLA_ERR_SHAPE, "B*L too large");
+    gla::GateArgs a;
+    a.x = x; a.w_down = w_down; a.w_up = w_up; a.g = g;
+    a.B = B; a.L = L; a.d_model = d_model; a.H = H; a.d_k = d_k; a.inv_tau = 1.f / tau;
+    a.dk_shift = 0;
+    while ((1 << a.dk_shift) < d_k) ++a.dk_shift;           // d_k is a power of two
+    a.tiles_per_group = 128;
+    const hipError_t e = gla::launch_gate_project(a, dtype == GLA_BF16 ? 1 : 0, rank, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "gate producer launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

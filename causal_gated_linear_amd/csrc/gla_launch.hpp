@@ -102,6 +102,19 @@ struct DeltaArgs {
     int xcd_remap;
 };
 size_t delta_workspace(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes);
+
+// The input-side gate producer (gla_gate.hip): g = log(sigmoid(W_up W_down x)) / tau.
+struct GateArgs {
+    const void *x;           // [B][L][d_model], element type T
+    const void *w_down;      // [rank][d_model], T
+    const void *w_up;        // [H * d_k][rank], T
+    float *g;                // [B][H][L][d_k] fp32 log-gates
+    int B, L, d_model, H, d_k;
+    int dk_shift;            // log2(d_k)
+    int tiles_per_group;     // 16-output tiles per workgroup (grid.y splits H*d_k/16)
+    float inv_tau;
+};
+hipError_t launch_gate_project(const GateArgs &a, int dtype, int rank, hipStream_t stream);
 hipError_t launch_delta_prefill(const DeltaArgs &a, int dtype, int chunk, hipStream_t stream);
 hipError_t launch_delta_decode(const DeltaArgs &a, int dtype, hipStream_t stream);
 

@@ -32,6 +32,15 @@ drawn by ``draw_delta`` / ``draw_delta_decode`` in the same order (q, k, v, z):
                      ~ N(0,1) rescaled to unit length per token (in fp32, before the
                      cast), v ~ N(0,1), write strength beta = sigmoid(z) in fp32 per
                      head and token, chunk 64
+
+The gate producer ("Gated Linear Attention", Recurrent Form: alpha_t =
+sigmoid(W_up W_down x_t)) has synthetic weights, drawn by ``draw_gate`` in the
+order x, W_down, W_up:
+
+  gate_project       bf16, B=8 L=4096 d_model=2048 (= H d_k of gla_prefill), rank 16,
+                     H=16 d_k=128, x ~ N(0,1), W_down ~ N(0,1)/sqrt(d_model),
+                     W_up ~ N(0,1)/sqrt(rank), tau 16: z is about N(0,1), so the
+                     produced gates follow the gla_prefill recipe logsigmoid(z)/16
 """
 from __future__ import annotations
 
@@ -176,3 +185,23 @@ def draw_delta_decode(w: Workload, *, steps, B=None, H=None, seed=None, device="
     v = torch.randn(steps, B, H, w.d_v, **f32)
     beta = torch.sigmoid(torch.randn(steps, B, H, **f32))
     return dict(q=q.to(w.dtype), k=k.to(w.dtype), v=v.to(w.dtype), beta=beta.contiguous())
+
+
+GATE_WORKLOAD = dict(B=8, L=4096, d_model=2048, rank=16, H=16, d_k=128, tau=16.0, dtype=torch.bfloat16, seed=7)
+
+
+def draw_gate(*, B=None, L=None, d_model=None, rank=None, H=None, d_k=None, dtype=None, seed=None,
+              device="cpu"):
+    """Draw x [B, L, d_model], W_down [rank, d_model] and W_up [H*d_k, rank] for the
+    gate producer (sizes default to GATE_WORKLOAD)."""
+    w = dict(GATE_WORKLOAD)
+    for k, v in dict(B=B, L=L, d_model=d_model, rank=rank, H=H, d_k=d_k, dtype=dtype, seed=seed).items():
+        if v is not None:
+            w[k] = v
+    gen = _gen(device, w["seed"])
+    f32 = dict(dtype=torch.float32, device=device, generator=gen)
+    x = torch.randn(w["B"], w["L"], w["d_model"], **f32)
+    wd = torch.randn(w["rank"], w["d_model"], **f32) / math.sqrt(w["d_model"])
+    wu = torch.randn(w["H"] * w["d_k"], w["rank"], **f32) / math.sqrt(w["rank"])
+    dt = w["dtype"]
+    return dict(x=x.to(dt), w_down=wd.to(dt), w_up=wu.to(dt))

@@ -263,6 +263,32 @@ int gla_decode_step_delta(const void *q, const void *k, const void *v, const flo
                           float *state, void *o, int B, int H, int d_k, int d_v, gla_dtype dtype,
                           gla_stream_t stream);
 
+/*
+ * gla_gate_project -- the input-side gate producer ("Gated Linear Attention", section
+ * "GLA / Recurrent Form" and its flow chart: alpha_t = sigmoid(W_up W_down x_t), a
+ * low-rank map from the token input to one gate per key dimension of every head).
+ * Writes the natural-log gates that gla_prefill_chunked takes with GLA_GATE_KEYDIM:
+ *
+ *     g[b][h][t][i] = log(sigmoid(z[b][t][h*d_k + i])) / tau,
+ *     z[b][t] = W_up (W_down x[b][t])
+ *
+ * tau = 1 is the page's form; tau > 1 gives alpha = sigmoid(z)^(1/tau).
+ *   x         in   [B][L][d_model], dtype
+ *   w_down    in   [rank][d_model], dtype
+ *   w_up      in   [H*d_k][rank], dtype
+ *   g         out  fp32 [B][H][L][d_k]; must not overlap x, w_down or w_up
+ *   d_model   a multiple of 32, at most 65536;  rank 16 or 32;  d_k 16, 32, 64 or 128
+ *   tau       positive and finite
+ * Arithmetic: fp32 accumulation; with bf16 inputs both products take bf16
+ * matrix-core operands (the rank-r code is rounded to bf16), with fp32 inputs fp32
+ * ones; log and exp are the hardware base-2 instructions.  All
+ * pointers 16-byte aligned.  L == 0 does nothing.  Errors: GLA_ERR_NULL,
+ * GLA_ERR_SHAPE, GLA_ERR_UNSUPPORTED, GLA_ERR_ALIGN, GLA_ERR_ALIAS, GLA_ERR_HIP.
+ */
+int gla_gate_project(const void *x, const void *w_down, const void *w_up, float *g, int B, int L,
+                     int d_model, int rank, int H, int d_k, float tau, gla_dtype dtype,
+                     gla_stream_t stream);
+
 /* gla_strerror -- static text for a gla_status value (never NULL). */
 const char *gla_strerror(int status);
 

@@ -33,7 +33,7 @@ def test_header_declares_expected_entry_points():
                                   "gla_prefill_chunked", "gla_decode_step", "gla_strerror",
                                   "gla_last_error_detail", "gla_prefill_chunked_norm",
                                   "gla_decode_step_norm", "gla_delta_workspace_bytes",
-                                  "gla_prefill_delta", "gla_decode_step_delta"])
+                                  "gla_prefill_delta", "gla_decode_step_delta", "gla_gate_project"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -310,3 +310,35 @@ DECODE_DELTA_BAD = {
 def test_decode_delta_rejects(lib, case):
     kw, want = DECODE_DELTA_BAD[case]
     assert _decode_delta(lib, **kw) == want
+
+
+def _gate(lib, **kw):
+    args = dict(x=A, wd=A + 64 * MB, wu=A + 65 * MB, g=A + 128 * MB, B=2, L=64, dm=256, r=16, H=2, dk=64,
+                tau=1.0, dtype=1)
+    args.update(kw)
+    P = ctypes.c_void_p
+    return lib.gla_gate_project(P(args["x"]), P(args["wd"]), P(args["wu"]), P(args["g"]), args["B"], args["L"],
+                                args["dm"], args["r"], args["H"], args["dk"], args["tau"], args["dtype"], None)
+
+
+GATE_BAD = {
+    "B_zero": (dict(B=0), _lib.GLA_ERR_SHAPE),
+    "L_negative": (dict(L=-1), _lib.GLA_ERR_SHAPE),
+    "d_model_48": (dict(dm=48), _lib.GLA_ERR_UNSUPPORTED),
+    "rank_8": (dict(r=8), _lib.GLA_ERR_UNSUPPORTED),
+    "d_k_24": (dict(dk=24), _lib.GLA_ERR_UNSUPPORTED),
+    "tau_zero": (dict(tau=0.0), _lib.GLA_ERR_SHAPE),
+    "tau_nan": (dict(tau=float("nan")), _lib.GLA_ERR_SHAPE),
+    "x_null": (dict(x=None), _lib.GLA_ERR_NULL),
+    "g_misaligned": (dict(g=A + 128 * MB + 4), _lib.GLA_ERR_ALIGN),
+    "g_overlaps_w_up": (dict(g=A + 65 * MB + 16), _lib.GLA_ERR_ALIAS),
+    "g_overlaps_x": (dict(g=A + 4096), _lib.GLA_ERR_ALIAS),
+    "dtype_3": (dict(dtype=3), _lib.GLA_ERR_UNSUPPORTED),
+}
+
+
+@pytest.mark.parametrize("case", sorted(GATE_BAD))
+def test_gate_project_rejects(lib, case):
+    kw, want = GATE_BAD[case]
+    assert _gate(lib, **kw) == want
+    assert lib.gla_last_error_detail().decode() != ""
