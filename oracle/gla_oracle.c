@@ -63,13 +63,22 @@
  * and head, passed as is; no gate, no feature map and no key normalisation inside
  * (callers scale keys); S_{-1} = s0 or zero (the page assumes zero).  beta is
  * [B][H][L].
+ *
+ * Outer-product gate (gla_oracle_forward_outer): "Gated Linear Attention", section
+ * "GLA / Recurrent Form", names the low-rank parameterisation G_t = alpha_t beta_t^T
+ * of the general gate G_t (.) S_{t-1}: the state decays along both dimensions,
+ *
+ *       S_t[i][j] = alpha_t[i] * beta_t[j] * S_{t-1}[i][j] + k~_i * v_t[j]
+ *
+ * with alpha_t = exp(g_t) per key dimension and beta_t = exp(gv_t) per value
+ * dimension (natural-log gates, gv [B][H][L][d_v]).  Read-out as above.
  */
 #include <math.h>
 #include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_GATE_NONE = 0, ORACLE_GATE_KEYDIM = 1, ORACLE_GATE_SCALAR = 2 };
+enum { ORACLE_GATE_NONE = 0, ORACLE_GATE_KEYDIM = 1, ORACLE_GATE_SCALAR = 2, ORACLE_GATE_OUTER = 3 };
 enum { ORACLE_PHI_IDENTITY = 0, ORACLE_PHI_ELU1 = 1 };
 
 /* elu(x) + 1 with elu's alpha = 1: x + 1 for x > 0, exp(x) otherwise. */
@@ -80,7 +89,7 @@ static double feature(double x, int phi)
 }
 
 typedef struct {
-    const double *q, *k, *v, *g, *s0, *z0, *beta;
+    const double *q, *k, *v, *g, *gv, *s0, *z0, *beta;
     double *o, *s_out, *z_out;
     int norm, delta;
     long B, H, L, dk, dv;
@@ -90,7 +99,7 @@ typedef struct {
 } job_t;
 
 static void run_head(const job_t *jb, long head, double *S, double *qf, double *kf, double *a,
-                     double *z)
+                     double *z, double *bv)
 {
     const long L = jb->L, dk = jb->dk, dv = jb->dv;
     const double *q = jb->q + head * L * dk;
@@ -125,14 +134,17 @@ static void run_head(const job_t *jb, long head, double *S, double *qf, double *
             kf[i] = feature(k[t * dk + i], jb->phi);
         }
         for (long i = 0; i < dk; ++i) {
-            if (jb->gate_mode == ORACLE_GATE_KEYDIM) a[i] = exp(jb->g[(head * L + t) * dk + i]);
+            if (jb->gate_mode == ORACLE_GATE_KEYDIM || jb->gate_mode == ORACLE_GATE_OUTER)
+                a[i] = exp(jb->g[(head * L + t) * dk + i]);
             else if (jb->gate_mode == ORACLE_GATE_SCALAR) a[i] = exp(jb->g[head * L + t]);
             else a[i] = 1.0;
         }
-        /* state update: decay the key rows, then add the outer product k~ v^T */
+        for (long j = 0; j < dv; ++j)        /* value-dimension gate: outer-product mode only */
+            bv[j] = jb->gate_mode == ORACLE_GATE_OUTER ? exp(jb->gv[(head * L + t) * dv + j]) : 1.0;
+        /* state update: decay the key rows (and value columns), then add k~ v^T */
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
-                S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];
+                S[i * dv + j] = a[i] * bv[j] * S[i * dv + j] + kf[i] * v[t * dv + j];
         /* normaliser state: the same decay, the feature-mapped key added */
         double den = 1.0;
         if (jb->norm) {
@@ -161,32 +173,34 @@ static void *worker(void *arg)
     double *kf = (double *)malloc(sizeof(double) * jb->dk);
     double *a = (double *)malloc(sizeof(double) * jb->dk);
     double *z = (double *)malloc(sizeof(double) * (jb->dk > jb->dv ? jb->dk : jb->dv));
-    if (S && qf && kf && a && z) {     /* on allocation failure take no head */
+    double *bv = (double *)malloc(sizeof(double) * jb->dv);
+    if (S && qf && kf && a && z && bv) {     /* on allocation failure take no head */
         for (;;) {
             pthread_mutex_lock(&jb->lock);
             long head = jb->next_head++;
             pthread_mutex_unlock(&jb->lock);
             if (head >= jb->B * jb->H) break;
-            run_head(jb, head, S, qf, kf, a, z);
+            run_head(jb, head, S, qf, kf, a, z, bv);
         }
     }
-    free(S); free(qf); free(kf); free(a); free(z);
+    free(S); free(qf); free(kf); free(a); free(z); free(bv);
     return NULL;
 }
 
 static int forward(const double *q, const double *k, const double *v, const double *g,
-                   int gate_mode, int phi, const double *s0, const double *z0, double *o,
-                   double *s_out, double *z_out, int norm, const double *beta, long B, long H,
-                   long L, long dk, long dv, int nthreads)
+                   const double *gv, int gate_mode, int phi, const double *s0, const double *z0,
+                   double *o, double *s_out, double *z_out, int norm, const double *beta, long B,
+                   long H, long L, long dk, long dv, int nthreads)
 {
     if (!q || !k || !v || !o || B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0) return -1;
     if (gate_mode != ORACLE_GATE_NONE && gate_mode != ORACLE_GATE_KEYDIM &&
-        gate_mode != ORACLE_GATE_SCALAR) return -1;
+        gate_mode != ORACLE_GATE_SCALAR && gate_mode != ORACLE_GATE_OUTER) return -1;
     if (gate_mode != ORACLE_GATE_NONE && !g) return -1;
+    if (gate_mode == ORACLE_GATE_OUTER && (!gv || norm)) return -1;
     if (phi != ORACLE_PHI_IDENTITY && phi != ORACLE_PHI_ELU1) return -1;
 
     job_t jb;
-    jb.q = q; jb.k = k; jb.v = v; jb.g = g; jb.s0 = s0; jb.o = o; jb.s_out = s_out;
+    jb.q = q; jb.k = k; jb.v = v; jb.g = g; jb.gv = gv; jb.s0 = s0; jb.o = o; jb.s_out = s_out;
     jb.z0 = z0; jb.z_out = z_out; jb.norm = norm;
     jb.beta = beta; jb.delta = beta != NULL;
     jb.B = B; jb.H = H; jb.L = L; jb.dk = dk; jb.dv = dv;
@@ -221,7 +235,8 @@ int gla_oracle_forward(const double *q, const double *k, const double *v, const 
                        int gate_mode, int phi, const double *s0, double *o, double *s_out,
                        long B, long H, long L, long dk, long dv, int nthreads)
 {
-    return forward(q, k, v, g, gate_mode, phi, s0, NULL, o, s_out, NULL, 0, NULL, B, H, L, dk, dv,
+    if (gate_mode == ORACLE_GATE_OUTER) return -1;
+    return forward(q, k, v, g, NULL, gate_mode, phi, s0, NULL, o, s_out, NULL, 0, NULL, B, H, L, dk, dv,
                    nthreads);
 }
 
@@ -232,7 +247,7 @@ int gla_oracle_forward_norm(const double *q, const double *k, const double *v, c
                             double *o, double *s_out, double *z_out, long B, long H, long L,
                             long dk, long dv, int nthreads)
 {
-    return forward(q, k, v, g, gate_mode, phi, s0, z0, o, s_out, z_out, 1, NULL, B, H, L, dk, dv,
+    return forward(q, k, v, g, NULL, gate_mode, phi, s0, z0, o, s_out, z_out, 1, NULL, B, H, L, dk, dv,
                    nthreads);
 }
 
@@ -242,6 +257,16 @@ int gla_oracle_delta(const double *q, const double *k, const double *v, const do
                      long dv, int nthreads)
 {
     if (!beta) return -1;
-    return forward(q, k, v, NULL, ORACLE_GATE_NONE, ORACLE_PHI_IDENTITY, s0, NULL, o, s_out, NULL, 0,
+    return forward(q, k, v, NULL, NULL, ORACLE_GATE_NONE, ORACLE_PHI_IDENTITY, s0, NULL, o, s_out, NULL, 0,
                    beta, B, H, L, dk, dv, nthreads);
+}
+
+/* The outer-product gate (see the header): g [B][H][L][d_k] and gv [B][H][L][d_v]
+ * natural-log gates, both required; s0 nullable (zero). */
+int gla_oracle_forward_outer(const double *q, const double *k, const double *v, const double *g,
+                             const double *gv, int phi, const double *s0, double *o, double *s_out,
+                             long B, long H, long L, long dk, long dv, int nthreads)
+{
+    return forward(q, k, v, g, gv, ORACLE_GATE_OUTER, phi, s0, NULL, o, s_out, NULL, 0, NULL, B, H, L,
+                   dk, dv, nthreads);
 }

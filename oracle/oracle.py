@@ -66,6 +66,10 @@ def _load(lib_path=None):
         lib.gla_oracle_delta.argtypes = [dp, dp, dp, dp, dp, dp, dp, ctypes.c_long, ctypes.c_long,
                                          ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_int]
         lib.gla_oracle_delta.restype = ctypes.c_int
+        lib.gla_oracle_forward_outer.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, dp, dp, dp, ctypes.c_long,
+                                                 ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                                 ctypes.c_int]
+        lib.gla_oracle_forward_outer.restype = ctypes.c_int
         _libs[lib_path] = lib
     return _libs[lib_path]
 
@@ -168,4 +172,24 @@ def forward_delta(q, k, v, beta, s0=None, nthreads=None, lib_path=None):
                                           B, H, L, dk, dv, nthreads)
     if rc != 0:
         raise RuntimeError("gla_oracle_delta failed with code %d" % rc)
+    return o, s
+
+
+def forward_outer(q, k, v, g, gv, feature_map=None, s0=None, nthreads=None, lib_path=None):
+    """The outer-product gate ("Gated Linear Attention", Recurrent Form, G_t = alpha_t
+    beta_t^T): S_t = (alpha_t beta_t^T) (.) S_{t-1} + phi(k_t) v_t^T, o_t = S_t^T phi(q_t),
+    with natural-log gates g [B, H, L, d_k] (alpha) and gv [B, H, L, d_v] (beta).
+    Returns (o, s_final) as float64 arrays."""
+    q, k, v, g, s0, _, (B, H, L, dk, dv) = _prepare(q, k, v, g, "keydim", s0)
+    gv = _f64(gv)
+    if gv is None or gv.shape != (B, H, L, dv):
+        raise ValueError("oracle: gv must be [B,H,L,d_v]")
+    o = np.zeros((B, H, L, dv), dtype=np.float64)
+    s = np.zeros((B, H, dk, dv), dtype=np.float64)
+    nthreads = default_threads() if nthreads is None else int(nthreads)
+    rc = _load(lib_path).gla_oracle_forward_outer(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gv),
+                                                  FEATURE_MAPS[feature_map], _ptr(s0), _ptr(o), _ptr(s),
+                                                  B, H, L, dk, dv, nthreads)
+    if rc != 0:
+        raise RuntimeError("gla_oracle_forward_outer failed with code %d" % rc)
     return o, s

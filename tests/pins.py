@@ -556,3 +556,95 @@ GATE_ERROR_PINS = {
     "gate_extremes": (pin_gate_extremes, 1e-14),
     "gate_sigmoid_identity": (pin_gate_sigmoid_identity, 1e-13),
 }
+
+
+# ---- the outer-product gate ("Gated Linear Attention", Recurrent Form: the low-rank
+# parameterisation G_t = alpha_t beta_t^T of the gate G_t (.) S_{t-1}) ----
+
+def _outer_inputs(seed, B, H, L, dk, dv, s0=True, scale=0.3):
+    q, k, v, g, S0 = rng_inputs(seed, B, H, L, dk, dv, gate="keydim", s0=s0, g_scale=scale)
+    gv = -scale * np.random.default_rng(seed + 500).random((B, H, L, dv))
+    return q, k, v, g, gv, S0
+
+
+def pin_outer_unrolled(fwd_outer, seed=50, fm=None, B=2, H=2, L=17, dk=4, dv=3):
+    """Explicit products: a write at token i reaches token n scaled by
+    prod_{m=i+1..n} alpha_m[c] beta_m[j] in entry (c, j); the initial state by the
+    product over all m <= n.  Outputs and the final state are both checked."""
+    q, k, v, g, gv, S0 = _outer_inputs(seed, B, H, L, dk, dv)
+    o, s = fwd_outer(q, k, v, g, gv, feature_map=fm, s0=S0)
+    qf, kf = _phi(q, fm), _phi(k, fm)
+    al, be = np.exp(g), np.exp(gv)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            for n in range(L):
+                Sn = S0[b, h] * np.outer(np.prod(al[b, h, :n + 1], axis=0), np.prod(be[b, h, :n + 1], axis=0))
+                for i in range(n + 1):
+                    w = np.outer(np.prod(al[b, h, i + 1:n + 1], axis=0), np.prod(be[b, h, i + 1:n + 1], axis=0))
+                    Sn = Sn + np.outer(kf[b, h, i], v[b, h, i]) * w
+                worst = max(worst, rel_err(o[b, h, n], qf[b, h, n] @ Sn))
+                if n == L - 1:
+                    worst = max(worst, rel_err(s[b, h], Sn))
+    return worst
+
+
+def pin_outer_uniform_is_scalar_mask(fwd_outer, seed=51, B=2, H=2, L=23, dk=5, dv=4):
+    """alpha_t = a_t 1 and beta_t = b_t 1 make G_t = (a_t b_t) 1 1^T, the Mamba2 scalar
+    gate: O = ((Q K^T) (.) D) V with the decay mask D_ts = prod_{m=s+1..t} a_m b_m for
+    s <= t (0 above the diagonal), evaluated as a matrix."""
+    q, k, v, _, _, _ = _outer_inputs(seed, B, H, L, dk, dv, s0=False)
+    r = np.random.default_rng(seed + 1)
+    la = -0.3 * r.random((B, H, L))
+    lb = -0.2 * r.random((B, H, L))
+    g = np.repeat(la[..., None], dk, axis=3)
+    gv = np.repeat(lb[..., None], dv, axis=3)
+    o, _ = fwd_outer(q, k, v, g, gv)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            c = np.cumsum(la[b, h] + lb[b, h])
+            D = np.tril(np.exp(c[:, None] - c[None, :]))
+            worst = max(worst, rel_err(o[b, h], ((q[b, h] @ k[b, h].T) * D) @ v[b, h]))
+    return worst
+
+
+def pin_outer_value_gate_only(fwd_outer, seed=52, L=9, dv=3):
+    """d_k = 1, q = k = 1, alpha = 1: each value column j is an independent geometric
+    accumulator, s_n[j] = beta_n[j] s_{n-1}[j] + v_n[j], evaluated in closed form as a
+    sum of products."""
+    r = np.random.default_rng(seed)
+    v = r.standard_normal((1, 1, L, dv))
+    gv = -0.5 * r.random((1, 1, L, dv))
+    S0 = r.standard_normal((1, 1, 1, dv))
+    ones = np.ones((1, 1, L, 1))
+    o, s = fwd_outer(ones, ones, v, np.zeros((1, 1, L, 1)), gv, s0=S0)
+    be = np.exp(gv[0, 0])
+    want = np.zeros((L, dv))
+    for n in range(L):
+        acc = S0[0, 0, 0] * np.prod(be[:n + 1], axis=0)
+        for i in range(n + 1):
+            acc = acc + v[0, 0, i] * np.prod(be[i + 1:n + 1], axis=0)
+        want[n] = acc
+    return max(rel_err(o[0, 0], want), rel_err(s[0, 0, 0], want[-1]))
+
+
+def pin_outer_chaining(fwd_outer, seed=53, B=2, H=2, L1=11, L2=8, dk=4, dv=5):
+    """run(L1 + L2) equals run(L1) followed by run(L2) from its final state, bit for bit."""
+    q, k, v, g, gv, S0 = _outer_inputs(seed, B, H, L1 + L2, dk, dv)
+    o, s = fwd_outer(q, k, v, g, gv, feature_map="elu1", s0=S0)
+    a, b_ = slice(0, L1), slice(L1, L1 + L2)
+    o1, s1 = fwd_outer(q[:, :, a], k[:, :, a], v[:, :, a], g[:, :, a], gv[:, :, a], feature_map="elu1", s0=S0)
+    o2, s2 = fwd_outer(q[:, :, b_], k[:, :, b_], v[:, :, b_], g[:, :, b_], gv[:, :, b_], feature_map="elu1", s0=s1)
+    with np.errstate(invalid="ignore"):
+        return float(max(np.abs(o - np.concatenate([o1, o2], axis=2)).max(), np.abs(s - s2).max()))
+
+
+OUTER_ERROR_PINS = {
+    # name: (callable on forward_outer, tolerance)
+    "outer_unrolled": (pin_outer_unrolled, 1e-12),
+    "outer_unrolled_elu1": (lambda f: pin_outer_unrolled(f, seed=54, fm="elu1"), 1e-12),
+    "outer_uniform_is_scalar_mask": (pin_outer_uniform_is_scalar_mask, 1e-12),
+    "outer_value_gate_only": (pin_outer_value_gate_only, 1e-13),
+    "outer_chaining": (pin_outer_chaining, 0.0),
+}

@@ -14,7 +14,7 @@ from tests import pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "gla_oracle.c")
 
-UPDATE = "S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];"
+UPDATE = "S[i * dv + j] = a[i] * bv[j] * S[i * dv + j] + kf[i] * v[t * dv + j];"
 READ = "acc += qf[i] * S[i * dv + j];"
 DELTA_ERR = "z[j] = bt * (v[t * dv + j] - pred);"
 
@@ -22,28 +22,37 @@ MUTANTS = {
     "no_decay": [(UPDATE, "S[i * dv + j] = S[i * dv + j] + kf[i] * v[t * dv + j];")],
     "gate_sign": [("a[i] = exp(jb->g[(head * L + t) * dk + i]);",
                    "a[i] = exp(-jb->g[(head * L + t) * dk + i]);")],
-    "decay_after_write": [(UPDATE, "S[i * dv + j] = a[i] * (S[i * dv + j] + kf[i] * v[t * dv + j]);")],
-    "gate_on_value_axis": [(UPDATE, "S[i * dv + j] = a[j % dk] * S[i * dv + j] + kf[i] * v[t * dv + j];")],
+    # the outer-product gate
+    "outer_value_gate_ignored": [("bv[j] = jb->gate_mode == ORACLE_GATE_OUTER ? exp(jb->gv[(head * L + t) * dv + j]) : 1.0;",
+                                  "bv[j] = 1.0;")],
+    "outer_value_gate_sign": [("exp(jb->gv[(head * L + t) * dv + j])", "exp(-jb->gv[(head * L + t) * dv + j])")],
+    "outer_value_gate_wrong_token": [("exp(jb->gv[(head * L + t) * dv + j])",
+                                      "exp(jb->gv[(head * L + (t > 0 ? t - 1 : 0)) * dv + j])")],
+    "outer_value_gate_key_index": [("exp(jb->gv[(head * L + t) * dv + j])",
+                                    "exp(jb->gv[(head * L + t) * dv + (j % dk)])")],
+    "outer_value_gate_on_write": [(UPDATE, "S[i * dv + j] = a[i] * S[i * dv + j] + bv[j] * kf[i] * v[t * dv + j];")],
+    "decay_after_write": [(UPDATE, "S[i * dv + j] = a[i] * bv[j] * (S[i * dv + j] + kf[i] * v[t * dv + j]);")],
+    "gate_on_value_axis": [(UPDATE, "S[i * dv + j] = a[j % dk] * bv[j] * S[i * dv + j] + kf[i] * v[t * dv + j];")],
     "wrong_readout_column": [(READ, "acc += qf[i] * S[i * dv + (dv - 1 - j)];")],
     "readout_uses_key": [(READ, "acc += kf[i] * S[i * dv + j];")],
-    "phi_on_value": [(UPDATE, "S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * feature(v[t * dv + j], jb->phi);")],
+    "phi_on_value": [(UPDATE, "S[i * dv + j] = a[i] * bv[j] * S[i * dv + j] + kf[i] * feature(v[t * dv + j], jb->phi);")],
     "phi_missing_on_query": [("qf[i] = feature(q[t * dk + i], jb->phi);", "qf[i] = q[t * dk + i];")],
     "elu_without_plus_one": [("return x > 0.0 ? x + 1.0 : exp(x);", "return x > 0.0 ? x : exp(x);")],
     "scalar_gate_head_offset": [("a[i] = exp(jb->g[head * L + t]);", "a[i] = exp(jb->g[t]);")],
     "initial_state_ignored": [("if (jb->s0) memcpy", "if (0) memcpy")],
     "exclusive_readout": [
-        ("""        /* state update: decay the key rows, then add the outer product k~ v^T */
+        ("""        /* state update: decay the key rows (and value columns), then add k~ v^T */
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
-                S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];
+                S[i * dv + j] = a[i] * bv[j] * S[i * dv + j] + kf[i] * v[t * dv + j];
 """, ""),
         ("""            o[t * dv + j] = jb->norm ? acc / den : acc;
         }""", """            o[t * dv + j] = jb->norm ? acc / den : acc;
         }
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
-                S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[t * dv + j];""")],
-    "off_by_one_value_row": [(UPDATE, "S[i * dv + j] = a[i] * S[i * dv + j] + kf[i] * v[(t > 0 ? t - 1 : 0) * dv + j];")],
+                S[i * dv + j] = a[i] * bv[j] * S[i * dv + j] + kf[i] * v[t * dv + j];""")],
+    "off_by_one_value_row": [(UPDATE, "S[i * dv + j] = a[i] * bv[j] * S[i * dv + j] + kf[i] * v[(t > 0 ? t - 1 : 0) * dv + j];")],
     # the normalised form
     "norm_z_no_decay": [("z[i] = a[i] * z[i] + kf[i];", "z[i] = z[i] + kf[i];")],
     "norm_den_uses_key": [("den += qf[i] * z[i];", "den += kf[i] * z[i];")],
@@ -74,8 +83,16 @@ MUTANTS = {
 }
 
 
-def _pin_results(fwd, fwd_norm, fwd_delta):
+def _pin_results(fwd, fwd_norm, fwd_delta, fwd_outer):
     failed = []
+    for name, (fn, tol) in pins.OUTER_ERROR_PINS.items():
+        try:
+            err = fn(fwd_outer)
+        except AssertionError:
+            failed.append(name)
+            continue
+        if not err <= tol:
+            failed.append(name)
     for name, (fn, tol) in pins.DELTA_ERROR_PINS.items():
         try:
             err = fn(fwd_delta)
@@ -120,5 +137,6 @@ def test_pins_reject_planted_mistake(mutant, tmp_path):
     fwd = functools.partial(oracle.forward, lib_path=lib)
     fwd_norm = functools.partial(oracle.forward_norm, lib_path=lib)
     fwd_delta = functools.partial(oracle.forward_delta, lib_path=lib)
-    failed = _pin_results(fwd, fwd_norm, fwd_delta)
+    fwd_outer = functools.partial(oracle.forward_outer, lib_path=lib)
+    failed = _pin_results(fwd, fwd_norm, fwd_delta, fwd_outer)
     assert failed, "planted mistake %r passed every pin" % mutant

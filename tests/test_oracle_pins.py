@@ -52,6 +52,21 @@ def test_oracle_delta_threads_agree_bitwise():
     assert np.array_equal(o1, o8) and np.array_equal(s1, s8)
 
 
+@pytest.mark.parametrize("name", sorted(pins.OUTER_ERROR_PINS))
+def test_oracle_outer_pin(name):
+    fn, tol = pins.OUTER_ERROR_PINS[name]
+    err = fn(oracle.forward_outer)
+    assert err <= tol, "%s: error %.3e above %.1e" % (name, err, tol)
+
+
+def test_oracle_outer_with_unit_value_gate_is_keydim():
+    """beta = 1 (gv = 0) leaves the key-dim gated recurrence, bit for bit."""
+    q, k, v, g, S0 = pins.rng_inputs(28, 2, 2, 15, 4, 5, gate="keydim", s0=True)
+    o1, s1 = oracle.forward(q, k, v, g=g, gate="keydim", s0=S0)
+    o2, s2 = oracle.forward_outer(q, k, v, g, np.zeros((2, 2, 15, 5)), s0=S0)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
 def test_oracle_norm_matches_unnormalised_state():
     """The normalised entry carries S exactly as the plain one does."""
     q, k, v, g, S0 = pins.rng_inputs(27, 2, 3, 21, 5, 4, gate="keydim", s0=True)
