@@ -30,6 +30,8 @@ SIGNATURES = [
     ("gla_prefill_delta", _I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     ("gla_decode_step_delta", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     ("gla_gate_project", _I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P]),
+    ("gla_prefill_outer", _I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    ("gla_decode_step_outer", _I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     ("gla_strerror", ctypes.c_char_p, [_I]),
     ("gla_last_error_detail", ctypes.c_char_p, []),
 ]

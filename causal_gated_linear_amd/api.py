@@ -263,6 +263,45 @@ def gate_project(x, w_down, w_up, H, d_k, tau=1.0, out=None, stream=None):
     return out
 
 
+def prefill_outer(q, k, v, log_gate, log_gate_v, initial_state=None, chunk=64, feature_map=None, out=None,
+                  final_state=None, stream=None):
+    """Prefill with the outer-product gate G_t = alpha_t beta_t^T (gla_prefill_outer).
+
+    q, k: [B, H, L, d_k]; v: [B, H, L, d_v]; log_gate: fp32 [B, H, L, d_k] (alpha);
+    log_gate_v: fp32 [B, H, L, d_v] (beta); initial_state: fp32 [B, H, d_k, d_v] or None.
+    Returns (o, s_final); ``final_state`` may be ``initial_state`` to update it in place.
+    """
+    lib = _lib.load()
+    B, H, L, dk, dv, dev, dt, _ = _check_prefill(q, k, v, log_gate, "keydim", initial_state)
+    _check_tensor(log_gate_v, "log_gate_v", (B, H, L, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor(out, "out", (B, H, L, dv), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
+    st = lib.gla_prefill_outer(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(log_gate_v), _ptr(initial_state),
+                               _ptr(out), _ptr(final_state), B, H, L, dk, dv, int(chunk), _DTYPES[dt],
+                               _lib.FEATURE_MAPS[feature_map], _stream_handle(stream))
+    _lib.check(st, "gla_prefill_outer")
+    return out, final_state
+
+
+def decode_step_outer(q, k, v, log_gate, log_gate_v, state=None, feature_map=None, out=None, stream=None):
+    """One step with the outer-product gate (gla_decode_step_outer); ``state`` is updated
+    in place.  log_gate: fp32 [B, H, d_k]; log_gate_v: fp32 [B, H, d_v].  Returns o."""
+    lib = _lib.load()
+    B, H, dk, dv, dev, dt, _, out = _check_decode(q, k, v, log_gate, "keydim", state, out)
+    _check_tensor(log_gate_v, "log_gate_v", (B, H, dv), torch.float32, dev)
+    st = lib.gla_decode_step_outer(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(log_gate_v), _ptr(state),
+                                   _ptr(out), B, H, dk, dv, _DTYPES[dt], _lib.FEATURE_MAPS[feature_map],
+                                   _stream_handle(stream))
+    _lib.check(st, "gla_decode_step_outer")
+    return out
+
+
 class DeviceState:
     """A zeroed fp32 state [B, H, d_k, d_v] from gla_state_alloc, owned by this object
     (freed with gla_state_free).  ``tensor()`` views it as a torch tensor (no copy)

@@ -36,6 +36,7 @@ def _units():
     units.append(("gla_scan.hip", "scan.o", []))
     units.append(("gla_delta.hip", "delta.o", []))
     units.append(("gla_gate.hip", "gate.o", []))
+    units.append(("gla_outer.hip", "outer.o", []))
     units.append(("gla_api.cpp", "api.o", ["-x", "hip"]))
     return units
 

@@ -553,4 +553,85 @@ int gla_gate_project(const void *x, const void *w_down, const void *w_up, float 
     return ok();
 }
 
+// ---- the outer-product gate --------------------------------------------------------
+
+int gla_prefill_outer(const void *q, const void *k, const void *v, const float *g, const float *gv,
+                      const float *s0, void *o, float *s_final, int B, int H, int L, int d_k, int d_v,
+                      int chunk, gla_dtype dtype, gla_feature_map phi, gla_stream_t stream)
+{
+    if (L < 0) return fail(GLA_ERR_SHAPE, "L=%d must be >= 0", L);
+    int st = check_common(B, H, d_k, d_v, dtype, GLA_GATE_KEYDIM, phi, g, L > 0);
+    if (st != GLA_OK) return st;
+    if (!chunk_supported(chunk))
+        return fail(GLA_ERR_UNSUPPORTED, "chunk=%d: must be 16, 32 or 64", chunk);
+    if ((long long)(L + chunk) * (d_k > d_v ? d_k : d_v) * 4 > 0x7fffffffLL)
+        return fail(GLA_ERR_SHAPE, "L=%d too long for one head (limit (L + chunk) * max(d_k, d_v) * 4 < 2^31)", L);
+    if (L > 0 && (!q || !k || !v || !gv || !o))
+        return fail(GLA_ERR_NULL, "q, k, v, g, gv and o are required when L > 0");
+    const void *ptrs[] = {q, k, v, gv, s0, o, s_final};
+    const char *names[] = {"q", "k", "v", "gv", "s0", "o", "s_final"};
+    for (int i = 0; i < 7; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    const size_t BH = (size_t)B * H, es = elem_size(dtype);
+    const size_t sbytes = BH * d_k * d_v * 4;
+    const Span sq = span(q, BH * L * d_k * es, "q"), sk = span(k, BH * L * d_k * es, "k");
+    const Span sv = span(v, BH * L * d_v * es, "v"), sg = span(g, BH * L * d_k * 4, "g");
+    const Span sgv = span(gv, BH * L * d_v * 4, "gv"), ss0 = span(s0, sbytes, "s0");
+    const Span so = span(o, BH * L * d_v * es, "o"), ssf = span(s_final, sbytes, "s_final");
+    const Span o_forbidden[] = {sq, sk, sv, sg, sgv, ss0, ssf};
+    for (const Span &x : o_forbidden)
+        if (overlap(so, x)) return fail(GLA_ERR_ALIAS, "o overlaps %s", x.name);
+    const Span sf_forbidden[] = {sq, sk, sv, sg, sgv};
+    for (const Span &x : sf_forbidden)
+        if (overlap(ssf, x)) return fail(GLA_ERR_ALIAS, "s_final overlaps %s", x.name);
+    if (overlap(ssf, ss0) && s_final != s0)
+        return fail(GLA_ERR_ALIAS, "s_final partially overlaps s0");
+    if (BH > 0x7fffffffUL) return fail(GLA_ERR_SHAPE, "B*H too large");
+    gla::OuterArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.gv = gv; a.s0 = s0; a.o = o; a.s_final = s_final;
+    a.BH = (int)BH; a.L = L; a.d_k = d_k; a.d_v = d_v; a.elu1 = phi == GLA_PHI_ELU1;
+    a.dvt = d_v < 64 ? d_v : 64;
+    a.n_vt = d_v / a.dvt;
+    const long grid = (long)BH * a.n_vt;
+    if (grid > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H too large");
+    a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
+    if (L == 0 && !s_final) return ok();
+    const hipError_t e = gla::launch_outer_prefill(a, dtype == GLA_BF16 ? 1 : 0, chunk, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "outer-gate prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int gla_decode_step_outer(const void *q, const void *k, const void *v, const float *g, const float *gv,
+                          float *state, void *o, int B, int H, int d_k, int d_v, gla_dtype dtype,
+                          gla_feature_map phi, gla_stream_t stream)
+{
+    int st = check_common(B, H, d_k, d_v, dtype, GLA_GATE_KEYDIM, phi, g, true);
+    if (st != GLA_OK) return st;
+    if (!q || !k || !v || !gv || !state || !o)
+        return fail(GLA_ERR_NULL, "q, k, v, g, gv, state and o are required");
+    const void *ptrs[] = {q, k, v, gv, state, o};
+    const char *names[] = {"q", "k", "v", "gv", "state", "o"};
+    for (int i = 0; i < 6; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    const size_t BH = (size_t)B * H, es = elem_size(dtype);
+    const Span sq = span(q, BH * d_k * es, "q"), sk = span(k, BH * d_k * es, "k");
+    const Span sv = span(v, BH * d_v * es, "v"), sg = span(g, BH * d_k * 4, "g");
+    const Span sgv = span(gv, BH * d_v * 4, "gv");
+    const Span sst = span(state, BH * d_k * d_v * 4, "state"), so = span(o, BH * d_v * es, "o");
+    const Span o_forbidden[] = {sq, sk, sv, sg, sgv, sst};
+    for (const Span &x : o_forbidden)
+        if (overlap(so, x)) return fail(GLA_ERR_ALIAS, "o overlaps %s", x.name);
+    const Span st_forbidden[] = {sq, sk, sv, sg, sgv};
+    for (const Span &x : st_forbidden)
+        if (overlap(sst, x)) return fail(GLA_ERR_ALIAS, "state overlaps %s", x.name);
+    if (BH > 0x7fffffffUL) return fail(GLA_ERR_SHAPE, "B*H too large");
+    gla::OuterArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.gv = gv; a.s_final = state; a.o = o;
+    a.BH = (int)BH; a.d_k = d_k; a.d_v = d_v; a.elu1 = phi == GLA_PHI_ELU1;
+    const hipError_t e = gla::launch_outer_decode(a, dtype == GLA_BF16 ? 1 : 0, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "outer-gate decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -180,4 +180,42 @@ __device__ __forceinline__ float buf_load4(Rsrc r, int off)
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+
+// Accumulator tile -> operand fragment of element type T (bf16 rounds to nearest even).
+template <typename T> __device__ __forceinline__ typename Frag<T>::type cvt4(f32x4 v)
+{
+    typename Frag<T>::type *tag = nullptr;
+    return frag_from_acc(tag, v);
+}
+__device__ __forceinline__ f32x4 widen4(bf16x4 v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
+__device__ __forceinline__ f32x4 widen4(f32x4 v) { return v; }
+
+// acc += A B over one 16-block (mac1) or two 16-blocks (mac2) of the contraction index
+__device__ __forceinline__ f32x4 mac1(bf16x4 a, bf16x4 b, f32x4 acc)
+{
+    const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    return mma2(a, z, b, z, acc);
+}
+__device__ __forceinline__ f32x4 mac1(f32x4 a, f32x4 b, f32x4 acc) { return mma1(a, b, acc); }
+__device__ __forceinline__ f32x4 mac2(bf16x4 a0, bf16x4 a1, bf16x4 b0, bf16x4 b1, f32x4 acc)
+{
+    return mma2(a0, a1, b0, b1, acc);
+}
+__device__ __forceinline__ f32x4 mac2(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 acc)
+{
+    return mma1(a1, b1, mma1(a0, b0, acc));
+}
+
+// Fragment of a column of a row-major LDS array: lane (x, grp) receives
+// base[(s0 + e) * ld + c0 + x], e = 0..3, where s0 already includes 4 * grp.
+__device__ __forceinline__ bf16x4 col_frag(const bf16 *base, int ld, int s0, int c0, int x)
+{
+    return lds_read_tr16(base + (s0 + (x >> 2)) * ld + c0 + 4 * (x & 3));
+}
+__device__ __forceinline__ f32x4 col_frag(const float *base, int ld, int s0, int c0, int x)
+{
+    const float *p = base + s0 * ld + c0 + x;
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+
 }  // namespace gla

@@ -115,6 +115,20 @@ struct GateArgs {
     float inv_tau;
 };
 hipError_t launch_gate_project(const GateArgs &a, int dtype, int rank, hipStream_t stream);
+
+// The outer-product gate (gla_outer.hip): S <- (alpha beta^T) (.) S + phi(k) v^T.
+struct OuterArgs {
+    const void *q, *k, *v;   // [B][H][L][d_k] / [B][H][L][d_v], element type T (decode: L absent)
+    const float *g, *gv;     // natural-log gates [B][H][L][d_k] and [B][H][L][d_v]
+    const float *s0;         // [B][H][d_k][d_v] or null (prefill)
+    void *o;                 // [B][H][L][d_v], T
+    float *s_final;          // [B][H][d_k][d_v] or null (prefill); the state (decode)
+    int BH, L, d_k, d_v, elu1;
+    int dvt, n_vt;           // value columns per workgroup (16, 32 or 64), tiles per head
+    int xcd_remap;
+};
+hipError_t launch_outer_prefill(const OuterArgs &a, int dtype, int chunk, hipStream_t stream);
+hipError_t launch_outer_decode(const OuterArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_delta_prefill(const DeltaArgs &a, int dtype, int chunk, hipStream_t stream);
 hipError_t launch_delta_decode(const DeltaArgs &a, int dtype, hipStream_t stream);
 

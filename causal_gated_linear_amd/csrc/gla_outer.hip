@@ -1,0 +1,383 @@
+// gla_outer.hip -- gated linear attention with the outer-product gate on gfx950.
+//
+// "Gated Linear Attention", section "GLA / Recurrent Form": of the general gate
+// G_t (.) S_{t-1}, the low-rank parameterisation G_t = alpha_t beta_t^T decays the
+// state along both dimensions:
+//
+//     S_t[i][j] = alpha_t[i] beta_t[j] S_{t-1}[i][j] + phi(k_t)[i] v_t[j],
+//     o_t = S_t^T phi(q_t)
+//
+// with natural-log gates g (alpha, [L][d_k]) and gv (beta, [L][d_v]).  Chunkwise, with
+// in-chunk inclusive cumulative log-gates A[t][i], Bv[t][j] and chunk totals
+// GA = A[C-1], GB = Bv[C-1]:
+//
+//     Q~ = phi(Q) e^A,  K^ = phi(K) e^-A,  V^ = V e^-Bv
+//     O  = ((Q~ K^^T masked to s <= t) V^ + Q~ S) (.) e^Bv
+//     S <- Diag(e^GA) (S + K^^T V^) Diag(e^GB)
+//
+// (the product of the gates between s and t factorises per key dimension and per
+// value dimension).  As for the key-dimension gate, e^-A and e^-Bv must stay finite:
+// the log-gates summed over one chunk stay above about -80 in every dimension.
+//
+// One workgroup per (head, value tile of up to 64 columns); wave w owns 16 value
+// columns and their state slice S[d_k][16] in accumulator registers.  Per chunk the
+// workgroup stages the raw rows (q, k, v, both gates) in LDS, then
+//   1. computes the cumulative sums A and Bv on the matrix cores as products with the
+//      lower-triangular ones matrix (fp32 operands: exact in the products), and each
+//      lane scales the q, k, v elements of its accumulator positions in place, writes
+//      e^Bv for the output and the chunk totals;
+//   2. computes the masked scores, O^T = (S^T Q~^T + V^^T P^T) (.) e^Bv^T and the
+//      two-sided state update, as in the other prefill kernels.
+// The next chunk's raw rows are requested before the current chunk is computed.
+#include "gla_device.hpp"
+#include "gla_launch.hpp"
+
+namespace gla {
+
+namespace {
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+template <typename T> constexpr int pad_of() { return sizeof(T) == 2 ? 16 : 4; }
+}  // namespace
+
+template <typename T, int DK, int C>
+struct OuterShape {
+    static constexpr int ES = sizeof(T), CE = 16 / ES, PAD = pad_of<T>();
+    static constexpr int NB = C / 16, NKB = DK / 16, DVT = 64;
+    static constexpr int LDK = DK + PAD, LDV = DVT + PAD;      // T rows
+    static constexpr int LDG = DK + 4, LDGV = DVT + 4;         // fp32 rows
+    // 16-byte pieces per chunk, and per thread (256 threads)
+    static constexpr int PQ = C * DK / CE, PG = C * DK / 4;
+    static constexpr int PVM = C * DVT / CE, PGVM = C * DVT / 4;   // at the widest tile
+    static constexpr int TQ = (PQ + 255) / 256, TG = (PG + 255) / 256;
+    static constexpr int TV = (PVM + 255) / 256, TGV = (PGVM + 255) / 256;
+};
+
+template <typename T, int DK, int C, bool ELU1>
+__global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
+{
+    typedef OuterShape<T, DK, C> SH;
+    constexpr int ES = SH::ES, CE = SH::CE, NB = SH::NB, NKB = SH::NKB;
+    constexpr int LDK = SH::LDK, LDV = SH::LDV, LDG = SH::LDG, LDGV = SH::LDGV;
+    __shared__ __align__(16) T sQ[C * LDK];
+    __shared__ __align__(16) T sK[C * LDK];
+    __shared__ __align__(16) T sV[C * LDV];
+    __shared__ __align__(16) float sG[C * LDG];       // raw key-dimension log-gates
+    __shared__ __align__(16) float sGV[C * LDGV];     // raw value-dimension log-gates
+    __shared__ __align__(16) float sEV[C * LDGV];     // e^Bv[t][j]
+    __shared__ __align__(16) float sEA[DK];           // e^GA
+    __shared__ __align__(16) float sEB[SH::DVT];      // e^GB
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int x = lane & 15, grp = lane >> 4;
+    int wgi = blockIdx.x;
+    if (a.xcd_remap) wgi = (wgi & 7) * (gridDim.x >> 3) + (wgi >> 3);
+    const int bh = wgi / a.n_vt, vt = wgi - bh * a.n_vt;
+    const int L = a.L, DV = a.d_v, DVT = a.dvt;
+    const int nch = (L + C - 1) / C;
+    const size_t hrow = (size_t)bh * L;
+    const int j0 = vt * DVT + 16 * w;                  // this wave's first value column
+    const bool active = 16 * w < DVT;                  // wave-uniform
+    const int PV = C * DVT / CE, PGV = C * DVT / 4;    // pieces of this tile's v and gv rows
+
+    // head views; rows past the end of the sequence read as zeros (zero log-gates)
+    const Rsrc rq = make_rsrc((const T *)a.q + hrow * DK, (unsigned)(L * DK * ES));
+    const Rsrc rk = make_rsrc((const T *)a.k + hrow * DK, (unsigned)(L * DK * ES));
+    const Rsrc rv = make_rsrc((const T *)a.v + hrow * DV, (unsigned)(L * DV * ES));
+    const Rsrc rg = make_rsrc(a.g + hrow * DK, (unsigned)(L * DK * 4));
+    const Rsrc rgv = make_rsrc(a.gv + hrow * DV, (unsigned)(L * DV * 4));
+
+    i32x4 gq[SH::TQ], gk[SH::TQ], gg[SH::TG], gvv[SH::TV], ggv[SH::TGV];
+    auto fetch = [&](int n) {
+        const int r0 = n * C;
+#pragma unroll
+        for (int i = 0; i < SH::TQ; ++i) {
+            const int p = tid + 256 * i;
+            if (SH::PQ % 256 == 0 || p < SH::PQ) {
+                gq[i] = buf_load16<i32x4>(rq, (r0 * DK + p * CE) * ES);
+                gk[i] = buf_load16<i32x4>(rk, (r0 * DK + p * CE) * ES);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SH::TG; ++i) {
+            const int p = tid + 256 * i;
+            if (SH::PG % 256 == 0 || p < SH::PG) gg[i] = buf_load16<i32x4>(rg, (r0 * DK + p * 4) * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < SH::TV; ++i) {
+            const int p = tid + 256 * i;
+            if (p < PV) {
+                const int r = p / (DVT / CE), c = (p - r * (DVT / CE)) * CE;
+                gvv[i] = buf_load16<i32x4>(rv, ((r0 + r) * DV + vt * DVT + c) * ES);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SH::TGV; ++i) {
+            const int p = tid + 256 * i;
+            if (p < PGV) {
+                const int r = p / (DVT / 4), c = (p - r * (DVT / 4)) * 4;
+                ggv[i] = buf_load16<i32x4>(rgv, ((r0 + r) * DV + vt * DVT + c) * 4);
+            }
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < SH::TQ; ++i) {
+            const int p = tid + 256 * i;
+            if (SH::PQ % 256 == 0 || p < SH::PQ) {
+                const int r = p / (DK / CE), c = (p - r * (DK / CE)) * CE;
+                *(i32x4 *)(sQ + r * LDK + c) = gq[i];
+                *(i32x4 *)(sK + r * LDK + c) = gk[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SH::TG; ++i) {
+            const int p = tid + 256 * i;
+            if (SH::PG % 256 == 0 || p < SH::PG) {
+                const int r = p / (DK / 4), c = (p - r * (DK / 4)) * 4;
+                *(i32x4 *)(sG + r * LDG + c) = gg[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SH::TV; ++i) {
+            const int p = tid + 256 * i;
+            if (p < PV) {
+                const int r = p / (DVT / CE), c = (p - r * (DVT / CE)) * CE;
+                *(i32x4 *)(sV + r * LDV + c) = gvv[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SH::TGV; ++i) {
+            const int p = tid + 256 * i;
+            if (p < PGV) {
+                const int r = p / (DVT / 4), c = (p - r * (DVT / 4)) * 4;
+                *(i32x4 *)(sGV + r * LDGV + c) = ggv[i];
+            }
+        }
+    };
+
+    // inclusive cumulative sum over the chunk's rows of column c0 + x of a fp32 gate
+    // array, for rows 16 tb + 4 grp + e (lane (x, grp), element e), in log2 units:
+    // the product of the lower-triangular ones matrix with the gate columns
+    auto cumsum = [&](const float *G, int ld, int tb, int c0) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int sb = 0; sb <= tb; ++sb) {
+            f32x4 m;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m[e] = (sb < tb || 4 * grp + e <= x) ? kLog2e : 0.f;
+            acc = mma1(m, col_frag(G, ld, 16 * sb + 4 * grp, c0, x), acc);
+        }
+        return acc;   // lane (x, grp) element e: row 16 tb + 4 grp + e, column c0 + x
+    };
+
+    // state slice: tile ib, lane (x, grp) element e holds S[16 ib + 4 grp + e][j0 + x]
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s[NKB];
+#pragma unroll
+    for (int ib = 0; ib < NKB; ++ib) {
+        s[ib] = zero;
+        if (active && a.s0) {
+            const float *p = a.s0 + ((size_t)bh * DK + 16 * ib + 4 * grp) * DV + j0 + x;
+            s[ib] = f32x4{p[0], p[DV], p[2 * DV], p[3 * DV]};
+        }
+    }
+
+    if (nch > 0) fetch(0);
+    for (int n = 0; n < nch; ++n) {
+        if (n > 0) lds_barrier();                      // the previous chunk's readers are done
+        stash();
+        lds_barrier();
+        if (n + 1 < nch) fetch(n + 1);
+        const int nvalid = min(C, L - n * C);
+
+        // 1. cumulative gates; scale q, k (key side) and v (value side) in place
+        const int nkt = NB * NKB, nvt = NB * (DVT / 16);
+        for (int id = w; id < nkt + nvt; id += 4) {
+            if (id < nkt) {
+                const int tb = id % NB, ib = id / NB;
+                const f32x4 A = cumsum(sG, LDG, tb, 16 * ib);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tb + 4 * grp + e, i = 16 * ib + x;
+                    const float up = exp2_fast(A[e]), down = exp2_fast(-A[e]);
+                    sQ[t * LDK + i] = from_f32<T>(feature(to_f32(sQ[t * LDK + i]), ELU1) * up);
+                    sK[t * LDK + i] = from_f32<T>(feature(to_f32(sK[t * LDK + i]), ELU1) * down);
+                    if (t == C - 1) sEA[i] = up;
+                }
+            } else {
+                const int tb = (id - nkt) % NB, jb = (id - nkt) / NB;
+                const f32x4 Bv = cumsum(sGV, LDGV, tb, 16 * jb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tb + 4 * grp + e, j = 16 * jb + x;
+                    const float up = exp2_fast(Bv[e]);
+                    sV[t * LDV + j] = from_f32<T>(to_f32(sV[t * LDV + j]) * exp2_fast(-Bv[e]));
+                    sEV[t * LDGV + j] = up;
+                    if (t == C - 1) sEB[j] = up;
+                }
+            }
+        }
+        lds_barrier();
+        if (!active) continue;
+
+        // 2. O^T = (S^T Q~^T + V^^T P^T) (.) e^Bv^T; lane (x, grp) element e:
+        //    O[16 tb + x][j0 + 4 grp + e]
+        T *og = (T *)a.o + (hrow + (size_t)n * C) * DV + j0 + 4 * grp;
+        const int jl = 16 * w;                         // this wave's columns within the tile
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            const T *qrow = sQ + (16 * tb + x) * LDK;
+            f32x4 o = contract_regs_rows<T, NKB>(s, qrow, grp, zero);
+            auto score = [&](int sb) {                 // P^T[s][t], s = 16 sb + 4 grp + e
+                f32x4 p = contract_rows(sK + (16 * sb + x) * LDK, qrow, NKB, grp, zero);
+                if (sb == tb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * grp + e > x) p[e] = 0.f;
+                }
+                return p;
+            };
+#pragma unroll
+            for (int sb = 0; sb <= tb; sb += 2) {
+                if (sb + 1 <= tb)
+                    o = mac2(col_frag(sV, LDV, 16 * sb + 4 * grp, jl, x),
+                             col_frag(sV, LDV, 16 * (sb + 1) + 4 * grp, jl, x), cvt4<T>(score(sb)),
+                             cvt4<T>(score(sb + 1)), o);
+                else
+                    o = mac1(col_frag(sV, LDV, 16 * sb + 4 * grp, jl, x), cvt4<T>(score(sb)), o);
+            }
+            o *= *(const f32x4 *)(sEV + (16 * tb + x) * LDGV + jl + 4 * grp);
+            if (16 * tb + x < nvalid) store4(og + (size_t)(16 * tb + x) * DV, o);
+        }
+
+        // 3. S <- Diag(e^GA) (S + K^^T V^) Diag(e^GB)
+        const float eb = sEB[jl + x];
+#pragma unroll
+        for (int ib = 0; ib < NKB; ++ib) {
+#pragma unroll
+            for (int sb = 0; sb + 1 < NB; sb += 2)
+                s[ib] = mac2(col_frag(sK, LDK, 16 * sb + 4 * grp, 16 * ib, x),
+                             col_frag(sK, LDK, 16 * (sb + 1) + 4 * grp, 16 * ib, x),
+                             col_frag(sV, LDV, 16 * sb + 4 * grp, jl, x),
+                             col_frag(sV, LDV, 16 * (sb + 1) + 4 * grp, jl, x), s[ib]);
+            if (NB % 2)
+                s[ib] = mac1(col_frag(sK, LDK, 16 * (NB - 1) + 4 * grp, 16 * ib, x),
+                             col_frag(sV, LDV, 16 * (NB - 1) + 4 * grp, jl, x), s[ib]);
+            s[ib] *= *(const f32x4 *)(sEA + 16 * ib + 4 * grp) * eb;
+        }
+    }
+
+    if (active && a.s_final) {
+#pragma unroll
+        for (int ib = 0; ib < NKB; ++ib) {
+            float *p = a.s_final + ((size_t)bh * DK + 16 * ib + 4 * grp) * DV + j0 + x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[(size_t)e * DV] = s[ib][e];
+        }
+    }
+}
+
+// One token on a resident fp32 state, in place: S <- (alpha beta^T) (.) S + phi(k) v^T,
+// o = S^T phi(q).  One workgroup per head; a thread owns a float4 column group (with its
+// four value gates) and every RS-th row; o is reduced across rows through LDS.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void outer_decode_kernel(const OuterArgs a)
+{
+    constexpr int CQ = DV / 4;
+    constexpr int NT = (DK * CQ) < 256 ? (DK * CQ) : 256;
+    constexpr int RS = NT / CQ;
+    constexpr int NPASS = DK / RS;
+    static_assert(NT >= DK && NT >= CQ && DK % RS == 0, "decode mapping");
+    __shared__ float sq[DK], sk[DK], sa[DK];
+    __shared__ f32x4 sred[RS][CQ];
+
+    const int tid = threadIdx.x;
+    const size_t bh = blockIdx.x;
+    const bool elu1 = a.elu1 != 0;
+    if (tid < DK) {
+        sq[tid] = feature(to_f32(((const T *)a.q)[bh * DK + tid]), elu1);
+        sk[tid] = feature(to_f32(((const T *)a.k)[bh * DK + tid]), elu1);
+        sa[tid] = exp2_fast(a.g[bh * DK + tid] * kLog2e);
+    }
+    const int c = tid % CQ, r0 = tid / CQ;
+    const T *vp = (const T *)a.v + bh * DV + 4 * c;
+    const f32x4 v = {to_f32(vp[0]), to_f32(vp[1]), to_f32(vp[2]), to_f32(vp[3])};
+    const f32x4 gb = *(const f32x4 *)(a.gv + bh * DV + 4 * c);
+    const f32x4 bv = {exp2_fast(gb[0] * kLog2e), exp2_fast(gb[1] * kLog2e), exp2_fast(gb[2] * kLog2e),
+                      exp2_fast(gb[3] * kLog2e)};
+    f32x4 *st = (f32x4 *)(a.s_final + bh * DK * DV) + c;
+    f32x4 s[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) s[p] = st[(size_t)(r0 + p * RS) * CQ];
+    __syncthreads();
+
+    f32x4 op = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        const int i = r0 + p * RS;
+        s[p] = sa[i] * (bv * s[p]) + sk[i] * v;
+        st[(size_t)i * CQ] = s[p];
+        op += sq[i] * s[p];
+    }
+    sred[r0][c] = op;
+    __syncthreads();
+    if (tid < CQ) {
+        f32x4 acc = sred[0][tid];
+#pragma unroll
+        for (int r = 1; r < RS; ++r) acc += sred[r][tid];
+        store4((T *)a.o + bh * DV + 4 * tid, acc);
+    }
+}
+
+template <typename T, int C, bool ELU1>
+static hipError_t launch_outer_c(const OuterArgs &a, hipStream_t stream)
+{
+    const int grid = a.BH * a.n_vt;
+    switch (a.d_k) {
+    case 16: hipLaunchKernelGGL((outer_prefill_kernel<T, 16, C, ELU1>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((outer_prefill_kernel<T, 32, C, ELU1>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((outer_prefill_kernel<T, 64, C, ELU1>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((outer_prefill_kernel<T, 128, C, ELU1>), dim3(grid), dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, bool ELU1>
+static hipError_t launch_outer_t(const OuterArgs &a, int chunk, hipStream_t stream)
+{
+    if (chunk == 16) return launch_outer_c<T, 16, ELU1>(a, stream);
+    if (chunk == 32) return launch_outer_c<T, 32, ELU1>(a, stream);
+    if (chunk == 64) return launch_outer_c<T, 64, ELU1>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_outer_prefill(const OuterArgs &a, int dtype, int chunk, hipStream_t stream)
+{
+    if (dtype == 1) return a.elu1 ? launch_outer_t<bf16, true>(a, chunk, stream) : launch_outer_t<bf16, false>(a, chunk, stream);
+    return a.elu1 ? launch_outer_t<float, true>(a, chunk, stream) : launch_outer_t<float, false>(a, chunk, stream);
+}
+
+template <typename T>
+static hipError_t launch_outer_decode_t(const OuterArgs &a, hipStream_t stream)
+{
+#define GLA_OUTER_DECODE(DK, DV)                                                                   \
+    if (a.d_k == DK && a.d_v == DV) {                                                              \
+        constexpr int NT = (DK * (DV / 4)) < 256 ? (DK * (DV / 4)) : 256;                          \
+        hipLaunchKernelGGL((outer_decode_kernel<T, DK, DV>), dim3(a.BH), dim3(NT), 0, stream, a);  \
+        return hipGetLastError();                                                                  \
+    }
+#define GLA_OUTER_DECODE_DV(DK) \
+    GLA_OUTER_DECODE(DK, 16) GLA_OUTER_DECODE(DK, 32) GLA_OUTER_DECODE(DK, 64) GLA_OUTER_DECODE(DK, 128)
+    GLA_OUTER_DECODE_DV(16) GLA_OUTER_DECODE_DV(32) GLA_OUTER_DECODE_DV(64) GLA_OUTER_DECODE_DV(128)
+#undef GLA_OUTER_DECODE_DV
+#undef GLA_OUTER_DECODE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_outer_decode(const OuterArgs &a, int dtype, hipStream_t stream)
+{
+    if (dtype == 1) return launch_outer_decode_t<bf16>(a, stream);
+    return launch_outer_decode_t<float>(a, stream);
+}
+
+}  // namespace gla

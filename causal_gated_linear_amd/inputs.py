@@ -33,6 +33,10 @@ drawn by ``draw_delta`` / ``draw_delta_decode`` in the same order (q, k, v, z):
                      cast), v ~ N(0,1), write strength beta = sigmoid(z) in fp32 per
                      head and token, chunk 64
 
+The outer-product gate (G_t = alpha_t beta_t^T, same section) reuses a workload's
+q, k, v and key-dim gates and adds value-dim log-gates from ``draw_value_gate``: the
+same recipe logsigmoid(z)/16, z ~ N(0,1), drawn with seed + 3571.
+
 The gate producer ("Gated Linear Attention", Recurrent Form: alpha_t =
 sigmoid(W_up W_down x_t)) has synthetic weights, drawn by ``draw_gate`` in the
 order x, W_down, W_up:
@@ -205,3 +209,15 @@ def draw_gate(*, B=None, L=None, d_model=None, rank=None, H=None, d_k=None, dtyp
     wu = torch.randn(w["H"] * w["d_k"], w["rank"], **f32) / math.sqrt(w["rank"])
     dt = w["dtype"]
     return dict(x=x.to(dt), w_down=wd.to(dt), w_up=wu.to(dt))
+
+
+def draw_value_gate(w: Workload, *, B=None, H=None, L=None, seed=None, device="cpu"):
+    """Value-dimension log-gates [B, H, L, d_v] for the outer-product gate, drawn like
+    the key-dimension gates (logsigmoid(z)/16) from their own seed."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    L = w.L if L is None else L
+    seed = (w.seed if seed is None else seed) + 3571
+    gen = _gen(device, seed)
+    z = torch.randn(B, H, L, w.d_v, dtype=torch.float32, device=device, generator=gen)
+    return _log_gate(z, "keydim").contiguous()

@@ -289,6 +289,37 @@ int gla_gate_project(const void *x, const void *w_down, const void *w_up, float 
                      int d_model, int rank, int H, int d_k, float tau, gla_dtype dtype,
                      gla_stream_t stream);
 
+/*
+ * gla_prefill_outer -- the outer-product gate ("Gated Linear Attention", section
+ * "GLA / Recurrent Form": the low-rank parameterisation G_t = alpha_t beta_t^T of the
+ * general gate G_t (.) S_{t-1}), which decays the state along both dimensions:
+ *
+ *     S_t[i][j] = alpha_t[i] beta_t[j] S_{t-1}[i][j] + phi(k_t)[i] v_t[j]
+ *     o_t = S_t^T phi(q_t)
+ *
+ * with alpha_t = exp(g_t) and beta_t = exp(gv_t).  Arguments as gla_prefill_chunked
+ * with a key-dimension gate, plus
+ *   gv        in   fp32 [B][H][L][d_v] value-dimension log-gates (finite, <= 0)
+ * No workspace.  As for the key-dimension gate, results are exact up to rounding
+ * while, in every key and every value dimension, the log-gates summed over one chunk
+ * stay above about -80.  o must not overlap any other argument; s_final must not
+ * overlap any input (it may equal s0).  Errors as gla_prefill_chunked (no
+ * GLA_ERR_WORKSPACE).
+ */
+int gla_prefill_outer(const void *q, const void *k, const void *v, const float *g, const float *gv,
+                      const float *s0, void *o, float *s_final, int B, int H, int L, int d_k, int d_v,
+                      int chunk, gla_dtype dtype, gla_feature_map phi, gla_stream_t stream);
+
+/*
+ * gla_decode_step_outer -- one token of the outer-product-gated recurrence on a
+ * resident state, in place: state[i][j] <- alpha_i beta_j state[i][j] + phi(k)_i v_j,
+ * then o = state^T phi(q).  Arguments as gla_decode_step with a key-dimension gate,
+ * plus gv fp32 [B][H][d_v].  Errors as gla_decode_step.
+ */
+int gla_decode_step_outer(const void *q, const void *k, const void *v, const float *g, const float *gv,
+                          float *state, void *o, int B, int H, int d_k, int d_v, gla_dtype dtype,
+                          gla_feature_map phi, gla_stream_t stream);
+
 /* gla_strerror -- static text for a gla_status value (never NULL). */
 const char *gla_strerror(int status);
 

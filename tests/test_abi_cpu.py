@@ -33,7 +33,8 @@ def test_header_declares_expected_entry_points():
                                   "gla_prefill_chunked", "gla_decode_step", "gla_strerror",
                                   "gla_last_error_detail", "gla_prefill_chunked_norm",
                                   "gla_decode_step_norm", "gla_delta_workspace_bytes",
-                                  "gla_prefill_delta", "gla_decode_step_delta", "gla_gate_project"])
+                                  "gla_prefill_delta", "gla_decode_step_delta", "gla_gate_project",
+                                  "gla_prefill_outer", "gla_decode_step_outer"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -342,3 +343,43 @@ def test_gate_project_rejects(lib, case):
     kw, want = GATE_BAD[case]
     assert _gate(lib, **kw) == want
     assert lib.gla_last_error_detail().decode() != ""
+
+
+def _prefill_outer(lib, **kw):
+    args = dict(q=A, k=A + 16 * MB, v=A + 32 * MB, g=A + 48 * MB, gv=A + 64 * MB, s0=None, o=A + 96 * MB,
+                s_final=A + 128 * MB, B=1, H=2, L=64, d_k=64, d_v=64, chunk=64, dtype=1, phi=0)
+    args.update(kw)
+    P = ctypes.c_void_p
+    return lib.gla_prefill_outer(P(args["q"]), P(args["k"]), P(args["v"]), P(args["g"]), P(args["gv"]),
+                                 P(args["s0"]), P(args["o"]), P(args["s_final"]), args["B"], args["H"], args["L"],
+                                 args["d_k"], args["d_v"], args["chunk"], args["dtype"], args["phi"], None)
+
+
+PREFILL_OUTER_BAD = {
+    "g_null": (dict(g=None), _lib.GLA_ERR_NULL),
+    "gv_null": (dict(gv=None), _lib.GLA_ERR_NULL),
+    "gv_misaligned": (dict(gv=A + 64 * MB + 4), _lib.GLA_ERR_ALIGN),
+    "d_v_8": (dict(d_v=8), _lib.GLA_ERR_UNSUPPORTED),
+    "chunk_48": (dict(chunk=48), _lib.GLA_ERR_UNSUPPORTED),
+    "phi_7": (dict(phi=7), _lib.GLA_ERR_UNSUPPORTED),
+    "o_overlaps_gv": (dict(o=A + 64 * MB + 512), _lib.GLA_ERR_ALIAS),
+    "s_final_overlaps_gv": (dict(s_final=A + 64 * MB + 1024), _lib.GLA_ERR_ALIAS),
+    "s_final_partially_overlaps_s0": (dict(s0=A + 200 * MB, s_final=A + 200 * MB + 256), _lib.GLA_ERR_ALIAS),
+    "L_past_32bit_head_offsets": (dict(L=4194304, d_k=128, d_v=128), _lib.GLA_ERR_SHAPE),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PREFILL_OUTER_BAD))
+def test_prefill_outer_rejects(lib, case):
+    kw, want = PREFILL_OUTER_BAD[case]
+    assert _prefill_outer(lib, **kw) == want
+    assert lib.gla_last_error_detail().decode() != ""
+
+
+def test_decode_outer_rejects(lib):
+    P = ctypes.c_void_p
+    call = lambda gv, state: lib.gla_decode_step_outer(P(A), P(A + MB), P(A + 2 * MB), P(A + 3 * MB), P(gv),
+                                                       P(state), P(A + 64 * MB), 2, 4, 128, 128, 1, 0, None)
+    assert call(None, A + 16 * MB) == _lib.GLA_ERR_NULL
+    assert call(A + 4 * MB + 8, A + 16 * MB) == _lib.GLA_ERR_ALIGN
+    assert call(A + 4 * MB, A + 4 * MB + 256) == _lib.GLA_ERR_ALIAS      # state overlaps gv

@@ -1,0 +1,140 @@
+"""GPU parity of the outer-product gate (gla_prefill_outer, gla_decode_step_outer)
+against the fp64 oracle ("Gated Linear Attention", Recurrent Form: G_t = alpha_t
+beta_t^T, S_t = G_t (.) S_{t-1} + phi(k_t) v_t^T, o_t = S_t^T phi(q_t)).
+
+Inputs: a workload's q, k, v and key-dim gates plus value-dim gates drawn with the
+same recipe.  Metric and bounds as the other parity tests (per-head normwise relative
+error, 2e-2 bf16 / 1e-4 fp32) on o and the final state.
+"""
+import dataclasses
+
+import pytest
+import torch
+
+from causal_gated_linear_amd import api, inputs
+from oracle import oracle
+from tests import util
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+W = inputs.WORKLOADS
+
+
+def _keydim(w, **kw):
+    return dataclasses.replace(w, gate="keydim", **kw)
+
+
+def _check(w, B, H, L, seed, chunk=None, with_init=False, in_place=False):
+    inp = inputs.draw(w, B=B, H=H, L=L, seed=seed)
+    gv = inputs.draw_value_gate(w, B=B, H=H, L=L, seed=seed)
+    s0 = inputs.draw_state(B, H, w.d_k, w.d_v, seed=seed + 1, scale=0.5) if with_init else None
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    s0d = None if s0 is None else s0.to(DEV)
+    o, s = api.prefill_outer(dev["q"], dev["k"], dev["v"], dev["g"], gv.to(DEV), initial_state=s0d,
+                             chunk=chunk or w.chunk, feature_map=w.feature_map,
+                             final_state=s0d if in_place else None)
+    torch.cuda.synchronize()
+    if in_place:
+        assert s.data_ptr() == s0d.data_ptr()
+    ro, rs = oracle.forward_outer(inp["q"], inp["k"], inp["v"], inp["g"], gv, feature_map=w.feature_map, s0=s0)
+    tol = util.TOL[w.dtype]
+    eo = util.assert_close(o, ro, tol, "outer o")
+    es = util.assert_close(s, rs, tol, "outer s_final")
+    print("outer %s B=%d H=%d L=%d chunk=%s: err o %.2e s %.2e" % (w.name, B, H, L, chunk or w.chunk, eo, es))
+
+
+SMALL = {
+    "fp32_single_head": ("fp32_single_head", 2, 3, 250),
+    "linear_elu1": ("linear_elu1", 2, 3, 209),
+    "gla_prefill": ("gla_prefill", 2, 2, 300),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+@pytest.mark.parametrize("with_init", [False, True])
+def test_prefill_outer_small(case, with_init):
+    name, B, H, L = SMALL[case]
+    _check(_keydim(W[name]), B, H, L, seed=1600 + len(case), with_init=with_init)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("name", ["fp32_single_head", "gla_prefill", "linear_elu1"])
+def test_prefill_outer_chunk_sizes(name, chunk):
+    _check(_keydim(W[name]), 1, 2, 3 * chunk + 7, seed=1650 + chunk, chunk=chunk, with_init=True)
+
+
+@pytest.mark.parametrize("L", [1, 15, 17, 64, 65, 129])
+def test_prefill_outer_lengths(L):
+    _check(_keydim(W["gla_prefill"]), 1, 2, L, seed=1670 + L, with_init=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 32), (16, 128), (64, 128)])
+@pytest.mark.parametrize("fm", [None, "elu1"])
+def test_prefill_outer_dims(dtype, dk, dv, fm):
+    w = inputs.Workload("outer_dims", dtype, 1, 2, 0, dk, dv, 64, "keydim", fm, True, seed=0)
+    _check(w, 1, 2, 150, seed=dk * 5 + dv, with_init=True)
+
+
+def test_prefill_outer_in_place_state():
+    _check(_keydim(W["gla_prefill"]), 1, 2, 200, seed=1690, with_init=True, in_place=True)
+
+
+def test_prefill_outer_full_size_sampled_heads():
+    """The gla_prefill shape (8x16x4096, d=128, chunk 64) with value-dim gates, checked
+    on sampled heads."""
+    w = W["gla_prefill"]
+    inp = inputs.draw(w, device=DEV)
+    gv = inputs.draw_value_gate(w, device=DEV)
+    o, s = api.prefill_outer(inp["q"], inp["k"], inp["v"], inp["g"], gv, chunk=w.chunk)
+    torch.cuda.synchronize()
+    heads = util.sample_heads(w.B, w.H, 4, seed=13)
+    pick = lambda t: torch.stack([t[b, h] for b, h in heads]).unsqueeze(1).cpu()
+    ro, rs = oracle.forward_outer(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(inp["g"]), pick(gv))
+    tol = util.TOL[w.dtype]
+    util.assert_close(util.pick_heads(o, heads), ro, tol, "full-size outer o")
+    util.assert_close(util.pick_heads(s, heads), rs, tol, "full-size outer s_final")
+
+
+def _decode_vs_oracle(w, B, H, T, seed):
+    d = inputs.draw_decode(w, steps=T, B=B, H=H, seed=seed)
+    gv = inputs.draw_value_gate(w, B=T, H=B * H, L=1, seed=seed).reshape(T, B, H, w.d_v)
+    s0 = inputs.draw_state(B, H, w.d_k, w.d_v, seed=seed + 1, scale=0.5)
+    state = s0.to(DEV)
+    dd = {k: v.to(DEV) for k, v in d.items()}
+    gvd = gv.to(DEV)
+    outs = [api.decode_step_outer(dd["q"][t], dd["k"][t], dd["v"][t], dd["g"][t], gvd[t].contiguous(), state=state,
+                                  feature_map=w.feature_map) for t in range(T)]
+    torch.cuda.synchronize()
+    seq = lambda x: x.movedim(0, 2).contiguous()
+    ro, rs = oracle.forward_outer(seq(d["q"]), seq(d["k"]), seq(d["v"]), seq(d["g"]), seq(gv),
+                                  feature_map=w.feature_map, s0=s0)
+    tol = util.TOL[w.dtype]
+    util.assert_close(torch.stack(outs, dim=2), ro, tol, "outer decode o")
+    util.assert_close(state, rs, tol, "outer decode state")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (128, 16), (16, 128), (64, 32), (128, 128)])
+def test_decode_outer_steps(dtype, dk, dv):
+    w = inputs.Workload("outer_dec", dtype, 2, 3, 0, dk, dv, 64, "keydim", "elu1", True, seed=0)
+    _decode_vs_oracle(w, 2, 3, 6, seed=1700 + dk + dv)
+
+
+def test_prefill_outer_then_decode():
+    w = W["gla_prefill"]
+    B, H, L, T = 1, 2, 130, 5
+    inp = inputs.draw(w, B=B, H=H, L=L + T, seed=1750)
+    gv = inputs.draw_value_gate(w, B=B, H=H, L=L + T, seed=1750)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    gvd = gv.to(DEV)
+    head = lambda x: x[:, :, :L].contiguous()
+    _, s = api.prefill_outer(head(dev["q"]), head(dev["k"]), head(dev["v"]), head(dev["g"]), head(gvd))
+    col = lambda x, t: x[:, :, t].contiguous()
+    outs = [api.decode_step_outer(col(dev["q"], t), col(dev["k"], t), col(dev["v"], t), col(dev["g"], t),
+                                  col(gvd, t), state=s) for t in range(L, L + T)]
+    torch.cuda.synchronize()
+    ro, rs = oracle.forward_outer(inp["q"], inp["k"], inp["v"], inp["g"], gv)
+    tol = util.TOL[w.dtype]
+    util.assert_close(torch.stack(outs, dim=2), ro[:, :, L:], tol, "decode after outer prefill o")
+    util.assert_close(s, rs, tol, "decode after outer prefill state")
