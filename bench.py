@@ -43,7 +43,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_KERNEL = "prefill_kernel"
 PREFILL_SOURCES = ("gla_prefill.hpp", "gla_prefill_inst.hip", "gla_device.hpp", "gla_launch.hpp")
 TRAFFIC_FILE = os.path.join(PROFILES, "prefill_kernel_bf16_dk128_L4096_traffic.txt")
-STATS_FILE = os.path.join(PROFILES, "prefill_decode_kernels_L4096_kernel_stats.txt")
+STATS_FILE = os.path.join(PROFILES, "gla_kernels_bench_workloads_kernel_stats.txt")
 COPY_MIB = 512                        # calibration copy: reads and writes this many MiB
 
 
@@ -304,6 +304,58 @@ def run_gate(args, torch, api, inputs):
             "tflops": flops / (per / 1e3) / 1e12}
 
 
+def run_outer(args, torch, api, inputs):
+    """The outer-product gate ("Gated Linear Attention", Recurrent Form, G_t = alpha_t
+    beta_t^T) at the gla_prefill shape with value-dim gates, and its decode step at
+    the decode shape."""
+    w = inputs.WORKLOADS["gla_prefill"]
+    inp = inputs.draw(w, device="cuda")
+    gv = inputs.draw_value_gate(w, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, w.d_v, dtype=w.dtype, device="cuda")
+    s = torch.empty(w.B, w.H, w.d_k, w.d_v, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for chunk in (32, 64):
+        def step():
+            api.prefill_outer(inp["q"], inp["k"], inp["v"], inp["g"], gv, chunk=chunk, out=o, final_state=s,
+                              stream=stream)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        n = max(5, args.steps // 4)
+        per = _events_ms(step, n, stream) / n
+        nbytes = prefill_bytes(w.B, w.H, w.L, w.d_k, w.d_v) + w.B * w.H * w.L * w.d_v * 4
+        gbs = nbytes / (per / 1e3) / 1e9
+        out["prefill_chunk%d" % chunk] = {
+            "workload": "outer-gate prefill: B=8 H=16 L=4096 d_k=d_v=128 chunk=%d, bf16 q/k/v, fp32 key- and "
+                        "value-dim log-gates" % chunk,
+            "ms_per_step": per, "tokens_per_s": w.B * w.L / (per / 1e3), "GB_per_s": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes}
+    del inp, gv, o, s
+    wd = inputs.WORKLOADS["decode"]
+    T = min(256, args.decode_steps)
+    d = inputs.draw_decode(wd, steps=T, device="cuda")
+    gvd = inputs.draw_value_gate(wd, B=T, H=wd.B * wd.H, L=1, device="cuda").reshape(T, wd.B, wd.H, wd.d_v)
+    state = inputs.draw_state(wd.B, wd.H, wd.d_k, wd.d_v, seed=19, scale=0.1, device="cuda")
+    od = torch.empty(wd.B, wd.H, wd.d_v, dtype=torch.bfloat16, device="cuda")
+    it = iter(range(T))
+
+    def dstep():
+        t = next(it)
+        api.decode_step_outer(d["q"][t], d["k"][t], d["v"][t], d["g"][t], gvd[t], state=state, out=od,
+                              stream=stream)
+
+    torch.cuda.synchronize()
+    dper = _events_ms(dstep, T, stream) / T
+    dbytes = decode_step_bytes(wd.B, wd.H, wd.d_k, wd.d_v) + wd.B * wd.H * wd.d_v * 4
+    out["decode"] = {"workload": "outer-gate decode: B=256 H=32 d=128 bf16 q/k/v, fp32 gates and state, %d steps"
+                                 % T, "ms_per_step": dper, "tokens_per_s": wd.B / (dper / 1e3),
+                     "GB_per_s": dbytes / (dper / 1e3) / 1e9,
+                     "hbm_frac": dbytes / (dper / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": dbytes}
+    return out
+
+
 def dataclass_replace(w, **kw):
     import dataclasses
     return dataclasses.replace(w, **kw)
@@ -430,12 +482,19 @@ def summarize_stats(d, command):
         with open(files[0]) as fh:
             return list(csv.DictReader(fh))
     stats, trace = find("*kernel_stats.csv"), find("*kernel_trace.csv")
-    lines = ["# rocprofv3 kernel statistics of the GLA kernels (kernel trace) for the bench.py workloads",
-             "#   prefill: B=8 H=16 L=4096 d_k=d_v=128 chunk 64, bf16, key-dim gates (grid 256)",
+    lines = ["# rocprofv3 kernel statistics of the library's kernels (kernel trace) for the bench.py workloads",
+             "#   headline prefill: B=8 H=16 L=4096 d_k=d_v=128 chunk 64, bf16, key-dim gates (grid 256)",
              "#   decode:  B=256 H=32 d=128 bf16, fp32 state; its state comes from a 512-token prefill "
              "(prefill grid 16384)",
-             "# kernel names are mangled: prefill_kernel<T, d_k, chunk, value-column tile, gate, elu1>,",
-             "#   DF16b = bf16, gate 1 = key-dim; decode_kernel<T, d_k, d_v>",
+             "#   other prefills: linear_elu1 (4x8x2048, d=64), scalar_long (1x32x32768, segmented: state-only "
+             "pass, segment scan, full pass), fp32_single_head, and the normalised form at the headline shape",
+             "#   delta rule at the headline shape: delta_prep_kernel (grid 8192) then delta_scan_kernel (grid 256); "
+             "delta decode at the decode shape",
+             "#   gate producer: 8x4096 tokens, d_model 2048 -> 16 heads x 128 (grid 512)",
+             "#   outer-product gate at the headline shape, chunk 32 and 64 (grid 256); its decode step",
+             "# kernel names are mangled: prefill_kernel<T, d_k, chunk, value-column tile, gate, elu1, "
+             "state-only, normalised>, DF16b = bf16, gate 1 = key-dim, 2 = scalar; decode_kernel<T, d_k, d_v, "
+             "normalised>; delta_scan_kernel<T, d_k, chunk>; outer_prefill_kernel<T, d_k, chunk, elu1>",
              "# command (from the repository root, REPO = its absolute path):", "#   " + command, "",
              "## rocprofv3 stats (all dispatches, warm-up included)",
              "%-8s %14s %12s %12s %12s  %s" % ("calls", "total_ns", "avg_ns", "min_ns", "max_ns", "kernel")]
@@ -575,6 +634,7 @@ def main():
         line["other_prefill"] = run_other_prefills(args, torch, api, inputs)
         line["delta"] = run_delta(args, torch, api, inputs)
         line["gate_producer"] = run_gate(args, torch, api, inputs)
+        line["outer_gate"] = run_outer(args, torch, api, inputs)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget_s)
     print(json.dumps(line))
