@@ -193,7 +193,7 @@ def delta_workspace_bytes(B, H, L, d_k, d_v, chunk, dtype=torch.bfloat16) -> int
     return int(_lib.load().gla_delta_workspace_bytes(B, H, L, d_k, d_v, chunk, _DTYPES[dtype]))
 
 
-def prefill_delta(q, k, v, beta, initial_state=None, chunk=64, out=None, final_state=None,
+def prefill_delta(q, k, v, beta, initial_state=None, chunk=32, out=None, final_state=None,
                   workspace=None, stream=None):
     """Chunkwise delta-rule prefill (gla_prefill_delta).
 

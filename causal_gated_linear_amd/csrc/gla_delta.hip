@@ -354,6 +354,305 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(const DeltaArgs a)
 }
 
 // ------------------------------------------------------------------------------------
+// delta_fused_kernel: both halves in one workgroup (chunks of 16 or 32 tokens)
+// ------------------------------------------------------------------------------------
+// One workgroup per (head, 64 value columns) walks the chunks in order.  While its
+// waves carry the state through chunk n (U = U~ + (-W) S, the outputs, S += K^T U,
+// as delta_scan_kernel), they also solve chunk n+1's triangular system (N, the
+// diagonal-block inverses, the block below the diagonal, then -W and U~ into LDS, as
+// delta_prep_kernel), one step of each between consecutive barriers, so the two
+// interleave and nothing goes through global memory.  N (strictly lower) and X^T
+// (upper triangle with the diagonal) share one fp32 array: the inverse of a unit
+// lower-triangular block is lower triangular, so its transpose fills exactly the
+// positions N leaves free.
+template <typename T, int DK, int C>
+struct DeltaFusedShape {
+    static constexpr int ES = sizeof(T), CE = 16 / ES, PAD = row_pad<T>();
+    static constexpr int NB = C / 16, NKB = DK / 16, DVT = 64;
+    static constexpr int LDK = DK + PAD;           // Q, K, -W rows
+    static constexpr int LDU = C + PAD;            // U~^T rows
+    static constexpr int LDV = DVT + 16 / ES;      // raw V rows
+    static constexpr int LDC = C + 4;              // N / X^T rows (fp32)
+    static constexpr int BUF = 3 * C * LDK + DVT * LDU;       // elements per chunk buffer
+    static constexpr int QP = C * DK / CE, QPT = (QP + 255) / 256;
+    static constexpr int VPT = (C * DVT / CE + 255) / 256;
+    static_assert(NB <= 2, "fused path: chunks of 16 or 32 tokens");
+};
+
+template <typename T, int DK, int C>
+constexpr int delta_fused_lds()
+{
+    typedef DeltaFusedShape<T, DK, C> SH;
+    return (2 * SH::BUF + 2 * C * SH::LDV) * (int)sizeof(T) + (C * SH::LDC + 2 * C) * 4;
+}
+
+template <typename T, int DK, int C>
+__global__ __launch_bounds__(256, 2) void delta_fused_kernel(const DeltaArgs a)
+{
+    typedef DeltaFusedShape<T, DK, C> SH;
+    constexpr int ES = SH::ES, CE = SH::CE, NB = SH::NB, NKB = SH::NKB;
+    constexpr int LDK = SH::LDK, LDU = SH::LDU, LDV = SH::LDV, LDC = SH::LDC, QP = SH::QP;
+    typedef typename Frag<T>::type F4;
+    __shared__ __align__(16) T sbuf[2 * SH::BUF];      // per chunk: Q, K, -W rows, U~^T
+    __shared__ __align__(16) T sVr[2][C * LDV];        // raw V rows of the chunk being solved
+    __shared__ __align__(16) float sNX[C * LDC];       // N (strictly lower) and X^T (upper)
+    __shared__ __align__(16) float sBt[2][C];          // write strengths
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int x = lane & 15, grp = lane >> 4;
+    int wgi = blockIdx.x;
+    if (a.xcd_remap) wgi = (wgi & 7) * (gridDim.x >> 3) + (wgi >> 3);
+    const int bh = wgi / a.n_vt, vt = wgi - bh * a.n_vt;
+    const int L = a.L, DV = a.d_v, DVT = a.dvt;
+    const int nch = (L + C - 1) / C;
+    const size_t hrow = (size_t)bh * L;
+    const int j0 = vt * DVT + 16 * w;
+    const bool active = 16 * w < DVT;                  // wave-uniform
+    const int VP = C * DVT / CE;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    const Rsrc rq = make_rsrc((const T *)a.q + hrow * DK, (unsigned)(L * DK * ES));
+    const Rsrc rk = make_rsrc((const T *)a.k + hrow * DK, (unsigned)(L * DK * ES));
+    const Rsrc rv = make_rsrc((const T *)a.v + hrow * DV, (unsigned)(L * DV * ES));
+    auto bQ = [&](int n) { return sbuf + (n & 1) * SH::BUF; };
+    auto bK = [&](int n) { return sbuf + (n & 1) * SH::BUF + C * LDK; };
+    auto bW = [&](int n) { return sbuf + (n & 1) * SH::BUF + 2 * C * LDK; };
+    auto bU = [&](int n) { return sbuf + (n & 1) * SH::BUF + 3 * C * LDK; };
+
+    // raw rows of a chunk: requested into registers, later written to LDS
+    i32x4 gq[SH::QPT], gk[SH::QPT], gv[SH::VPT];
+    float gb = 0.f;
+    auto fetch = [&](int n) {
+        const int base = n * C * DK * ES;
+#pragma unroll
+        for (int i = 0; i < SH::QPT; ++i) {
+            const int p = tid + 256 * i;
+            if (QP % 256 == 0 || p < QP) {
+                gq[i] = buf_load16<i32x4>(rq, base + 16 * p);
+                gk[i] = buf_load16<i32x4>(rk, base + 16 * p);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SH::VPT; ++i) {
+            const int p = tid + 256 * i;
+            if (p < VP) {
+                const int r = p / (DVT / CE), c = (p - r * (DVT / CE)) * CE;
+                gv[i] = buf_load16<i32x4>(rv, ((n * C + r) * DV + vt * DVT + c) * ES);
+            }
+        }
+        gb = (tid < C && n * C + tid < L) ? a.beta[hrow + n * C + tid] : 0.f;
+    };
+    auto stash = [&](int n) {
+        T *sQ = bQ(n), *sK = bK(n), *sV = sVr[n & 1];
+#pragma unroll
+        for (int i = 0; i < SH::QPT; ++i) {
+            const int p = tid + 256 * i;
+            if (QP % 256 == 0 || p < QP) {
+                const int r = p / (DK / CE), c = (p - r * (DK / CE)) * CE;
+                *(i32x4 *)(sQ + r * LDK + c) = gq[i];
+                *(i32x4 *)(sK + r * LDK + c) = gk[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SH::VPT; ++i) {
+            const int p = tid + 256 * i;
+            if (p < VP) {
+                const int r = p / (DVT / CE), c = (p - r * (DVT / CE)) * CE;
+                *(i32x4 *)(sV + r * LDV + c) = gv[i];
+            }
+        }
+        if (tid < C) sBt[n & 1][tid] = gb;
+    };
+
+    // ---- the triangular solve of chunk m, in four steps ------------------------------
+    // A: N = tril(diag(beta) K K^T, -1), strictly lower entries only
+    auto solveA = [&](int m) {
+        const T *sK = bK(m);
+        const float *bt = sBt[m & 1];
+        for (int id = w; id < NB * (NB + 1) / 2; id += 4) {
+            const int tb = id > 0, sb = id == 2;       // tiles (0,0), (1,0), (1,1)
+            const f32x4 g = contract_rows(sK + (16 * tb + x) * LDK, sK + (16 * sb + x) * LDK, NKB, grp, zero);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tb + 4 * grp + e, s = 16 * sb + x;
+                if (s < t) sNX[t * LDC + s] = bt[t] * g[e];
+            }
+        }
+    };
+    // B: the diagonal blocks' inverses, stored transposed (upper triangle with diagonal)
+    auto solveB = [&]() {
+        if (w < NB && lane < 16) {
+            const int b = w, j = lane;
+            const float *nb = sNX + 16 * b * LDC + 16 * b;
+            float xs[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+                for (int mm = 0; mm < r; ++mm) acc -= nb[r * LDC + mm] * xs[mm];
+                xs[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (r >= j) sNX[(16 * b + j) * LDC + 16 * b + r] = xs[r];
+        }
+    };
+    // fragment of X[row][16 cb + 4 grp + e] for row = 16 rb + x (the lower triangle of
+    // X, read from its transpose); zero above the diagonal
+    auto xrow = [&](int rb, int cb) {
+        f32x4 v = col_frag(sNX, LDC, 16 * cb + 4 * grp, 16 * rb, x);
+        if (rb == cb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * grp + e > x) v[e] = 0.f;
+        }
+        return v;
+    };
+    // C: the block below the diagonal (two blocks): X_10 = -X_11 N_10 X_00
+    auto solveC = [&]() {
+        if (NB == 2 && w == 0) {
+            // R = N_10 X_00: A = N_10 rows, B = X_00 columns = X_00^T rows (masked)
+            f32x4 b0 = lds_frag(sNX + x * LDC, 0, grp);       // X^T[x][4 grp + e] = X[4 grp + e][x]
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * grp + e < x) b0[e] = 0.f;            // X_00 is zero above its diagonal
+            const f32x4 r = mma1(lds_frag(sNX + (16 + x) * LDC, 0, grp), b0, zero);
+            const f32x4 xr = mma1(xrow(1, 1), r, zero);       // X_11 R
+            *(f32x4 *)(sNX + x * LDC + 16 + 4 * grp) = -xr;  // X^T block (0, 1)
+        }
+    };
+    // D: -W and U~ of chunk m into its buffer
+    auto solveD = [&](int m) {
+        const T *sK = bK(m), *sV = sVr[m & 1];
+        T *sW = bW(m), *sU = bU(m);
+        const float *bt = sBt[m & 1];
+        auto xb = [&](int tb, int sb) -> F4 {
+            return cvt4<T>(xrow(tb, sb) * *(const f32x4 *)(bt + 16 * sb + 4 * grp));
+        };
+        const int nvb = DVT / 16;
+        for (int id = w; id < (NKB + nvb) * NB; id += 4) {
+            const int tb = id % NB, cb = id / NB;
+            f32x4 acc = zero;
+            if (cb < NKB) {       // lane (x, grp) element e: W[16 tb + x][16 cb + 4 grp + e]
+                if (tb == 1)
+                    acc = mac2(col_frag(sK, LDK, 4 * grp, 16 * cb, x), col_frag(sK, LDK, 16 + 4 * grp, 16 * cb, x),
+                               xb(1, 0), xb(1, 1), acc);
+                else
+                    acc = mac1(col_frag(sK, LDK, 4 * grp, 16 * cb, x), xb(0, 0), acc);
+                store4(sW + (16 * tb + x) * LDK + 16 * cb + 4 * grp, -acc);
+            } else {              // lane (x, grp) element e: U~[16 tb + 4 grp + e][16 jb + x]
+                const int jb = cb - NKB;
+                if (tb == 1)
+                    acc = mac2(xb(1, 0), xb(1, 1), col_frag(sV, LDV, 4 * grp, 16 * jb, x),
+                               col_frag(sV, LDV, 16 + 4 * grp, 16 * jb, x), acc);
+                else
+                    acc = mac1(xb(0, 0), col_frag(sV, LDV, 4 * grp, 16 * jb, x), acc);
+                store4(sU + (16 * jb + x) * LDU + 16 * tb + 4 * grp, acc);
+            }
+        }
+    };
+
+    // ---- the state pass over chunk n ---------------------------------------------------
+    f32x4 s[NKB], u[2];
+#pragma unroll
+    for (int ib = 0; ib < NKB; ++ib) {
+        s[ib] = zero;
+        if (active && a.s0) {
+            const float *p = a.s0 + ((size_t)bh * DK + 16 * ib + 4 * grp) * DV + j0 + x;
+            s[ib] = f32x4{p[0], p[DV], p[2 * DV], p[3 * DV]};
+        }
+    }
+    auto scanU = [&](int n) {            // U = U~ + (-W) S
+        const T *sW = bW(n), *sU = bU(n) + 16 * w * LDU;
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            f32x4 acc = widen4(lds_frag(sU + x * LDU, tb, grp));
+            const T *wrow = sW + (16 * tb + x) * LDK;
+#pragma unroll
+            for (int ib = 0; ib + 1 < NKB; ib += 2)
+                acc = mac2(lds_frag(wrow, ib, grp), lds_frag(wrow, ib + 1, grp), cvt4<T>(s[ib]),
+                           cvt4<T>(s[ib + 1]), acc);
+            if (NKB % 2) acc = mac1(lds_frag(wrow, NKB - 1, grp), cvt4<T>(s[NKB - 1]), acc);
+            u[tb] = acc;
+        }
+    };
+    auto scanO = [&](int n) {            // O^T = S^T Q^T + U^T P^T, stored
+        const T *sQ = bQ(n), *sK = bK(n);
+        const int nvalid = min(C, L - n * C);
+        T *og = (T *)a.o + (hrow + (size_t)n * C) * DV + j0 + 4 * grp;
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            const T *qrow = sQ + (16 * tb + x) * LDK;
+            f32x4 o = contract_regs_rows<T, NKB>(s, qrow, grp, zero);
+            auto score = [&](int sb) {
+                f32x4 p = contract_rows(sK + (16 * sb + x) * LDK, qrow, NKB, grp, zero);
+                if (sb == tb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * grp + e > x) p[e] = 0.f;
+                }
+                return p;
+            };
+            if (tb == 1)
+                o = mac2(cvt4<T>(u[0]), cvt4<T>(u[1]), cvt4<T>(score(0)), cvt4<T>(score(1)), o);
+            else
+                o = mac1(cvt4<T>(u[0]), cvt4<T>(score(0)), o);
+            if (16 * tb + x < nvalid) store4(og + (size_t)(16 * tb + x) * DV, o);
+        }
+    };
+    auto scanS = [&](int n) {            // S += K^T U
+        const T *sK = bK(n);
+#pragma unroll
+        for (int ib = 0; ib < NKB; ++ib) {
+            if (NB == 2)
+                s[ib] = mac2(col_frag(sK, LDK, 4 * grp, 16 * ib, x), col_frag(sK, LDK, 16 + 4 * grp, 16 * ib, x),
+                             cvt4<T>(u[0]), cvt4<T>(u[1]), s[ib]);
+            else
+                s[ib] = mac1(col_frag(sK, LDK, 4 * grp, 16 * ib, x), cvt4<T>(u[0]), s[ib]);
+        }
+    };
+
+    if (nch > 0) {
+        fetch(0);
+        stash(0);
+        lds_barrier();
+        solveA(0);
+        lds_barrier();
+        solveB();
+        lds_barrier();
+        solveC();
+        lds_barrier();
+        solveD(0);
+        if (nch > 1) fetch(1);
+    }
+    for (int n = 0; n < nch; ++n) {
+        const bool more = n + 1 < nch;                 // uniform
+        if (more) stash(n + 1);
+        if (n + 2 < nch) fetch(n + 2);
+        lds_barrier();                                 // chunk n's -W, U~ and chunk n+1's rows visible
+        if (more) solveA(n + 1);
+        if (active) scanU(n);
+        lds_barrier();
+        if (more) solveB();
+        if (active) scanO(n);
+        lds_barrier();
+        if (more) solveC();
+        if (active) scanS(n);
+        lds_barrier();
+        if (more) solveD(n + 1);
+    }
+
+    if (active && a.s_final) {
+#pragma unroll
+        for (int ib = 0; ib < NKB; ++ib) {
+            float *p = a.s_final + ((size_t)bh * DK + 16 * ib + 4 * grp) * DV + j0 + x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[(size_t)e * DV] = s[ib][e];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // delta_decode_kernel: one token on a resident fp32 state, in place
 // ------------------------------------------------------------------------------------
 // One workgroup per head; a thread owns a float4 column group and every RS-th row.
@@ -422,10 +721,32 @@ __global__ __launch_bounds__(256) void delta_decode_kernel(const DeltaArgs a)
 // ------------------------------------------------------------------------------------
 // launches
 // ------------------------------------------------------------------------------------
+// Chunks of 16 or 32 tokens run in the fused kernel (its LDS fits for every d_k and
+// both element types); chunks of 64 in the two kernels with the workspace between.
+bool delta_fused(int chunk) { return chunk == 16 || chunk == 32; }
+
 size_t delta_workspace(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes)
 {
+    if (delta_fused(chunk)) return 0;
     const size_t lp = (size_t)(L + chunk - 1) / chunk * chunk;
     return (size_t)BH * lp * (d_k + d_v) * elem_bytes;
+}
+
+template <typename T, int C>
+static hipError_t launch_delta_fused(const DeltaArgs &a, hipStream_t stream)
+{
+    const int grid = a.BH * a.n_vt;
+#define GLA_FUSED(DK)                                                                                \
+    case DK:                                                                                         \
+        static_assert(delta_fused_lds<T, DK, C>() <= kLdsBytes, "fused delta LDS");                 \
+        hipLaunchKernelGGL((delta_fused_kernel<T, DK, C>), dim3(grid), dim3(256), 0, stream, a);     \
+        break;
+    switch (a.d_k) {
+    GLA_FUSED(16) GLA_FUSED(32) GLA_FUSED(64) GLA_FUSED(128)
+    default: return hipErrorInvalidValue;
+    }
+#undef GLA_FUSED
+    return hipGetLastError();
 }
 
 template <typename T, int C>
@@ -451,8 +772,8 @@ static hipError_t launch_delta_c(const DeltaArgs &a, hipStream_t stream)
 template <typename T>
 static hipError_t launch_delta_t(const DeltaArgs &a, int chunk, hipStream_t stream)
 {
-    if (chunk == 16) return launch_delta_c<T, 16>(a, stream);
-    if (chunk == 32) return launch_delta_c<T, 32>(a, stream);
+    if (chunk == 16) return launch_delta_fused<T, 16>(a, stream);
+    if (chunk == 32) return launch_delta_fused<T, 32>(a, stream);
     if (chunk == 64) return launch_delta_c<T, 64>(a, stream);
     return hipErrorInvalidValue;
 }

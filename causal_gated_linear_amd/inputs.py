@@ -31,7 +31,7 @@ drawn by ``draw_delta`` / ``draw_delta_decode`` in the same order (q, k, v, z):
   delta_prefill      bf16, B=8 H=16 L=4096 d=128 (the gla_prefill shape), q and k
                      ~ N(0,1) rescaled to unit length per token (in fp32, before the
                      cast), v ~ N(0,1), write strength beta = sigmoid(z) in fp32 per
-                     head and token, chunk 64
+                     head and token, chunk 32
 
 The outer-product gate (G_t = alpha_t beta_t^T, same section) reuses a workload's
 q, k, v and key-dim gates and adds value-dim log-gates from ``draw_value_gate``: the
@@ -83,7 +83,7 @@ WORKLOADS = {
                             "scalar", None, True, seed=4),
     "decode": Workload("decode", torch.bfloat16, 256, 32, 512, 128, 128, 64,
                        "keydim", None, True, decode_steps=1024, seed=5),
-    "delta_prefill": Workload("delta_prefill", torch.bfloat16, 8, 16, 4096, 128, 128, 64,
+    "delta_prefill": Workload("delta_prefill", torch.bfloat16, 8, 16, 4096, 128, 128, 32,
                               None, None, False, seed=6),
 }
 

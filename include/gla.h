@@ -216,9 +216,10 @@ int gla_decode_step_norm(const void *q, const void *k, const void *v, const floa
  * normalisation are applied: callers scale keys (unit-norm keys and beta in [0, 1]
  * keep every step I - beta k k^T a contraction) and queries themselves.
  *
- * gla_delta_workspace_bytes -- bytes of device workspace gla_prefill_delta needs:
- * B*H*ceil(L/chunk)*chunk*(d_k + d_v) elements of the input dtype.  0 for L == 0
- * or invalid sizes (gla_prefill_delta reports those).
+ * gla_delta_workspace_bytes -- bytes of device workspace gla_prefill_delta needs: 0
+ * for chunks of 16 or 32 tokens (one fused kernel), and for chunks of 64
+ * B*H*ceil(L/chunk)*chunk*(d_k + d_v) elements of the input dtype.  0 for L == 0 or
+ * invalid sizes (gla_prefill_delta reports those).
  */
 size_t gla_delta_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chunk,
                                  gla_dtype dtype);
@@ -226,9 +227,11 @@ size_t gla_delta_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chun
 /*
  * gla_prefill_delta -- all outputs of a prompt under the delta rule.  Within a chunk
  * of `chunk` tokens the writes solve one unit lower-triangular system (the page's
- * prefill argument applied to a chunk that starts from a nonzero state); the
- * chunk's state-free parts are computed for all chunks in parallel into the
- * workspace, then a pass over each head's chunks in order carries the state.
+ * prefill argument applied to a chunk that starts from a nonzero state).  Chunks of
+ * 16 or 32 tokens: one kernel solves chunk n+1's system while it carries the state
+ * through chunk n (no workspace).  Chunks of 64: the chunks' state-free parts are
+ * computed for all chunks in parallel into the workspace, then a pass over each
+ * head's chunks in order carries the state.
  *   q, k      in   [B][H][L][d_k], dtype
  *   v         in   [B][H][L][d_v], dtype
  *   beta      in   fp32 [B][H][L] write strengths (4-byte aligned)
@@ -238,7 +241,7 @@ size_t gla_delta_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chun
  *                  equal s0 (in-place update) but must not partially overlap it
  *   chunk     16, 32 or 64
  *   workspace device scratch of at least gla_delta_workspace_bytes(...) bytes,
- *             16-byte aligned; contents are clobbered
+ *             16-byte aligned (NULL allowed when that is 0); contents are clobbered
  * Sizes and dtypes as for gla_prefill_chunked.  o must not overlap any other
  * argument; s_final and the workspace must not overlap any input.  Errors:
  * GLA_ERR_NULL, GLA_ERR_SHAPE, GLA_ERR_UNSUPPORTED, GLA_ERR_ALIGN, GLA_ERR_ALIAS,

@@ -279,9 +279,12 @@ def test_prefill_delta_rejects(lib, case):
 
 
 def test_delta_workspace_bytes(lib):
-    """-W rows [B*H][padded L][d_k] and U~ [B*H][padded L][d_v], in the input dtype."""
+    """Chunks of 64: -W rows [B*H][padded L][d_k] and U~ [B*H][padded L][d_v], in the
+    input dtype.  Chunks of 16 or 32 run fused and need none."""
     assert lib.gla_delta_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 8 * 16 * 4096 * 256 * 2
-    assert lib.gla_delta_workspace_bytes(1, 2, 100, 64, 32, 32, 0) == 2 * 128 * 96 * 4
+    assert lib.gla_delta_workspace_bytes(1, 2, 100, 64, 32, 64, 0) == 2 * 128 * 96 * 4
+    assert lib.gla_delta_workspace_bytes(8, 16, 4096, 128, 128, 32, 1) == 0
+    assert lib.gla_delta_workspace_bytes(8, 16, 4096, 128, 128, 16, 0) == 0
     assert lib.gla_delta_workspace_bytes(1, 2, 0, 64, 32, 32, 0) == 0
     assert lib.gla_delta_workspace_bytes(1, 2, 100, 48, 32, 32, 0) == 0
 

@@ -21,7 +21,7 @@ DEV = "cuda"
 WD = inputs.WORKLOADS["delta_prefill"]
 
 
-def _w(dtype=torch.bfloat16, dk=128, dv=128, chunk=64):
+def _w(dtype=torch.bfloat16, dk=128, dv=128, chunk=32):
     return dataclasses.replace(WD, dtype=dtype, d_k=dk, d_v=dv, chunk=chunk)
 
 
@@ -43,10 +43,12 @@ def _check(w, B, H, L, seed, chunk=None, with_init=False, in_place=False):
         w.dtype, w.d_k, w.d_v, B, H, L, chunk or w.chunk, with_init, eo, es))
 
 
+# chunks of 16 and 32 run in the fused kernel, chunks of 64 in the two-kernel path
+@pytest.mark.parametrize("chunk", [32, 64])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("with_init", [False, True])
-def test_prefill_delta_small(dtype, with_init):
-    _check(_w(dtype), 2, 3, 250, seed=1200 + int(with_init), with_init=with_init)
+def test_prefill_delta_small(dtype, with_init, chunk):
+    _check(_w(dtype, chunk=chunk), 2, 3, 250, seed=1200 + int(with_init), with_init=with_init)
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64])
@@ -55,26 +57,30 @@ def test_prefill_delta_chunk_sizes(dtype, chunk):
     _check(_w(dtype), 1, 2, 3 * chunk + 7, seed=1210 + chunk, chunk=chunk, with_init=True)
 
 
-@pytest.mark.parametrize("L", [1, 15, 17, 64, 65, 129])
-def test_prefill_delta_lengths(L):
-    _check(_w(), 1, 2, L, seed=1230 + L, with_init=True)
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("L", [1, 15, 17, 33, 64, 65, 129])
+def test_prefill_delta_lengths(L, chunk):
+    _check(_w(chunk=chunk), 1, 2, L, seed=1230 + L, with_init=True)
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 32), (16, 128), (64, 128), (128, 16)])
-def test_prefill_delta_dims(dtype, dk, dv):
-    _check(_w(dtype, dk, dv), 1, 2, 150, seed=dk * 3 + dv, with_init=True)
+def test_prefill_delta_dims(dtype, dk, dv, chunk):
+    _check(_w(dtype, dk, dv, chunk), 1, 2, 150, seed=dk * 3 + dv, with_init=True)
 
 
+@pytest.mark.parametrize("chunk", [32, 64])
 @pytest.mark.parametrize("tile", ["16", "32", "64"])
-def test_prefill_delta_value_tiles(tile, monkeypatch):
+def test_prefill_delta_value_tiles(tile, chunk, monkeypatch):
     """Narrower value tiles per workgroup (more workgroups, idle waves) give the same result."""
     monkeypatch.setenv("GLA_DELTA_TILE", tile)
-    _check(_w(), 2, 2, 200, seed=1250 + int(tile), with_init=True)
+    _check(_w(chunk=chunk), 2, 2, 200, seed=1250 + int(tile), with_init=True)
 
 
-def test_prefill_delta_in_place_state():
-    _check(_w(), 1, 2, 200, seed=1260, with_init=True, in_place=True)
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_prefill_delta_in_place_state(chunk):
+    _check(_w(chunk=chunk), 1, 2, 200, seed=1260, with_init=True, in_place=True)
 
 
 def test_prefill_delta_empty_copies_state():
@@ -101,10 +107,11 @@ def test_prefill_delta_zero_strength_keeps_state():
                       "beta=0 output")
 
 
-def test_prefill_delta_full_size_sampled_heads():
-    """The delta_prefill shape (8x16x4096, d=128, chunk 64) in the launch configuration
-    the benchmark times, checked on sampled heads."""
-    w = WD
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_prefill_delta_full_size_sampled_heads(chunk):
+    """The delta_prefill shape (8x16x4096, d=128; chunk 32 is the launch configuration
+    the benchmark times), checked on sampled heads."""
+    w = dataclasses.replace(WD, chunk=chunk)
     inp = inputs.draw_delta(w, device=DEV)
     o, s = api.prefill_delta(inp["q"], inp["k"], inp["v"], inp["beta"], chunk=w.chunk)
     torch.cuda.synchronize()
