@@ -22,10 +22,10 @@
 // One workgroup per (head, value tile of up to 64 columns); wave w owns 16 value
 // columns and their state slice S[d_k][16] in accumulator registers.  Per chunk the
 // workgroup stages the raw rows (q, k, v, both gates) in LDS, then
-//   1. computes the cumulative sums A and Bv on the matrix cores as products with the
-//      lower-triangular ones matrix (fp32 operands: exact in the products), and each
-//      lane scales the q, k, v elements of its accumulator positions in place, writes
-//      e^Bv for the output and the chunk totals;
+//   1. computes the cumulative sums A and Bv: a thread owns four columns of a segment
+//      of rows, sums them serially, and the segments finish the scan with shuffles
+//      across consecutive lanes; it then scales its rows' q, k, v elements in place
+//      and writes e^Bv for the output and the chunk totals;
 //   2. computes the masked scores, O^T = (S^T Q~^T + V^^T P^T) (.) e^Bv^T and the
 //      two-sided state update, as in the other prefill kernels.
 // The next chunk's raw rows are requested before the current chunk is computed.
@@ -50,6 +50,10 @@ struct OuterShape {
     static constexpr int PVM = C * DVT / CE, PGVM = C * DVT / 4;   // at the widest tile
     static constexpr int TQ = (PQ + 255) / 256, TG = (PG + 255) / 256;
     static constexpr int TV = (PVM + 255) / 256, TGV = (PGVM + 255) / 256;
+    // cumulative-gate scan: row segments per four-column group (key side, value side)
+    static constexpr int KSEG = C < 256 / (DK / 4) ? C : 256 / (DK / 4);
+    static constexpr int VSEG = C < 256 / (DVT / 4) ? C : 256 / (DVT / 4);
+    static_assert(KSEG <= 64 && VSEG <= 64, "a segment group stays within one wave");
 };
 
 template <typename T, int DK, int C, bool ELU1>
@@ -155,20 +159,6 @@ __global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
         }
     };
 
-    // inclusive cumulative sum over the chunk's rows of column c0 + x of a fp32 gate
-    // array, for rows 16 tb + 4 grp + e (lane (x, grp), element e), in log2 units:
-    // the product of the lower-triangular ones matrix with the gate columns
-    auto cumsum = [&](const float *G, int ld, int tb, int c0) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int sb = 0; sb <= tb; ++sb) {
-            f32x4 m;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m[e] = (sb < tb || 4 * grp + e <= x) ? kLog2e : 0.f;
-            acc = mma1(m, col_frag(G, ld, 16 * sb + 4 * grp, c0, x), acc);
-        }
-        return acc;   // lane (x, grp) element e: row 16 tb + 4 grp + e, column c0 + x
-    };
-
     // state slice: tile ib, lane (x, grp) element e holds S[16 ib + 4 grp + e][j0 + x]
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 s[NKB];
@@ -189,30 +179,89 @@ __global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
         if (n + 1 < nch) fetch(n + 1);
         const int nvalid = min(C, L - n * C);
 
-        // 1. cumulative gates; scale q, k (key side) and v (value side) in place
-        const int nkt = NB * NKB, nvt = NB * (DVT / 16);
-        for (int id = w; id < nkt + nvt; id += 4) {
-            if (id < nkt) {
-                const int tb = id % NB, ib = id / NB;
-                const f32x4 A = cumsum(sG, LDG, tb, 16 * ib);
+        // 1. cumulative gates; scale q, k (key side) and v (value side) in place.
+        //    A thread owns four columns of a segment of rows: it sums its rows serially,
+        //    the segments of a column group (consecutive lanes) finish the scan with
+        //    shuffles, then it scales its rows' elements.
+        {
+            constexpr int NCG = DK / 4, NSEG = SH::KSEG, RPT = C / NSEG;
+            const int cg = tid / NSEG, seg = tid % NSEG;
+            if (cg < NCG) {                                    // whole waves
+                float pre[RPT][4], run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * tb + 4 * grp + e, i = 16 * ib + x;
-                    const float up = exp2_fast(A[e]), down = exp2_fast(-A[e]);
-                    sQ[t * LDK + i] = from_f32<T>(feature(to_f32(sQ[t * LDK + i]), ELU1) * up);
-                    sK[t * LDK + i] = from_f32<T>(feature(to_f32(sK[t * LDK + i]), ELU1) * down);
-                    if (t == C - 1) sEA[i] = up;
+                for (int r = 0; r < RPT; ++r) {
+                    const f32x4 g = *(const f32x4 *)(sG + (seg * RPT + r) * LDG + 4 * cg);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pre[r][e] = run[e] += g[e] * kLog2e;
                 }
-            } else {
-                const int tb = (id - nkt) % NB, jb = (id - nkt) / NB;
-                const f32x4 Bv = cumsum(sGV, LDGV, tb, 16 * jb);
+                float excl[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * tb + 4 * grp + e, j = 16 * jb + x;
-                    const float up = exp2_fast(Bv[e]);
-                    sV[t * LDV + j] = from_f32<T>(to_f32(sV[t * LDV + j]) * exp2_fast(-Bv[e]));
-                    sEV[t * LDGV + j] = up;
-                    if (t == C - 1) sEB[j] = up;
+                    float incl = run[e];
+#pragma unroll
+                    for (int off = 1; off < NSEG; off <<= 1) {
+                        const float up = __shfl_up(incl, off, NSEG);
+                        if (seg >= off) incl += up;
+                    }
+                    excl[e] = incl - run[e];
+                }
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    const int t = seg * RPT + r;
+                    T *qp = sQ + t * LDK + 4 * cg, *kp = sK + t * LDK + 4 * cg;
+                    const f32x4 qv = widen4(*(const typename Frag<T>::type *)qp);
+                    const f32x4 kv = widen4(*(const typename Frag<T>::type *)kp);
+                    f32x4 qo, ko, up;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float b = excl[e] + pre[r][e];
+                        up[e] = exp2_fast(b);
+                        qo[e] = feature(qv[e], ELU1) * up[e];
+                        ko[e] = feature(kv[e], ELU1) * exp2_fast(-b);
+                    }
+                    *(typename Frag<T>::type *)qp = cvt4<T>(qo);
+                    *(typename Frag<T>::type *)kp = cvt4<T>(ko);
+                    if (t == C - 1) *(f32x4 *)(sEA + 4 * cg) = up;
+                }
+            }
+        }
+        {
+            constexpr int NCG = SH::DVT / 4, NSEG = SH::VSEG, RPT = C / NSEG;
+            const int cg = tid / NSEG, seg = tid % NSEG;
+            if (cg < NCG && 4 * cg < DVT) {                    // all lanes of a segment group agree
+                float pre[RPT][4], run[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    const f32x4 g = *(const f32x4 *)(sGV + (seg * RPT + r) * LDGV + 4 * cg);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pre[r][e] = run[e] += g[e] * kLog2e;
+                }
+                float excl[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float incl = run[e];
+#pragma unroll
+                    for (int off = 1; off < NSEG; off <<= 1) {
+                        const float up = __shfl_up(incl, off, NSEG);
+                        if (seg >= off) incl += up;
+                    }
+                    excl[e] = incl - run[e];
+                }
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    const int t = seg * RPT + r;
+                    T *vp = sV + t * LDV + 4 * cg;
+                    const f32x4 vv = widen4(*(const typename Frag<T>::type *)vp);
+                    f32x4 vo, up;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float b = excl[e] + pre[r][e];
+                        up[e] = exp2_fast(b);
+                        vo[e] = vv[e] * exp2_fast(-b);
+                    }
+                    *(typename Frag<T>::type *)vp = cvt4<T>(vo);
+                    *(f32x4 *)(sEV + t * LDGV + 4 * cg) = up;
+                    if (t == C - 1) *(f32x4 *)(sEB + 4 * cg) = up;
                 }
             }
         }
