@@ -325,6 +325,231 @@ __global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
     }
 }
 
+// Producer/consumer form of the same computation, for the sizes whose two operand
+// buffers fit in LDS.  Eight waves: the four producer waves load the raw rows of
+// chunk n+1 straight into registers in the scan's own layout (a thread owns four
+// columns of a segment of rows), run the cumulative gates and write Q~, K^, V^,
+// e^Bv and the chunk totals into one LDS buffer, while the four consumer waves run
+// chunk n's products from the other buffer; one barrier per chunk.
+template <typename T, int DK, int C>
+constexpr int outer_pc_lds()
+{
+    typedef OuterShape<T, DK, C> SH;
+    return 2 * ((2 * C * SH::LDK + C * SH::LDV) * (int)sizeof(T) + (C * SH::LDGV + DK + SH::DVT) * 4);
+}
+
+template <typename T> __device__ __forceinline__ typename Frag<T>::type buf_load_frag(Rsrc r, int off);
+template <> __device__ __forceinline__ bf16x4 buf_load_frag<bf16>(Rsrc r, int off)
+{
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(bf16x4, __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)));
+}
+template <> __device__ __forceinline__ f32x4 buf_load_frag<float>(Rsrc r, int off)
+{
+    return buf_load16<f32x4>(r, off);
+}
+
+template <typename T, int DK, int C, bool ELU1>
+__global__ __launch_bounds__(512) void outer_pc_kernel(const OuterArgs a)
+{
+    typedef OuterShape<T, DK, C> SH;
+    constexpr int ES = SH::ES, NB = SH::NB, NKB = SH::NKB;
+    constexpr int LDK = SH::LDK, LDV = SH::LDV, LDGV = SH::LDGV;
+    constexpr int KNCG = DK / 4, KSEG = SH::KSEG, KRPT = C / KSEG;
+    constexpr int VNCG = SH::DVT / 4, VSEG = SH::VSEG, VRPT = C / VSEG;
+    typedef typename Frag<T>::type F4;
+    __shared__ __align__(16) T sQ[2][C * LDK];
+    __shared__ __align__(16) T sK[2][C * LDK];
+    __shared__ __align__(16) T sV[2][C * LDV];
+    __shared__ __align__(16) float sEV[2][C * LDGV];
+    __shared__ __align__(16) float sEA[2][DK];
+    __shared__ __align__(16) float sEB[2][SH::DVT];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int x = lane & 15, grp = lane >> 4;
+    const bool producer = w < 4;                       // wave-uniform
+    int wgi = blockIdx.x;
+    if (a.xcd_remap) wgi = (wgi & 7) * (gridDim.x >> 3) + (wgi >> 3);
+    const int bh = wgi / a.n_vt, vt = wgi - bh * a.n_vt;
+    const int L = a.L, DV = a.d_v, DVT = a.dvt;
+    const int nch = (L + C - 1) / C;
+    const size_t hrow = (size_t)bh * L;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- producers ---------------------------------------------------------------------
+    const Rsrc rq = make_rsrc((const T *)a.q + hrow * DK, (unsigned)(L * DK * ES));
+    const Rsrc rk = make_rsrc((const T *)a.k + hrow * DK, (unsigned)(L * DK * ES));
+    const Rsrc rv = make_rsrc((const T *)a.v + hrow * DV, (unsigned)(L * DV * ES));
+    const Rsrc rg = make_rsrc(a.g + hrow * DK, (unsigned)(L * DK * 4));
+    const Rsrc rgv = make_rsrc(a.gv + hrow * DV, (unsigned)(L * DV * 4));
+    const int kcg = tid / KSEG, kseg = tid % KSEG, vcg = tid / VSEG, vseg = tid % VSEG;
+    const bool klane = producer && kcg < KNCG;                 // whole waves
+    const bool vlane = producer && vcg < VNCG && 4 * vcg < DVT;   // whole segment groups
+    f32x4 rgk[KRPT], rgvv[VRPT];
+    F4 rqq[KRPT], rkk[KRPT], rvv[VRPT];
+    auto load = [&](int n) {
+        if (klane) {
+#pragma unroll
+            for (int r = 0; r < KRPT; ++r) {
+                const int t = n * C + kseg * KRPT + r;         // rows past L read as zeros
+                rgk[r] = buf_load16<f32x4>(rg, (t * DK + 4 * kcg) * 4);
+                rqq[r] = buf_load_frag<T>(rq, (t * DK + 4 * kcg) * ES);
+                rkk[r] = buf_load_frag<T>(rk, (t * DK + 4 * kcg) * ES);
+            }
+        }
+        if (vlane) {
+#pragma unroll
+            for (int r = 0; r < VRPT; ++r) {
+                const int t = n * C + vseg * VRPT + r;
+                rgvv[r] = buf_load16<f32x4>(rgv, (t * DV + vt * DVT + 4 * vcg) * 4);
+                rvv[r] = buf_load_frag<T>(rv, (t * DV + vt * DVT + 4 * vcg) * ES);
+            }
+        }
+    };
+    // inclusive prefix sums (log2 units) of a thread's rows, and the exclusive offset
+    // of its segment within the column group (segments on consecutive lanes)
+    auto scan = [&](const f32x4 *g, int nr, int nseg, int seg, float (*pre)[4], float *excl) {
+        float run[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < nr; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pre[r][e] = run[e] += g[r][e] * kLog2e;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float incl = run[e];
+            for (int off = 1; off < nseg; off <<= 1) {
+                const float up = __shfl_up(incl, off, nseg);
+                if (seg >= off) incl += up;
+            }
+            excl[e] = incl - run[e];
+        }
+    };
+    auto produce = [&](int n) {
+        const int b = n & 1;
+        if (klane) {
+            float pre[KRPT][4], excl[4];
+            scan(rgk, KRPT, KSEG, kseg, pre, excl);
+#pragma unroll
+            for (int r = 0; r < KRPT; ++r) {
+                const int t = kseg * KRPT + r;
+                const f32x4 qv = widen4(rqq[r]), kv = widen4(rkk[r]);
+                f32x4 qo, ko, up;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float bb = excl[e] + pre[r][e];
+                    up[e] = exp2_fast(bb);
+                    qo[e] = feature(qv[e], ELU1) * up[e];
+                    ko[e] = feature(kv[e], ELU1) * exp2_fast(-bb);
+                }
+                *(F4 *)(sQ[b] + t * LDK + 4 * kcg) = cvt4<T>(qo);
+                *(F4 *)(sK[b] + t * LDK + 4 * kcg) = cvt4<T>(ko);
+                if (t == C - 1) *(f32x4 *)(sEA[b] + 4 * kcg) = up;
+            }
+        }
+        if (vlane) {
+            float pre[VRPT][4], excl[4];
+            scan(rgvv, VRPT, VSEG, vseg, pre, excl);
+#pragma unroll
+            for (int r = 0; r < VRPT; ++r) {
+                const int t = vseg * VRPT + r;
+                const f32x4 vv = widen4(rvv[r]);
+                f32x4 vo, up;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float bb = excl[e] + pre[r][e];
+                    up[e] = exp2_fast(bb);
+                    vo[e] = vv[e] * exp2_fast(-bb);
+                }
+                *(F4 *)(sV[b] + t * LDV + 4 * vcg) = cvt4<T>(vo);
+                *(f32x4 *)(sEV[b] + t * LDGV + 4 * vcg) = up;
+                if (t == C - 1) *(f32x4 *)(sEB[b] + 4 * vcg) = up;
+            }
+        }
+    };
+
+    // ---- consumers ---------------------------------------------------------------------
+    const int c = w - 4, jl = 16 * c, j0 = vt * DVT + jl;
+    const bool active = !producer && jl < DVT;          // wave-uniform
+    f32x4 s[NKB];
+#pragma unroll
+    for (int ib = 0; ib < NKB; ++ib) {
+        s[ib] = zero;
+        if (active && a.s0) {
+            const float *p = a.s0 + ((size_t)bh * DK + 16 * ib + 4 * grp) * DV + j0 + x;
+            s[ib] = f32x4{p[0], p[DV], p[2 * DV], p[3 * DV]};
+        }
+    }
+    auto consume = [&](int n) {
+        const int b = n & 1;
+        const T *Q = sQ[b], *K = sK[b], *V = sV[b];
+        const int nvalid = min(C, L - n * C);
+        T *og = (T *)a.o + (hrow + (size_t)n * C) * DV + j0 + 4 * grp;
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {               // O^T = (S^T Q~^T + V^^T P^T) (.) e^Bv^T
+            const T *qrow = Q + (16 * tb + x) * LDK;
+            f32x4 o = contract_regs_rows<T, NKB>(s, qrow, grp, zero);
+            auto score = [&](int sb) {
+                f32x4 p = contract_rows(K + (16 * sb + x) * LDK, qrow, NKB, grp, zero);
+                if (sb == tb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * grp + e > x) p[e] = 0.f;
+                }
+                return p;
+            };
+#pragma unroll
+            for (int sb = 0; sb <= tb; sb += 2) {
+                if (sb + 1 <= tb)
+                    o = mac2(col_frag(V, LDV, 16 * sb + 4 * grp, jl, x), col_frag(V, LDV, 16 * (sb + 1) + 4 * grp, jl, x),
+                             cvt4<T>(score(sb)), cvt4<T>(score(sb + 1)), o);
+                else
+                    o = mac1(col_frag(V, LDV, 16 * sb + 4 * grp, jl, x), cvt4<T>(score(sb)), o);
+            }
+            o *= *(const f32x4 *)(sEV[b] + (16 * tb + x) * LDGV + jl + 4 * grp);
+            if (16 * tb + x < nvalid) store4(og + (size_t)(16 * tb + x) * DV, o);
+        }
+        const float eb = sEB[b][jl + x];                 // S <- Diag(e^GA)(S + K^^T V^)Diag(e^GB)
+#pragma unroll
+        for (int ib = 0; ib < NKB; ++ib) {
+#pragma unroll
+            for (int sb = 0; sb + 1 < NB; sb += 2)
+                s[ib] = mac2(col_frag(K, LDK, 16 * sb + 4 * grp, 16 * ib, x),
+                             col_frag(K, LDK, 16 * (sb + 1) + 4 * grp, 16 * ib, x),
+                             col_frag(V, LDV, 16 * sb + 4 * grp, jl, x),
+                             col_frag(V, LDV, 16 * (sb + 1) + 4 * grp, jl, x), s[ib]);
+            if (NB % 2)
+                s[ib] = mac1(col_frag(K, LDK, 16 * (NB - 1) + 4 * grp, 16 * ib, x),
+                             col_frag(V, LDV, 16 * (NB - 1) + 4 * grp, jl, x), s[ib]);
+            s[ib] *= *(const f32x4 *)(sEA[b] + 16 * ib + 4 * grp) * eb;
+        }
+    };
+
+    if (producer && nch > 0) {
+        load(0);
+        produce(0);
+        if (nch > 1) load(1);
+    }
+    for (int n = 0; n < nch; ++n) {
+        lds_barrier();                                   // buffer n ready, buffer n+1 free
+        if (producer) {
+            if (n + 1 < nch) {
+                produce(n + 1);
+                if (n + 2 < nch) load(n + 2);
+            }
+        } else if (active) {
+            consume(n);
+        }
+    }
+
+    if (active && a.s_final) {
+#pragma unroll
+        for (int ib = 0; ib < NKB; ++ib) {
+            float *p = a.s_final + ((size_t)bh * DK + 16 * ib + 4 * grp) * DV + j0 + x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[(size_t)e * DV] = s[ib][e];
+        }
+    }
+}
+
 // One token on a resident fp32 state, in place: S <- (alpha beta^T) (.) S + phi(k) v^T,
 // o = S^T phi(q).  One workgroup per head; a thread owns a float4 column group (with its
 // four value gates) and every RS-th row; o is reduced across rows through LDS.
@@ -377,15 +602,26 @@ __global__ __launch_bounds__(256) void outer_decode_kernel(const OuterArgs a)
     }
 }
 
+// The producer/consumer kernel where its two buffers fit in LDS, else the
+// single-role kernel (fp32 with d_k = 128 and chunks of 64).
+template <typename T, int DK, int C, bool ELU1>
+static void launch_outer_dk(const OuterArgs &a, int grid, hipStream_t stream)
+{
+    if constexpr (outer_pc_lds<T, DK, C>() <= kLdsBytes)
+        hipLaunchKernelGGL((outer_pc_kernel<T, DK, C, ELU1>), dim3(grid), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL((outer_prefill_kernel<T, DK, C, ELU1>), dim3(grid), dim3(256), 0, stream, a);
+}
+
 template <typename T, int C, bool ELU1>
 static hipError_t launch_outer_c(const OuterArgs &a, hipStream_t stream)
 {
     const int grid = a.BH * a.n_vt;
     switch (a.d_k) {
-    case 16: hipLaunchKernelGGL((outer_prefill_kernel<T, 16, C, ELU1>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((outer_prefill_kernel<T, 32, C, ELU1>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((outer_prefill_kernel<T, 64, C, ELU1>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((outer_prefill_kernel<T, 128, C, ELU1>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 16: launch_outer_dk<T, 16, C, ELU1>(a, grid, stream); break;
+    case 32: launch_outer_dk<T, 32, C, ELU1>(a, grid, stream); break;
+    case 64: launch_outer_dk<T, 64, C, ELU1>(a, grid, stream); break;
+    case 128: launch_outer_dk<T, 128, C, ELU1>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
