@@ -13,7 +13,8 @@
 //     U = U~ - W S,   O = Q S + tril(Q K^T) U  (diagonal included: o_t reads S_t),
 //     S <- S + K^T U.
 //
-// X, W and U~ depend only on the chunk's own keys, values and strengths:
+// X, W and U~ depend only on the chunk's own keys, values and strengths.  Chunks of
+// 64 tokens use two kernels with a workspace between them:
 //   delta_prep_kernel  one workgroup per (head, chunk), all chunks in parallel:
 //       N = tril(diag(beta) K K^T, -1) on the matrix cores; the inverses of the 16x16
 //       diagonal blocks of I + N by substitution in fp32 (one lane per column); the
@@ -29,6 +30,9 @@
 //       stored per block, then S += K^T U.  The chunk's Q, K, -W and U~ rows are staged
 //       in LDS; the next chunk's rows are requested before the current one is
 //       computed, into a second LDS buffer where two fit.
+// Chunks of 16 or 32 tokens use one kernel, delta_fused_kernel, which interleaves
+// the two: between the barriers that separate the steps of chunk n's state pass it
+// solves chunk n+1's system into the other LDS buffer (see its own comment).
 // bf16 inputs: bf16 matrix-core operands, fp32 accumulation and fp32 X; fp32 inputs:
 // fp32 matrix-core products throughout.
 #include "gla_device.hpp"
