@@ -118,14 +118,15 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a)
         const int b = lane >> 4, j = lane & 15;
         if (b < NB) {
             const float *nb = sN + 16 * b * LDC + 16 * b;
+            // column-wise (right-looking): once x_m is final, its multiples are
+            // subtracted from every later row, so the dependent chain is 16 steps long
             float xs[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = r == j ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) xs[r] = r == j ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) acc -= nb[r * LDC + m] * xs[m];
-                xs[r] = acc;
-            }
+            for (int m = 0; m < 16; ++m)
+#pragma unroll
+                for (int r = m + 1; r < 16; ++r) xs[r] -= nb[r * LDC + m] * xs[m];
 #pragma unroll
             for (int r = 0; r < 16; ++r) sX[(16 * b + r) * LDC + 16 * b + j] = xs[r];
         }
@@ -360,12 +361,12 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(const DeltaArgs a)
 // ------------------------------------------------------------------------------------
 // delta_fused_kernel: both halves in one workgroup (chunks of 16 or 32 tokens)
 // ------------------------------------------------------------------------------------
-// One workgroup per (head, 64 value columns) walks the chunks in order.  While its
+// One workgroup per (head, 64 value columns) walks the chunks in order.  While four
 // waves carry the state through chunk n (U = U~ + (-W) S, the outputs, S += K^T U,
-// as delta_scan_kernel), they also solve chunk n+1's triangular system (N, the
-// diagonal-block inverses, the block below the diagonal, then -W and U~ into LDS, as
-// delta_prep_kernel), one step of each between consecutive barriers, so the two
-// interleave and nothing goes through global memory.  N (strictly lower) and X^T
+// as delta_scan_kernel), four other waves solve chunk n+1's triangular system (N,
+// the diagonal-block inverses, the block below the diagonal, then -W and U~ into
+// LDS, as delta_prep_kernel), one step of each between consecutive barriers, so the
+// two run side by side and nothing goes through global memory.  N (strictly lower) and X^T
 // (upper triangle with the diagonal) share one fp32 array: the inverse of a unit
 // lower-triangular block is lower triangular, so its transpose fills exactly the
 // positions N leaves free.
@@ -391,7 +392,7 @@ constexpr int delta_fused_lds()
 }
 
 template <typename T, int DK, int C>
-__global__ __launch_bounds__(256, 2) void delta_fused_kernel(const DeltaArgs a)
+__global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
 {
     typedef DeltaFusedShape<T, DK, C> SH;
     constexpr int ES = SH::ES, CE = SH::CE, NB = SH::NB, NKB = SH::NKB;
@@ -402,16 +403,20 @@ __global__ __launch_bounds__(256, 2) void delta_fused_kernel(const DeltaArgs a)
     __shared__ __align__(16) float sNX[C * LDC];       // N (strictly lower) and X^T (upper)
     __shared__ __align__(16) float sBt[2][C];          // write strengths
 
+    // waves 0-3 solve the chunks' systems (and load their rows); waves 4-7 carry the
+    // state, wave 4 + c owning value columns 16 c .. 16 c + 15 of the tile
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int x = lane & 15, grp = lane >> 4;
+    const bool solver = w < 4;                         // wave-uniform
+    const int wc = w - 4;
     int wgi = blockIdx.x;
     if (a.xcd_remap) wgi = (wgi & 7) * (gridDim.x >> 3) + (wgi >> 3);
     const int bh = wgi / a.n_vt, vt = wgi - bh * a.n_vt;
     const int L = a.L, DV = a.d_v, DVT = a.dvt;
     const int nch = (L + C - 1) / C;
     const size_t hrow = (size_t)bh * L;
-    const int j0 = vt * DVT + 16 * w;
-    const bool active = 16 * w < DVT;                  // wave-uniform
+    const int j0 = vt * DVT + 16 * wc;
+    const bool active = !solver && 16 * wc < DVT;      // wave-uniform
     const int VP = C * DVT / CE;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -488,14 +493,13 @@ __global__ __launch_bounds__(256, 2) void delta_fused_kernel(const DeltaArgs a)
         if (w < NB && lane < 16) {
             const int b = w, j = lane;
             const float *nb = sNX + 16 * b * LDC + 16 * b;
-            float xs[16];
+            float xs[16];                              // column-wise, as in delta_prep_kernel
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = r == j ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) xs[r] = r == j ? 1.f : 0.f;
 #pragma unroll
-                for (int mm = 0; mm < r; ++mm) acc -= nb[r * LDC + mm] * xs[mm];
-                xs[r] = acc;
-            }
+            for (int mm = 0; mm < 16; ++mm)
+#pragma unroll
+                for (int r = mm + 1; r < 16; ++r) xs[r] -= nb[r * LDC + mm] * xs[mm];
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (r >= j) sNX[(16 * b + j) * LDC + 16 * b + r] = xs[r];
@@ -567,7 +571,7 @@ __global__ __launch_bounds__(256, 2) void delta_fused_kernel(const DeltaArgs a)
         }
     }
     auto scanU = [&](int n) {            // U = U~ + (-W) S
-        const T *sW = bW(n), *sU = bU(n) + 16 * w * LDU;
+        const T *sW = bW(n), *sU = bU(n) + 16 * wc * LDU;
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             f32x4 acc = widen4(lds_frag(sU + x * LDU, tb, grp));
@@ -617,22 +621,26 @@ __global__ __launch_bounds__(256, 2) void delta_fused_kernel(const DeltaArgs a)
     };
 
     if (nch > 0) {
-        fetch(0);
-        stash(0);
+        if (solver) {
+            fetch(0);
+            stash(0);
+        }
         lds_barrier();
-        solveA(0);
+        if (solver) solveA(0);
         lds_barrier();
-        solveB();
+        if (solver) solveB();
         lds_barrier();
-        solveC();
+        if (solver) solveC();
         lds_barrier();
-        solveD(0);
-        if (nch > 1) fetch(1);
+        if (solver) {
+            solveD(0);
+            if (nch > 1) fetch(1);
+        }
     }
     for (int n = 0; n < nch; ++n) {
-        const bool more = n + 1 < nch;                 // uniform
+        const bool more = solver && n + 1 < nch;       // wave-uniform
         if (more) stash(n + 1);
-        if (n + 2 < nch) fetch(n + 2);
+        if (solver && n + 2 < nch) fetch(n + 2);
         lds_barrier();                                 // chunk n's -W, U~ and chunk n+1's rows visible
         if (more) solveA(n + 1);
         if (active) scanU(n);
@@ -743,7 +751,7 @@ static hipError_t launch_delta_fused(const DeltaArgs &a, hipStream_t stream)
 #define GLA_FUSED(DK)                                                                                \
     case DK:                                                                                         \
         static_assert(delta_fused_lds<T, DK, C>() <= kLdsBytes, "fused delta LDS");                 \
-        hipLaunchKernelGGL((delta_fused_kernel<T, DK, C>), dim3(grid), dim3(256), 0, stream, a);     \
+        hipLaunchKernelGGL((delta_fused_kernel<T, DK, C>), dim3(grid), dim3(512), 0, stream, a);     \
         break;
     switch (a.d_k) {
     GLA_FUSED(16) GLA_FUSED(32) GLA_FUSED(64) GLA_FUSED(128)
