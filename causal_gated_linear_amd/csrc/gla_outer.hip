@@ -581,7 +581,7 @@ __global__ __launch_bounds__(256) void outer_decode_kernel(const OuterArgs a)
     f32x4 *st = (f32x4 *)(a.s_final + bh * DK * DV) + c;
     f32x4 s[NPASS];
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) s[p] = st[(size_t)(r0 + p * RS) * CQ];
+    for (int p = 0; p < NPASS; ++p) s[p] = __builtin_nontemporal_load(st + (size_t)(r0 + p * RS) * CQ);
     __syncthreads();
 
     f32x4 op = {0.f, 0.f, 0.f, 0.f};
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(256) void outer_decode_kernel(const OuterArgs a)
     for (int p = 0; p < NPASS; ++p) {
         const int i = r0 + p * RS;
         s[p] = sa[i] * (bv * s[p]) + sk[i] * v;
-        st[(size_t)i * CQ] = s[p];
+        __builtin_nontemporal_store(s[p], st + (size_t)i * CQ);
         op += sq[i] * s[p];
     }
     sred[r0][c] = op;
