@@ -17,8 +17,9 @@
 // accumulator tiles of zd^T are then, unchanged, the right operand of the
 // up-projection z^T = W_up zd^T, which runs on the matrix cores one 16-row tile of
 // W_up at a time; each tile's outputs go through log-sigmoid and are stored
-// as 16-byte row pieces.  The write of g (4 bytes per token and key dimension)
-// dominates the traffic.
+// as 16-byte row pieces, non-temporally (g is written once and read by a later
+// kernel, far beyond the caches).  The write of g (4 bytes per token and key
+// dimension) dominates the traffic.
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
 
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void gate_project_kernel(const GateArgs a)
             f32x4 g;
 #pragma unroll
             for (int e = 0; e < 4; ++e) g[e] = log_sigmoid(z[e]) * inv_tau;
-            if (store) *(f32x4 *)(gt + h * hstride + i) = g;
+            if (store) __builtin_nontemporal_store(g, (f32x4 *)(gt + h * hstride + i));   // streamed once
         }
     }
 }
