@@ -1,7 +1,9 @@
 """Writes ``prefill_4token.json``: a four-token prefill x_0..x_3 (the shape of the
 worked example in "Attention is recurrent", section Prefill, whose numbers did not
 survive the page) with small rational inputs and key-dimension gates, and the outputs
-the fp64 oracle computes for it.  Calls only ``oracle/``.
+the fp64 oracle computes for it; and ``delta_4token.json``: the same four-token shape
+under the delta rule (the page's Delta attention and the Prefill section after it,
+again with its numbers lost), with rational write strengths.  Calls only ``oracle/``.
 
 Run from the repository root:  python -m tests.golden.make_golden
 """
@@ -28,6 +30,20 @@ def main():
     case = dict(source="oracle/gla_oracle.c via tests/golden/make_golden.py",
                 q=q, k=k, v=v, alpha=alpha, o=o[0, 0].tolist(), s_final=s[0, 0].tolist())
     with open(os.path.join(HERE, "prefill_4token.json"), "w") as f:
+        json.dump(case, f, indent=1)
+        f.write("\n")
+
+    # the delta rule: four tokens, d_k = 3, d_v = 2, S_{-1} = 0 as on the page
+    kd = [[1, 0, 0], [1, 1, 0], [0, 1, 1], [1, 0, 1]]
+    qd = [[0, 1, 1], [1, 0, -1], [2, 1, 0], [1, 1, 1]]
+    vd = [[1, 2], [-1, 0], [3, 1], [0, -2]]
+    beta = ["1/2", "1/4", "3/4", "1"]
+    b = np.array([float(Fraction(x)) for x in beta])
+    o, s = oracle.forward_delta(np.array(qd, float).reshape(1, 1, 4, 3), np.array(kd, float).reshape(1, 1, 4, 3),
+                                np.array(vd, float).reshape(1, 1, 4, 2), b.reshape(1, 1, 4))
+    case = dict(source="oracle/gla_oracle.c via tests/golden/make_golden.py",
+                q=qd, k=kd, v=vd, beta=beta, o=o[0, 0].tolist(), s_final=s[0, 0].tolist())
+    with open(os.path.join(HERE, "delta_4token.json"), "w") as f:
         json.dump(case, f, indent=1)
         f.write("\n")
 

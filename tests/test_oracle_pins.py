@@ -140,3 +140,50 @@ def test_golden_prefill_4token():
                           np.array(case["v"], float).reshape(1, 1, L, dv),
                           g=np.log(alpha).reshape(1, 1, L, dk), gate="keydim")
     assert pins.rel_err(o[0, 0], want) < 1e-14
+
+
+def _gauss_jordan(A, B):
+    """Exact solution X of A X = B in Fractions by Gauss-Jordan elimination with row
+    pivoting (a general solver: it does not use A's triangular structure)."""
+    n, m = len(A), len(B[0])
+    M = [list(A[i]) + list(B[i]) for i in range(n)]
+    for c in range(n):
+        piv = next(r for r in range(c, n) if M[r][c] != 0)
+        M[c], M[piv] = M[piv], M[c]
+        inv = 1 / M[c][c]
+        M[c] = [x * inv for x in M[c]]
+        for r in range(n):
+            if r != c and M[r][c] != 0:
+                f = M[r][c]
+                M[r] = [x - f * y for x, y in zip(M[r], M[c])]
+    return [row[n:] for row in M]
+
+
+def test_golden_delta_4token():
+    """A four-token delta prefill (the shape of the page's Delta attention / Prefill
+    example, whose numbers did not survive): the stored outputs, written by
+    ``golden/make_golden.py`` from the oracle, must equal exact rational arithmetic on
+    the page's lower-triangular system (T U = diag(beta) V with
+    T = I + tril(diag(beta) K K^T, -1), O = tril(Q K^T) U, S = K^T U), solved by a
+    general elimination; and the oracle must still reproduce them."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "delta_4token.json")) as f:
+        case = json.load(f)
+    Q = [[Fraction(x) for x in r] for r in case["q"]]
+    K = [[Fraction(x) for x in r] for r in case["k"]]
+    V = [[Fraction(x) for x in r] for r in case["v"]]
+    be = [Fraction(x) for x in case["beta"]]
+    L, dk, dv = len(Q), len(Q[0]), len(V[0])
+    dot = lambda a, b: sum(x * y for x, y in zip(a, b))
+    T = [[Fraction(int(i == j)) + (be[i] * dot(K[i], K[j]) if j < i else 0) for j in range(L)] for i in range(L)]
+    U = _gauss_jordan(T, [[be[i] * V[i][j] for j in range(dv)] for i in range(L)])
+    O = [[sum(dot(Q[t], K[s]) * U[s][j] for s in range(t + 1)) for j in range(dv)] for t in range(L)]
+    S = [[sum(K[s][i] * U[s][j] for s in range(L)) for j in range(dv)] for i in range(dk)]
+    exact_o = np.array([[float(x) for x in r] for r in O])
+    exact_s = np.array([[float(x) for x in r] for r in S])
+    want_o, want_s = np.array(case["o"]), np.array(case["s_final"])
+    assert pins.rel_err(want_o, exact_o) < 1e-14 and pins.rel_err(want_s, exact_s) < 1e-14
+    o, s = oracle.forward_delta(np.array(case["q"], float).reshape(1, 1, L, dk),
+                                np.array(case["k"], float).reshape(1, 1, L, dk),
+                                np.array(case["v"], float).reshape(1, 1, L, dv),
+                                np.array([float(x) for x in be]).reshape(1, 1, L))
+    assert pins.rel_err(o[0, 0], want_o) < 1e-14 and pins.rel_err(s[0, 0], want_s) < 1e-14
