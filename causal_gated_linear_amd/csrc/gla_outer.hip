@@ -44,6 +44,12 @@ struct OuterShape {
     static constexpr int ES = sizeof(T), CE = 16 / ES, PAD = pad_of<T>();
     static constexpr int NB = C / 16, NKB = DK / 16, DVT = 64;
     static constexpr int LDK = DK + PAD, LDV = DVT + PAD;      // T rows
+    // key rows of the producer/consumer kernel, whose accesses to them are all 8 bytes
+    // wide: with bf16 a pad of 12 makes the row stride an odd multiple of 8 bytes, so
+    // the 16 lanes of an 8-byte row read hit 16 different bank pairs (gfx950 serves
+    // them together over 128 bytes); transposing reads and the producers' writes stay
+    // within 2-way conflicts
+    static constexpr int LDKP = DK + (ES == 2 ? 12 : PAD);
     static constexpr int LDG = DK + 4, LDGV = DVT + 4;         // fp32 rows
     // 16-byte pieces per chunk, and per thread (256 threads)
     static constexpr int PQ = C * DK / CE, PG = C * DK / 4;
@@ -335,7 +341,7 @@ template <typename T, int DK, int C>
 constexpr int outer_pc_lds()
 {
     typedef OuterShape<T, DK, C> SH;
-    return 2 * ((2 * C * SH::LDK + C * SH::LDV) * (int)sizeof(T) + (C * SH::LDGV + DK + SH::DVT) * 4);
+    return 2 * ((2 * C * SH::LDKP + C * SH::LDV) * (int)sizeof(T) + (C * SH::LDGV + DK + SH::DVT) * 4);
 }
 
 template <typename T> __device__ __forceinline__ typename Frag<T>::type buf_load_frag(Rsrc r, int off);
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(512) void outer_pc_kernel(const OuterArgs a)
 {
     typedef OuterShape<T, DK, C> SH;
     constexpr int ES = SH::ES, NB = SH::NB, NKB = SH::NKB;
-    constexpr int LDK = SH::LDK, LDV = SH::LDV, LDGV = SH::LDGV;
+    constexpr int LDK = SH::LDKP, LDV = SH::LDV, LDGV = SH::LDGV;
     constexpr int KNCG = DK / 4, KSEG = SH::KSEG, KRPT = C / KSEG;
     constexpr int VNCG = SH::DVT / 4, VSEG = SH::VSEG, VRPT = C / VSEG;
     typedef typename Frag<T>::type F4;
