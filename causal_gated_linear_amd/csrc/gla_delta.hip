@@ -374,7 +374,11 @@ template <typename T, int DK, int C>
 struct DeltaFusedShape {
     static constexpr int ES = sizeof(T), CE = 16 / ES, PAD = row_pad<T>();
     static constexpr int NB = C / 16, NKB = DK / 16, DVT = 64;
-    static constexpr int LDK = DK + PAD;           // Q, K, -W rows
+    // Q, K, -W rows.  With bf16 a pad of 12 makes the row stride an odd multiple of 8
+    // bytes, so the 16 lanes of an 8-byte row read (served together over 128 bytes on
+    // gfx950) hit 16 different bank pairs; rows are then only 8-byte aligned, and every
+    // access to them is 8 bytes wide
+    static constexpr int LDK = DK + (ES == 2 ? 12 : PAD);
     static constexpr int LDU = C + PAD;            // U~^T rows
     static constexpr int LDV = DVT + 16 / ES;      // raw V rows
     static constexpr int LDC = C + 4;              // N / X^T rows (fp32)
@@ -458,8 +462,11 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
             const int p = tid + 256 * i;
             if (QP % 256 == 0 || p < QP) {
                 const int r = p / (DK / CE), c = (p - r * (DK / CE)) * CE;
-                *(i32x4 *)(sQ + r * LDK + c) = gq[i];
-                *(i32x4 *)(sK + r * LDK + c) = gk[i];
+                typedef int i32x2 __attribute__((ext_vector_type(2)));
+                *(i32x2 *)(sQ + r * LDK + c) = i32x2{gq[i][0], gq[i][1]};    // 8-byte aligned rows
+                *(i32x2 *)(sQ + r * LDK + c + CE / 2) = i32x2{gq[i][2], gq[i][3]};
+                *(i32x2 *)(sK + r * LDK + c) = i32x2{gk[i][0], gk[i][1]};
+                *(i32x2 *)(sK + r * LDK + c + CE / 2) = i32x2{gk[i][2], gk[i][3]};
             }
         }
 #pragma unroll
