@@ -112,7 +112,7 @@ template <> struct Op<float> {
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
 // swizzle codes of PrefillShape::swz beyond plain row masks
-constexpr int kSwz16 = 0x100, kSwzV8 = 0x101, kSwzO8 = 0x102;
+constexpr int kSwz16 = 0x100, kSwz8 = 0x101, kSwzO8 = 0x102;
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <typename T, int DK, int C, int DVT>
@@ -136,10 +136,10 @@ struct PrefillShape {
     static constexpr int KSTEPS = (DK + SW - 1) / SW;
     static constexpr int CSTEPS = (C + SW - 1) / SW;
     static constexpr int KCH = DK / CE, VCH = DVT / CE;   // 16-byte chunks per row
-    // swizzle codes (see swz): rows of at least 16 chunks use kSwz16; value rows of 8
-    // chunks use kSwzV8; narrower rows mask the row bits
-    static constexpr int SWK = KCH >= 16 ? kSwz16 : cmin(KCH, 8) - 1;
-    static constexpr int SWV = VCH >= 16 ? kSwz16 : (VCH == 8 ? kSwzV8 : VCH - 1);
+    // swizzle codes (see swz): rows of at least 16 chunks use kSwz16, operand rows of
+    // 8 chunks kSwz8; narrower rows mask the row bits
+    static constexpr int SWK = KCH >= 16 ? kSwz16 : (KCH == 8 ? kSwz8 : KCH - 1);
+    static constexpr int SWV = VCH >= 16 ? kSwz16 : (VCH == 8 ? kSwz8 : VCH - 1);
     // producer gate mapping: producer p owns key columns [p*CW, (p+1)*CW); a lane
     // has column group cg (one 16-byte chunk, CE columns) and row segment rs (RPS
     // consecutive rows); column groups vary fastest across lanes
@@ -179,18 +179,18 @@ struct PrefillShape {
     //   kSwz16 (rows of 16 or more chunks): r0 | r1 << 1 | (r0 ^ r2) << 2 | (r0 ^ r3) << 3
     //     -- fragment reads of 16 rows, transposing reads of 8 rows and the producers'
     //        row-piece writes touch every bank once;
-    //   kSwzV8 (value rows of 8 chunks): row & 6 -- transposing reads of 8 rows hit
-    //     distinct 32-byte bank groups;
+    //   kSwz8 (operand rows of 8 chunks): row & 6 -- transposing reads of 8 rows hit
+    //     distinct 32-byte bank groups, and fragment reads and row-piece writes touch
+    //     every bank once;
     //   kSwzO8 (output staging rows of 8 chunks): row & 7 -- the 16-byte read-back of
     //     two rows per 16 lanes hits every bank once;
-    //   7 (key rows of 8 chunks): (row & 3) << 1 | (row >> 2) & 1;
     //   otherwise row & sw.
     static __device__ __forceinline__ int swz(int row, int sw)
     {
         if (sw == kSwz16) return (row & 3) | ((((row >> 2) ^ row) & 1) << 2) | ((((row >> 3) ^ row) & 1) << 3);
-        if (sw == kSwzV8) return row & 6;
+        if (sw == kSwz8) return row & 6;
         if (sw == kSwzO8) return row & 7;
-        return sw == 7 ? (((row & 3) << 1) | ((row >> 2) & 1)) : (row & sw);
+        return row & sw;
     }
     static __device__ __forceinline__ int sw_off(int row, int col, int len, int sw)
     {
