@@ -438,14 +438,26 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     widen<T, CE>(r_.k[r], kk);
 #pragma unroll
                     for (int e = 0; e < CE; ++e) {
-                        if constexpr (ELU1) {
-                            if constexpr (!SO) q[e] = feature(q[e], true);
-                            kk[e] = feature(kk[e], true);
-                        }
-                        if constexpr (GATE == kGateKeydim) {
+                        if constexpr (ELU1 && GATE == kGateKeydim) {
+                            // phi(x) 2^(+-b) with one exponential: (x + 1) 2^(+-b) for
+                            // x > 0, else 2^(x log2(e) +- b)
                             const float b = excl[e] + bc[r][e];
-                            if constexpr (!SO) q[e] *= exp2_fast(b);
-                            kk[e] *= exp2_fast(-b);
+                            if constexpr (!SO) {
+                                const float x = q[e];
+                                q[e] = (x > 0.f ? x + 1.f : 1.f) * exp2_fast(x > 0.f ? b : fmaf(x, kLog2e, b));
+                            }
+                            const float x = kk[e];
+                            kk[e] = (x > 0.f ? x + 1.f : 1.f) * exp2_fast(x > 0.f ? -b : fmaf(x, kLog2e, -b));
+                        } else {
+                            if constexpr (ELU1) {
+                                if constexpr (!SO) q[e] = feature(q[e], true);
+                                kk[e] = feature(kk[e], true);
+                            }
+                            if constexpr (GATE == kGateKeydim) {
+                                const float b = excl[e] + bc[r][e];
+                                if constexpr (!SO) q[e] *= exp2_fast(b);
+                                kk[e] *= exp2_fast(-b);
+                            }
                         }
                     }
                     VC qv, kv;

@@ -83,6 +83,16 @@ def test_prefill_dims(dtype, dk, dv, gate):
     _check_all_heads(w, 2, 2, 150, seed=dk * 1000 + dv + (0 if gate is None else len(gate)), with_s0=True)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(32, 64), (128, 128), (64, 16)])
+@pytest.mark.parametrize("gate", ["keydim", "scalar"])
+def test_prefill_elu1_with_gates(dtype, dk, dv, gate):
+    """phi = elu + 1 together with gates (the key-dimension path forms phi(x) e^(+-B)
+    with one exponential), against the oracle's phi then gate."""
+    w = inputs.Workload("elu1_gated", dtype, 2, 2, 150, dk, dv, 64, gate, "elu1", True, seed=0)
+    _check_all_heads(w, 2, 2, 150, seed=7 * dk + dv + len(gate), with_s0=True)
+
+
 def test_prefill_empty_sequence_copies_state():
     w = W["gla_prefill"]
     s0 = inputs.draw_state(2, 3, 128, 128, seed=5).to(DEV)
