@@ -96,6 +96,16 @@ def _events_ms(fn, n, stream):
     return start.elapsed_time(stop)
 
 
+def _settle(torch, step, seconds):
+    """Untimed launches of ``step`` for at least ``seconds`` (one at a time), so that a
+    workload is timed in its steady state: the first launches after a switch of
+    workload and inputs run measurably slower."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        step()
+        torch.cuda.synchronize()
+
+
 def run_prefill(args, torch, api, inputs):
     w = inputs.WORKLOADS["gla_prefill"]
     inp = inputs.draw(w, device="cuda")
@@ -147,6 +157,7 @@ def run_other_prefills(args, torch, api, inputs):
             api.prefill(inp["q"], inp["k"], inp["v"], log_gate=inp["g"], gate=w.gate, chunk=w.chunk,
                         feature_map=w.feature_map, out=o, final_state=s, stream=stream)
 
+        _settle(torch, step, args.settle_s / 4)
         for _ in range(3):
             step()
         torch.cuda.synchronize()
@@ -173,6 +184,7 @@ def run_other_prefills(args, torch, api, inputs):
         api.prefill_norm(inp["q"], inp["k"], inp["v"], log_gate=inp["g"], gate="keydim", chunk=w.chunk,
                          feature_map="elu1", out=o, final_state=s, final_norm=z, stream=stream)
 
+    _settle(torch, step_norm, args.settle_s / 4)
     for _ in range(3):
         step_norm()
     torch.cuda.synchronize()
@@ -244,6 +256,7 @@ def run_delta(args, torch, api, inputs):
         api.prefill_delta(inp["q"], inp["k"], inp["v"], inp["beta"], chunk=w.chunk, out=o, final_state=s,
                           workspace=ws, stream=stream)
 
+    _settle(torch, step, args.settle_s / 4)
     for _ in range(3):
         step()
     torch.cuda.synchronize()
@@ -296,6 +309,7 @@ def run_gate(args, torch, api, inputs):
     def step():
         api.gate_project(d["x"], d["w_down"], d["w_up"], w["H"], w["d_k"], tau=w["tau"], out=g, stream=stream)
 
+    _settle(torch, step, args.settle_s / 4)
     for _ in range(3):
         step()
     torch.cuda.synchronize()
@@ -330,6 +344,7 @@ def run_outer(args, torch, api, inputs):
             api.prefill_outer(inp["q"], inp["k"], inp["v"], inp["g"], gv, chunk=chunk, out=o, final_state=s,
                               stream=stream)
 
+        _settle(torch, step, args.settle_s / 4)
         for _ in range(3):
             step()
         torch.cuda.synchronize()

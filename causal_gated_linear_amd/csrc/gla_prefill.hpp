@@ -609,6 +609,21 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         F qf[SH::KSTEPS];
 #pragma unroll
         for (int k = 0; k < SH::KSTEPS; ++k) qf[k] = frag_k(Q, t, k);
+        // normalised: this lane's share of Q~_t . z, formed before the score products
+        // so that it overlaps them, as four partial sums (a short dependent chain)
+        float dz = 0.f;
+        if constexpr (NM) {
+            float dzp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < SH::KSTEPS; ++k) {
+                constexpr int NE = sizeof(F) / sizeof(T);
+                const int i0 = SH::SW * k + (SH::BF ? 8 : 4) * grp;
+#pragma unroll
+                for (int e = 0; e < NE; ++e)
+                    if (!SH::BF || DK % 32 == 0 || i0 + e < DK) dzp[e & 3] += to_f32(qf[k][e]) * sZ[par][i0 + e];
+            }
+            dz = (dzp[0] + dzp[1]) + (dzp[2] + dzp[3]);
+        }
         // score tiles P^T[s-block sb][t-block TB]: lane holds P[t][16sb + 4grp + r]
         f32x4 pt[TB + 2];
         // the next s-block's key fragments are requested before the current block's
@@ -645,15 +660,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         // its share, the four lane groups of column x are then added
         float rden = 1.f;
         if constexpr (NM) {
-            float dz = 0.f, dp = 0.f;
-#pragma unroll
-            for (int k = 0; k < SH::KSTEPS; ++k) {
-                constexpr int NE = sizeof(F) / sizeof(T);
-                const int i0 = SH::SW * k + (SH::BF ? 8 : 4) * grp;
-#pragma unroll
-                for (int e = 0; e < NE; ++e)
-                    if (!SH::BF || DK % 32 == 0 || i0 + e < DK) dz += to_f32(qf[k][e]) * sZ[par][i0 + e];
-            }
+            float dp = 0.f;
 #pragma unroll
             for (int sb = 0; sb <= TB; ++sb) dp += pt[sb][0] + pt[sb][1] + pt[sb][2] + pt[sb][3];
             float den = dz * inter_scale + dp;
