@@ -59,11 +59,14 @@ template <typename T, int C>
 __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a)
 {
     constexpr int NB = C / 16, CE = 16 / sizeof(T), PAD = row_pad<T>();
-    constexpr int LDM = 128 + PAD;                 // K and V row stride (d_k, d_v <= 128)
+    // K rows (8-byte row reads and transposing reads; with bf16 a pad of 12 gives an
+    // odd multiple of 8 bytes, conflict-free for the row reads on gfx950) and V rows
+    // (transposing reads only, conflict-free with a pad of 16); d_k, d_v <= 128
+    constexpr int LDMK = 128 + (sizeof(T) == 2 ? 12 : PAD), LDMV = 128 + PAD;
     constexpr int LDC = C + 4;                     // N and X row stride (fp32)
     typedef typename Frag<T>::type F4;
-    __shared__ __align__(16) T sK[C * LDM];
-    __shared__ __align__(16) T sV[C * LDM];
+    __shared__ __align__(16) T sK[C * LDMK];
+    __shared__ __align__(16) T sV[C * LDMV];
     __shared__ __align__(16) float sN[C * LDC];
     __shared__ __align__(16) float sX[C * LDC];
     __shared__ __align__(16) float sB[C];
@@ -84,13 +87,15 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a)
             const int r = e / kc, c = (e - r * kc) * CE;
             i32x4 val = {0, 0, 0, 0};
             if (r < nvalid) val = *(const i32x4 *)(kg + (size_t)r * dk + c);
-            *(i32x4 *)(sK + r * LDM + c) = val;
+            typedef int i32x2 __attribute__((ext_vector_type(2)));
+            *(i32x2 *)(sK + r * LDMK + c) = i32x2{val[0], val[1]};          // 8-byte aligned rows
+            *(i32x2 *)(sK + r * LDMK + c + CE / 2) = i32x2{val[2], val[3]};
         }
         for (int e = tid; e < C * vc; e += 256) {
             const int r = e / vc, c = (e - r * vc) * CE;
             i32x4 val = {0, 0, 0, 0};
             if (r < nvalid) val = *(const i32x4 *)(vg + (size_t)r * dv + c);
-            *(i32x4 *)(sV + r * LDM + c) = val;
+            *(i32x4 *)(sV + r * LDMV + c) = val;
         }
         if (tid < C) sB[tid] = tid < nvalid ? a.beta[hrow + tid] : 0.f;
     }
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a)
         while ((tb + 1) * (tb + 2) / 2 <= id) ++tb;
         const int sb = id - tb * (tb + 1) / 2;
         // lane (x, grp) element e: (K K^T)[16 tb + 4 grp + e][16 sb + x]
-        const f32x4 g = contract_rows(sK + (16 * tb + x) * LDM, sK + (16 * sb + x) * LDM, dk / 16, grp, zero);
+        const f32x4 g = contract_rows(sK + (16 * tb + x) * LDMK, sK + (16 * sb + x) * LDMK, dk / 16, grp, zero);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * tb + 4 * grp + e, s = 16 * sb + x;
@@ -168,18 +173,18 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a)
             // lane (x, grp) element e: W^T[16 cb + 4 grp + e][16 tb + x] = W[t][i..i+3]
             int sb = 0;
             for (; sb + 1 <= tb; sb += 2)
-                acc = mac2(col_frag(sK, LDM, 16 * sb + 4 * grp, 16 * cb, x),
-                           col_frag(sK, LDM, 16 * (sb + 1) + 4 * grp, 16 * cb, x), xb(tb, sb), xb(tb, sb + 1), acc);
-            if (sb <= tb) acc = mac1(col_frag(sK, LDM, 16 * sb + 4 * grp, 16 * cb, x), xb(tb, sb), acc);
+                acc = mac2(col_frag(sK, LDMK, 16 * sb + 4 * grp, 16 * cb, x),
+                           col_frag(sK, LDMK, 16 * (sb + 1) + 4 * grp, 16 * cb, x), xb(tb, sb), xb(tb, sb + 1), acc);
+            if (sb <= tb) acc = mac1(col_frag(sK, LDMK, 16 * sb + 4 * grp, 16 * cb, x), xb(tb, sb), acc);
             store4(wg + (size_t)(16 * tb + x) * dk + 16 * cb + 4 * grp, -acc);
         } else {
             const int jb = cb - nkb;
             // lane (x, grp) element e: U~[16 tb + 4 grp + e][16 jb + x] = U~^T[j][t..t+3]
             int sb = 0;
             for (; sb + 1 <= tb; sb += 2)
-                acc = mac2(xb(tb, sb), xb(tb, sb + 1), col_frag(sV, LDM, 16 * sb + 4 * grp, 16 * jb, x),
-                           col_frag(sV, LDM, 16 * (sb + 1) + 4 * grp, 16 * jb, x), acc);
-            if (sb <= tb) acc = mac1(xb(tb, sb), col_frag(sV, LDM, 16 * sb + 4 * grp, 16 * jb, x), acc);
+                acc = mac2(xb(tb, sb), xb(tb, sb + 1), col_frag(sV, LDMV, 16 * sb + 4 * grp, 16 * jb, x),
+                           col_frag(sV, LDMV, 16 * (sb + 1) + 4 * grp, 16 * jb, x), acc);
+            if (sb <= tb) acc = mac1(xb(tb, sb), col_frag(sV, LDMV, 16 * sb + 4 * grp, 16 * jb, x), acc);
             store4(ug + (size_t)(16 * jb + x) * C + 16 * tb + 4 * grp, acc);
         }
     }
@@ -192,7 +197,9 @@ template <typename T, int DK, int C>
 struct DeltaScanShape {
     static constexpr int ES = sizeof(T), CE = 16 / ES, PAD = row_pad<T>();
     static constexpr int NB = C / 16, NKB = DK / 16;
-    static constexpr int LDK = DK + PAD;           // Q, K, -W row stride
+    // Q, K, -W rows: with bf16 a pad of 12 gives an odd multiple of 8 bytes, so the
+    // 8-byte row reads are conflict-free on gfx950; every access to them is 8 bytes
+    static constexpr int LDK = DK + (ES == 2 ? 12 : PAD);
     static constexpr int LDU = C + PAD;            // U~^T row stride
     static constexpr int DVT_MAX = 64;
     static constexpr int BUF = 3 * C * LDK + DVT_MAX * LDU;   // elements per buffer
@@ -255,9 +262,13 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(const DeltaArgs a)
             const int p = tid + 256 * i;
             if (QP % 256 == 0 || p < QP) {
                 const int r = p / (DK / CE), c = (p - r * (DK / CE)) * CE;
-                *(i32x4 *)(sQ + r * LDK + c) = gq[i];
-                *(i32x4 *)(sK + r * LDK + c) = gk[i];
-                *(i32x4 *)(sW + r * LDK + c) = gw[i];
+                typedef int i32x2 __attribute__((ext_vector_type(2)));
+                *(i32x2 *)(sQ + r * LDK + c) = i32x2{gq[i][0], gq[i][1]};    // 8-byte aligned rows
+                *(i32x2 *)(sQ + r * LDK + c + CE / 2) = i32x2{gq[i][2], gq[i][3]};
+                *(i32x2 *)(sK + r * LDK + c) = i32x2{gk[i][0], gk[i][1]};
+                *(i32x2 *)(sK + r * LDK + c + CE / 2) = i32x2{gk[i][2], gk[i][3]};
+                *(i32x2 *)(sW + r * LDK + c) = i32x2{gw[i][0], gw[i][1]};
+                *(i32x2 *)(sW + r * LDK + c + CE / 2) = i32x2{gw[i][2], gw[i][3]};
             }
         }
 #pragma unroll
