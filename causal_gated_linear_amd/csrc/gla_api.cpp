@@ -319,14 +319,18 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
         char *w = (char *)workspace;
         float *ds = (float *)w, *sin = (float *)(w + gla::round256(states));
         float *gam = (float *)(w + 2 * gla::round256(states));
-        gla::PrefillArgs a1 = a;                   // pass 1: segment states from zero
+        // pass 1: the states from zero of every segment but the last (whose state
+        // only feeds s_final, which pass 2 writes)
+        gla::PrefillArgs a1 = a;
         a1.s0 = nullptr; a1.s_final = ds; a1.o = nullptr; a1.gam = gam;
+        a1.nseg = plan.nseg - 1;
+        a1.xcd_remap = (a1.n_vt > 1 && ((long)BH * a1.nseg * a1.n_vt) % 8 == 0) ? 1 : 0;
         e = gla::launch_prefill(a1, dt, d_k, chunk, plan.dvt, true, hs);
-        if (e == hipSuccess)                       // scan over segments
-            e = gla::launch_segment_scan(ds, gate == GLA_GATE_NONE ? nullptr : gam, s0, sin, s_final,
+        if (e == hipSuccess)                       // scan over segments: initial states
+            e = gla::launch_segment_scan(ds, gate == GLA_GATE_NONE ? nullptr : gam, s0, sin,
                                          (int)BH, plan.nseg, d_k, d_v, hs);
         gla::PrefillArgs a2 = a;                   // pass 2: outputs of every segment
-        a2.s0 = sin; a2.s_final = nullptr;
+        a2.s0 = sin; a2.s_final = s_final; a2.final_last_seg = 1;
         if (e == hipSuccess) e = gla::launch_prefill(a2, dt, d_k, chunk, plan.dvt, false, hs);
     }
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

@@ -24,6 +24,9 @@ struct PrefillArgs {
     // then indexed [BH][nseg][d_k][d_v].  nseg = 1, seg_len = L: whole sequences.
     int nseg, seg_len;
     float *gam;              // state-only pass: segment totals of the log2-gates [BH][nseg][d_k]
+    // 1: only the last segment's workgroups store their final state, into s_final
+    // indexed [BH][d_k][d_v] (the full pass of a segmented prefill)
+    int final_last_seg = 0;
     // normalised form: outputs divided by phi(q) . z, z the normaliser state
     int norm;
     const float *z0;         // [B][H][d_k] or null
@@ -77,11 +80,11 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, i
                           bool state_only, hipStream_t stream);
 
 // Enqueue the scan over segments: for every head and state element, in segment
-// order, sin[seg] = S; S = exp2(gam[seg]) * S + ds[seg], from S = s0 (or 0); then
-// s_final = S (if not null).  gam may be null (no gate).
+// order, sin[seg] = S; S = exp2(gam[seg]) * S + ds[seg], from S = s0 (or 0).  ds and
+// gam hold the nseg - 1 first segments ([BH][nseg - 1][...]); the last segment's
+// final state comes from the full pass.  gam may be null (no gate).
 hipError_t launch_segment_scan(const float *ds, const float *gam, const float *s0, float *sin,
-                               float *s_final, int BH, int nseg, int d_k, int d_v,
-                               hipStream_t stream);
+                               int BH, int nseg, int d_k, int d_v, hipStream_t stream);
 
 // Enqueue one decode step.  Sizes must already be valid.
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int d_k, int d_v, hipStream_t stream);

@@ -857,7 +857,8 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 lds_barrier();
             }
         }
-        if (a.s_final) {
+        if (a.s_final && (!a.final_last_seg || seg == a.nseg - 1)) {
+            const size_t sh = a.final_last_seg ? (size_t)bh : (size_t)bhs;
 #pragma unroll
             for (int k = 0; k < NSLOT; ++k) {
                 if (tile_ok(k)) {
@@ -865,7 +866,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = 16 * it + 4 * grp + r;
-                        a.s_final[((size_t)bhs * DK + i) * DV + vt * DVT + 16 * jt + x] = S[k][r];
+                        a.s_final[(sh * DK + i) * DV + vt * DVT + 16 * jt + x] = S[k][r];
                     }
                 }
             }
