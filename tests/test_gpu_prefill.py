@@ -221,6 +221,30 @@ def test_prefill_segment_counts(monkeypatch, nseg):
     _check_all_heads(W["scalar_long"], 1, 2, 64 * 20 + 3, seed=700 + nseg, with_s0=True)
 
 
+@pytest.mark.parametrize("gate", ["keydim", "scalar"])
+def test_prefill_segmented_weak_gates_carry_state(monkeypatch, gate):
+    """Segments with weak gates, so that the state carried across segments matters:
+    a mistake in the scan over segments (a dropped or misplaced gate total or segment
+    state) would move the later segments' outputs well beyond the tolerance.  With the
+    workloads' own gates the carried state has mostly decayed by the next segment."""
+    monkeypatch.setenv("GLA_PREFILL_SEGMENTS", "3")
+    w = W["gla_prefill"] if gate == "keydim" else W["scalar_long"]
+    B, H, L = 1, 2, 64 * 21                         # three segments of 7 chunks
+    inp = inputs.draw(w, B=B, H=H, L=L, seed=950 + len(gate))
+    inp["g"] = inp["g"] * 0.01                      # weak decay, still <= 0
+    o, s = _run_gpu(w, _to(inp, DEV))
+    ro, rs = oracle.forward(inp["q"], inp["k"], inp["v"], g=inp["g"], gate=gate, feature_map=None)
+    tol = util.TOL[w.dtype]
+    # the last segment restarted from a zero state is far from the whole-sequence result
+    t0 = 64 * 14
+    tail = {key: t[:, :, t0:].contiguous() for key, t in inp.items()}
+    ro_tail, _ = oracle.forward(tail["q"], tail["k"], tail["v"], g=tail["g"], gate=gate, feature_map=None)
+    assert util.head_errors(ro_tail, ro[:, :, t0:]).min() > 10 * tol
+    eo = util.assert_close(o, ro, tol, "%s weak-gate segmented o" % gate)
+    es = util.assert_close(s, rs, tol, "%s weak-gate segmented s_final" % gate)
+    print("%s weak gates, 3 segments: err o %.2e s %.2e" % (gate, eo, es))
+
+
 def test_prefill_segmented_in_place_state():
     """s_final may be s0 on the segmented path too (the scan reads s0 before it writes)."""
     w = W["gla_prefill"]
