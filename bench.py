@@ -96,6 +96,43 @@ def _events_ms(fn, n, stream):
     return start.elapsed_time(stop)
 
 
+PEAKS_SRC = os.path.join(ROOT, "bench_peaks.hip")
+PEAKS_LIB = os.path.join(ROOT, "bench_peaks.so")
+
+
+def build_peaks():
+    """Compile bench_peaks.hip (achievable-peak kernels for this report) for gfx950."""
+    import subprocess
+    hipcc = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc"
+    cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PEAKS_SRC, "-o", PEAKS_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for bench_peaks.hip:\n" + r.stdout + r.stderr)
+    return PEAKS_LIB
+
+
+def achievable_peaks():
+    """This card's achievable HBM rate for the prefill's traffic mix and dense bf16
+    matrix-core rate, measured now (bench_peaks.hip); None where unavailable."""
+    import ctypes
+    out = {"hbm_GBs": None, "mfma_bf16_tflops": None,
+           "note": "bench_peaks.hip: a streaming kernel with the prefill's read:write mix (5:1, "
+                   "non-temporal 16-byte accesses) and a loop of independent bf16 16x16x32 products"}
+    if not os.path.exists(PEAKS_LIB):
+        out["note"] += "; not built"
+        return out
+    lib = ctypes.CDLL(PEAKS_LIB)
+    for name, key in (("peaks_stream", "hbm_GBs"), ("peaks_mfma", "mfma_bf16_tflops")):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(ctypes.c_double)]
+        v = ctypes.c_double(0.0)
+        if fn(ctypes.byref(v)) == 0:
+            out[key] = v.value
+    return out
+
+
 def _settle(torch, step, seconds):
     """Untimed launches of ``step`` for at least ``seconds`` (one at a time), so that a
     workload is timed in its steady state: the first launches after a switch of
@@ -669,6 +706,13 @@ def main():
         line["delta"] = run_delta(args, torch, api, inputs)
         line["gate_producer"] = run_gate(args, torch, api, inputs)
         line["outer_gate"] = run_outer(args, torch, api, inputs)
+    pk = achievable_peaks()
+    hbm_ach, mfma_ach = pk["hbm_GBs"], pk["mfma_bf16_tflops"]
+    line["roofline"]["achievable_peak"] = hbm_ach
+    line["roofline"]["achievable_frac"] = achieved_gbs / hbm_ach if hbm_ach else None
+    line["mfma"]["achievable_peak_tflops"] = mfma_ach
+    line["mfma"]["achievable_frac"] = tflops / mfma_ach if mfma_ach else None
+    line["achievable_peaks"] = pk
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget_s)
     print(json.dumps(line))
