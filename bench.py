@@ -524,6 +524,53 @@ def summarize_traffic(dirs, command):
     print("\n".join(lines))
 
 
+TRAFFIC_ALL_FILE = os.path.join(PROFILES, "gla_kernels_bench_workloads_traffic.txt")
+
+
+def summarize_traffic_all(dirs, command):
+    """HBM traffic of every library kernel in a bench run: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch, summed over counter instances) grouped by (kernel, grid), each
+    scaled by bytes / counter of the calibration copy kernel."""
+    fdir, wdir, cfdir, cwdir = dirs
+    copy_bytes = COPY_MIB * 2**20
+    cf, _, _ = _per_dispatch(_counter_rows(cfdir), "MulFunctor", "FETCH_SIZE")
+    cw, _, _ = _per_dispatch(_counter_rows(cwdir), "MulFunctor", "WRITE_SIZE")
+    kf, kw = copy_bytes / cf, copy_bytes / cw
+
+    def groups(d, counter):
+        per, key = {}, {}
+        for r in _counter_rows(d):
+            name = r["Kernel_Name"]
+            if r["Counter_Name"] != counter or not (name.startswith("_ZN3gla") or "gla::" in name):
+                continue
+            grid = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            key[r["Dispatch_Id"]] = (name, grid)
+        out = {}
+        for disp, v in per.items():
+            out.setdefault(key[disp], []).append(v)
+        return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
+
+    fg, wg = groups(fdir, "FETCH_SIZE"), groups(wdir, "WRITE_SIZE")
+    lines = ["# HBM traffic of the library's kernels for the bench.py workloads, per dispatch",
+             "# (the workloads and their algorithmic bytes per launch are those of bench.py's JSON line:",
+             "#  bytes_per_launch / bytes_per_step; the segmented scalar_long prefill runs three kernels)",
+             "# commands (run from the repository root, each a rocprofv3 --pmc pass of its own):"] + \
+            ["#   " + c for c in command.split(" ;; ")] + \
+            ["# calibration: copy kernel reads and writes %d bytes per launch; fetch scale %.2f, "
+             "write scale %.2f bytes per counter unit" % (copy_bytes, kf, kw), "",
+             "%-8s %-6s %12s %12s %12s  %s" % ("grid", "calls", "fetch_MB", "write_MB", "total_MB", "kernel")]
+    for k in sorted(set(fg) | set(wg), key=lambda k: -((fg.get(k, (0, 0))[0]) * kf + wg.get(k, (0, 0))[0] * kw)):
+        f = fg.get(k, (0.0, 0))[0] * kf / 1e6
+        w_ = wg.get(k, (0.0, 0))[0] * kw / 1e6
+        calls = max(fg.get(k, (0, 0))[1], wg.get(k, (0, 0))[1])
+        lines.append("%-8d %-6d %12.1f %12.1f %12.1f  %s" % (k[1], calls, f, w_, f + w_, _demangle(k[0])))
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(TRAFFIC_ALL_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _demangle(name):
     import subprocess
     try:
@@ -635,12 +682,16 @@ def main():
     ap.add_argument("--copy-kernel", action="store_true")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--summarize-traffic-all", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="per-kernel HBM traffic of a whole bench run (counter passes over bench.py)")
     ap.add_argument("--command", default="", help="profile command recorded in a summary")
     args = ap.parse_args()
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats, args.command)
     if args.summarize_traffic:
         return summarize_traffic(args.summarize_traffic, args.command)
+    if args.summarize_traffic_all:
+        return summarize_traffic_all(args.summarize_traffic_all, args.command)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the GLA kernels here are single-GPU "
               "(heads and batch shard across GPUs with no communication; see the design "
