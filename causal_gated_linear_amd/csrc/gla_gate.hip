@@ -154,17 +154,47 @@ __global__ __launch_bounds__(256) void gate_project_kernel(const GateArgs a)
     const bool store = x < nrows;
     float *gt = a.g + ((size_t)b * a.H * a.L + l) * a.d_k;    // g[b][0][l][0]
     const size_t hstride = (size_t)a.L * a.d_k;
+    // Two adjacent tiles of one head cover 128 bytes of each token's row.  Lanes x and
+    // x ^ 8 swap their second tile's values, so that each store instruction writes
+    // whole 128-byte row pieces of 8 tokens (half-line non-temporal writes cost extra
+    // HBM traffic): the first store holds tokens 0..7 of the wave, the second 8..15.
+    const bool pairable = a.d_k >= 32;                         // both tiles in one head
+    const long tok8 = row0 + (x ^ 8);
+    const long b8 = tok8 / a.L, l8 = tok8 - b8 * a.L;
+    float *gt8 = a.g + ((size_t)b8 * a.H * a.L + l8) * a.d_k;   // row of token x ^ 8
+    const bool lo = x < 8;
+    const bool store_a = (x & 7) < nrows, store_b = (x & 7) + 8 < nrows;
+    auto tile_gates = [&](int tile) __attribute__((always_inline)) -> f32x4 {
+        const f32x4 z = up_step(wu + (size_t)(16 * tile + x) * R + 4 * grp, zd, NR, f32x4{0.f, 0.f, 0.f, 0.f});
+        // lane (x, grp) element e: z[t = row0 + x][n = 16 tile + 4 grp + e]
+        f32x4 g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[e] = log_sigmoid(z[e]) * inv_tau;
+        return g;
+    };
     for (int t0 = og * a.tiles_per_group; t0 < ntile; t0 += 8) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 8; u += 2) {
             if (t0 + u >= ntile) break;                            // wave-uniform
-            const f32x4 z = up_step(wu + (size_t)(16 * (t0 + u) + x) * R + 4 * grp, zd, NR, f32x4{0.f, 0.f, 0.f, 0.f});
-            // lane (x, grp) element e: z[t = row0 + x][n = 16 (t0 + u) + 4 grp + e]
-            const int n = 16 * (t0 + u) + 4 * grp, h = n >> a.dk_shift, i = n & (a.d_k - 1);
-            f32x4 g;
+            const int n0 = 16 * (t0 + u) + 4 * grp, h0 = n0 >> a.dk_shift, i0 = n0 & (a.d_k - 1);
+            const f32x4 g0 = tile_gates(t0 + u);
+            if (!pairable || t0 + u + 1 >= ntile) {                // wave-uniform
+                if (store) __builtin_nontemporal_store(g0, (f32x4 *)(gt + h0 * hstride + i0));
+                if (t0 + u + 1 < ntile) {
+                    const int n1 = n0 + 16, h1 = n1 >> a.dk_shift, i1 = n1 & (a.d_k - 1);
+                    const f32x4 g1 = tile_gates(t0 + u + 1);
+                    if (store) __builtin_nontemporal_store(g1, (f32x4 *)(gt + h1 * hstride + i1));
+                }
+                continue;
+            }
+            const f32x4 g1 = tile_gates(t0 + u + 1);
+            f32x4 r;                                               // tile u+1 of token x ^ 8
 #pragma unroll
-            for (int e = 0; e < 4; ++e) g[e] = log_sigmoid(z[e]) * inv_tau;
-            if (store) __builtin_nontemporal_store(g, (f32x4 *)(gt + h * hstride + i));   // streamed once
+            for (int e = 0; e < 4; ++e) r[e] = __shfl_xor(g1[e], 8, 64);
+            float *own = gt + h0 * hstride + i0;                   // token x, tile u
+            float *oth = gt8 + h0 * hstride + i0 + 16;             // token x ^ 8, tile u+1
+            if (store_a) __builtin_nontemporal_store(lo ? g0 : r, (f32x4 *)(lo ? own : oth));
+            if (store_b) __builtin_nontemporal_store(lo ? r : g0, (f32x4 *)(lo ? oth : own));
         }
     }
 }
