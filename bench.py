@@ -133,6 +133,24 @@ def achievable_peaks():
     return out
 
 
+def _cold_ms(torch, step, stream, n, flush):
+    """Median per-launch time of ``step`` with the caches flushed before each launch:
+    ``flush`` (a 1 GiB device buffer) is overwritten outside the timed interval, which
+    evicts the L2 caches and the 256 MB last-level cache."""
+    times = []
+    for _ in range(n):
+        flush.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return times[len(times) // 2]
+
+
 def _settle(torch, step, seconds):
     """Untimed launches of ``step`` for at least ``seconds`` (one at a time), so that a
     workload is timed in its steady state: the first launches after a switch of
@@ -203,8 +221,13 @@ def run_other_prefills(args, torch, api, inputs):
         es = 2 if w.dtype == torch.bfloat16 else 4
         nbytes = prefill_bytes(w.B, w.H, w.L, w.d_k, w.d_v, es=es, gate=w.gate or "none")
         gbs = nbytes / (per / 1e3) / 1e9
-        out[name] = {"ms_per_step": per, "tokens_per_s": w.B * w.L / (per / 1e3), "GB_per_s": gbs,
-                     "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes,
+        cold = None
+        if nbytes < 2**28:                       # fits the last-level cache: also time it cold
+            flush = torch.empty(2**28, dtype=torch.float32, device="cuda")
+            cold = _cold_ms(torch, step, stream, 15, flush)
+            del flush
+        out[name] = {"ms_per_step": per, "ms_per_step_cold": cold, "tokens_per_s": w.B * w.L / (per / 1e3),
+                     "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes,
                      "shape": "B=%d H=%d L=%d d_k=%d d_v=%d chunk=%d %s gate=%s phi=%s" % (
                          w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, str(w.dtype).replace("torch.", ""), w.gate,
                          w.feature_map or "identity")}
