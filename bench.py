@@ -191,10 +191,22 @@ def run_prefill(args, torch, api, inputs):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = ms / args.steps
+    # after the timed region: the same number of launches, each between its own pair of
+    # events (back to back on the stream), for the spread of single-launch times
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    one = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    launch_stats = {"launches": len(one), "min_ms": one[0], "median_ms": one[len(one) // 2],
+                    "p90_ms": one[min(len(one) - 1, (9 * len(one)) // 10)]}
     nbytes = prefill_bytes(w.B, w.H, w.L, w.d_k, w.d_v)
     flops = prefill_flops(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)
     return dict(w=w, inp=inp, ms_per_step=per, wall_s=wall, bytes=nbytes, flops=flops,
-                settle_launches=settle)
+                settle_launches=settle, launch_stats=launch_stats)
 
 
 def run_other_prefills(args, torch, api, inputs):
@@ -742,6 +754,8 @@ def main():
         "warmup": args.warmup,
         "settle": {"seconds": args.settle_s, "launches": pf["settle_launches"],
                    "note": "untimed headline launches before the warm-up steps (clock ramp)"},
+        "launch_stats": dict(pf["launch_stats"], note="after the timed region: single launches, each "
+                             "between its own events"),
         "ms_per_step": pf["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
