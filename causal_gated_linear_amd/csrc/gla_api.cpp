@@ -75,8 +75,12 @@ int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes)
 // from zero, a scan over segments turns those into each segment's initial state,
 // and the full pass then runs all segments in parallel.  Used when the widest tile
 // gives fewer than 256 workgroups and the sequences have at least 64 chunks;
-// segments keep at least 16 chunks.  GLA_PREFILL_SEGMENTS=<n> overrides the count.
+// segments keep at least 16 chunks.  Sequences of 32 to 63 chunks are split too when
+// even the narrowest tile leaves CUs idle (fewer than 256 workgroups), into segments
+// of at least 4 chunks, so that each tile's chain of chunks is short.
+// GLA_PREFILL_SEGMENTS=<n> overrides the count.
 constexpr int kSegMinChunks = 16, kSegMinSeqChunks = 64;
+constexpr int kSegShortMinChunks = 4, kSegShortSeqChunks = 32;
 
 PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes)
 {
@@ -87,8 +91,11 @@ PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_by
         if (dvt == 16 && tile_usable(t, d_k, d_v, chunk, elem_bytes)) dvt = t;
     const long wgs = (long)BH * (d_v / dvt);
     int nseg = 1;
-    if (nchunks >= kSegMinSeqChunks)
+    if (nchunks >= kSegMinSeqChunks) {
         while (wgs * nseg < 256 && nchunks / (2 * nseg) >= kSegMinChunks) nseg *= 2;
+    } else if (nchunks >= kSegShortSeqChunks && (long)BH * (d_v / 16) < 256) {
+        while (wgs * nseg * 2 <= 256 && nchunks / (2 * nseg) >= kSegShortMinChunks) nseg *= 2;
+    }
     const char *env = getenv("GLA_PREFILL_SEGMENTS");
     if (env && atoi(env) >= 1) nseg = atoi(env) < nchunks ? atoi(env) : (nchunks > 0 ? nchunks : 1);
     if (nseg > 1) {

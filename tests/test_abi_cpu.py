@@ -158,7 +158,11 @@ def test_workspace_for_few_long_sequences(lib):
     rnd = lambda x: (x + 255) // 256 * 256
     assert n == 2 * rnd(32 * 4 * 128 * 128 * 4) + rnd(32 * 4 * 128 * 4)   # 4 segments of 8192 tokens
     assert lib.gla_prefill_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 0   # enough heads
-    assert lib.gla_prefill_workspace_bytes(1, 2, 64 * 63, 64, 64, 64, 1) == 0   # too short
+    assert lib.gla_prefill_workspace_bytes(1, 2, 64 * 31, 64, 64, 64, 1) == 0   # too short
+    # 32 to 63 chunks on too few heads for even the narrowest tile: short segments
+    assert lib.gla_prefill_workspace_bytes(1, 2, 64 * 63, 64, 64, 64, 1) > 0
+    assert lib.gla_prefill_workspace_bytes(4, 8, 2048, 64, 64, 64, 1) > 0
+    assert lib.gla_prefill_workspace_bytes(8, 16, 2048, 64, 64, 64, 1) == 0   # enough heads
 
 
 def test_workspace_query_is_host_only(lib):
