@@ -558,7 +558,6 @@ int gla_gate_project(const void *x, const void *w_down, const void *w_up, float 
     a.B = B; a.L = L; a.d_model = d_model; a.H = H; a.d_k = d_k; a.inv_tau = 1.f / tau;
     a.dk_shift = 0;
     while ((1 << a.dk_shift) < d_k) ++a.dk_shift;           // d_k is a power of two
-    a.tiles_per_group = 128;
     const hipError_t e = gla::launch_gate_project(a, dtype == GLA_BF16 ? 1 : 0, rank, (hipStream_t)stream);
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "gate producer launch: %s", hipGetErrorString(e));
     return ok();

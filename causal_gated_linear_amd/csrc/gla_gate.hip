@@ -16,10 +16,11 @@
 // row-contiguous loads (x comes from HBM once; W_down stays in cache).  The
 // accumulator tiles of zd^T are then, unchanged, the right operand of the
 // up-projection z^T = W_up zd^T, which runs on the matrix cores one 16-row tile of
-// W_up at a time; each tile's outputs go through log-sigmoid and are stored
-// as 16-byte row pieces, non-temporally (g is written once and read by a later
-// kernel, far beyond the caches).  The write of g (4 bytes per token and key
-// dimension) dominates the traffic.
+// W_up at a time, from the workgroup's rows of W_up staged in LDS (64 KB, in the
+// space the down-projection used) before the first store; each tile's outputs go
+// through log-sigmoid and are stored as 16-byte row pieces, non-temporally (g is
+// written once and read by a later kernel, far beyond the caches).  The write of g
+// (4 bytes per token and key dimension) dominates the traffic.
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
 
@@ -27,14 +28,14 @@ namespace gla {
 
 namespace {
 
-// log(sigmoid(z)) = min(z, 0) - log(1 + e^-|z|), with the hardware base-2 exp and
-// log.  Where e^-|z| is below fp32's epsilon, 1 + e^-|z| rounds to 1 and the term it
-// drops is below 6e-8 in absolute value.
-__device__ __forceinline__ float log_sigmoid(float z)
+// log(sigmoid(z)) / tau = min(z, 0) / tau - log(1 + e^-|z|) / tau, with the hardware
+// base-2 exp and log (c = -ln 2 / tau).  Where e^-|z| is below fp32's epsilon,
+// 1 + e^-|z| rounds to 1 and the term it drops is below 6e-8 / tau in absolute value.
+// min(z, 0) / tau is taken as min(z / tau, 0) (tau > 0).
+__device__ __forceinline__ float log_sigmoid_scaled(float z, float inv_tau, float c)
 {
-    constexpr float kLn2 = 0.6931471805599453f;
     const float e = exp2_fast(-fabsf(z) * kLog2e);
-    return fminf(z, 0.f) - __builtin_amdgcn_logf(1.f + e) * kLn2;
+    return fmaf(c, __builtin_amdgcn_logf(1.f + e), fminf(z * inv_tau, 0.f));
 }
 
 // 16-byte operand piece: 8 bf16 or 4 fp32 consecutive elements of a row.
@@ -48,21 +49,41 @@ __device__ __forceinline__ f32x4 mma_piece(bf16x8 a, bf16x8 b, f32x4 c)
 }
 __device__ __forceinline__ f32x4 mma_piece(f32x4 a, f32x4 b, f32x4 c) { return mma1(a, b, c); }
 
-// Up-projection step: z += W_up[n][4 grp + e, 16 + 4 grp + e] x zd over one or two
-// 16-blocks of the rank, from the accumulator tiles of zd^T.  bf16 weights: bf16
-// matrix-core operands (the rank-r code rounded to bf16); fp32 weights: fp32.
-__device__ __forceinline__ f32x4 up_step(const bf16 *w, const f32x4 *zd, int nr, f32x4 acc)
+// Staged W_up rows in LDS: row r (R elements, no padding).  For bf16 the 8-byte
+// pieces of a row are permuted by an even XOR of the row index, so that the 16
+// lanes of one ds_read_b64 (rows x = 0..15, one piece) hit distinct banks, while
+// each 16-byte piece of the staging copy stays contiguous.
+template <typename T, int R>
+__device__ __forceinline__ int up_off(int row, int elem)
+{
+    if constexpr (sizeof(T) == 2) {
+        const int sw = R == 16 ? 2 * ((row >> 3) & 1) : 2 * ((row >> 2) & 3);
+        return row * R + ((((elem >> 2) ^ sw)) << 2) + (elem & 3);
+    } else {
+        return row * R + elem;
+    }
+}
+
+// Up-projection step: z = W_up[row][:] x zd over the rank (one or two 16-blocks),
+// with row = 16 tile + x of the staged rows and the accumulator tiles of zd^T.  bf16
+// weights: bf16 matrix-core operands (the rank-r code rounded to bf16); fp32 weights:
+// fp32.
+template <int R>
+__device__ __forceinline__ f32x4 up_step(const bf16 *su, int row, int grp, const f32x4 *zd)
 {
     const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    const f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     bf16x4 *tag = nullptr;
-    const bf16x4 a0 = *(const bf16x4 *)w;
-    if (nr == 1) return mma2(a0, z, frag_from_acc(tag, zd[0]), z, acc);
-    return mma2(a0, *(const bf16x4 *)(w + 16), frag_from_acc(tag, zd[0]), frag_from_acc(tag, zd[1]), acc);
+    const bf16x4 a0 = *(const bf16x4 *)(su + up_off<bf16, R>(row, 4 * grp));
+    if constexpr (R == 16) return mma2(a0, z, frag_from_acc(tag, zd[0]), z, acc);
+    else return mma2(a0, *(const bf16x4 *)(su + up_off<bf16, R>(row, 16 + 4 * grp)),
+                     frag_from_acc(tag, zd[0]), frag_from_acc(tag, zd[1]), acc);
 }
-__device__ __forceinline__ f32x4 up_step(const float *w, const f32x4 *zd, int nr, f32x4 acc)
+template <int R>
+__device__ __forceinline__ f32x4 up_step(const float *su, int row, int grp, const f32x4 *zd)
 {
-    acc = mma1(*(const f32x4 *)w, zd[0], acc);
-    if (nr == 2) acc = mma1(*(const f32x4 *)(w + 16), zd[1], acc);
+    f32x4 acc = mma1(*(const f32x4 *)(su + up_off<float, R>(row, 4 * grp)), zd[0], f32x4{0.f, 0.f, 0.f, 0.f});
+    if constexpr (R == 32) acc = mma1(*(const f32x4 *)(su + up_off<float, R>(row, 16 + 4 * grp)), zd[1], acc);
     return acc;
 }
 
@@ -95,8 +116,12 @@ __global__ __launch_bounds__(256) void gate_project_kernel(const GateArgs a)
     constexpr int MB = 512 / ES, LDX = MB + KW, NU = MB / KSTEP;
     constexpr int PPR = MB / KW;                               // 16-byte pieces per row chunk
     constexpr int XP = 64 * PPR / 256, WP = (R * PPR + 255) / 256;
-    __shared__ __align__(16) T sX[64 * LDX];
-    __shared__ __align__(16) T sW[R * LDX];
+    // One LDS block: the x and W_down chunks of the down-projection, then the
+    // workgroup's rows of W_up (TPG tiles of 16 rows, 64 KB) for the up-projection.
+    constexpr int TPG = gate_tiles_per_group(ES, R);
+    constexpr int NXW = (64 + R) * LDX, NUP = TPG * 16 * R;
+    __shared__ __align__(16) T smem[NXW > NUP ? NXW : NUP];
+    T *const sX = smem, *const sW = smem + 64 * LDX;
     const long tok0 = (long)blockIdx.x * 64;
     const int brows = (int)max(0L, min(64L, ntok - tok0));
     const Rsrc rx = make_rsrc((const T *)a.x + tok0 * dm, (unsigned)(brows * dm * ES));
@@ -142,13 +167,33 @@ __global__ __launch_bounds__(256) void gate_project_kernel(const GateArgs a)
         }
     }
 
+    // stage rows [16 tile0, 16 ntile) of W_up, 16-byte pieces; every global load of
+    // the kernel is issued before its first store
+    const int tile0 = og * TPG;
+    const int ntile = min(a.H * a.d_k / 16, tile0 + TPG);
+    {
+        constexpr int PPU = R * ES / 16, UP = TPG * 16 * PPU / 256;
+        const int npiece = 16 * (ntile - tile0) * PPU;
+        const char *wsrc = (const char *)a.w_up + (size_t)16 * tile0 * R * ES;
+        P gu[UP];
+#pragma unroll
+        for (int i = 0; i < UP; ++i) {
+            const int p = tid + 256 * i;
+            if (p < npiece) gu[i] = *(const P *)(wsrc + (size_t)p * 16);
+        }
+        __syncthreads();                                       // down-projection's LDS reads done
+#pragma unroll
+        for (int i = 0; i < UP; ++i) {
+            const int p = tid + 256 * i, r = p / PPU;
+            if (p < npiece) *(P *)(smem + up_off<T, R>(r, (p - r * PPU) * KW)) = gu[i];
+        }
+        __syncthreads();
+    }
+
     if (nrows == 0) return;                                    // wave-uniform; no barrier follows
 
-    // up-projection per 16-row tile of W_up (outputs n), then log-sigmoid and store;
-    // batches of NV tiles request their W_up fragments before the first product
-    const int ntile = min(a.H * a.d_k / 16, (og + 1) * a.tiles_per_group);
-    const T *wu = (const T *)a.w_up;
-    const float inv_tau = a.inv_tau;
+    // up-projection per 16-row tile of W_up (outputs n), then log-sigmoid and store
+    const float inv_tau = a.inv_tau, c_log = -0.6931471805599453f * a.inv_tau;
     const long tok = row0 + x;
     const long b = tok / a.L, l = tok - b * a.L;
     const bool store = x < nrows;
@@ -164,30 +209,34 @@ __global__ __launch_bounds__(256) void gate_project_kernel(const GateArgs a)
     float *gt8 = a.g + ((size_t)b8 * a.H * a.L + l8) * a.d_k;   // row of token x ^ 8
     const bool lo = x < 8;
     const bool store_a = (x & 7) < nrows, store_b = (x & 7) + 8 < nrows;
-    auto tile_gates = [&](int tile) __attribute__((always_inline)) -> f32x4 {
-        const f32x4 z = up_step(wu + (size_t)(16 * tile + x) * R + 4 * grp, zd, NR, f32x4{0.f, 0.f, 0.f, 0.f});
+    auto gates = [&](const f32x4 &z) __attribute__((always_inline)) -> f32x4 {
         // lane (x, grp) element e: z[t = row0 + x][n = 16 tile + 4 grp + e]
         f32x4 g;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) g[e] = log_sigmoid(z[e]) * inv_tau;
+        for (int e = 0; e < 4; ++e) g[e] = log_sigmoid_scaled(z[e], inv_tau, c_log);
         return g;
     };
-    for (int t0 = og * a.tiles_per_group; t0 < ntile; t0 += 8) {
+    for (int t0 = tile0; t0 < ntile; t0 += 8) {
+        // the batch's 8 products first (tile index clamped to the staged rows), so that
+        // their LDS reads and matrix-core latencies overlap
+        f32x4 zz[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) zz[u] = up_step<R>(smem, 16 * (min(t0 + u, ntile - 1) - tile0) + x, grp, zd);
 #pragma unroll
         for (int u = 0; u < 8; u += 2) {
             if (t0 + u >= ntile) break;                            // wave-uniform
             const int n0 = 16 * (t0 + u) + 4 * grp, h0 = n0 >> a.dk_shift, i0 = n0 & (a.d_k - 1);
-            const f32x4 g0 = tile_gates(t0 + u);
+            const f32x4 g0 = gates(zz[u]);
             if (!pairable || t0 + u + 1 >= ntile) {                // wave-uniform
                 if (store) __builtin_nontemporal_store(g0, (f32x4 *)(gt + h0 * hstride + i0));
                 if (t0 + u + 1 < ntile) {
                     const int n1 = n0 + 16, h1 = n1 >> a.dk_shift, i1 = n1 & (a.d_k - 1);
-                    const f32x4 g1 = tile_gates(t0 + u + 1);
+                    const f32x4 g1 = gates(zz[u + 1]);
                     if (store) __builtin_nontemporal_store(g1, (f32x4 *)(gt + h1 * hstride + i1));
                 }
                 continue;
             }
-            const f32x4 g1 = tile_gates(t0 + u + 1);
+            const f32x4 g1 = gates(zz[u + 1]);
             f32x4 r;                                               // tile u+1 of token x ^ 8
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e] = __shfl_xor(g1[e], 8, 64);
@@ -204,8 +253,8 @@ hipError_t launch_gate_project(const GateArgs &a, int dtype, int rank, hipStream
     const long ntok = (long)a.B * a.L;
     const unsigned grid = (unsigned)((ntok + 63) / 64);
     if (grid == 0) return hipSuccess;
-    const int ntile = a.H * a.d_k / 16;
-    const dim3 g2(grid, (ntile + a.tiles_per_group - 1) / a.tiles_per_group);
+    const int ntile = a.H * a.d_k / 16, tpg = gate_tiles_per_group(dtype == 1 ? 2 : 4, rank);
+    const dim3 g2(grid, (ntile + tpg - 1) / tpg);
 #define GLA_GATE_LAUNCH(T, R) \
     hipLaunchKernelGGL((gate_project_kernel<T, R>), g2, dim3(256), 0, stream, a)
     if (dtype == 1) {

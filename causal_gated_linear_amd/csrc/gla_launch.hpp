@@ -114,9 +114,11 @@ struct GateArgs {
     float *g;                // [B][H][L][d_k] fp32 log-gates
     int B, L, d_model, H, d_k;
     int dk_shift;            // log2(d_k)
-    int tiles_per_group;     // 16-output tiles per workgroup (grid.y splits H*d_k/16)
     float inv_tau;
 };
+// 16-output tiles per workgroup of the gate producer (grid.y splits H*d_k/16): as
+// many as 64 KB of W_up rows hold.
+constexpr int gate_tiles_per_group(int elem_size, int rank) { return 65536 / (16 * rank * elem_size); }
 hipError_t launch_gate_project(const GateArgs &a, int dtype, int rank, hipStream_t stream);
 
 // The outer-product gate (gla_outer.hip): S <- (alpha beta^T) (.) S + phi(k) v^T.
