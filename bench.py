@@ -339,13 +339,15 @@ def run_delta(args, torch, api, inputs):
     gbs = nbytes / (per / 1e3) / 1e9
     tfl = flops / (per / 1e3) / 1e12
     out = {"prefill": {
-        "workload": "delta_prefill: B=8 H=16 L=4096 d_k=d_v=128 chunk=64, bf16 q/k/v (unit-length q, k), "
-                    "fp32 beta = sigmoid(N(0,1)), fp32 final state",
+        "workload": "delta_prefill: B=%d H=%d L=%d d_k=%d d_v=%d chunk=%d, bf16 q/k/v (unit-length q, k), "
+                    "fp32 beta = sigmoid(N(0,1)), fp32 final state" % (w.B, w.H, w.L, w.d_k, w.d_v, w.chunk),
         "ms_per_step": per, "tokens_per_s": w.B * w.L / (per / 1e3), "GB_per_s": gbs,
         "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes, "tflops": tfl,
         "mfma_frac": tfl / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": flops,
         "workspace_bytes": int(ws.numel()),
-        "kernels": "delta_prep_kernel (all chunks in parallel) then delta_scan_kernel (chunks in order)"}}
+        "kernels": ("delta_fused_kernel (each chunk's system solved beside the previous chunk's state update)"
+                    if w.chunk <= 32 else
+                    "delta_prep_kernel (all chunks in parallel) then delta_scan_kernel (chunks in order)")}}
     del inp, o, s, ws
     wd = inputs.WORKLOADS["decode"]
     T = min(256, args.decode_steps)
@@ -633,13 +635,13 @@ def summarize_stats(d, command):
              "(prefill grid 16384)",
              "#   other prefills: linear_elu1 (4x8x2048, d=64), scalar_long (1x32x32768, segmented: state-only "
              "pass, segment scan, full pass), fp32_single_head, and the normalised form at the headline shape",
-             "#   delta rule at the headline shape: delta_prep_kernel (grid 8192) then delta_scan_kernel (grid 256); "
+             "#   delta rule at the headline shape, chunk 32: delta_fused_kernel (grid 256); "
              "delta decode at the decode shape",
              "#   gate producer: 8x4096 tokens, d_model 2048 -> 16 heads x 128 (grid 512)",
              "#   outer-product gate at the headline shape, chunk 32 and 64 (grid 256); its decode step",
              "# kernel names are mangled: prefill_kernel<T, d_k, chunk, value-column tile, gate, elu1, "
              "state-only, normalised>, DF16b = bf16, gate 1 = key-dim, 2 = scalar; decode_kernel<T, d_k, d_v, "
-             "normalised>; delta_scan_kernel<T, d_k, chunk>; outer_prefill_kernel<T, d_k, chunk, elu1>",
+             "normalised>; delta_fused_kernel<T, d_k, chunk>; outer_prefill_kernel<T, d_k, chunk, elu1>",
              "# command (from the repository root, REPO = its absolute path):", "#   " + command, "",
              "## rocprofv3 stats (all dispatches, warm-up included)",
              "%-8s %14s %12s %12s %12s  %s" % ("calls", "total_ns", "avg_ns", "min_ns", "max_ns", "kernel")]
