@@ -40,6 +40,16 @@ def test_gate_head_dims(dk, dtype):
     _check(1, 70, 64, 16, 2, dk, dtype, 1.0, seed=1520 + dk)
 
 
+@pytest.mark.parametrize("H,dk", [(17, 128), (137, 16)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rank", [16, 32])
+def test_gate_output_groups(H, dk, dtype, rank):
+    """More 16-output tiles than one workgroup stages of W_up (64 KB: 128 tiles for
+    bf16 rank 16, 64 for bf16 rank 32 and fp32 rank 16, 32 for fp32 rank 32), with a
+    partial last group: 136 tiles, or 137 tiles of d_k = 16 whose last one is unpaired."""
+    _check(2, 70, 64, rank, H, dk, dtype, 16.0, seed=1580 + H + rank)
+
+
 @pytest.mark.parametrize("B,L", [(1, 1), (3, 1), (1, 64), (2, 64), (1, 65), (5, 13)])
 def test_gate_token_counts(B, L):
     """Token counts below, at and across the 64-token workgroup, and workgroups that
