@@ -637,7 +637,7 @@ def summarize_stats(d, command):
              "pass, segment scan, full pass), fp32_single_head, and the normalised form at the headline shape",
              "#   delta rule at the headline shape, chunk 32: delta_fused_kernel (grid 256); "
              "delta decode at the decode shape",
-             "#   gate producer: 8x4096 tokens, d_model 2048 -> 16 heads x 128 (grid 512)",
+             "#   gate producer: 8x4096 tokens, d_model 2048 -> 16 heads x 128 (grid 256, persistent: 2 blocks of 64 tokens each)",
              "#   outer-product gate at the headline shape, chunk 32 and 64 (grid 256); its decode step",
              "# kernel names are mangled: prefill_kernel<T, d_k, chunk, value-column tile, gate, elu1, "
              "state-only, normalised>, DF16b = bf16, gate 1 = key-dim, 2 = scalar; decode_kernel<T, d_k, d_v, "

@@ -10,17 +10,20 @@
 //
 // straight into the prefill's [B][H][L][d_k] layout.
 //
-// One workgroup per 64 tokens (16 per wave) and group of 16-output tiles.  Each
-// wave first computes its tokens' rank-r codes zd^T = W_down x^T on the matrix
-// cores, from x and W_down row chunks that the workgroup stages in LDS with
-// row-contiguous loads (x comes from HBM once; W_down stays in cache).  The
-// accumulator tiles of zd^T are then, unchanged, the right operand of the
-// up-projection z^T = W_up zd^T, which runs on the matrix cores one 16-row tile of
-// W_up at a time, from the workgroup's rows of W_up staged in LDS (64 KB, in the
-// space the down-projection used) before the first store; each tile's outputs go
-// through log-sigmoid and are stored as 16-byte row pieces, non-temporally (g is
-// written once and read by a later kernel, far beyond the caches).  The write of g
-// (4 bytes per token and key dimension) dominates the traffic.
+// Persistent workgroups (one per CU and group of 16-output tiles) walk the token
+// blocks of 64 tokens with a stride of the grid.  Four reader waves compute the
+// next block's rank-r codes zd^T = W_down x^T on the matrix cores, with operand
+// fragments loaded straight from memory (x from HBM once, W_down from the cache),
+// while four writer waves turn the current block's codes into gates: the
+// up-projection z^T = W_up zd^T on the matrix cores, one 16-row tile of W_up at a
+// time from the workgroup's rows of W_up staged in LDS (64 KB) at the start, then
+// log-sigmoid, and stores as 16-byte row pieces, non-temporally (g is written once
+// and read by a later kernel, far beyond the caches).  The codes pass through LDS,
+// double-buffered, with one barrier per block.  Reading x and writing g thus overlap
+// across the chip, and no wave issues both loads and stores: loads and stores share
+// one in-order completion counter, so a load issued after a store would wait for
+// that store's write.  The write of g (4 bytes per token and key dimension)
+// dominates the traffic.
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
 
@@ -90,125 +93,96 @@ __device__ __forceinline__ f32x4 up_step(const float *su, int row, int grp, cons
 }  // namespace
 
 template <typename T, int R>
-__global__ __launch_bounds__(256) void gate_project_kernel(const GateArgs a)
+__global__ __launch_bounds__(512) void gate_project_kernel(const GateArgs a)
 {
     constexpr int ES = sizeof(T);
     constexpr int KW = 16 / ES;                    // contraction elements per lane per step
     constexpr int KSTEP = 4 * KW;                  // contraction width of one step (32 or 16)
     constexpr int NR = R / 16;                     // 16-row tiles of the rank
+    constexpr int LDZ = R + 4;                     // row stride of the staged codes (floats)
+    constexpr int TPG = gate_tiles_per_group(ES, R);
     typedef typename Piece<T>::type P;
+    __shared__ __align__(16) T sU[TPG * 16 * R];              // the group's rows of W_up
+    __shared__ __align__(16) float sZ[2][64 * LDZ];            // codes of two token blocks
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int x = lane & 15, grp = lane >> 4;
-    const long row0 = (long)blockIdx.x * 64 + 16 * w;        // this wave's first token
+    const bool reader = w < 4;                                 // wave-uniform
+    const int wr = w & 3;                                      // token rows 16 wr .. of a block
     const int og = blockIdx.y;                                 // group of 16-output tiles
     const int dm = a.d_model;
     const long ntok = (long)a.B * a.L;
-    const int nrows = (int)max(0L, min(16L, ntok - row0));  // 0 for idle waves of the last block
-
-    // down-projection: zd^T[j][t] = sum_m W_down[j][m] x[t][m]; lane (x, grp) element e
-    // of tile jt holds zd[t = row0 + x][j = 16 jt + 4 grp + e].
-    // The contraction runs in chunks of MB columns (512 bytes of a row).  The
-    // workgroup stages the chunk of its 64 tokens' x rows and of W_down in LDS, each
-    // 32 lanes reading one 512-byte row piece; the next chunk is requested into
-    // registers before the current one is multiplied.  Pieces past d_model (or past
-    // the last token) read as zeros through the range checks.
-    constexpr int MB = 512 / ES, LDX = MB + KW, NU = MB / KSTEP;
-    constexpr int PPR = MB / KW;                               // 16-byte pieces per row chunk
-    constexpr int XP = 64 * PPR / 256, WP = (R * PPR + 255) / 256;
-    // One LDS block: the x and W_down chunks of the down-projection, then the
-    // workgroup's rows of W_up (TPG tiles of 16 rows, 64 KB) for the up-projection.
-    constexpr int TPG = gate_tiles_per_group(ES, R);
-    constexpr int NXW = (64 + R) * LDX, NUP = TPG * 16 * R;
-    __shared__ __align__(16) T smem[NXW > NUP ? NXW : NUP];
-    T *const sX = smem, *const sW = smem + 64 * LDX;
-    const long tok0 = (long)blockIdx.x * 64;
-    const int brows = (int)max(0L, min(64L, ntok - tok0));
-    const Rsrc rx = make_rsrc((const T *)a.x + tok0 * dm, (unsigned)(brows * dm * ES));
-    const Rsrc rwd = make_rsrc(a.w_down, (unsigned)(R * dm * ES));
-    const int tid = threadIdx.x;
-    P gx[XP], gw[WP];
-    auto fetch = [&](int m0) {
-#pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            const int p = tid + 256 * i, r = p / PPR, c = m0 + (p - r * PPR) * KW;
-            gx[i] = buf_load16<P>(rx, (c < dm ? r * dm + c : brows * dm) * ES);
-        }
-#pragma unroll
-        for (int i = 0; i < WP; ++i) {
-            const int p = tid + 256 * i, r = p / PPR, c = m0 + (p - r * PPR) * KW;
-            if (R * PPR % 256 == 0 || p < R * PPR) gw[i] = buf_load16<P>(rwd, (c < dm ? r * dm + c : R * dm) * ES);
-        }
-    };
-    f32x4 zd[NR];
-#pragma unroll
-    for (int jt = 0; jt < NR; ++jt) zd[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    fetch(0);
-    for (int m0 = 0; m0 < dm; m0 += MB) {
-        __syncthreads();                                       // previous chunk consumed
-#pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            const int p = tid + 256 * i, r = p / PPR;
-            *(P *)(sX + r * LDX + (p - r * PPR) * KW) = gx[i];
-        }
-#pragma unroll
-        for (int i = 0; i < WP; ++i) {
-            const int p = tid + 256 * i, r = p / PPR;
-            if (R * PPR % 256 == 0 || p < R * PPR) *(P *)(sW + r * LDX + (p - r * PPR) * KW) = gw[i];
-        }
-        __syncthreads();
-        fetch(m0 + MB);                                        // past the end: zeros, unused
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const P xb = *(const P *)(sX + (16 * w + x) * LDX + u * KSTEP + KW * grp);
-#pragma unroll
-            for (int jt = 0; jt < NR; ++jt)
-                zd[jt] = mma_piece(*(const P *)(sW + (16 * jt + x) * LDX + u * KSTEP + KW * grp), xb, zd[jt]);
-        }
-    }
-
-    // stage rows [16 tile0, 16 ntile) of W_up, 16-byte pieces; every global load of
-    // the kernel is issued before its first store
+    const long nblk = (ntok + 63) / 64;
+    const int nk = (int)((nblk - blockIdx.x + gridDim.x - 1) / gridDim.x);   // blocks of this workgroup
     const int tile0 = og * TPG;
     const int ntile = min(a.H * a.d_k / 16, tile0 + TPG);
+
+    // stage rows [16 tile0, 16 ntile) of W_up, 16-byte pieces, all waves
     {
-        constexpr int PPU = R * ES / 16, UP = TPG * 16 * PPU / 256;
+        constexpr int PPU = R * ES / 16, UP = TPG * 16 * PPU / 512;
         const int npiece = 16 * (ntile - tile0) * PPU;
         const char *wsrc = (const char *)a.w_up + (size_t)16 * tile0 * R * ES;
         P gu[UP];
 #pragma unroll
         for (int i = 0; i < UP; ++i) {
-            const int p = tid + 256 * i;
+            const int p = tid + 512 * i;
             if (p < npiece) gu[i] = *(const P *)(wsrc + (size_t)p * 16);
         }
-        __syncthreads();                                       // down-projection's LDS reads done
 #pragma unroll
         for (int i = 0; i < UP; ++i) {
-            const int p = tid + 256 * i, r = p / PPU;
-            if (p < npiece) *(P *)(smem + up_off<T, R>(r, (p - r * PPU) * KW)) = gu[i];
+            const int p = tid + 512 * i, r = p / PPU;
+            if (p < npiece) *(P *)(sU + up_off<T, R>(r, (p - r * PPU) * KW)) = gu[i];
         }
-        __syncthreads();
     }
 
-    if (nrows == 0) return;                                    // wave-uniform; no barrier follows
+    // Readers: rank-r codes zd[t][j] = sum_m W_down[j][m] x[t][m] of one 64-token block
+    // on the matrix cores, reader wr taking tokens 16 wr .. 16 wr + 15.  Operand
+    // fragments come straight from memory (x once from HBM, W_down from the cache),
+    // D steps ahead of their products; pieces past d_model or past the last token read
+    // as zeros through the range checks.  The accumulator tiles go to sZ[buf] in their
+    // lane layout: lane (x, grp) element e of tile jt is zd[16 wr + x][16 jt + 4 grp + e].
+    const Rsrc rwd = make_rsrc(a.w_down, (unsigned)(R * dm * ES));
+    auto codes = [&](long blk, int buf) __attribute__((always_inline)) {
+        constexpr int D = 8;
+        const long tok0 = blk * 64;
+        const int brows = (int)max(0L, min(64L, ntok - tok0));
+        const Rsrc rx = make_rsrc((const T *)a.x + tok0 * dm, (unsigned)(brows * dm * ES));
+        const int xrow = 16 * wr + x, nstep = dm / KSTEP;
+        P xc[D], wc[D][NR], xn[D], wn[D][NR];
+        auto load = [&](int u, P &xv, P (&wv)[NR]) __attribute__((always_inline)) {
+            const int m = u * KSTEP + KW * grp;
+            xv = buf_load16<P>(rx, (m < dm ? xrow * dm + m : brows * dm) * ES);
+#pragma unroll
+            for (int jt = 0; jt < NR; ++jt) wv[jt] = buf_load16<P>(rwd, (m < dm ? (16 * jt + x) * dm + m : R * dm) * ES);
+        };
+        f32x4 acc[NR];
+#pragma unroll
+        for (int jt = 0; jt < NR; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < D; ++i) load(i, xc[i], wc[i]);
+        for (int s0 = 0; s0 < nstep; s0 += D) {
+#pragma unroll
+            for (int i = 0; i < D; ++i) load(s0 + D + i, xn[i], wn[i]);      // zeros past the end
+#pragma unroll
+            for (int i = 0; i < D; ++i)
+#pragma unroll
+                for (int jt = 0; jt < NR; ++jt) acc[jt] = mma_piece(wc[i][jt], xc[i], acc[jt]);
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                xc[i] = xn[i];
+#pragma unroll
+                for (int jt = 0; jt < NR; ++jt) wc[i][jt] = wn[i][jt];
+            }
+        }
+#pragma unroll
+        for (int jt = 0; jt < NR; ++jt) *(f32x4 *)(sZ[buf] + (16 * wr + x) * LDZ + 16 * jt + 4 * grp) = acc[jt];
+    };
 
-    // up-projection per 16-row tile of W_up (outputs n), then log-sigmoid and store
+    // Writers: up-projection of one block from its staged codes, log-sigmoid, stores.
     const float inv_tau = a.inv_tau, c_log = -0.6931471805599453f * a.inv_tau;
-    const long tok = row0 + x;
-    const long b = tok / a.L, l = tok - b * a.L;
-    const bool store = x < nrows;
-    float *gt = a.g + ((size_t)b * a.H * a.L + l) * a.d_k;    // g[b][0][l][0]
     const size_t hstride = (size_t)a.L * a.d_k;
-    // Two adjacent tiles of one head cover 128 bytes of each token's row.  Lanes x and
-    // x ^ 8 swap their second tile's values, so that each store instruction writes
-    // whole 128-byte row pieces of 8 tokens (half-line non-temporal writes cost extra
-    // HBM traffic): the first store holds tokens 0..7 of the wave, the second 8..15.
-    const bool pairable = a.d_k >= 32;                         // both tiles in one head
-    const long tok8 = row0 + (x ^ 8);
-    const long b8 = tok8 / a.L, l8 = tok8 - b8 * a.L;
-    float *gt8 = a.g + ((size_t)b8 * a.H * a.L + l8) * a.d_k;   // row of token x ^ 8
+    const bool pairable = a.d_k >= 32;                         // both tiles of a pair in one head
     const bool lo = x < 8;
-    const bool store_a = (x & 7) < nrows, store_b = (x & 7) + 8 < nrows;
     auto gates = [&](const f32x4 &z) __attribute__((always_inline)) -> f32x4 {
         // lane (x, grp) element e: z[t = row0 + x][n = 16 tile + 4 grp + e]
         f32x4 g;
@@ -216,47 +190,84 @@ __global__ __launch_bounds__(256) void gate_project_kernel(const GateArgs a)
         for (int e = 0; e < 4; ++e) g[e] = log_sigmoid_scaled(z[e], inv_tau, c_log);
         return g;
     };
-    for (int t0 = tile0; t0 < ntile; t0 += 8) {
-        // the batch's 8 products first (tile index clamped to the staged rows), so that
-        // their LDS reads and matrix-core latencies overlap
-        f32x4 zz[8];
+    auto outputs = [&](long blk, int buf) __attribute__((always_inline)) {
+        const long row0 = blk * 64 + 16 * wr;                  // this wave's first token
+        const int nrows = (int)max(0L, min(16L, ntok - row0));
+        if (nrows == 0) return;                                // wave-uniform
+        f32x4 zd[NR];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) zz[u] = up_step<R>(smem, 16 * (min(t0 + u, ntile - 1) - tile0) + x, grp, zd);
+        for (int jt = 0; jt < NR; ++jt) zd[jt] = *(const f32x4 *)(sZ[buf] + (16 * wr + x) * LDZ + 16 * jt + 4 * grp);
+        const long tok = row0 + x;
+        const long b = tok / a.L, l = tok - b * a.L;
+        const bool store = x < nrows;
+        float *gt = a.g + ((size_t)b * a.H * a.L + l) * a.d_k;    // g[b][0][l][0]
+        // Two adjacent tiles of one head cover 128 bytes of each token's row.  Lanes x
+        // and x ^ 8 swap their second tile's values, so that each store instruction
+        // writes whole 128-byte row pieces of 8 tokens (half-line non-temporal writes
+        // cost extra HBM traffic): the first store holds tokens 0..7 of the wave, the
+        // second 8..15.
+        const long tok8 = row0 + (x ^ 8);
+        const long b8 = tok8 / a.L, l8 = tok8 - b8 * a.L;
+        float *gt8 = a.g + ((size_t)b8 * a.H * a.L + l8) * a.d_k;   // row of token x ^ 8
+        const bool store_a = (x & 7) < nrows, store_b = (x & 7) + 8 < nrows;
+        for (int t0 = tile0; t0 < ntile; t0 += 8) {
+            // the batch's 8 products first (tile index clamped to the staged rows), so
+            // that their LDS reads and matrix-core latencies overlap
+            f32x4 zz[8];
 #pragma unroll
-        for (int u = 0; u < 8; u += 2) {
-            if (t0 + u >= ntile) break;                            // wave-uniform
-            const int n0 = 16 * (t0 + u) + 4 * grp, h0 = n0 >> a.dk_shift, i0 = n0 & (a.d_k - 1);
-            const f32x4 g0 = gates(zz[u]);
-            if (!pairable || t0 + u + 1 >= ntile) {                // wave-uniform
-                if (store) __builtin_nontemporal_store(g0, (f32x4 *)(gt + h0 * hstride + i0));
-                if (t0 + u + 1 < ntile) {
-                    const int n1 = n0 + 16, h1 = n1 >> a.dk_shift, i1 = n1 & (a.d_k - 1);
-                    const f32x4 g1 = gates(zz[u + 1]);
-                    if (store) __builtin_nontemporal_store(g1, (f32x4 *)(gt + h1 * hstride + i1));
+            for (int u = 0; u < 8; ++u) zz[u] = up_step<R>(sU, 16 * (min(t0 + u, ntile - 1) - tile0) + x, grp, zd);
+#pragma unroll
+            for (int u = 0; u < 8; u += 2) {
+                if (t0 + u >= ntile) break;                        // wave-uniform
+                const int n0 = 16 * (t0 + u) + 4 * grp, h0 = n0 >> a.dk_shift, i0 = n0 & (a.d_k - 1);
+                const f32x4 g0 = gates(zz[u]);
+                if (!pairable || t0 + u + 1 >= ntile) {            // wave-uniform
+                    if (store) __builtin_nontemporal_store(g0, (f32x4 *)(gt + h0 * hstride + i0));
+                    if (t0 + u + 1 < ntile) {
+                        const int n1 = n0 + 16, h1 = n1 >> a.dk_shift, i1 = n1 & (a.d_k - 1);
+                        const f32x4 g1 = gates(zz[u + 1]);
+                        if (store) __builtin_nontemporal_store(g1, (f32x4 *)(gt + h1 * hstride + i1));
+                    }
+                    continue;
                 }
-                continue;
-            }
-            const f32x4 g1 = gates(zz[u + 1]);
-            f32x4 r;                                               // tile u+1 of token x ^ 8
+                const f32x4 g1 = gates(zz[u + 1]);
+                f32x4 r;                                           // tile u+1 of token x ^ 8
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = __shfl_xor(g1[e], 8, 64);
-            float *own = gt + h0 * hstride + i0;                   // token x, tile u
-            float *oth = gt8 + h0 * hstride + i0 + 16;             // token x ^ 8, tile u+1
-            if (store_a) __builtin_nontemporal_store(lo ? g0 : r, (f32x4 *)(lo ? own : oth));
-            if (store_b) __builtin_nontemporal_store(lo ? r : g0, (f32x4 *)(lo ? oth : own));
+                for (int e = 0; e < 4; ++e) r[e] = __shfl_xor(g1[e], 8, 64);
+                float *own = gt + h0 * hstride + i0;               // token x, tile u
+                float *oth = gt8 + h0 * hstride + i0 + 16;         // token x ^ 8, tile u+1
+                if (store_a) __builtin_nontemporal_store(lo ? g0 : r, (f32x4 *)(lo ? own : oth));
+                if (store_b) __builtin_nontemporal_store(lo ? r : g0, (f32x4 *)(lo ? oth : own));
+            }
         }
+    };
+
+    // Blocks blockIdx.x + k gridDim.x, k < nk: the readers compute block k + 1's codes
+    // while the writers emit block k's gates; one barrier per block hands over the
+    // codes and frees their buffer.
+    if (reader) codes(blockIdx.x, 0);
+    __syncthreads();                                           // W_up staged, first codes ready
+    for (int k = 0; k < nk; ++k) {
+        if (reader) {
+            if (k + 1 < nk) codes(blockIdx.x + (long)(k + 1) * gridDim.x, (k + 1) & 1);
+        } else {
+            outputs(blockIdx.x + (long)k * gridDim.x, k & 1);
+        }
+        __syncthreads();
     }
 }
 
 hipError_t launch_gate_project(const GateArgs &a, int dtype, int rank, hipStream_t stream)
 {
     const long ntok = (long)a.B * a.L;
-    const unsigned grid = (unsigned)((ntok + 63) / 64);
-    if (grid == 0) return hipSuccess;
+    const long nblk = (ntok + 63) / 64;
+    if (nblk == 0) return hipSuccess;
     const int ntile = a.H * a.d_k / 16, tpg = gate_tiles_per_group(dtype == 1 ? 2 : 4, rank);
-    const dim3 g2(grid, (ntile + tpg - 1) / tpg);
+    // persistent workgroups, one per CU and group of output tiles, each walking the
+    // token blocks with a stride of the grid
+    const dim3 g2((unsigned)min(nblk, 256L), (ntile + tpg - 1) / tpg);
 #define GLA_GATE_LAUNCH(T, R) \
-    hipLaunchKernelGGL((gate_project_kernel<T, R>), g2, dim3(256), 0, stream, a)
+    hipLaunchKernelGGL((gate_project_kernel<T, R>), g2, dim3(512), 0, stream, a)
     if (dtype == 1) {
         if (rank == 16) GLA_GATE_LAUNCH(bf16, 16);
         else if (rank == 32) GLA_GATE_LAUNCH(bf16, 32);
