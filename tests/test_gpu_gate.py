@@ -57,6 +57,14 @@ def test_gate_token_counts(B, L):
     _check(B, L, 32, 16, 2, 16, torch.bfloat16, 1.0, seed=1540 + 7 * B + L)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gate_blocks_per_workgroup(dtype):
+    """More 64-token blocks than workgroups: 601 blocks (the last one 17 tokens) over
+    256 persistent workgroups, so some carry 3 blocks and reuse their first code
+    buffer; every token is checked."""
+    _check(1, 64 * 600 + 17, 32, 16, 1, 16, dtype, 16.0, seed=1600)
+
+
 def test_gate_empty():
     d = inputs.draw_gate(B=2, L=1, d_model=32, rank=16, H=2, d_k=16, seed=1560)
     x = torch.empty(2, 0, 32, dtype=torch.bfloat16, device=DEV)
