@@ -221,6 +221,30 @@ def test_prefill_segment_counts(monkeypatch, nseg):
     _check_all_heads(W["scalar_long"], 1, 2, 64 * 20 + 3, seed=700 + nseg, with_s0=True)
 
 
+@pytest.mark.parametrize("name", ["gla_prefill", "scalar_long"])
+def test_prefill_value_tiles_agree(monkeypatch, name):
+    """Each value-column tile width (64, 32, 16; the launch picks one from the head
+    count) gives the oracle's result, and the same bits: a tile changes only how many
+    value columns one workgroup owns, not the arithmetic of any column."""
+    w = W[name]
+    B, H, L = 1, 2, 64 * 5 + 7
+    inp = inputs.draw(w, B=B, H=H, L=L, seed=990 + len(name))
+    s0 = inputs.draw_state(B, H, w.d_k, w.d_v, seed=991 + len(name), scale=0.5)
+    ro, rs = oracle.forward(inp["q"], inp["k"], inp["v"], g=inp["g"], gate=w.gate,
+                            feature_map=w.feature_map, s0=s0)
+    tol = util.TOL[w.dtype]
+    outs = {}
+    for tile in ("64", "32", "16"):
+        monkeypatch.setenv("GLA_PREFILL_TILE", tile)
+        o, s = _run_gpu(w, _to(inp, DEV), s0=s0.to(DEV))
+        util.assert_close(o, ro, tol, "%s o, value tile %s" % (name, tile))
+        util.assert_close(s, rs, tol, "%s s_final, value tile %s" % (name, tile))
+        outs[tile] = (o.cpu(), s.cpu())
+    for tile in ("32", "16"):
+        assert torch.equal(outs[tile][0], outs["64"][0]), "o differs between value tiles %s and 64" % tile
+        assert torch.equal(outs[tile][1], outs["64"][1]), "s_final differs between value tiles %s and 64" % tile
+
+
 @pytest.mark.parametrize("gate", ["keydim", "scalar"])
 def test_prefill_segmented_weak_gates_carry_state(monkeypatch, gate):
     """Segments with weak gates, so that the state carried across segments matters:
