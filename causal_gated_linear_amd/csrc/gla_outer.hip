@@ -16,8 +16,11 @@
 //     S <- Diag(e^GA) (S + K^^T V^) Diag(e^GB)
 //
 // (the product of the gates between s and t factorises per key dimension and per
-// value dimension).  As for the key-dimension gate, e^-A and e^-Bv must stay finite:
-// the log-gates summed over one chunk stay above about -80 in every dimension.
+// value dimension).  The factors e^-A and e^-Bv, and their product in K^^T V^, must
+// stay well inside the fp32 range: a chunk whose lowest key-side and lowest
+// value-side cumulative log2-gates add up to less than -kFastLim is computed token
+// by token instead (gla_slow.hpp), exact for any gate in [0, 1].  The consumer waves
+// run that loop on their own state registers; the rows are staged in LDS.
 //
 // One workgroup per (head, value tile of up to 64 columns); wave w owns 16 value
 // columns and their state slice S[d_k][16] in accumulator registers.  Per chunk the
@@ -31,12 +34,34 @@
 // The next chunk's raw rows are requested before the current chunk is computed.
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
+#include "gla_slow.hpp"
 
 namespace gla {
 
 namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <typename T> constexpr int pad_of() { return sizeof(T) == 2 ? 16 : 4; }
+
+// Minimum over the 64 lanes, in registers only: DPP shifts within each 16-lane row
+// (a lane whose source is outside the row keeps its own value), then the rows' last
+// lanes read as scalars.
+template <int SHIFT> __device__ __forceinline__ float row_shr_keep(float v)
+{
+    const int b = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x110 + SHIFT, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_min(float v)
+{
+    v = fminf(v, row_shr_keep<1>(v));
+    v = fminf(v, row_shr_keep<2>(v));
+    v = fminf(v, row_shr_keep<4>(v));
+    v = fminf(v, row_shr_keep<8>(v));
+    const int b = __builtin_bit_cast(int, v);
+    return fminf(fminf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31))),
+                 fminf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63))));
+}
 }  // namespace
 
 template <typename T, int DK, int C>
@@ -76,6 +101,7 @@ __global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
     __shared__ __align__(16) float sEV[C * LDGV];     // e^Bv[t][j]
     __shared__ __align__(16) float sEA[DK];           // e^GA
     __shared__ __align__(16) float sEB[SH::DVT];      // e^GB
+    __shared__ __align__(16) float sMin[4][2];        // per wave: lowest key / value chunk total
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int x = lane & 15, grp = lane >> 4;
@@ -188,7 +214,9 @@ __global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
         // 1. cumulative gates; scale q, k (key side) and v (value side) in place.
         //    A thread owns four columns of a segment of rows: it sums its rows serially,
         //    the segments of a column group (consecutive lanes) finish the scan with
-        //    shuffles, then it scales its rows' elements.
+        //    shuffles, then it scales its rows' elements.  kmin / vmin: the lowest
+        //    cumulative log2-gate of the thread's columns (gates <= 0: the chunk totals).
+        float kmin = 0.f, vmin = 0.f;
         {
             constexpr int NCG = DK / 4, NSEG = SH::KSEG, RPT = C / NSEG;
             const int cg = tid / NSEG, seg = tid % NSEG;
@@ -210,6 +238,7 @@ __global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
                         if (seg >= off) incl += up;
                     }
                     excl[e] = incl - run[e];
+                    kmin = fminf(kmin, excl[e] + pre[RPT - 1][e]);
                 }
 #pragma unroll
                 for (int r = 0; r < RPT; ++r) {
@@ -252,6 +281,7 @@ __global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
                         if (seg >= off) incl += up;
                     }
                     excl[e] = incl - run[e];
+                    vmin = fminf(vmin, excl[e] + pre[RPT - 1][e]);
                 }
 #pragma unroll
                 for (int r = 0; r < RPT; ++r) {
@@ -271,7 +301,39 @@ __global__ __launch_bounds__(256) void outer_prefill_kernel(const OuterArgs a)
                 }
             }
         }
+        kmin = wave_min(kmin);
+        vmin = wave_min(vmin);
+        if (lane == 0) {
+            sMin[w][0] = kmin;
+            sMin[w][1] = vmin;
+        }
         lds_barrier();
+        {
+            float km = sMin[0][0], vm = sMin[0][1];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) {
+                km = fminf(km, sMin[i][0]);
+                vm = fminf(vm, sMin[i][1]);
+            }
+            if (__builtin_amdgcn_readfirstlane(km + vm < -kFastLim ? 1 : 0)) {
+                // out of the factorised range: the chunk token by token (the staged rows
+                // were scaled in place, so they are staged again from memory)
+                const SlowStage<T> st{sG, sGV, sQ, sK, sV};
+                T *out = (T *)a.o + (hrow + (size_t)n * C) * DV + vt * DVT;
+                f32x4 zz[NKB] = {};
+                for (int r0 = 0; r0 < nvalid; r0 += C) {
+                    slow_stage<T, DK, C, 256, ELU1, true, true>(st, rq, rk, rv, rg, rgv, n * C + r0, DV, vt * DVT,
+                                                                DVT, tid);
+                    lds_barrier();
+                    if (active)
+                        slow_tokens<T, DK, NKB, 16, 16, true, false, true>(st, s, zz, 4 * grp, 16 * w + x, DVT,
+                                                                       min(C, nvalid - r0), out + (size_t)r0 * DV
+                                                                       + 16 * w + x, DV, lane < 16);
+                    lds_barrier();
+                }
+                continue;
+            }
+        }
         if (!active) continue;
 
         // 2. O^T = (S^T Q~^T + V^^T P^T) (.) e^Bv^T; lane (x, grp) element e:
@@ -344,6 +406,16 @@ constexpr int outer_pc_lds()
     return 2 * ((2 * C * SH::LDKP + C * SH::LDV) * (int)sizeof(T) + (C * SH::LDGV + DK + SH::DVT) * 4);
 }
 
+// Rows staged at a time by the producer/consumer kernel's token-by-token chunks: the
+// largest of C, 32, 16, 8 whose phi(q) and phi(k) rows fit in the Q~ buffers and whose
+// alpha, beta and v rows fit in the e^Bv buffers.
+constexpr int outer_slow_rows(int c, int q_bytes, int ev_bytes, int dk, int es)
+{
+    for (int sr : {64, 32, 16, 8})
+        if (sr <= c && 2 * sr * dk * es <= q_bytes && sr * (dk * 4 + 64 * 4 + 64 * es) <= ev_bytes) return sr;
+    return 0;
+}
+
 template <typename T> __device__ __forceinline__ typename Frag<T>::type buf_load_frag(Rsrc r, int off);
 template <> __device__ __forceinline__ bf16x4 buf_load_frag<bf16>(Rsrc r, int off)
 {
@@ -370,6 +442,7 @@ __global__ __launch_bounds__(512) void outer_pc_kernel(const OuterArgs a)
     __shared__ __align__(16) float sEV[2][C * LDGV];
     __shared__ __align__(16) float sEA[2][DK];
     __shared__ __align__(16) float sEB[2][SH::DVT];
+    __shared__ __align__(16) float sMin[2][4][2];     // per producer wave: lowest key / value chunk total
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int x = lane & 15, grp = lane >> 4;
@@ -431,9 +504,12 @@ __global__ __launch_bounds__(512) void outer_pc_kernel(const OuterArgs a)
     };
     auto produce = [&](int n) {
         const int b = n & 1;
+        float kmin = 0.f, vmin = 0.f;                  // lowest cumulative log2-gates (chunk totals)
         if (klane) {
             float pre[KRPT][4], excl[4];
             scan(rgk, KRPT, KSEG, kseg, pre, excl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kmin = fminf(kmin, excl[e] + pre[KRPT - 1][e]);
 #pragma unroll
             for (int r = 0; r < KRPT; ++r) {
                 const int t = kseg * KRPT + r;
@@ -455,6 +531,8 @@ __global__ __launch_bounds__(512) void outer_pc_kernel(const OuterArgs a)
             float pre[VRPT][4], excl[4];
             scan(rgvv, VRPT, VSEG, vseg, pre, excl);
 #pragma unroll
+            for (int e = 0; e < 4; ++e) vmin = fminf(vmin, excl[e] + pre[VRPT - 1][e]);
+#pragma unroll
             for (int r = 0; r < VRPT; ++r) {
                 const int t = vseg * VRPT + r;
                 const f32x4 vv = widen4(rvv[r]);
@@ -470,7 +548,30 @@ __global__ __launch_bounds__(512) void outer_pc_kernel(const OuterArgs a)
                 if (t == C - 1) *(f32x4 *)(sEB[b] + 4 * vcg) = up;
             }
         }
+        kmin = wave_min(kmin);
+        vmin = wave_min(vmin);
+        if (lane == 0) {
+            sMin[b][w][0] = kmin;
+            sMin[b][w][1] = vmin;
+        }
     };
+    // the chunk in buffer b is out of the factorised range (read after the barrier
+    // that publishes the producers' totals: every wave takes the same decision)
+    auto chunk_far = [&](int b) -> bool {
+        float km = sMin[b][0][0], vm = sMin[b][0][1];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            km = fminf(km, sMin[b][i][0]);
+            vm = fminf(vm, sMin[b][i][1]);
+        }
+        return __builtin_amdgcn_readfirstlane(km + vm < -kFastLim ? 1 : 0) != 0;
+    };
+    // Such a chunk runs token by token on the consumers' state registers; the consumer
+    // waves stage its rows from memory in groups of SR rows into the two operand
+    // buffers' space (both free here: the producers fill the next one afterwards), and
+    // the producers pass the same barriers.
+    constexpr int SR = outer_slow_rows(C, (int)sizeof(sQ), (int)sizeof(sEV), DK, ES);
+    static_assert(SR > 0, "token-loop staging within the operand buffers");
 
     // ---- consumers ---------------------------------------------------------------------
     const int c = w - 4, jl = 16 * c, j0 = vt * DVT + jl;
@@ -529,20 +630,55 @@ __global__ __launch_bounds__(512) void outer_pc_kernel(const OuterArgs a)
         }
     };
 
-    if (producer && nch > 0) {
-        load(0);
-        produce(0);
-        if (nch > 1) load(1);
-    }
-    for (int n = 0; n < nch; ++n) {
-        lds_barrier();                                   // buffer n ready, buffer n+1 free
-        if (producer) {
+    // The two roles run separate loops that meet at the same barriers.  A chunk out of
+    // range takes the consumers out of their loop into the token-by-token block after
+    // it, which rejoins the loop at the next chunk; the producers pass the same
+    // barriers and then prepare the next chunk as usual.
+    if (producer) {
+        if (nch > 0) {
+            load(0);
+            produce(0);
+            if (nch > 1) load(1);
+        }
+        for (int n = 0; n < nch; ++n) {
+            lds_barrier();                               // buffer n ready, buffer n+1 free
+            if (chunk_far(n & 1)) {
+                for (int r0 = 0; r0 < min(C, L - n * C); r0 += SR) {
+                    lds_barrier();
+                    lds_barrier();
+                }
+            }
             if (n + 1 < nch) {
                 produce(n + 1);
                 if (n + 2 < nch) load(n + 2);
             }
-        } else if (active) {
-            consume(n);
+        }
+    } else {
+        int n = 0;
+        for (;;) {
+            for (; n < nch; ++n) {
+                lds_barrier();                           // buffer n ready
+                if (chunk_far(n & 1)) break;
+                if (active) consume(n);
+            }
+            if (n >= nch) break;
+            const int nvalid = min(C, L - n * C);
+            float *const ev = &sEV[0][0];
+            const SlowStage<T> st{ev, ev + SR * DK, &sQ[0][0], &sQ[0][0] + SR * DK,
+                                  (T *)(ev + SR * DK + SR * SH::DVT)};
+            T *out = (T *)a.o + (hrow + (size_t)n * C) * DV + vt * DVT;
+            f32x4 zz[NKB] = {};
+            for (int r0 = 0; r0 < nvalid; r0 += SR) {
+                slow_stage<T, DK, SR, 256, ELU1, true, true>(st, rq, rk, rv, rg, rgv, n * C + r0, DV, vt * DVT, DVT,
+                                                             tid - 256);
+                lds_barrier();
+                if (active)
+                    slow_tokens<T, DK, NKB, 16, 16, true, false, true>(st, s, zz, 4 * grp, jl + x, DVT,
+                                                                       min(SR, nvalid - r0),
+                                                                       out + (size_t)r0 * DV + jl + x, DV, lane < 16);
+                lds_barrier();
+            }
+            ++n;
         }
     }
 

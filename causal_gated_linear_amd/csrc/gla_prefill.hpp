@@ -15,7 +15,10 @@
 // Scalar gates (one log-gate b per token) use the exact mask form instead, so no
 // factor exceeds 1: P = (phi(Q) phi(K)^T) * exp(b_t - b_s), O_inter = exp(b_t) phi(Q) S,
 // S <- exp(Gamma) S + (phi(K) * exp(Gamma - b))^T V.  The key-dim factorisation needs
-// exp(-B) finite: the in-chunk cumulative log-gate must stay above about -80.
+// exp(-B) well inside the fp32 range: a chunk whose cumulative log2-gate falls below
+// -kFastLim in some key dimension (flagged by the producers) is computed token by
+// token instead, by every wave of the workgroup (gla_slow.hpp), which is exact for
+// any gate in [0, 1].
 //
 // Decomposition: one workgroup per (batch*head, tile of DVT value columns) walks the
 // chunks of its head in order, with two kinds of wavefronts:
@@ -53,6 +56,7 @@
 
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
+#include "gla_slow.hpp"
 
 namespace gla {
 
@@ -277,6 +281,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     __shared__ __attribute__((aligned(16))) float sEG[NBUF][DK];     // exp(Gamma_i)
     __shared__ __attribute__((aligned(16))) float sB[NBUF][C + 1];   // scalar gate: B_t, then Gamma (log2)
     __shared__ __attribute__((aligned(16))) float sZ[NM ? 2 : 1][NM ? DK : 4];   // normaliser z, by parity
+    __shared__ __attribute__((aligned(16))) int sFlag[NBUF][4];      // per producer: chunk out of range
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -401,6 +406,15 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     const float incl = group_scan<RSEG, SH::CG>(run[e], lane);
                     excl[e] = incl - run[e];
                     tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64);
+                }
+                if constexpr (GATE == kGateKeydim) {
+                    // the chunk total is the lowest cumulative log2-gate of a column
+                    // (gates are <= 0); below -kFastLim the chunk runs token by token
+                    float m = tot[0];
+#pragma unroll
+                    for (int e = 1; e < CE; ++e) m = fminf(m, tot[e]);
+                    const bool far = __ballot(m < -kFastLim) != 0;
+                    if (lane == 0) sFlag[buf][p] = far ? 1 : 0;
                 }
                 if constexpr (GATE == kGateScalar) {
 #pragma unroll
@@ -802,12 +816,76 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         if constexpr (!SO) write_state(par ^ 1);
     };
 
+    // ---------------- chunks out of the factorised form's range -------------------------
+    // Whether the chunk in operand buffer `buf` has a cumulative log2-gate below
+    // -kFastLim (the producers' flags, read after the barrier that publishes them, so
+    // every wave takes the same decision).
+    auto chunk_far = [&](int buf) __attribute__((always_inline)) -> bool {
+        int f = 0;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) f |= sFlag[buf][i];
+        return __builtin_amdgcn_readfirstlane(f) != 0;
+    };
+    // The chunk starting at t0, token by token (gla_slow.hpp), by the consumer waves;
+    // the producers pass the same barriers (slow_barriers) and keep the rows they hold
+    // for the next chunks.  The consumers hand their fp32 state tiles over through the
+    // space of the bf16 state copies (as [j][i]) and take them back at the end; the
+    // operand buffers stage the rows.  Neither is needed otherwise at this point: the
+    // chunk's own operands are not used, and the producers fill the next chunk's buffer
+    // only afterwards.
+    constexpr int SR = NBUF == 2 ? C : C / 2;        // rows staged at a time
+    static_assert(SR * DK * 4 <= (int)sizeof(sQ) && 2 * SR * DK * ES <= (int)sizeof(sK) &&
+                  SR * DVT * ES <= (int)sizeof(sV) && DVT * DK * 4 <= (int)sizeof(sS) &&
+                  (!NM || DK * 4 <= (int)sizeof(sZ)), "token-loop staging within the operand buffers");
+    auto slow_barriers = [&](int t0) __attribute__((always_inline)) {
+        const int groups = (min(L - t0, C) + SR - 1) / SR;
+        for (int i = 0; i < 2 * groups + 3; ++i) lds_barrier();
+    };
+    auto slow_chunk = [&](int t0) __attribute__((always_inline)) {
+        float *const PS = (float *)&sS[0][0];
+        float *const PZ = &sZ[0][0];
+        const int nvalid = min(L - t0, C);
+        // S[16it + 4grp + r][16jt + x] -> PS[16jt + x][16it + 4grp + r]
+#pragma unroll
+        for (int k = 0; k < NSLOT; ++k) {
+            if (tile_ok(k)) {
+                const int it = tile_i(k), jt = tile_j(k);
+                *(f32x4 *)(PS + (16 * jt + x) * DK + 16 * it + 4 * grp) = S[k];
+            }
+        }
+        if constexpr (NM) {
+#pragma unroll
+            for (int m = 0; m < NZ; ++m)
+                if (z_ok(m) && x == 0) *(f32x4 *)(PZ + 16 * (c + NC * m) + 4 * grp) = Z[m];
+        }
+        lds_barrier();
+        const SlowStage<T> st{(float *)&sQ[0][0], nullptr, &sK[0][0], &sK[0][0] + SR * DK, &sV[0][0]};
+        slow_chunk_lds<T, DK, DVT, SR, 64 * NC, ELU1, !SO, NM, false>(
+            PS, PZ, st, rq, rk, rvv, rg, rg, t0, nvalid, DV, vt * DVT, SO ? nullptr : oh + (size_t)t0 * DV, tid - 64 * NP);
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < NSLOT; ++k) {
+            if (tile_ok(k)) {
+                const int it = tile_i(k), jt = tile_j(k);
+                S[k] = *(const f32x4 *)(PS + (16 * jt + x) * DK + 16 * it + 4 * grp);
+            }
+        }
+        if constexpr (NM) {
+#pragma unroll
+            for (int m = 0; m < NZ; ++m)
+                if (z_ok(m)) Z[m] = *(const f32x4 *)(PZ + 16 * (c + NC * m) + 4 * grp);
+        }
+        lds_barrier();
+    };
+    constexpr bool KD = GATE == kGateKeydim;
+
     // ---------------- pipeline ---------------------------------------------------------
     // The two roles run separate loops (so their registers are not live at the same
     // time) that meet at the same number of barriers.  With two buffers both run
     // 1 + 2*npairs barriers over chunk pairs; producers always request and prepare
-    // (rows are clamped into range, surplus operands are never read), so the loop has
-    // no branch around its global loads.  With one buffer: 2 * nchunks barriers.
+    // (rows past the end read as zeros, surplus operands are never read), so the loop
+    // has no branch around its global loads.  With one buffer: 2 * nchunks barriers.
+    // A chunk out of the factorised range adds the same barriers on both sides.
     if (producer) {
         if constexpr (NBUF == 2) {
             const int npairs = (nchunks + 1) / 2;
@@ -819,8 +897,15 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
             }
             lds_barrier();
             for (int n = 0; n < 2 * npairs; n += 2) {
+                // chunk n (buffer 0) out of range: the consumers compute it token by token
+                if constexpr (KD) {
+                    if (n < nchunks && chunk_far(0)) slow_barriers(n * C);
+                }
                 produce(R[1], (n + 1) * C, 1, (n + 3) * C);
                 lds_barrier();
+                if constexpr (KD) {
+                    if (n + 1 < nchunks && chunk_far(1)) slow_barriers((n + 1) * C);
+                }
                 produce(R[0], (n + 2) * C, 0, (n + 4) * C);
                 lds_barrier();
             }
@@ -829,6 +914,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
             for (int n = 0; n < nchunks; ++n) {
                 produce(R[0], n * C, 0, (n + 1) * C);
                 lds_barrier();
+                if constexpr (KD) {
+                    if (chunk_far(0)) slow_barriers(n * C);
+                }
                 lds_barrier();
             }
         }
@@ -846,15 +934,39 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         if constexpr (NBUF == 2) {
             const int npairs = (nchunks + 1) / 2;
             lds_barrier();
-            for (int n = 0; n < 2 * npairs; ++n) {
-                if (n < nchunks) consume(n * C, n & 1, n & 1);
+            // a chunk out of range leaves the loop for the token-by-token block below,
+            // which rejoins it at the next chunk (keeps that block out of the loop body)
+            int n = 0;
+            for (;;) {
+                for (; n < 2 * npairs; ++n) {
+                    if (n < nchunks) {
+                        if (KD && chunk_far(n & 1)) break;
+                        consume(n * C, n & 1, n & 1);
+                    }
+                    lds_barrier();
+                }
+                if (n >= 2 * npairs) break;
+                slow_chunk(n * C);
+                if constexpr (!SO) write_state((n & 1) ^ 1);
+                write_z((n & 1) ^ 1);
                 lds_barrier();
+                ++n;
             }
         } else {
-            for (int n = 0; n < nchunks; ++n) {
+            int n = 0;
+            for (;;) {
+                for (; n < nchunks; ++n) {
+                    lds_barrier();
+                    if (KD && chunk_far(0)) break;
+                    consume(n * C, 0, n & 1);
+                    lds_barrier();
+                }
+                if (n >= nchunks) break;
+                slow_chunk(n * C);
+                if constexpr (!SO) write_state((n & 1) ^ 1);
+                write_z((n & 1) ^ 1);
                 lds_barrier();
-                consume(n * C, 0, n & 1);
-                lds_barrier();
+                ++n;
             }
         }
         if (a.s_final && (!a.final_last_seg || seg == a.nseg - 1)) {

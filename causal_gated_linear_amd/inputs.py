@@ -37,6 +37,18 @@ The outer-product gate (G_t = alpha_t beta_t^T, same section) reuses a workload'
 q, k, v and key-dim gates and adds value-dim log-gates from ``draw_value_gate``: the
 same recipe logsigmoid(z)/16, z ~ N(0,1), drawn with seed + 3571.
 
+Strong gates.  The pages put every gate in (0, 1) with no lower bound ("Gated Linear
+Attention", Recurrent Form), so the key-dim and outer-gate prefills are also checked
+with log-gates far below the workloads' logsigmoid(z)/16, drawn by ``draw_strong_gate``
+([B, H, L, d], fp32, from its own seed):
+
+  tau1      logsigmoid(z), z ~ N(0,1): the page's own sigma(W_up W_down x), tau = 1
+  const3    g = -3 everywhere (alpha = 0.0498)
+  vanish    g = -1000 everywhere (alpha underflows to 0 even in fp64)
+  mixed     half of the dimensions logsigmoid(z)/16, the other half logsigmoid(z) - 6
+  bursts    logsigmoid(z)/16, with every token t = 37 (mod 53) set to -200 in every
+            dimension (a reset), so that strong and weak chunks alternate
+
 The gate producer ("Gated Linear Attention", Recurrent Form: alpha_t =
 sigmoid(W_up W_down x_t)) has synthetic weights, drawn by ``draw_gate`` in the
 order x, W_down, W_up:
@@ -221,3 +233,26 @@ def draw_value_gate(w: Workload, *, B=None, H=None, L=None, seed=None, device="c
     gen = _gen(device, seed)
     z = torch.randn(B, H, L, w.d_v, dtype=torch.float32, device=device, generator=gen)
     return _log_gate(z, "keydim").contiguous()
+
+
+STRONG_GATES = ("tau1", "const3", "vanish", "mixed", "bursts")
+
+
+def draw_strong_gate(kind, B, H, L, d, *, seed, device="cpu"):
+    """Log-gates [B, H, L, d] (fp32) of one of the STRONG_GATES recipes above."""
+    gen = _gen(device, seed)
+    z = torch.randn(B, H, L, d, dtype=torch.float32, device=device, generator=gen)
+    if kind == "tau1":
+        g = F.logsigmoid(z)
+    elif kind == "const3":
+        g = torch.full_like(z, -3.0)
+    elif kind == "vanish":
+        g = torch.full_like(z, -1000.0)
+    elif kind == "mixed":
+        g = torch.where(torch.arange(d, device=device) % 2 == 0, F.logsigmoid(z) / 16.0, F.logsigmoid(z) - 6.0)
+    elif kind == "bursts":
+        g = F.logsigmoid(z) / 16.0
+        g[:, :, 37::53, :] = -200.0
+    else:
+        raise ValueError(kind)
+    return g.contiguous()

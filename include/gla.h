@@ -34,13 +34,13 @@
  *    key-dim gates g: [B][H][L][d_k]; scalar gates g: [B][H][L]; states s0,
  *    s_final, state: [B][H][d_k][d_v], always fp32; gates always fp32 natural-log
  *    values g = log(alpha), finite and <= 0 (outside that domain results are
- *    undefined; the library does not scan device data to check it).  Key-dim
- *    gates in gla_prefill_chunked: the chunkwise form scales keys by
- *    exp(-(sum of the chunk's log-gates up to that token)), so results are exact up
- *    to rounding while, in every key dimension, the log-gates summed over any one
- *    chunk stay above about -80 (chunk 64: a mean log-gate above -1.25); stronger
- *    gates need a smaller chunk.  Scalar gates and gla_decode_step have no such
- *    limit.
+ *    undefined; the library does not scan device data to check it).  Every finite
+ *    log-gate <= 0 is exact up to rounding, however strong: the chunkwise
+ *    form scales keys by exp(-(sum of the chunk's log-gates up to that token)), and a
+ *    chunk whose log-gates sum below -100 / log2(e) (about -69.3) in some key
+ *    dimension is computed token by token instead, inside the same launch.  Such
+ *    chunks cost several times a regular chunk; the result does not depend on which
+ *    form a chunk took beyond rounding.
  *  - q, k, v and o share one dtype (GLA_F32 or GLA_BF16); bf16 results are rounded
  *    to nearest even.  Arithmetic: fp32 accumulation and fp32 state; with bf16
  *    inputs the matrix-core operands are bf16.
@@ -303,11 +303,11 @@ int gla_gate_project(const void *x, const void *w_down, const void *w_up, float 
  * with alpha_t = exp(g_t) and beta_t = exp(gv_t).  Arguments as gla_prefill_chunked
  * with a key-dimension gate, plus
  *   gv        in   fp32 [B][H][L][d_v] value-dimension log-gates (finite, <= 0)
- * No workspace.  As for the key-dimension gate, results are exact up to rounding
- * while, in every key and every value dimension, the log-gates summed over one chunk
- * stay above about -80.  o must not overlap any other argument; s_final must not
- * overlap any input (it may equal s0).  Errors as gla_prefill_chunked (no
- * GLA_ERR_WORKSPACE).
+ * No workspace.  Every gate strength is exact up to rounding: a chunk whose lowest
+ * key-dimension and lowest value-dimension log-gate sums add up to less than
+ * -100 / log2(e) is computed token by token instead (as for the key-dimension gate).
+ * o must not overlap any other argument; s_final must not overlap any input (it may
+ * equal s0).  Errors as gla_prefill_chunked (no GLA_ERR_WORKSPACE).
  */
 int gla_prefill_outer(const void *q, const void *k, const void *v, const float *g, const float *gv,
                       const float *s0, void *o, float *s_final, int B, int H, int L, int d_k, int d_v,
