@@ -12,7 +12,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgla.so")
 
-# (name, restype, argtypes) for every entry point of include/gla.h
+# (name, restype, argtypes) for every entry point of include/gla.h and the test hook
+# of include/gla_testing.h
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
@@ -33,6 +34,7 @@ SIGNATURES = [
     ("gla_prefill_outer", _I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     ("gla_decode_step_outer", _I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     ("gla_strerror", ctypes.c_char_p, [_I]),
+    ("gla_testing_set_plan", _I, [_I, _I, _I]),
     ("gla_last_error_detail", ctypes.c_char_p, []),
 ]
 

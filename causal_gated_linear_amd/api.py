@@ -41,6 +41,16 @@ def _check_tensor(t, name, shape, dtype, device):
     _need(t.device == device, "%s is on %s, expected %s" % (name, t.device, device))
 
 
+def _workspace(nbytes, dev, stream):
+    """A device workspace of nbytes for a launch on ``stream``.  The tensor is freed when
+    the caller returns, while the kernel may still run: record the launch stream, so
+    the caching allocator reuses the memory only after the work queued there."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
 def workspace_bytes(B, H, L, d_k, d_v, chunk, dtype=torch.bfloat16) -> int:
     """Bytes of device workspace gla_prefill_chunked needs for these sizes."""
     return int(_lib.load().gla_prefill_workspace_bytes(B, H, L, d_k, d_v, chunk, _DTYPES[dtype]))
@@ -90,7 +100,7 @@ def prefill(q, k, v, log_gate=None, gate=None, initial_state=None, chunk=64, fea
         _check_tensor(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
     need = workspace_bytes(B, H, L, dk, dv, chunk, dt)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace(need, dev, stream)
     if workspace is not None:
         _need(workspace.is_contiguous() and workspace.device == dev, "workspace must be contiguous on %s" % dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -107,7 +117,8 @@ def prefill_norm(q, k, v, log_gate=None, gate=None, initial_state=None, initial_
                  feature_map=None, out=None, final_state=None, final_norm=None, stream=None):
     """Normalised chunkwise prefill (gla_prefill_chunked_norm): as ``prefill``, with the
     normaliser state z (fp32 [B, H, d_k]); o_t = S_t^T phi(q_t) / phi(q_t) . z_t.
-    Returns (o, s_final, z_final); ``final_norm`` may be ``initial_norm`` (in place)."""
+    Returns (o, s_final, z_final); ``final_state`` may be ``initial_state`` (in place),
+    ``final_norm`` must be a buffer of its own."""
     lib = _lib.load()
     B, H, L, dk, dv, dev, dt, gate = _check_prefill(q, k, v, log_gate, gate, initial_state)
     if initial_norm is not None:
@@ -214,7 +225,7 @@ def prefill_delta(q, k, v, beta, initial_state=None, chunk=32, out=None, final_s
         _check_tensor(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
     need = delta_workspace_bytes(B, H, L, dk, dv, chunk, dt)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace(need, dev, stream)
     if workspace is not None:
         _need(workspace.is_contiguous() and workspace.device == dev, "workspace must be contiguous on %s" % dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

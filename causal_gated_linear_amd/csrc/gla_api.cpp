@@ -16,8 +16,12 @@
 
 #include "gla.h"
 #include "gla_launch.hpp"
+#include "gla_testing.h"
 
 namespace gla {
+// Launch-plan choices forced by gla_testing_set_plan (0: automatic).
+static int g_force_prefill_tile = 0, g_force_prefill_segments = 0, g_force_delta_tile = 0;
+
 hipError_t launch_prefill_0_16(const PrefillArgs &, int, int, bool, hipStream_t);
 hipError_t launch_prefill_0_32(const PrefillArgs &, int, int, bool, hipStream_t);
 hipError_t launch_prefill_0_64(const PrefillArgs &, int, int, bool, hipStream_t);
@@ -49,8 +53,8 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, i
 }
 
 // Launch shape: the widest value tile (64, 32 or 16 columns) that fits in LDS and
-// still gives at least 256 workgroups for the 256 compute units.
-// GLA_PREFILL_TILE=<columns> overrides the choice (a tuning knob).
+// still gives at least 256 workgroups for the 256 compute units (a test can force
+// another usable width through gla_testing_set_plan).
 static bool tile_usable(int dvt, int d_k, int d_v, int chunk, int elem_bytes)
 {
     return dvt <= d_v && d_v % dvt == 0 && prefill_nbuf(elem_bytes, d_k, chunk, dvt) > 0;
@@ -58,11 +62,8 @@ static bool tile_usable(int dvt, int d_k, int d_v, int chunk, int elem_bytes)
 
 int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes)
 {
-    const char *env = getenv("GLA_PREFILL_TILE");
-    if (env) {
-        const int dvt = atoi(env);
-        if ((dvt == 16 || dvt == 32 || dvt == 64) && tile_usable(dvt, d_k, d_v, chunk, elem_bytes)) return dvt;
-    }
+    const int forced = g_force_prefill_tile;
+    if (forced && tile_usable(forced, d_k, d_v, chunk, elem_bytes)) return forced;
     const long bh = BH;
     if (tile_usable(64, d_k, d_v, chunk, elem_bytes) && bh * (d_v / 64) >= 256) return 64;
     if (tile_usable(32, d_k, d_v, chunk, elem_bytes) && bh * (d_v / 32) >= 256) return 32;
@@ -78,7 +79,7 @@ int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes)
 // segments keep at least 16 chunks.  Sequences of 32 to 63 chunks are split too when
 // even the narrowest tile leaves CUs idle (fewer than 256 workgroups), into segments
 // of at least 4 chunks, so that each tile's chain of chunks is short.
-// GLA_PREFILL_SEGMENTS=<n> overrides the count.
+// gla_testing_set_plan can force the count.
 constexpr int kSegMinChunks = 16, kSegMinSeqChunks = 64;
 constexpr int kSegShortMinChunks = 4, kSegShortSeqChunks = 32;
 
@@ -96,8 +97,8 @@ PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_by
     } else if (nchunks >= kSegShortSeqChunks && (long)BH * (d_v / 16) < 256) {
         while (wgs * nseg * 2 <= 256 && nchunks / (2 * nseg) >= kSegShortMinChunks) nseg *= 2;
     }
-    const char *env = getenv("GLA_PREFILL_SEGMENTS");
-    if (env && atoi(env) >= 1) nseg = atoi(env) < nchunks ? atoi(env) : (nchunks > 0 ? nchunks : 1);
+    const int forced = g_force_prefill_segments;
+    if (forced >= 1) nseg = forced < nchunks ? forced : (nchunks > 0 ? nchunks : 1);
     if (nseg > 1) {
         const int cps = (nchunks + nseg - 1) / nseg;   // chunks per segment
         p.nseg = (nchunks + cps - 1) / cps;
@@ -205,6 +206,18 @@ const char *gla_strerror(int status)
 
 const char *gla_last_error_detail(void) { return g_detail.c_str(); }
 
+int gla_testing_set_plan(int prefill_tile, int prefill_segments, int delta_tile)
+{
+    auto tile_ok = [](int t) { return t == 0 || t == 16 || t == 32 || t == 64; };
+    if (!tile_ok(prefill_tile) || !tile_ok(delta_tile) || prefill_segments < 0)
+        return fail(GLA_ERR_UNSUPPORTED, "gla_testing_set_plan(%d, %d, %d): tiles must be 0, 16, 32 or 64 and "
+                    "segments >= 0", prefill_tile, prefill_segments, delta_tile);
+    gla::g_force_prefill_tile = prefill_tile;
+    gla::g_force_prefill_segments = prefill_segments;
+    gla::g_force_delta_tile = delta_tile;
+    return ok();
+}
+
 int gla_state_alloc(int B, int H, int d_k, int d_v, float **state, gla_stream_t stream)
 {
     if (!state) return fail(GLA_ERR_NULL, "state out-pointer is NULL");
@@ -299,8 +312,10 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
     const Span zf_forbidden[] = {sq, sk, sv, sg, sw, ss0};
     for (const Span &x : zf_forbidden)
         if (overlap(szf, x)) return fail(GLA_ERR_ALIAS, "z_final overlaps %s", x.name);
-    if (overlap(szf, sz0) && z_final != z0)
-        return fail(GLA_ERR_ALIAS, "z_final partially overlaps z0");
+    // every value-column workgroup of a head reads all of z0 when it starts, and one of
+    // them writes z_final when it ends: an in-place z would race between workgroups
+    if (overlap(szf, sz0))
+        return fail(GLA_ERR_ALIAS, "z_final overlaps z0 (in-place normaliser state is not supported)");
 
     gla::PrefillPlan plan = gla::prefill_plan((int)BH, L, d_k, d_v, chunk, (int)es);
     if (norm) plan = {gla::prefill_tile((int)BH, d_k, d_v, chunk, (int)es), 1, L};
@@ -479,8 +494,7 @@ int gla_prefill_delta(const void *q, const void *k, const void *v, const float *
     a.ws_u = workspace ? (char *)workspace + BH * lp * d_k * es : nullptr;
     a.BH = (int)BH; a.L = L; a.d_k = d_k; a.d_v = d_v;
     a.dvt = d_v < 64 ? d_v : 64;
-    const char *env = getenv("GLA_DELTA_TILE");
-    if (env && (atoi(env) == 16 || atoi(env) == 32 || atoi(env) == 64) && atoi(env) <= d_v) a.dvt = atoi(env);
+    if (gla::g_force_delta_tile && gla::g_force_delta_tile <= d_v) a.dvt = gla::g_force_delta_tile;
     a.n_vt = d_v / a.dvt;
     const long grid = (long)BH * a.n_vt;
     a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;

@@ -179,7 +179,8 @@ int gla_decode_step(const void *q, const void *k, const void *v, const float *g,
  * Arguments as gla_prefill_chunked, plus
  *   z0        in   fp32 [B][H][d_k] initial normaliser state, or NULL for zero
  *   z_final   out  fp32 [B][H][d_k] normaliser state after the last token, or NULL;
- *                  may equal z0 but must not partially overlap it
+ *                  must not overlap z0 (GLA_ERR_ALIAS): every workgroup of a head
+ *                  reads all of z0, so it cannot be rewritten in place
  * No workspace is used.  The denominator must not vanish: no epsilon is added.  With
  * phi = elu+1 (positive features) and z0 = 0 it is positive for every token; with
  * the identity map it can be zero or negative, and such outputs are undefined.  o

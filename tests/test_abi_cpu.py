@@ -12,6 +12,7 @@ from causal_gated_linear_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gla.h")
+TEST_HEADER = os.path.join(ROOT, "include", "gla_testing.h")
 
 
 @pytest.fixture(scope="module")
@@ -22,8 +23,8 @@ def lib():
     return _lib.load()
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(*headers):
+    text = "".join(open(h).read() for h in (headers or (HEADER,)))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(gla_[a-z_]+)\s*\(", text)))
 
@@ -39,9 +40,26 @@ def test_header_declares_expected_entry_points():
 
 def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(_lib.LIB_PATH)
-    for name in _declared():
+    both = _declared(HEADER, TEST_HEADER)
+    assert _declared(TEST_HEADER) == ["gla_testing_set_plan"]
+    for name in both:
         assert hasattr(raw, name), name
-    assert sorted(n for n, _, _ in _lib.SIGNATURES) == _declared()
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == both
+
+
+def test_testing_plan_hook(lib):
+    """gla_testing_set_plan validates its values, and the workspace query follows the
+    forced segment count (then returns to the automatic plan)."""
+    for bad in [(8, 0, 0), (0, -1, 0), (0, 0, 128), (48, 0, 0)]:
+        assert lib.gla_testing_set_plan(*bad) == _lib.GLA_ERR_UNSUPPORTED
+    args = (1, 2, 64 * 20, 128, 128, 64, _lib.GLA_BF16)
+    assert lib.gla_prefill_workspace_bytes(*args) == 0          # 2 heads of 20 chunks: one segment
+    try:
+        assert lib.gla_testing_set_plan(0, 3, 0) == _lib.GLA_OK
+        assert lib.gla_prefill_workspace_bytes(*args) > 0
+    finally:
+        assert lib.gla_testing_set_plan(0, 0, 0) == _lib.GLA_OK
+    assert lib.gla_prefill_workspace_bytes(*args) == 0
 
 
 def test_strerror_covers_every_status(lib):
@@ -208,6 +226,7 @@ PREFILL_NORM_BAD = {
     "o_overlaps_z_final": (dict(z_final=A + 96 * MB + 256), _lib.GLA_ERR_ALIAS),
     "z_final_overlaps_k": (dict(z_final=A + 16 * MB + 64), _lib.GLA_ERR_ALIAS),
     "z_final_partially_overlaps_z0": (dict(z0=A + 200 * MB, z_final=A + 200 * MB + 16), _lib.GLA_ERR_ALIAS),
+    "z_final_equals_z0": (dict(z0=A + 200 * MB, z_final=A + 200 * MB), _lib.GLA_ERR_ALIAS),
     "s_final_overlaps_z0": (dict(z0=A + 128 * MB + 32), _lib.GLA_ERR_ALIAS),
 }
 
@@ -390,3 +409,4 @@ def test_decode_outer_rejects(lib):
     assert call(None, A + 16 * MB) == _lib.GLA_ERR_NULL
     assert call(A + 4 * MB + 8, A + 16 * MB) == _lib.GLA_ERR_ALIGN
     assert call(A + 4 * MB, A + 4 * MB + 256) == _lib.GLA_ERR_ALIAS      # state overlaps gv
+
