@@ -23,6 +23,7 @@ SIGNATURES = [
     ("gla_prefill_workspace_bytes", _SZ, [_I, _I, _I, _I, _I, _I, _I]),
     ("gla_prefill_chunked", _I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                  _P, _SZ, _P]),
+    ("gla_prefill_chunked_noalloc", _I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     ("gla_decode_step", _I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     ("gla_prefill_chunked_norm", _I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                       _I, _I, _I, _P]),

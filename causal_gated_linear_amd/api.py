@@ -113,6 +113,30 @@ def prefill(q, k, v, log_gate=None, gate=None, initial_state=None, chunk=64, fea
     return out, final_state
 
 
+def prefill_noalloc(q, k, v, log_gate=None, gate=None, initial_state=None, chunk=64, feature_map=None,
+                    out=None, final_state=None, stream=None):
+    """gla_prefill_chunked_noalloc: ``prefill`` without a workspace; the library's own
+    per-GPU scratch array serves segmented sizes (at most 32 MiB of workspace).  The
+    C entry point allocates nothing; pass ``out`` and ``final_state`` to keep this
+    wrapper from allocating them.  Returns (o, s_final)."""
+    lib = _lib.load()
+    B, H, L, dk, dv, dev, dt, gate = _check_prefill(q, k, v, log_gate, gate, initial_state)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor(out, "out", (B, H, L, dv), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
+    st = lib.gla_prefill_chunked_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _lib.GATES[gate],
+                                         _ptr(initial_state), _ptr(out), _ptr(final_state), B, H, L, dk, dv,
+                                         int(chunk), _DTYPES[dt], _lib.FEATURE_MAPS[feature_map],
+                                         _stream_handle(stream))
+    _lib.check(st, "gla_prefill_chunked_noalloc")
+    return out, final_state
+
+
 def prefill_norm(q, k, v, log_gate=None, gate=None, initial_state=None, initial_norm=None, chunk=64,
                  feature_map=None, out=None, final_state=None, final_norm=None, stream=None):
     """Normalised chunkwise prefill (gla_prefill_chunked_norm): as ``prefill``, with the

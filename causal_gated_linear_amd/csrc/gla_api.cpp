@@ -12,6 +12,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "gla.h"
@@ -184,6 +185,36 @@ int check_common(int B, int H, int d_k, int d_v, gla_dtype dtype, gla_gate_mode 
     return GLA_OK;
 }
 
+// ---- scratch of the allocation-free prefill (gla_prefill_chunked_noalloc) ----------
+// A segmented prefill's workspace (segment states and gate totals) comes from this
+// array: each device the library runs on holds its own copy until the process ends.
+// Its device address is looked up once per device, with that device current; host
+// code uses only that address, never the array's name.  Nothing in it must start at
+// zero: every byte a launch reads was written earlier in the same call.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+int scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GLA_ERR_HIP, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GLA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,7 +300,7 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
                         gla_gate_mode gate, const float *s0, const float *z0, void *o, float *s_final,
                         float *z_final, int B, int H, int L, int d_k, int d_v, int chunk,
                         gla_dtype dtype, gla_feature_map phi, void *workspace,
-                        size_t workspace_bytes, gla_stream_t stream, bool norm)
+                        size_t workspace_bytes, gla_stream_t stream, bool norm, bool use_scratch = false)
 {
     if (L < 0) return fail(GLA_ERR_SHAPE, "L=%d must be >= 0", L);
     int st = check_common(B, H, d_k, d_v, dtype, gate, phi, g, L > 0);
@@ -288,7 +319,10 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(GLA_ERR_ALIGN, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
     const size_t need = norm ? 0 : gla_prefill_workspace_bytes(B, H, L, d_k, d_v, chunk, dtype);
-    if (need > 0 && (!workspace || workspace_bytes < need))
+    if (use_scratch && need > kScratchBytes)
+        return fail(GLA_ERR_WORKSPACE, "these sizes need %zu bytes of scratch; the allocation-free prefill "
+                    "holds %zu (use gla_prefill_chunked with a workspace)", need, kScratchBytes);
+    if (!use_scratch && need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
 
@@ -330,6 +364,10 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
     if (grid > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H too large");
     a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
     if (L == 0 && !s_final && !z_final) return ok();
+    if (use_scratch && plan.nseg > 1) {             // validation done: now the HIP lookup
+        st = scratch_address(&workspace);
+        if (st != GLA_OK) return st;
+    }
     const int dt = dtype == GLA_BF16 ? 1 : 0;
     const hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
@@ -367,6 +405,15 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
 {
     return prefill_impl(q, k, v, g, gate, s0, nullptr, o, s_final, nullptr, B, H, L, d_k, d_v, chunk,
                         dtype, phi, workspace, workspace_bytes, stream, false);
+}
+
+int gla_prefill_chunked_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                gla_gate_mode gate, const float *s0, void *o, float *s_final, int B, int H,
+                                int L, int d_k, int d_v, int chunk, gla_dtype dtype, gla_feature_map phi,
+                                gla_stream_t stream)
+{
+    return prefill_impl(q, k, v, g, gate, s0, nullptr, o, s_final, nullptr, B, H, L, d_k, d_v, chunk, dtype, phi,
+                        nullptr, 0, stream, false, true);
 }
 
 int gla_prefill_chunked_norm(const void *q, const void *k, const void *v, const float *g,

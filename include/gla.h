@@ -147,6 +147,24 @@ int gla_prefill_chunked(const void *q, const void *k, const void *v, const float
                         gla_stream_t stream);
 
 /*
+ * gla_prefill_chunked_noalloc -- gla_prefill_chunked for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation).  It allocates nothing and takes no workspace: when the sizes need one
+ * (few long sequences, split into segments), it uses a scratch array that the library
+ * holds in the device memory of each GPU it runs on, 32 MiB, kept until the process
+ * ends; that covers the workspace of every size the library's launch plan segments.
+ * Arguments, results and errors as gla_prefill_chunked without the workspace; a
+ * workspace need (gla_prefill_workspace_bytes) above 32 MiB returns GLA_ERR_WORKSPACE.  Every call on one GPU shares that GPU's array: calls that may
+ * overlap in time on one GPU (other streams, other threads) race, so callers order
+ * them on one stream or otherwise serialise them.  The first call on a device looks up
+ * the array's address there (a HIP call, after validation).
+ */
+int gla_prefill_chunked_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                gla_gate_mode gate, const float *s0, void *o, float *s_final, int B, int H,
+                                int L, int d_k, int d_v, int chunk, gla_dtype dtype, gla_feature_map phi,
+                                gla_stream_t stream);
+
+/*
  * gla_decode_step -- one token of the recurrence on a resident state: for every
  * (b, h), state <- Diag(alpha) state + phi(k) v^T in place, then
  * o = state^T phi(q) ("Attention is recurrent", Linear attention and Gated linear

@@ -35,7 +35,8 @@ def test_header_declares_expected_entry_points():
                                   "gla_last_error_detail", "gla_prefill_chunked_norm",
                                   "gla_decode_step_norm", "gla_delta_workspace_bytes",
                                   "gla_prefill_delta", "gla_decode_step_delta", "gla_gate_project",
-                                  "gla_prefill_outer", "gla_decode_step_outer"])
+                                  "gla_prefill_outer", "gla_decode_step_outer",
+                                  "gla_prefill_chunked_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -410,3 +411,31 @@ def test_decode_outer_rejects(lib):
     assert call(A + 4 * MB + 8, A + 16 * MB) == _lib.GLA_ERR_ALIGN
     assert call(A + 4 * MB, A + 4 * MB + 256) == _lib.GLA_ERR_ALIAS      # state overlaps gv
 
+
+def test_prefill_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """The allocation-free prefill holds 32 MiB of scratch, which covers every size the
+    automatic plan segments (at most about 254 head-segments of 128 KiB of states).  A
+    plan forced through the test hook to more segments needs more and is rejected on
+    the host, before any HIP call."""
+    P = ctypes.c_void_p
+    B, H, L = 1, 16, 64 * 2000
+    assert lib.gla_prefill_workspace_bytes(B, H, L, 128, 128, 64, _lib.GLA_BF16) <= 32 << 20
+    try:
+        assert lib.gla_testing_set_plan(0, 64, 0) == _lib.GLA_OK      # 16 heads x 64 segments
+        assert lib.gla_prefill_workspace_bytes(B, H, L, 128, 128, 64, _lib.GLA_BF16) > 32 << 20
+        st = lib.gla_prefill_chunked_noalloc(P(A), P(A + 256 * MB), P(A + 512 * MB), P(A + 768 * MB), 1, None,
+                                             P(A + 1280 * MB), None, B, H, L, 128, 128, 64, _lib.GLA_BF16, 0,
+                                             None)
+        detail = lib.gla_last_error_detail().decode()
+    finally:
+        lib.gla_testing_set_plan(0, 0, 0)
+    assert st == _lib.GLA_ERR_WORKSPACE
+    assert "scratch" in detail
+
+
+def test_prefill_noalloc_scratch_covers_every_automatic_plan(lib):
+    """The largest automatic segmented workspace over head counts and lengths (d = 128,
+    the widest state) stays within the 32 MiB of scratch."""
+    worst = max(lib.gla_prefill_workspace_bytes(1, bh, 64 * 4096, 128, 128, 64, _lib.GLA_BF16)
+                for bh in range(1, 300))
+    assert 0 < worst <= 32 << 20
