@@ -41,7 +41,7 @@ BF16_MFMA_PEAK_TFLOPS = 2516.6        # dense bf16 MFMA, TFLOP/s (256 CU x 4096 
 
 PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_KERNEL = "prefill_kernel"
-PREFILL_SOURCES = ("gla_prefill.hpp", "gla_prefill_inst.hip", "gla_device.hpp", "gla_launch.hpp")
+PREFILL_SOURCES = ("gla_prefill.hpp", "gla_prefill_inst.hip", "gla_device.hpp", "gla_launch.hpp", "gla_slow.hpp")
 TRAFFIC_FILE = os.path.join(PROFILES, "prefill_kernel_bf16_dk128_L4096_traffic.txt")
 STATS_FILE = os.path.join(PROFILES, "gla_kernels_bench_workloads_kernel_stats.txt")
 COPY_MIB = 512                        # calibration copy: reads and writes this many MiB
@@ -203,15 +203,20 @@ def run_prefill(args, torch, api, inputs):
     one = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     launch_stats = {"launches": len(one), "min_ms": one[0], "median_ms": one[len(one) // 2],
                     "p90_ms": one[min(len(one) - 1, (9 * len(one)) // 10)]}
+    flush = torch.empty(2**28, dtype=torch.float32, device="cuda")
+    launch_stats["cold_median_ms"] = _cold_ms(torch, step, stream, 15, flush)
+    del flush
     nbytes = prefill_bytes(w.B, w.H, w.L, w.d_k, w.d_v)
     flops = prefill_flops(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)
     return dict(w=w, inp=inp, ms_per_step=per, wall_s=wall, bytes=nbytes, flops=flops,
                 settle_launches=settle, launch_stats=launch_stats)
 
 
-def run_other_prefills(args, torch, api, inputs):
+def run_other_prefills(args, torch, api, inputs, baselines=None):
     """The other prefill workloads, timed the same way (reported beside the headline;
-    fewer steps).  Bytes follow the same convention as the headline workload."""
+    fewer steps), each also with the caches flushed before every launch.  Bytes follow
+    the same convention as the headline workload.  With ``baselines`` (a dict), the
+    oracle is timed on each workload's inputs too (cpu_baseline_prefill)."""
     out = {}
     for name in ("linear_elu1", "scalar_long", "fp32_single_head"):
         w = inputs.WORKLOADS[name]
@@ -233,11 +238,11 @@ def run_other_prefills(args, torch, api, inputs):
         es = 2 if w.dtype == torch.bfloat16 else 4
         nbytes = prefill_bytes(w.B, w.H, w.L, w.d_k, w.d_v, es=es, gate=w.gate or "none")
         gbs = nbytes / (per / 1e3) / 1e9
-        cold = None
-        if nbytes < 2**28:                       # fits the last-level cache: also time it cold
-            flush = torch.empty(2**28, dtype=torch.float32, device="cuda")
-            cold = _cold_ms(torch, step, stream, 15, flush)
-            del flush
+        flush = torch.empty(2**28, dtype=torch.float32, device="cuda")
+        cold = _cold_ms(torch, step, stream, 15, flush)
+        del flush
+        if baselines is not None:
+            baselines[name] = cpu_baseline_prefill(w, inp, args.cpu_budget_s / 5)
         out[name] = {"ms_per_step": per, "ms_per_step_cold": cold, "tokens_per_s": w.B * w.L / (per / 1e3),
                      "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes,
                      "shape": "B=%d H=%d L=%d d_k=%d d_v=%d chunk=%d %s gate=%s phi=%s" % (
@@ -276,9 +281,14 @@ def run_decode(args, torch, api, inputs):
     w = inputs.WORKLOADS["decode"]
     pre = inputs.draw(w, device="cuda")
     _, state = api.prefill(pre["q"], pre["k"], pre["v"], log_gate=pre["g"], gate="keydim", chunk=w.chunk)
-    del pre
     T = args.decode_steps
     d = inputs.draw_decode(w, steps=T, device="cuda")
+    # one head of every sequence, prompt then steps, for the oracle beside the decode
+    bi = torch.arange(w.B, device="cuda")
+    hi = (7 * bi) % w.H
+    sample = {key: torch.cat([pre[key][bi, hi], d[key][:, bi, hi].transpose(0, 1)], dim=1).unsqueeze(1).cpu()
+              for key in ("q", "k", "v", "g")}
+    del pre
     o = torch.empty(w.B, w.H, w.d_v, dtype=w.dtype, device="cuda")
     stream = torch.cuda.current_stream()
     saved = state.clone()
@@ -296,6 +306,12 @@ def run_decode(args, torch, api, inputs):
 
     ms = _events_ms(step, T, stream)
     per = ms / T
+    # single steps with the caches flushed before each (the 512 MiB state exceeds them
+    # anyway; the step inputs do not)
+    flush = torch.empty(2**28, dtype=torch.float32, device="cuda")
+    it = iter(range(T))
+    cold = _cold_ms(torch, step, stream, min(T, 15), flush)
+    del flush
     nbytes = decode_step_bytes(w.B, w.H, w.d_k, w.d_v)
     # the normalised step (elu+1, normaliser state z updated beside S), fewer steps
     z = torch.ones(w.B, w.H, w.d_k, dtype=torch.float32, device="cuda")
@@ -309,8 +325,8 @@ def run_decode(args, torch, api, inputs):
 
     per_n = _events_ms(step_norm, Tn, stream) / Tn
     nbytes_n = nbytes + w.B * w.H * w.d_k * 8
-    return dict(w=w, steps=T, ms_per_step=per, bytes=nbytes, norm_steps=Tn, norm_ms_per_step=per_n,
-                norm_bytes=nbytes_n)
+    return dict(w=w, steps=T, ms_per_step=per, ms_per_step_cold=cold, bytes=nbytes, norm_steps=Tn,
+                norm_ms_per_step=per_n, norm_bytes=nbytes_n, oracle_sample=sample)
 
 
 def run_delta(args, torch, api, inputs):
@@ -672,6 +688,93 @@ def summarize_stats(d, command):
     print("\n".join(lines))
 
 
+def _oracle_seconds(fn, budget_s):
+    """Runs ``fn`` (one oracle call, returns its seconds) until ``budget_s`` has passed;
+    returns (runs, seconds)."""
+    reps, t = 0, 0.0
+    while reps == 0 or t < budget_s:
+        t += fn()
+        reps += 1
+    return reps, t
+
+
+def cpu_baseline_prefill(w, inp, budget_s):
+    """The fp64 oracle on a sample of one prefill workload's heads (the same input
+    bits), about ``budget_s`` seconds; tokens/s scaled to the whole workload."""
+    from oracle import oracle
+    threads = oracle.default_threads()
+    heads_all = [(b, h) for b in range(w.B) for h in range(w.H)]
+    g = inp.get("g")
+
+    def run(heads):
+        pick = lambda t: None if t is None else t[[b for b, _ in heads], [h for _, h in heads]].unsqueeze(1).cpu()
+        q, k, v, gg = pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(g)
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, g=gg, gate=w.gate, feature_map=w.feature_map, nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe = heads_all[:min(threads, len(heads_all))]
+    t_probe = run(probe)
+    n = int(min(len(heads_all), max(len(probe), len(probe) * budget_s / max(t_probe, 1e-3))))
+    n = max(len(probe), n // len(probe) * len(probe))
+    heads = heads_all[:n]
+    reps, t = _oracle_seconds(lambda: run(heads), budget_s)
+    return {"value": reps * n * w.L / w.H / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": t, "heads_sampled": n, "heads_total": len(heads_all),
+            "sample": "%d of %d heads x %d runs (L=%d, d_k=%d, d_v=%d, gate=%s, phi=%s), fp64 token recurrence; "
+                      "tokens/s = B*L tokens, scaled as sampled heads / H" % (
+                          n, len(heads_all), reps, w.L, w.d_k, w.d_v, w.gate, w.feature_map or "identity")}
+
+
+def cpu_baseline_decode(dc, budget_s):
+    """The fp64 oracle beside the decode workload: on one head of every sequence, the
+    recurrence over the 512-token prompt plus the 1024 steps, minus the prompt alone:
+    T(1536) - T(512) is the oracle's time for the steps; tokens/s scales it to all
+    heads (one token per sequence per step)."""
+    from oracle import oracle
+    w, smp = dc["w"], dc["oracle_sample"]
+    threads = oracle.default_threads()
+    n = smp["q"].shape[0]
+    T = dc["steps"]
+
+    def run(L):
+        cut = lambda x: x[:, :, :L].contiguous()
+        t0 = time.perf_counter()
+        oracle.forward(cut(smp["q"]), cut(smp["k"]), cut(smp["v"]), g=cut(smp["g"]), gate="keydim",
+                       nthreads=threads)
+        return time.perf_counter() - t0
+
+    reps_f, t_full = _oracle_seconds(lambda: run(w.L + T), budget_s * 0.75)
+    reps_p, t_pre = _oracle_seconds(lambda: run(w.L), budget_s * 0.25)
+    steps_s = max(t_full / reps_f - t_pre / reps_p, 1e-9)          # the T steps on n heads
+    whole = steps_s * (w.B * w.H) / n                              # the T steps on every head
+    return {"value": w.B * T / whole, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": t_full + t_pre, "heads_sampled": n, "heads_total": w.B * w.H,
+            "ms_per_step_all_heads": whole / T * 1e3,
+            "sample": "one head of each of the %d sequences: T(%d tokens) - T(%d tokens) of the fp64 token "
+                      "recurrence (%d and %d runs), scaled to all %d heads; tokens/s = sequences x steps / time"
+                      % (n, w.L + T, w.L, reps_f, reps_p, w.B * w.H)}
+
+
+def cpu_baseline_per_core(pf, budget_s):
+    """The oracle on one thread, one head of the headline prefill: tokens/s of one
+    core, counted as head-tokens (L per head)."""
+    from oracle import oracle
+    inp, w = pf["inp"], pf["w"]
+    pick = lambda t: t[0:1, 0:1].cpu()
+    q, k, v, g = pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(inp["g"])
+
+    def run():
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, g=g, gate="keydim", nthreads=1)
+        return time.perf_counter() - t0
+
+    reps, t = _oracle_seconds(run, budget_s)
+    return {"head_tokens_per_s": reps * w.L / t, "tokens_per_s_equiv": reps * w.L / w.H / t, "cores": 1,
+            "runs": reps, "seconds": t,
+            "sample": "one head of the headline prefill (L=%d, d=%d), one thread" % (w.L, w.d_k)}
+
+
 def cpu_baseline(pf, budget_s):
     """The fp64 oracle, unchanged, on a sample of the prefill workload's heads (same
     input bits), sized to roughly ``budget_s`` seconds on this host's cores."""
@@ -715,7 +818,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the other prefill workloads")
-    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0,
+                    help="total seconds of oracle time beside the GPU figures (split over the workloads)")
     ap.add_argument("--copy-kernel", action="store_true")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
@@ -783,6 +887,7 @@ def main():
         line["decode"] = {"workload": "decode: B=256 H=32 d=128 fp32 state, %d steps after a 512-token "
                                       "prefill" % dc["steps"],
                           "tokens_per_s": dc["w"].B / dper, "ms_per_step": dc["ms_per_step"],
+                          "ms_per_step_cold": dc["ms_per_step_cold"],
                           "GB_per_s": dgbs, "hbm_frac": dgbs / HBM_PEAK_GBS,
                           "bytes_per_step": dc["bytes"]}
         nper = dc["norm_ms_per_step"] / 1e3
@@ -791,8 +896,9 @@ def main():
                                "GB_per_s": dc["norm_bytes"] / nper / 1e9,
                                "hbm_frac": dc["norm_bytes"] / nper / 1e9 / HBM_PEAK_GBS,
                                "bytes_per_step": dc["norm_bytes"]}
+    other_baselines = None if args.no_cpu_baseline else {}
     if not args.no_others:
-        line["other_prefill"] = run_other_prefills(args, torch, api, inputs)
+        line["other_prefill"] = run_other_prefills(args, torch, api, inputs, other_baselines)
         line["delta"] = run_delta(args, torch, api, inputs)
         line["gate_producer"] = run_gate(args, torch, api, inputs)
         line["outer_gate"] = run_outer(args, torch, api, inputs)
@@ -804,7 +910,13 @@ def main():
     line["mfma"]["achievable_frac"] = tflops / mfma_ach if mfma_ach else None
     line["achievable_peaks"] = pk
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget_s)
+        line["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget_s * 0.5)
+        per_w = {"gla_prefill": dict(line["cpu_baseline"])}
+        per_w.update(other_baselines or {})
+        if not args.no_decode:
+            per_w["decode"] = cpu_baseline_decode(dc, args.cpu_budget_s * 0.25)
+        line["cpu_baseline"]["per_workload"] = per_w
+        line["cpu_baseline"]["per_core"] = cpu_baseline_per_core(pf, args.cpu_budget_s * 0.1)
     print(json.dumps(line))
 
 
