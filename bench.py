@@ -116,14 +116,16 @@ def achievable_peaks():
     """This card's achievable HBM rate for the prefill's traffic mix and dense bf16
     matrix-core rate, measured now (bench_peaks.hip); None where unavailable."""
     import ctypes
-    out = {"hbm_GBs": None, "mfma_bf16_tflops": None,
+    out = {"hbm_GBs": None, "hbm_inplace_GBs": None, "mfma_bf16_tflops": None,
            "note": "bench_peaks.hip: a streaming kernel with the prefill's read:write mix (5:1, "
-                   "non-temporal 16-byte accesses) and a loop of independent bf16 16x16x32 products"}
+                   "non-temporal 16-byte accesses), an in-place non-temporal scaling of 512 MiB (the "
+                   "decode step's pattern) and a loop of independent bf16 16x16x32 products"}
     if not os.path.exists(PEAKS_LIB):
         out["note"] += "; not built"
         return out
     lib = ctypes.CDLL(PEAKS_LIB)
-    for name, key in (("peaks_stream", "hbm_GBs"), ("peaks_mfma", "mfma_bf16_tflops")):
+    for name, key in (("peaks_stream", "hbm_GBs"), ("peaks_inplace", "hbm_inplace_GBs"),
+                      ("peaks_mfma", "mfma_bf16_tflops")):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(ctypes.c_double)]
@@ -909,6 +911,9 @@ def main():
     line["mfma"]["achievable_peak_tflops"] = mfma_ach
     line["mfma"]["achievable_frac"] = tflops / mfma_ach if mfma_ach else None
     line["achievable_peaks"] = pk
+    if "decode" in line and pk.get("hbm_inplace_GBs"):
+        line["decode"]["achievable_peak"] = pk["hbm_inplace_GBs"]
+        line["decode"]["achievable_frac"] = line["decode"]["GB_per_s"] / pk["hbm_inplace_GBs"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget_s * 0.5)
         per_w = {"gla_prefill": dict(line["cpu_baseline"])}

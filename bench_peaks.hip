@@ -3,6 +3,9 @@
 // delivers as well as against its datasheet:
 //   peaks_stream  a streaming kernel with the headline prefill's traffic mix (five
 //                 bytes read per byte written; 16-byte non-temporal accesses), in GB/s;
+//   peaks_inplace an in-place scaling of 512 MiB with 16-byte non-temporal loads and
+//                 stores, four per thread: the decode step's access pattern without its
+//                 arithmetic, in GB/s (bytes read plus bytes written);
 //   peaks_mfma    a loop of independent bf16 16x16x32 matrix-core products on
 //                 register operands (no memory traffic), in TFLOP/s.
 // Measurement infrastructure only: not part of the library's entry points.
@@ -25,6 +28,24 @@ __global__ __launch_bounds__(256) void stream_mix(const f4 *in, f4 *out, size_t 
 #pragma unroll
     for (int r = 0; r < kReads; ++r) s += __builtin_nontemporal_load(in + (size_t)r * nout + j);
     __builtin_nontemporal_store(s, out + j);
+}
+
+constexpr int kInplacePer = 4;                     // float4 per thread
+
+__global__ __launch_bounds__(256) void stream_inplace(f4 *buf, size_t n)
+{
+    const size_t j0 = (size_t)blockIdx.x * 256 * kInplacePer + threadIdx.x;
+    f4 v[kInplacePer];
+#pragma unroll
+    for (int r = 0; r < kInplacePer; ++r) {
+        const size_t j = j0 + (size_t)r * 256;
+        v[r] = j < n ? __builtin_nontemporal_load(buf + j) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int r = 0; r < kInplacePer; ++r) {
+        const size_t j = j0 + (size_t)r * 256;
+        if (j < n) __builtin_nontemporal_store(v[r] * 0.5f, buf + j);
+    }
 }
 
 __global__ __launch_bounds__(256) void mfma_loop(float *sink, int iters)
@@ -90,6 +111,24 @@ int peaks_stream(double *gbs)
     (void)hipFree(in);
     (void)hipFree(out);
     if (rc == 0) *gbs = (double)(kReads + 1) * nout * sizeof(f4) / (ms * 1e-3) / 1e9;
+    return rc;
+}
+
+// In-place streaming rate over a 512 MiB buffer (read and written once per launch), in
+// GB/s counting both directions.  Returns 0, or -1 on a HIP error.
+int peaks_inplace(double *gbs)
+{
+    const size_t n = (size_t)512 << 20 >> 4;
+    f4 *buf = nullptr;
+    if (hipMalloc(&buf, n * sizeof(f4)) != hipSuccess) return -1;
+    int rc = hipMemset(buf, 0, n * sizeof(f4)) == hipSuccess ? 0 : -1;
+    const unsigned grid = (unsigned)((n + 256 * kInplacePer - 1) / (256 * kInplacePer));
+    double ms = 0.0;
+    if (rc == 0)
+        rc = best_ms([&] { hipLaunchKernelGGL(stream_inplace, dim3(grid), dim3(256), 0, 0, buf, n); }, 20, 5, &ms);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(buf);
+    if (rc == 0) *gbs = 2.0 * n * sizeof(f4) / (ms * 1e-3) / 1e9;
     return rc;
 }
 
