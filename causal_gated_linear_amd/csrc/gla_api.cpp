@@ -143,6 +143,8 @@ int ok()
 
 bool dim_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_supported(int c) { return c == 16 || c == 32 || c == 64; }
+// the GLA prefills also take chunks of 128 rows when d_k <= 64
+bool prefill_chunk_supported(int c, int d_k) { return chunk_supported(c) || (c == 128 && d_k <= 64); }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 size_t elem_size(gla_dtype dt) { return dt == GLA_BF16 ? 2 : 4; }
 
@@ -286,8 +288,9 @@ int gla_state_free(float *state, gla_stream_t stream)
 size_t gla_prefill_workspace_bytes(int B, int H, int L, int d_k, int d_v, int chunk,
                                    gla_dtype dtype)
 {
-    if (B <= 0 || H <= 0 || L < 0 || !dim_supported(d_k) || !dim_supported(d_v) || !chunk_supported(chunk) ||
-        (dtype != GLA_F32 && dtype != GLA_BF16) || (long long)B * H > 0x7fffffffLL)
+    if (B <= 0 || H <= 0 || L < 0 || !dim_supported(d_k) || !dim_supported(d_v) ||
+        !prefill_chunk_supported(chunk, d_k) || (dtype != GLA_F32 && dtype != GLA_BF16) ||
+        (long long)B * H > 0x7fffffffLL)
         return 0;
     const int BH = B * H;
     const gla::PrefillPlan p = gla::prefill_plan(BH, L, d_k, d_v, chunk, (int)elem_size(dtype));
@@ -305,8 +308,9 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
     if (L < 0) return fail(GLA_ERR_SHAPE, "L=%d must be >= 0", L);
     int st = check_common(B, H, d_k, d_v, dtype, gate, phi, g, L > 0);
     if (st != GLA_OK) return st;
-    if (!chunk_supported(chunk))
-        return fail(GLA_ERR_UNSUPPORTED, "chunk=%d: must be 16, 32 or 64", chunk);
+    if (!prefill_chunk_supported(chunk, d_k))
+        return fail(GLA_ERR_UNSUPPORTED, "chunk=%d: must be 16, 32 or 64, or 128 when d_k <= 64 (d_k=%d)",
+                    chunk, d_k);
     // the kernel addresses one head's rows (and the rows of its last chunk past L)
     // with 32-bit byte offsets: (L + chunk) * max(d_k, d_v) * 4 must stay below 2^31
     if ((long long)(L + chunk) * (d_k > d_v ? d_k : d_v) * 4 > 0x7fffffffLL)

@@ -55,6 +55,11 @@ hipError_t GLA_CAT3(launch_prefill_, GLA_INST_BF16, GLA_INST_DK)(const PrefillAr
     if (chunk == C && dvt == DVT) return dispatch_mode<C, DVT>(a, state_only, stream);
 #define GLA_CASES(C) GLA_CASE(C, 16) GLA_CASE(C, 32) GLA_CASE(C, 64)
     GLA_CASES(16) GLA_CASES(32) GLA_CASES(64)
+#if GLA_INST_DK <= 64
+    // chunks of 128 rows: only for d_k <= 64 (at d_k = 128 one operand buffer would
+    // fill the LDS and the chunk's fragments would not fit in registers)
+    GLA_CASES(128)
+#endif
 #undef GLA_CASES
 #undef GLA_CASE
     return hipErrorInvalidValue;

@@ -44,7 +44,11 @@
  *  - q, k, v and o share one dtype (GLA_F32 or GLA_BF16); bf16 results are rounded
  *    to nearest even.  Arithmetic: fp32 accumulation and fp32 state; with bf16
  *    inputs the matrix-core operands are bf16.
- *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}; chunk in {16, 32, 64}, and
+ *    for the GLA prefills (gla_prefill_chunked, _noalloc and _norm) also 128 when
+ *    d_k <= 64 (toward the parallel end of the chunkwise form; at d_k = 128 a chunk
+ *    of 128 rows leaves room for only one operand buffer in a compute unit's 160 KiB
+ *    of LDS and its fragments do not fit in registers, so it is rejected);
  *    B, H >= 1; L >= 0 (L need not be a multiple of chunk; L == 0 only copies the
  *    initial state to s_final); per head (L + chunk) * max(d_k, d_v) * 4 < 2^31
  *    bytes (L up to about 4.19 million tokens at d = 128), else GLA_ERR_SHAPE.
@@ -320,7 +324,7 @@ int gla_gate_project(const void *x, const void *w_down, const void *w_up, float 
  *     o_t = S_t^T phi(q_t)
  *
  * with alpha_t = exp(g_t) and beta_t = exp(gv_t).  Arguments as gla_prefill_chunked
- * with a key-dimension gate, plus
+ * with a key-dimension gate (chunk 16, 32 or 64 only), plus
  *   gv        in   fp32 [B][H][L][d_v] value-dimension log-gates (finite, <= 0)
  * No workspace.  Every gate strength is exact up to rounding: a chunk whose lowest
  * key-dimension and lowest value-dimension log-gate sums add up to less than

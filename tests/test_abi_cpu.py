@@ -94,7 +94,8 @@ PREFILL_BAD = {
     "L_negative": (dict(L=-1), _lib.GLA_ERR_SHAPE),
     "d_k_48": (dict(d_k=48), _lib.GLA_ERR_UNSUPPORTED),
     "d_v_256": (dict(d_v=256), _lib.GLA_ERR_UNSUPPORTED),
-    "chunk_128": (dict(chunk=128), _lib.GLA_ERR_UNSUPPORTED),
+    "chunk_128_at_d_k_128": (dict(chunk=128, d_k=128), _lib.GLA_ERR_UNSUPPORTED),
+    "chunk_256": (dict(chunk=256), _lib.GLA_ERR_UNSUPPORTED),
     "chunk_8": (dict(chunk=8), _lib.GLA_ERR_UNSUPPORTED),
     "L_past_32bit_head_offsets": (dict(L=4194304, d_k=128, d_v=128), _lib.GLA_ERR_SHAPE),
     "segmented_without_workspace": (dict(B=1, H=2, L=64 * 65), _lib.GLA_ERR_WORKSPACE),
@@ -159,6 +160,22 @@ def test_empty_prefill_may_omit_inputs(lib):
     fails on the chunk size, so nothing is launched)."""
     assert _prefill(lib, L=0, q=None, k=None, v=None, o=None, g=None, chunk=8) == _lib.GLA_ERR_UNSUPPORTED
     assert _prefill(lib, L=1, g=None) == _lib.GLA_ERR_NULL
+
+
+def test_chunk_128_accepted_for_small_key_dims(lib):
+    """Chunks of 128 rows pass validation for d_k <= 64 (in the plain, allocation-free
+    and normalised prefills) and fail only on the deliberately misaligned s_final;
+    at d_k = 128 they are rejected."""
+    for dk in (16, 32, 64):
+        for dv in (16, 64, 128):
+            assert _prefill(lib, chunk=128, d_k=dk, d_v=dv, s_final=A + 128 * MB + 4) == _lib.GLA_ERR_ALIGN
+            assert _prefill_norm(lib, chunk=128, d_k=dk, d_v=dv, s_final=A + 128 * MB + 4) == _lib.GLA_ERR_ALIGN
+    assert _prefill(lib, chunk=128, d_k=128, d_v=64) == _lib.GLA_ERR_UNSUPPORTED
+    assert "128" in lib.gla_last_error_detail().decode()
+    assert _prefill_norm(lib, chunk=128, d_k=128) == _lib.GLA_ERR_UNSUPPORTED
+    # few long sequences at chunk 128 are segmented like any other chunk size
+    assert lib.gla_prefill_workspace_bytes(1, 2, 128 * 70, 64, 64, 128, 1) > 0
+    assert lib.gla_prefill_workspace_bytes(1, 2, 128 * 70, 128, 64, 128, 1) == 0
 
 
 def test_state_alloc_rejects(lib):
@@ -388,6 +405,7 @@ PREFILL_OUTER_BAD = {
     "gv_misaligned": (dict(gv=A + 64 * MB + 4), _lib.GLA_ERR_ALIGN),
     "d_v_8": (dict(d_v=8), _lib.GLA_ERR_UNSUPPORTED),
     "chunk_48": (dict(chunk=48), _lib.GLA_ERR_UNSUPPORTED),
+    "chunk_128": (dict(chunk=128), _lib.GLA_ERR_UNSUPPORTED),
     "phi_7": (dict(phi=7), _lib.GLA_ERR_UNSUPPORTED),
     "o_overlaps_gv": (dict(o=A + 64 * MB + 512), _lib.GLA_ERR_ALIAS),
     "s_final_overlaps_gv": (dict(s_final=A + 64 * MB + 1024), _lib.GLA_ERR_ALIAS),
@@ -436,6 +454,9 @@ def test_prefill_noalloc_rejects_sizes_beyond_its_scratch(lib):
 def test_prefill_noalloc_scratch_covers_every_automatic_plan(lib):
     """The largest automatic segmented workspace over head counts and lengths (d = 128,
     the widest state) stays within the 32 MiB of scratch."""
-    worst = max(lib.gla_prefill_workspace_bytes(1, bh, 64 * 4096, 128, 128, 64, _lib.GLA_BF16)
-                for bh in range(1, 300))
+    worst = max(lib.gla_prefill_workspace_bytes(1, bh, 64 * 4096, 128, 128, chunk, dt)
+                for bh in range(1, 300) for chunk in (16, 32, 64) for dt in (_lib.GLA_BF16, _lib.GLA_F32))
     assert 0 < worst <= 32 << 20
+    worst128 = max(lib.gla_prefill_workspace_bytes(1, bh, 128 * 2048, 64, dv, 128, dt)
+                   for bh in range(1, 300) for dv in (64, 128) for dt in (_lib.GLA_BF16, _lib.GLA_F32))
+    assert 0 < worst128 <= 32 << 20
