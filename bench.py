@@ -656,10 +656,10 @@ def summarize_stats(d, command):
              "#   delta rule at the headline shape, chunk 32: delta_fused_kernel (grid 256); "
              "delta decode at the decode shape",
              "#   gate producer: 8x4096 tokens, d_model 2048 -> 16 heads x 128 (grid 256, persistent: 2 blocks of 64 tokens each)",
-             "#   outer-product gate at the headline shape, chunk 32 and 64 (grid 256); its decode step",
+             "#   outer-product gate at the headline shape, chunk 32 and 64 (prefill_kernel with gate 3, grid 256); its decode step",
              "# kernel names are mangled: prefill_kernel<T, d_k, chunk, value-column tile, gate, elu1, "
              "state-only, normalised>, DF16b = bf16, gate 1 = key-dim, 2 = scalar; decode_kernel<T, d_k, d_v, "
-             "normalised>; delta_fused_kernel<T, d_k, chunk>; outer_prefill_kernel<T, d_k, chunk, elu1>",
+             "normalised>; delta_fused_kernel<T, d_k, chunk>; gate 3 = outer-product gate (key and value gates)",
              "# command (from the repository root, REPO = its absolute path):", "#   " + command, "",
              "## rocprofv3 stats (all dispatches, warm-up included)",
              "%-8s %14s %12s %12s %12s  %s" % ("calls", "total_ns", "avg_ns", "min_ns", "max_ns", "kernel")]

@@ -56,18 +56,18 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, i
 // Launch shape: the widest value tile (64, 32 or 16 columns) that fits in LDS and
 // still gives at least 256 workgroups for the 256 compute units (a test can force
 // another usable width through gla_testing_set_plan).
-static bool tile_usable(int dvt, int d_k, int d_v, int chunk, int elem_bytes)
+static bool tile_usable(int dvt, int d_k, int d_v, int chunk, int elem_bytes, bool outer = false)
 {
-    return dvt <= d_v && d_v % dvt == 0 && prefill_nbuf(elem_bytes, d_k, chunk, dvt) > 0;
+    return dvt <= d_v && d_v % dvt == 0 && prefill_nbuf(elem_bytes, d_k, chunk, dvt, outer) > 0;
 }
 
-int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes)
+int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes, bool outer = false)
 {
     const int forced = g_force_prefill_tile;
-    if (forced && tile_usable(forced, d_k, d_v, chunk, elem_bytes)) return forced;
+    if (forced && tile_usable(forced, d_k, d_v, chunk, elem_bytes, outer)) return forced;
     const long bh = BH;
-    if (tile_usable(64, d_k, d_v, chunk, elem_bytes) && bh * (d_v / 64) >= 256) return 64;
-    if (tile_usable(32, d_k, d_v, chunk, elem_bytes) && bh * (d_v / 32) >= 256) return 32;
+    if (tile_usable(64, d_k, d_v, chunk, elem_bytes, outer) && bh * (d_v / 64) >= 256) return 64;
+    if (tile_usable(32, d_k, d_v, chunk, elem_bytes, outer) && bh * (d_v / 32) >= 256) return 32;
     return 16;
 }
 
@@ -91,6 +91,8 @@ PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_by
     int dvt = 16;
     for (int t : {64, 32})
         if (dvt == 16 && tile_usable(t, d_k, d_v, chunk, elem_bytes)) dvt = t;
+    if (g_force_prefill_tile && tile_usable(g_force_prefill_tile, d_k, d_v, chunk, elem_bytes))
+        dvt = g_force_prefill_tile;
     const long wgs = (long)BH * (d_v / dvt);
     int nseg = 1;
     if (nchunks >= kSegMinSeqChunks) {
@@ -663,16 +665,20 @@ int gla_prefill_outer(const void *q, const void *k, const void *v, const float *
     if (overlap(ssf, ss0) && s_final != s0)
         return fail(GLA_ERR_ALIAS, "s_final partially overlaps s0");
     if (BH > 0x7fffffffUL) return fail(GLA_ERR_SHAPE, "B*H too large");
-    gla::OuterArgs a = {};
+    // the prefill kernel with value-side gates: one workgroup per (head, value tile)
+    gla::PrefillArgs a = {};
     a.q = q; a.k = k; a.v = v; a.g = g; a.gv = gv; a.s0 = s0; a.o = o; a.s_final = s_final;
-    a.BH = (int)BH; a.L = L; a.d_k = d_k; a.d_v = d_v; a.elu1 = phi == GLA_PHI_ELU1;
-    a.dvt = d_v < 64 ? d_v : 64;
-    a.n_vt = d_v / a.dvt;
+    a.BH = (int)BH; a.L = L; a.d_v = d_v;
+    a.gate = gla::kGateOuter; a.elu1 = phi == GLA_PHI_ELU1;
+    const int dvt = gla::prefill_tile((int)BH, d_k, d_v, chunk, (int)es, true);
+    a.n_vt = d_v / dvt;
+    a.nseg = 1; a.seg_len = L; a.gam = nullptr;
+    a.norm = 0; a.z0 = nullptr; a.z_final = nullptr;
     const long grid = (long)BH * a.n_vt;
     if (grid > 0x7fffffffL) return fail(GLA_ERR_SHAPE, "B*H too large");
     a.xcd_remap = (a.n_vt > 1 && grid % 8 == 0) ? 1 : 0;
     if (L == 0 && !s_final) return ok();
-    const hipError_t e = gla::launch_outer_prefill(a, dtype == GLA_BF16 ? 1 : 0, chunk, (hipStream_t)stream);
+    const hipError_t e = gla::launch_prefill(a, dtype == GLA_BF16 ? 1 : 0, d_k, chunk, dvt, false, (hipStream_t)stream);
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "outer-gate prefill launch: %s", hipGetErrorString(e));
     return ok();
 }

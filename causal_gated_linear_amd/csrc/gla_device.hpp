@@ -179,6 +179,35 @@ __device__ __forceinline__ float buf_load4(Rsrc r, int off)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// one load of sizeof(V) bytes (8 or 16)
+template <typename V>
+__device__ __forceinline__ V buf_load(Rsrc r, int off)
+{
+    static_assert(sizeof(V) == 8 || sizeof(V) == 16, "8- or 16-byte load");
+    if constexpr (sizeof(V) == 16) return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    else return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// Minimum over the 64 lanes (all active), in registers only: DPP shifts within each
+// 16-lane row (a lane whose source is outside the row keeps its own value), then the
+// rows' last lanes read as scalars.
+template <int SHIFT> __device__ __forceinline__ float row_shr_keep(float v)
+{
+    const int b = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x110 + SHIFT, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_min(float v)
+{
+    v = fminf(v, row_shr_keep<1>(v));
+    v = fminf(v, row_shr_keep<2>(v));
+    v = fminf(v, row_shr_keep<4>(v));
+    v = fminf(v, row_shr_keep<8>(v));
+    const int b = __builtin_bit_cast(int, v);
+    return fminf(fminf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31))),
+                 fminf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63))));
+}
 
 
 // Accumulator tile -> operand fragment of element type T (bf16 rounds to nearest even).

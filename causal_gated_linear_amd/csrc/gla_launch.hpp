@@ -7,7 +7,10 @@
 
 namespace gla {
 
-enum { kGateNone = 0, kGateKeydim = 1, kGateScalar = 2 };
+// gate modes of the prefill kernel: none, key-dimension gates, one scalar gate per
+// token, and the outer-product gate (key-dimension gates g and value-dimension gates
+// gv, the latter only through gla_prefill_outer)
+enum { kGateNone = 0, kGateKeydim = 1, kGateScalar = 2, kGateOuter = 3 };
 
 struct PrefillArgs {
     const void *q, *k, *v;   // [B][H][L][d_k] / [B][H][L][d_v], element type T
@@ -31,6 +34,8 @@ struct PrefillArgs {
     int norm;
     const float *z0;         // [B][H][d_k] or null
     float *z_final;          // [B][H][d_k] or null
+    // outer-product gate: value-dimension log-gates (natural log) [B][H][L][d_v]
+    const float *gv = nullptr;
 };
 
 struct DecodeArgs {
@@ -49,16 +54,20 @@ struct DecodeArgs {
 // state operand, and the output staging rows of the consumer waves (at most
 // 4 x 16 x dvt).
 constexpr int kLdsBytes = 163840;                  // LDS per compute unit on gfx950
-constexpr int prefill_lds_bytes(int es, int dk, int c, int dvt, int nbuf)
+// The outer-product gate has no K~ rows but adds, per buffer, exp(Bv) for every
+// (row, value column) in fp32 rows of dvt + 4, exp of the value-side chunk totals and
+// the producers' gate minima.
+constexpr int prefill_lds_bytes(int es, int dk, int c, int dvt, int nbuf, bool outer = false)
 {
-    const int buf = (3 * c * dk + dvt * c) * es + 4 * (dk + c + 4);
+    const int buf = outer ? (2 * c * dk + dvt * c) * es + 4 * (dk + c + 4) + 4 * (c * (dvt + 4) + dvt + 8)
+                          : (3 * c * dk + dvt * c) * es + 4 * (dk + c + 4);
     return nbuf * buf + 2 * dvt * dk * es + 4 * 16 * dvt * es + 128;
 }
 // Operand buffers that fit (2: producer/consumer overlap, 1: alternating, 0: none).
-constexpr int prefill_nbuf(int es, int dk, int c, int dvt)
+constexpr int prefill_nbuf(int es, int dk, int c, int dvt, bool outer = false)
 {
-    return prefill_lds_bytes(es, dk, c, dvt, 2) <= kLdsBytes ? 2
-           : prefill_lds_bytes(es, dk, c, dvt, 1) <= kLdsBytes ? 1 : 0;
+    return prefill_lds_bytes(es, dk, c, dvt, 2, outer) <= kLdsBytes ? 2
+           : prefill_lds_bytes(es, dk, c, dvt, 1, outer) <= kLdsBytes ? 1 : 0;
 }
 
 // Launch plan of a prefill: value columns per workgroup (16, 32 or 64) and, for
@@ -121,18 +130,16 @@ struct GateArgs {
 constexpr int gate_tiles_per_group(int elem_size, int rank) { return 65536 / (16 * rank * elem_size); }
 hipError_t launch_gate_project(const GateArgs &a, int dtype, int rank, hipStream_t stream);
 
-// The outer-product gate (gla_outer.hip): S <- (alpha beta^T) (.) S + phi(k) v^T.
+// One decode step with the outer-product gate (gla_outer.hip):
+// S <- (alpha beta^T) (.) S + phi(k) v^T, o = S^T phi(q).  Its chunkwise prefill is the
+// prefill kernel's kGateOuter mode.
 struct OuterArgs {
-    const void *q, *k, *v;   // [B][H][L][d_k] / [B][H][L][d_v], element type T (decode: L absent)
-    const float *g, *gv;     // natural-log gates [B][H][L][d_k] and [B][H][L][d_v]
-    const float *s0;         // [B][H][d_k][d_v] or null (prefill)
-    void *o;                 // [B][H][L][d_v], T
-    float *s_final;          // [B][H][d_k][d_v] or null (prefill); the state (decode)
-    int BH, L, d_k, d_v, elu1;
-    int dvt, n_vt;           // value columns per workgroup (16, 32 or 64), tiles per head
-    int xcd_remap;
+    const void *q, *k, *v;   // [B][H][d_k] / [B][H][d_v], element type T
+    const float *g, *gv;     // natural-log gates [B][H][d_k] and [B][H][d_v]
+    void *o;                 // [B][H][d_v], T
+    float *s_final;          // the state [B][H][d_k][d_v], updated in place
+    int BH, d_k, d_v, elu1;
 };
-hipError_t launch_outer_prefill(const OuterArgs &a, int dtype, int chunk, hipStream_t stream);
 hipError_t launch_outer_decode(const OuterArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_delta_prefill(const DeltaArgs &a, int dtype, int chunk, hipStream_t stream);
 hipError_t launch_delta_decode(const DeltaArgs &a, int dtype, hipStream_t stream);

@@ -17,8 +17,18 @@
 // S <- exp(Gamma) S + (phi(K) * exp(Gamma - b))^T V.  The key-dim factorisation needs
 // exp(-B) well inside the fp32 range: a chunk whose cumulative log2-gate falls below
 // -kFastLim in some key dimension (flagged by the producers) is computed token by
-// token instead, by every wave of the workgroup (gla_slow.hpp), which is exact for
-// any gate in [0, 1].
+// token instead, by the consumer waves (gla_slow.hpp), which is exact for any gate
+// in [0, 1].
+//
+// Outer-product gate ("Gated Linear Attention", GLA / Recurrent Form: G_t = alpha_t
+// beta_t^T, a key-side and a value-side gate): the gate products between s and t
+// factorise per key dimension and per value dimension, so with the value side's
+// in-chunk cumulative log-gates Bv[t][j] and totals GB[j] the same chunk step becomes
+//   V^ = V * exp(-Bv),   O = (P V^ + Q~ S) (.) exp(Bv),
+//   S <- Diag(exp Gamma) (S + K^^T V^) Diag(exp GB).
+// The producers scan the value gates of their value columns as they scan the key
+// gates (a lane holds four value columns of a few rows); a chunk whose lowest key
+// and value totals add up to less than -kFastLim runs token by token.
 //
 // Decomposition: one workgroup per (batch*head, tile of DVT value columns) walks the
 // chunks of its head in order, with two kinds of wavefronts:
@@ -119,7 +129,7 @@ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int kSwz16 = 0x100, kSwz8 = 0x101, kSwzO8 = 0x102;
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <typename T, int DK, int C, int DVT>
+template <typename T, int DK, int C, int DVT, bool OUTER = false>
 struct PrefillShape {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int CE = 16 / sizeof(T);      // elements per 16-byte chunk
@@ -166,8 +176,17 @@ struct PrefillShape {
     static constexpr int SCH = DVS / CE, SWS = SCH >= 16 ? kSwz16 : (SCH == 8 ? kSwzO8 : SCH - 1);
     static constexpr int OCH = 16 * SCH;           // chunks per staged block
     static constexpr int OCPL = cmax(1, OCH / 64); // chunks per lane
-    static constexpr int NBUF = prefill_nbuf((int)sizeof(T), DK, C, DVT);
+    // outer-product gate, value side: producer p owns value columns [p*CWV, (p+1)*CWV)
+    // of the tile; a lane has four of them (column group cgv: one f32x4 of gates) for
+    // RPSV consecutive rows (row segment rsv); column groups vary fastest across lanes
+    static constexpr int CWV = DVT / NP;
+    static constexpr int CGV = cmax(1, CWV / 4);
+    static constexpr int RSEGV = cmin(64 / CGV, C);
+    static constexpr int RPSV = C / RSEGV;
+    static constexpr int LEV = DVT + 4;            // fp32 row length of exp(Bv) in LDS
+    static constexpr int NBUF = prefill_nbuf((int)sizeof(T), DK, C, DVT, OUTER);
     static_assert(NBUF >= 1, "LDS budget");
+    static_assert(!OUTER || (CWV >= 4 && CWV % 4 == 0 && 16 % CGV == 0 && RPSV >= 1), "value gate mapping");
     static_assert(CW >= CE && CW % CE == 0 && 64 % CG == 0, "producer gate mapping");
     static_assert(NVP < 64 * NP || NVP % (64 * NP) == 0, "producer value mapping");
     static_assert(RPS >= 1, "rows per lane");
@@ -261,7 +280,7 @@ __device__ __forceinline__ float group_scan(float v, int lane)
 template <typename T, int DK, int C, int DVT, int GATE, bool ELU1, bool SO, bool NM>
 __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_kernel(const PrefillArgs a)
 {
-    using SH = PrefillShape<T, DK, C, DVT>;
+    using SH = PrefillShape<T, DK, C, DVT, GATE == kGateOuter>;
     using O = Op<T>;
     using V4 = typename Vec4<T>::type;
     using VC = typename VecN<T, SH::CE>::type;       // one 16-byte chunk
@@ -274,6 +293,8 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * DK];      // Q~ [t][i]
     __shared__ __attribute__((aligned(16))) T sK[NBUF][C * DK];      // K^ [s][i]
     constexpr bool KU = GATE == kGateScalar;        // separate K~ operand for the state
+    constexpr bool OG = GATE == kGateOuter;         // outer-product gate: value-side gates too
+    constexpr bool KG = GATE == kGateKeydim || OG;  // key-dimension gates (factorised)
     __shared__ __attribute__((aligned(16))) T sKU[KU ? NBUF : 1][KU ? C * DK : CE];  // scalar: K~ [s][i]
     __shared__ __attribute__((aligned(16))) T sV[NBUF][C * DVT];     // V [s][j]
     __shared__ __attribute__((aligned(16))) T sS[2][DVT * DK];       // state^T [j][i], by parity
@@ -282,6 +303,11 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     __shared__ __attribute__((aligned(16))) float sB[NBUF][C + 1];   // scalar gate: B_t, then Gamma (log2)
     __shared__ __attribute__((aligned(16))) float sZ[NM ? 2 : 1][NM ? DK : 4];   // normaliser z, by parity
     __shared__ __attribute__((aligned(16))) int sFlag[NBUF][4];      // per producer: chunk out of range
+    // outer-product gate: exp(Bv) [t][j] for the outputs, exp of the value-side chunk
+    // totals, and per producer the lowest key-side and value-side log2 totals
+    __shared__ __attribute__((aligned(16))) float sEV[OG ? NBUF : 1][OG ? C * SH::LEV : 4];
+    __shared__ __attribute__((aligned(16))) float sEGV[OG ? NBUF : 1][OG ? DVT : 4];
+    __shared__ __attribute__((aligned(16))) float sMin[OG ? NBUF : 1][2][4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -306,8 +332,10 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     const Rsrc rvv = make_rsrc((const T *)a.v + hrow * DV, (unsigned)(L * DV * ES));
     T *__restrict__ oh = SO ? nullptr : (T *)a.o + hrow * DV + vt * DVT;
     Rsrc rg = make_rsrc(a.g, 0u);                  // no gates: never read
-    if constexpr (GATE == kGateKeydim) rg = make_rsrc(a.g + hrow * DK, (unsigned)(L * DK * 4));
+    if constexpr (KG) rg = make_rsrc(a.g + hrow * DK, (unsigned)(L * DK * 4));
     if constexpr (GATE == kGateScalar) rg = make_rsrc(a.g + hrow, (unsigned)(L * 4));
+    Rsrc rgv = make_rsrc(a.gv, 0u);                // value-side gates (outer-product gate only)
+    if constexpr (OG) rgv = make_rsrc(a.gv + hrow * DV, (unsigned)(L * DV * 4));
     const int nchunks = (L + C - 1) / C;
 
     // ---------------- producers -------------------------------------------------------
@@ -318,11 +346,17 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     const bool gate_lane = (SH::CG * RSEG == 64) || rs < RSEG;
     const int ic = p * CW + CE * cg;               // first of this lane's CE key columns
     const bool v_lane = SH::NVP >= 64 * NP || tid < SH::NVP;
+    // outer-product gate: the value mapping follows the value-gate scan instead
+    const int cgv = lane % SH::CGV, rsv = lane / SH::CGV;
+    const bool vg_lane = SH::CGV * SH::RSEGV == 64 || rsv < SH::RSEGV;
+    const int jc = p * SH::CWV + 4 * cgv;          // first of this lane's four value columns
 
     struct Raw {
         VC q[RPS], k[RPS];
         f32x4 g[RPS][CE / 4];
-        VC v[NVL];
+        VC v[OG ? 1 : NVL];
+        V4 vv[OG ? SH::RPSV : 1];                  // outer: four value columns of RPSV rows
+        f32x4 gv[OG ? SH::RPSV : 1];               // outer: their value-side log-gates
     };
     float gsum[CE];                                // state-only pass: gate totals so far
 #pragma unroll
@@ -341,7 +375,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         if (gate_lane) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
-                if constexpr (GATE == kGateKeydim) {
+                if constexpr (KG) {
 #pragma unroll
                     for (int h = 0; h < CE / 4; ++h)
                         r_.g[r][h] = buf_load16<f32x4>(rg, (t0 + rs * RPS + r) * DK * 4 + (ic + 4 * h) * 4);
@@ -362,7 +396,13 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         }
     };
     auto load_v = [&](Raw &r_, int t0) __attribute__((always_inline)) {
-        if (v_lane) {
+        if constexpr (OG) {
+            if (vg_lane) {
+#pragma unroll
+                for (int r = 0; r < SH::RPSV; ++r)
+                    r_.vv[r] = buf_load<V4>(rvv, (t0 + rsv * SH::RPSV + r) * DV * ES + (vt * DVT + jc) * ES);
+            }
+        } else if (v_lane) {
 #pragma unroll
             for (int h = 0; h < NVL; ++h) {
                 const int id = tid + 64 * NP * h;
@@ -370,8 +410,18 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
             }
         }
     };
+    auto load_gv = [&](Raw &r_, int t0) __attribute__((always_inline)) {
+        if constexpr (OG) {
+            if (vg_lane) {
+#pragma unroll
+                for (int r = 0; r < SH::RPSV; ++r)
+                    r_.gv[r] = buf_load16<f32x4>(rgv, ((t0 + rsv * SH::RPSV + r) * DV + vt * DVT + jc) * 4);
+            }
+        }
+    };
     auto load_raw = [&](Raw &r_, int t0) __attribute__((always_inline)) {
         load_g(r_, t0);
+        load_gv(r_, t0);
         load_qk(r_, t0);
         load_v(r_, t0);
     };
@@ -382,6 +432,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     auto produce = [&](Raw &r_, int t0, int buf, int t_next) __attribute__((always_inline)) {
         // No branch here depends on a pending load: a branch would make the compiler's
         // wait analysis wait for every outstanding load at the join.
+        [[maybe_unused]] float kmin = 0.f, vmin = 0.f;   // outer: lowest key / value log2 totals
         if (gate_lane) {
             float bc[RPS][CE];
             float excl[CE], tot[CE];
@@ -407,14 +458,19 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     excl[e] = incl - run[e];
                     tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64);
                 }
-                if constexpr (GATE == kGateKeydim) {
+                if constexpr (KG) {
                     // the chunk total is the lowest cumulative log2-gate of a column
                     // (gates are <= 0); below -kFastLim the chunk runs token by token
+                    // (outer gate: the key-side and value-side lowest totals together)
                     float m = tot[0];
 #pragma unroll
                     for (int e = 1; e < CE; ++e) m = fminf(m, tot[e]);
-                    const bool far = __ballot(m < -kFastLim) != 0;
-                    if (lane == 0) sFlag[buf][p] = far ? 1 : 0;
+                    if constexpr (OG) {
+                        kmin = m;
+                    } else {
+                        const bool far = __ballot(m < -kFastLim) != 0;
+                        if (lane == 0) sFlag[buf][p] = far ? 1 : 0;
+                    }
                 }
                 if constexpr (GATE == kGateScalar) {
 #pragma unroll
@@ -442,7 +498,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     for (int e = 0; e < CE; ++e) uv[e] = from_f32<T>((ELU1 ? feature(kk[e], true) : kk[e]) * f);
                     *(VC *)(sKU[buf] + SH::rk(t, ic)) = uv;
                 }
-                if constexpr (GATE != kGateKeydim && !ELU1) {
+                if constexpr (!KG && !ELU1) {
                     // q and k enter the products as they are
                     if constexpr (!SO) *(VC *)(sQ[buf] + SH::rk(t, ic)) = r_.q[r];
                     if constexpr (!(SO && KU)) *(VC *)(sK[buf] + SH::rk(t, ic)) = r_.k[r];
@@ -452,7 +508,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     widen<T, CE>(r_.k[r], kk);
 #pragma unroll
                     for (int e = 0; e < CE; ++e) {
-                        if constexpr (ELU1 && GATE == kGateKeydim) {
+                        if constexpr (ELU1 && KG) {
                             // phi(x) 2^(+-b) with one exponential: (x + 1) 2^(+-b) for
                             // x > 0, else 2^(x log2(e) +- b)
                             const float b = excl[e] + bc[r][e];
@@ -467,7 +523,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                                 if constexpr (!SO) q[e] = feature(q[e], true);
                                 kk[e] = feature(kk[e], true);
                             }
-                            if constexpr (GATE == kGateKeydim) {
+                            if constexpr (KG) {
                                 const float b = excl[e] + bc[r][e];
                                 if constexpr (!SO) q[e] *= exp2_fast(b);
                                 kk[e] *= exp2_fast(-b);
@@ -498,7 +554,57 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 }
             }
         }
-        if (v_lane) {
+        if constexpr (OG) {
+            // value side of the outer-product gate: cumulative log2-gates Bv down the
+            // rows of each value column (the key side's scan on this mapping), then
+            // V^ = v exp(-Bv), exp(Bv) for the outputs and exp of the chunk totals
+            if (vg_lane) {
+                float bcv[SH::RPSV][4], run[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < SH::RPSV; ++r) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        run[e] += r_.gv[r][e] * kLog2e;
+                        bcv[r][e] = run[e];
+                    }
+                }
+                load_gv(r_, t_next);               // value gates consumed: refill them now
+                float exv[4], totv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float incl = group_scan<SH::RSEGV, SH::CGV>(run[e], lane);
+                    exv[e] = incl - run[e];
+                    totv[e] = __shfl(incl, (SH::RSEGV - 1) * SH::CGV + cgv, 64);
+                }
+                vmin = fminf(fminf(totv[0], totv[1]), fminf(totv[2], totv[3]));
+#pragma unroll
+                for (int r = 0; r < SH::RPSV; ++r) {
+                    const int t = rsv * SH::RPSV + r;
+                    f32x4 ev;
+                    V4 vh;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float b = exv[e] + bcv[r][e];
+                        ev[e] = exp2_fast(b);
+                        vh[e] = from_f32<T>((float)r_.vv[r][e] * exp2_fast(-b));
+                    }
+                    *(V4 *)(sV[buf] + SH::rv(t, jc)) = vh;
+                    *(f32x4 *)(sEV[buf] + t * SH::LEV + jc) = ev;
+                }
+                load_v(r_, t_next);                // v consumed: refill it now
+                if (rsv == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sEGV[buf][jc + e] = exp2_fast(totv[e]);
+                }
+            }
+            // all lanes again: the wave's lowest totals for the range check
+            kmin = wave_min(kmin);
+            vmin = wave_min(vmin);
+            if (lane == 0) {
+                sMin[buf][0][p] = kmin;
+                sMin[buf][1][p] = vmin;
+            }
+        } else if (v_lane) {
             // store first, then refill the same registers (a load issued while the old
             // values are still live would land in other registers and need a copy,
             // and the copy a wait for the load)
@@ -714,6 +820,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 for (int sb = 0; sb <= TB; ++sb) acc = O::mma(vf[sl][sb], O::from_acc(pt[sb]), acc);
             }
             if constexpr (NM) acc *= rden;
+            if constexpr (OG) acc *= *(const f32x4 *)(sEV[buf] + t * SH::LEV + 16 * (j0 + jj) + 4 * grp);
             *(V4 *)(stage + SH::ro(x, 16 * jj + 4 * grp)) = narrow4<T>(acc);
         }
         // read the block back row-contiguous and store 16-byte chunks (wave-local:
@@ -768,7 +875,8 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs) acc = O::mma(af[ia][cs], bfr[cs], acc);
-                    if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * (c + NC * ia) + 4 * grp);
+                    if constexpr (KG) acc *= *(const f32x4 *)(sEG[buf] + 16 * (c + NC * ia) + 4 * grp);
+                    if constexpr (OG) acc *= sEGV[buf][16 * jt + x];
                     S[k] = acc;
                 }
             }
@@ -782,7 +890,8 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs)
                         acc = O::mma(frag_tr(KS, DK, SH::SWK, 16 * it, cs), vfrag(jt, cs), acc);
-                    if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
+                    if constexpr (KG) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
+                    if constexpr (OG) acc *= sEGV[buf][16 * jt + x];
                     S[k] = acc;
                 }
             }
@@ -807,7 +916,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs) acc = O::mma(frag_tr(KS, DK, SH::SWK, 16 * it, cs), ones[cs], acc);
-                    if constexpr (GATE == kGateKeydim) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
+                    if constexpr (KG) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
                     Z[m] = acc;
                 }
             }
@@ -822,8 +931,18 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     // every wave takes the same decision).
     auto chunk_far = [&](int buf) __attribute__((always_inline)) -> bool {
         int f = 0;
+        if constexpr (OG) {
+            float mk = sMin[buf][0][0], mv = sMin[buf][1][0];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) f |= sFlag[buf][i];
+            for (int i = 1; i < NP; ++i) {
+                mk = fminf(mk, sMin[buf][0][i]);
+                mv = fminf(mv, sMin[buf][1][i]);
+            }
+            f = mk + mv < -kFastLim ? 1 : 0;
+        } else {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) f |= sFlag[buf][i];
+        }
         return __builtin_amdgcn_readfirstlane(f) != 0;
     };
     // The chunk starting at t0, token by token (gla_slow.hpp), by the consumer waves;
@@ -836,7 +955,8 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     constexpr int SR = NBUF == 2 ? C : C / 2;        // rows staged at a time
     static_assert(SR * DK * 4 <= (int)sizeof(sQ) && 2 * SR * DK * ES <= (int)sizeof(sK) &&
                   SR * DVT * ES <= (int)sizeof(sV) && DVT * DK * 4 <= (int)sizeof(sS) &&
-                  (!NM || DK * 4 <= (int)sizeof(sZ)), "token-loop staging within the operand buffers");
+                  (!NM || DK * 4 <= (int)sizeof(sZ)) && (!OG || SR * DVT * 4 <= (int)sizeof(sEV)),
+                  "token-loop staging within the operand buffers");
     auto slow_barriers = [&](int t0) __attribute__((always_inline)) {
         const int groups = (min(L - t0, C) + SR - 1) / SR;
         for (int i = 0; i < 2 * groups + 3; ++i) lds_barrier();
@@ -859,9 +979,10 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 if (z_ok(m) && x == 0) *(f32x4 *)(PZ + 16 * (c + NC * m) + 4 * grp) = Z[m];
         }
         lds_barrier();
-        const SlowStage<T> st{(float *)&sQ[0][0], nullptr, &sK[0][0], &sK[0][0] + SR * DK, &sV[0][0]};
-        slow_chunk_lds<T, DK, DVT, SR, 64 * NC, ELU1, !SO, NM, false>(
-            PS, PZ, st, rq, rk, rvv, rg, rg, t0, nvalid, DV, vt * DVT, SO ? nullptr : oh + (size_t)t0 * DV, tid - 64 * NP);
+        const SlowStage<T> st{(float *)&sQ[0][0], OG ? &sEV[0][0] : nullptr, &sK[0][0], &sK[0][0] + SR * DK,
+                              &sV[0][0]};
+        slow_chunk_lds<T, DK, DVT, SR, 64 * NC, ELU1, !SO, NM, OG>(
+            PS, PZ, st, rq, rk, rvv, rg, rgv, t0, nvalid, DV, vt * DVT, SO ? nullptr : oh + (size_t)t0 * DV, tid - 64 * NP);
         lds_barrier();
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) {
@@ -877,7 +998,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         }
         lds_barrier();
     };
-    constexpr bool KD = GATE == kGateKeydim;
+    constexpr bool KD = KG;                          // chunks may leave the factorised range
 
     // ---------------- pipeline ---------------------------------------------------------
     // The two roles run separate loops (so their registers are not live at the same

@@ -35,9 +35,25 @@ static hipError_t dispatch_gate(const PrefillArgs &a, hipStream_t stream)
                   : launch_prefill_inst<InstT, DK, C, DVT, kGateNone, false, SO, NM>(a, stream);
 }
 
+// the outer-product gate: the plain full pass only (no segments, no normaliser), with
+// chunks of at most 64 rows
+template <int C, int DVT>
+static hipError_t dispatch_outer(const PrefillArgs &a, hipStream_t stream)
+{
+    constexpr int DK = GLA_INST_DK;
+    if constexpr (C > 64 || prefill_nbuf((int)sizeof(InstT), DK, C, DVT, true) == 0) {
+        return hipErrorInvalidValue;               // never chosen
+    } else {
+        return a.elu1 ? launch_prefill_inst<InstT, DK, C, DVT, kGateOuter, true, false, false>(a, stream)
+                      : launch_prefill_inst<InstT, DK, C, DVT, kGateOuter, false, false, false>(a, stream);
+    }
+}
+
 template <int C, int DVT>
 static hipError_t dispatch_mode(const PrefillArgs &a, bool state_only, hipStream_t stream)
 {
+    if (a.gate == kGateOuter)
+        return state_only || a.norm ? hipErrorInvalidValue : dispatch_outer<C, DVT>(a, stream);
     if constexpr (prefill_nbuf((int)sizeof(InstT), GLA_INST_DK, C, DVT) == 0) {
         return hipErrorInvalidValue;               // does not fit in LDS; never chosen
     } else {

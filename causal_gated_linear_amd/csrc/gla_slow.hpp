@@ -17,9 +17,9 @@
 // included).  The normalised form also carries z_t = alpha_t (*) z_{t-1} + phi(k_t)
 // and divides o_t by phi(q_t) . z_t ("Transformers are RNNs" notes).
 //
-// All threads of the workgroup stage SR rows at a time into LDS (alpha = exp(g)
-// and beta = exp(gv) in fp32, phi(q), phi(k) and v in the input type) from global
-// memory; then the token loop runs on lanes that each own one value column j and
+// The staging threads (the caller's consumer waves) copy SR rows at a time into LDS
+// (alpha = exp(g) and beta = exp(gv) in fp32, phi(q), phi(k) and v in the input type)
+// from global memory; then the token loop runs on lanes that each own one value column j and
 // NG groups of four key rows, so the sum over i is a reduction over the lanes that
 // share j (lanes JPW apart).  Each staged group ends with a workgroup barrier;
 // callers call the staging and the token loop in the same order on every wave.
@@ -106,8 +106,8 @@ __device__ __forceinline__ void slow_stage(const SlowStage<T> &st, Rsrc rq, Rsrc
     }
     if constexpr (VG) {
         const int gpr = dvt / 4;
-    #pragma unroll 1
-    for (int p = tid; p < SR * gpr; p += NT) {
+#pragma unroll 1
+        for (int p = tid; p < SR * gpr; p += NT) {
             const int r = p / gpr, c = (p % gpr) * 4;
             const f32x4 g = buf_load16<f32x4>(rgv, ((row + r) * DV + vcol + c) * 4);
             f32x4 be;
