@@ -12,13 +12,12 @@
 //   O  = P V + Q~ S                                       (intra-chunk + carried state)
 //   S <- Diag(exp Gamma) (S + K^^T V)                     (the weighted scan step)
 //
-// Scalar gates (one log-gate b per token) use the exact mask form instead, so no
-// factor exceeds 1: P = (phi(Q) phi(K)^T) * exp(b_t - b_s), O_inter = exp(b_t) phi(Q) S,
-// S <- exp(Gamma) S + (phi(K) * exp(Gamma - b))^T V.  The key-dim factorisation needs
-// exp(-B) well inside the fp32 range: a chunk whose cumulative log2-gate falls below
-// -kFastLim in some key dimension (flagged by the producers) is computed token by
-// token instead, by the consumer waves (gla_slow.hpp), which is exact for any gate
-// in [0, 1].
+// Scalar gates (one log-gate b per token, the same in every key dimension) take the
+// same form with one factor per row, exp(+-b_t), computed once per row.  The
+// factorisation needs exp(-B) well inside the fp32 range: a chunk whose cumulative
+// log2-gate falls below -kFastLim in some key dimension (flagged by the producers) is
+// computed token by token instead, by the consumer waves (gla_slow.hpp), which is
+// exact for any gate in [0, 1].
 //
 // Outer-product gate ("Gated Linear Attention", GLA / Recurrent Form: G_t = alpha_t
 // beta_t^T, a key-side and a value-side gate): the gate products between s and t
@@ -269,9 +268,12 @@ __device__ __forceinline__ float group_scan(float v, int lane)
 }
 
 
-// SO (state only): the first pass of a segmented prefill.  Each workgroup runs the
-// state recurrence over its segment from a zero state and stores that state and the
-// segment's gate totals; no outputs, no Q~.
+// SO (state only): the first pass of a segmented prefill.  Each workgroup computes its
+// segment's state from a zero start and the segment's gate totals; no outputs, no Q~.
+// It walks the segment's chunks last to first and adds each chunk's writes already
+// decayed to the segment's end, S += (phi(K) * exp(Gamma_c - B + later))^T V, with
+// `later` the gate total of the chunks after it: every exponent is <= 0, so no chunk
+// leaves the factorised range and this pass needs no token-by-token chunks.
 // NM (normalised, "Transformers are RNNs" notes: the weighted sum of values over the
 // sum of the same weights): the consumers also carry the normaliser state z, the
 // state of a value that is 1 in every token, z <- Diag(e^Gamma)(z + K^^T 1), with the
@@ -292,15 +294,13 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 
     __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * DK];      // Q~ [t][i]
     __shared__ __attribute__((aligned(16))) T sK[NBUF][C * DK];      // K^ [s][i]
-    constexpr bool KU = GATE == kGateScalar;        // separate K~ operand for the state
     constexpr bool OG = GATE == kGateOuter;         // outer-product gate: value-side gates too
-    constexpr bool KG = GATE == kGateKeydim || OG;  // key-dimension gates (factorised)
-    __shared__ __attribute__((aligned(16))) T sKU[KU ? NBUF : 1][KU ? C * DK : CE];  // scalar: K~ [s][i]
+    constexpr bool KG = GATE == kGateKeydim || OG;  // gates per key dimension
+    constexpr bool FG = GATE != kGateNone;          // factorised: Q~ = q e^B, K^ = k e^-B
     __shared__ __attribute__((aligned(16))) T sV[NBUF][C * DVT];     // V [s][j]
     __shared__ __attribute__((aligned(16))) T sS[2][DVT * DK];       // state^T [j][i], by parity
     __shared__ __attribute__((aligned(16))) T sO[NC][16 * SH::DVS];  // output staging, per consumer
     __shared__ __attribute__((aligned(16))) float sEG[NBUF][DK];     // exp(Gamma_i)
-    __shared__ __attribute__((aligned(16))) float sB[NBUF][C + 1];   // scalar gate: B_t, then Gamma (log2)
     __shared__ __attribute__((aligned(16))) float sZ[NM ? 2 : 1][NM ? DK : 4];   // normaliser z, by parity
     __shared__ __attribute__((aligned(16))) int sFlag[NBUF][4];      // per producer: chunk out of range
     // outer-product gate: exp(Bv) [t][j] for the outputs, exp of the value-side chunk
@@ -458,7 +458,15 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     excl[e] = incl - run[e];
                     tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64);
                 }
-                if constexpr (KG) {
+                if constexpr (GATE == kGateScalar) {     // one gate per row: the same in every column
+#pragma unroll
+                    for (int e = 1; e < CE; ++e) { excl[e] = excl[0]; tot[e] = tot[0]; }
+#pragma unroll
+                    for (int r = 0; r < RPS; ++r)
+#pragma unroll
+                        for (int e = 1; e < CE; ++e) bc[r][e] = bc[r][0];
+                }
+                if constexpr (FG) {
                     // the chunk total is the lowest cumulative log2-gate of a column
                     // (gates are <= 0); below -kFastLim the chunk runs token by token
                     // (outer gate: the key-side and value-side lowest totals together)
@@ -472,43 +480,25 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                         if (lane == 0) sFlag[buf][p] = far ? 1 : 0;
                     }
                 }
-                if constexpr (GATE == kGateScalar) {
-#pragma unroll
-                    for (int e = 1; e < CE; ++e) { excl[e] = excl[0]; tot[e] = tot[0]; }
-#pragma unroll
-                    for (int r = 0; r < RPS; ++r)
-#pragma unroll
-                        for (int e = 1; e < CE; ++e) bc[r][e] = bc[r][0];
-                }
             }
 #pragma unroll
             for (int r = 0; r < RPS; ++r) {
                 const int t = rs * RPS + r;
-                if constexpr (GATE == kGateScalar) {
-                    // scalar gate: the row factors are applied by the consumers
-                    if (p == 0 && cg == 0) sB[buf][t] = excl[0] + bc[r][0];
-                }
-                if constexpr (KU) {
-                    // scalar gate: K~ = phi(k) exp(Gamma - b_t) for the state update
-                    const float f = exp2_fast(tot[0] - (excl[0] + bc[r][0]));
-                    float kk[CE];
-                    widen<T, CE>(r_.k[r], kk);
-                    VC uv;
-#pragma unroll
-                    for (int e = 0; e < CE; ++e) uv[e] = from_f32<T>((ELU1 ? feature(kk[e], true) : kk[e]) * f);
-                    *(VC *)(sKU[buf] + SH::rk(t, ic)) = uv;
-                }
-                if constexpr (!KG && !ELU1) {
+                if constexpr (!FG && !ELU1) {
                     // q and k enter the products as they are
                     if constexpr (!SO) *(VC *)(sQ[buf] + SH::rk(t, ic)) = r_.q[r];
-                    if constexpr (!(SO && KU)) *(VC *)(sK[buf] + SH::rk(t, ic)) = r_.k[r];
+                    *(VC *)(sK[buf] + SH::rk(t, ic)) = r_.k[r];
                 } else {
                     float q[CE], kk[CE];
                     if constexpr (!SO) widen<T, CE>(r_.q[r], q);
                     widen<T, CE>(r_.k[r], kk);
 #pragma unroll
                     for (int e = 0; e < CE; ++e) {
-                        if constexpr (ELU1 && KG) {
+                        // key exponent: -b, or for the state-only pass (chunks last to
+                        // first) Gamma - b + the later chunks' total, which is <= 0
+                        [[maybe_unused]] const float kb =
+                            SO ? tot[e] - (excl[e] + bc[r][e]) + gsum[e] : -(excl[e] + bc[r][e]);
+                        if constexpr (ELU1 && FG) {
                             // phi(x) 2^(+-b) with one exponential: (x + 1) 2^(+-b) for
                             // x > 0, else 2^(x log2(e) +- b)
                             const float b = excl[e] + bc[r][e];
@@ -517,16 +507,18 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                                 q[e] = (x > 0.f ? x + 1.f : 1.f) * exp2_fast(x > 0.f ? b : fmaf(x, kLog2e, b));
                             }
                             const float x = kk[e];
-                            kk[e] = (x > 0.f ? x + 1.f : 1.f) * exp2_fast(x > 0.f ? -b : fmaf(x, kLog2e, -b));
+                            kk[e] = (x > 0.f ? x + 1.f : 1.f) * exp2_fast(x > 0.f ? kb : fmaf(x, kLog2e, kb));
                         } else {
                             if constexpr (ELU1) {
                                 if constexpr (!SO) q[e] = feature(q[e], true);
                                 kk[e] = feature(kk[e], true);
                             }
-                            if constexpr (KG) {
+                            if constexpr (FG) {
+                                // (a scalar gate's b is the same in every column: its two
+                                // exponentials are computed once per row)
                                 const float b = excl[e] + bc[r][e];
                                 if constexpr (!SO) q[e] *= exp2_fast(b);
-                                kk[e] *= exp2_fast(-b);
+                                kk[e] *= exp2_fast(kb);
                             }
                         }
                     }
@@ -549,9 +541,6 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
                 for (int e = 0; e < CE; ++e)
                     sEG[buf][ic + e] = GATE == kGateNone ? 1.f : exp2_fast(tot[e]);
-                if constexpr (GATE == kGateScalar) {
-                    if (p == 0 && cg == 0) sB[buf][C] = tot[0];
-                }
             }
         }
         if constexpr (OG) {
@@ -761,21 +750,13 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < SH::KSTEPS; ++k) acc = O::mma(kf[sb & 1][k], qf[k], acc);
-            if constexpr (GATE == kGateScalar) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * sb + 4 * grp + r;
-                    acc[r] = s <= t ? acc[r] * exp2_fast(sB[buf][t] - sB[buf][s]) : 0.f;
-                }
-            } else if (sb == TB) {
+            if (sb == TB) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] = 4 * grp + r <= x ? acc[r] : 0.f;
             }
             pt[sb] = acc;
         }
         pt[TB + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float inter_scale = 1.f;
-        if constexpr (GATE == kGateScalar) inter_scale = exp2_fast(sB[buf][t]);
         // normalised: denominator of row t = Q~_t . z + sum_{s <= t} P_ts; a lane sums
         // its share, the four lane groups of column x are then added
         float rden = 1.f;
@@ -783,7 +764,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
             float dp = 0.f;
 #pragma unroll
             for (int sb = 0; sb <= TB; ++sb) dp += pt[sb][0] + pt[sb][1] + pt[sb][2] + pt[sb][3];
-            float den = dz * inter_scale + dp;
+            float den = dz + dp;
             den += __shfl_xor(den, 16, 64);
             den += __shfl_xor(den, 32, 64);
             rden = 1.f / den;
@@ -810,7 +791,6 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < SH::KSTEPS; ++k) acc = O::mma(sf[sl][k], qf[k], acc);
-            if constexpr (GATE == kGateScalar) acc *= inter_scale;
             if constexpr (SH::BF) {
 #pragma unroll
                 for (int sp = 0; 2 * sp <= TB; ++sp)
@@ -842,7 +822,6 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         const int nvalid = min(L - t0, C);
         const T *Q = sQ[buf], *K = sK[buf], *V = sV[buf], *SS = sS[par];
         const T *KS = K;                           // keys of the state update
-        if constexpr (KU) KS = sKU[buf];
         auto vfrag = [&](int jt, int cs) __attribute__((always_inline)) -> F {
             return frag_tr(V, DVT, SH::SWV, 16 * jt, cs);
         };
@@ -872,10 +851,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 for (int ia = 0; ia < SH::IPC; ++ia) {
                     const int k = jt * SH::IPC + ia;
                     f32x4 acc = S[k];
-                    if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs) acc = O::mma(af[ia][cs], bfr[cs], acc);
-                    if constexpr (KG) acc *= *(const f32x4 *)(sEG[buf] + 16 * (c + NC * ia) + 4 * grp);
+                    if constexpr (FG && !SO) acc *= *(const f32x4 *)(sEG[buf] + 16 * (c + NC * ia) + 4 * grp);
                     if constexpr (OG) acc *= sEGV[buf][16 * jt + x];
                     S[k] = acc;
                 }
@@ -886,11 +864,10 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 if (tile_ok(k)) {
                     const int it = tile_i(k), jt = tile_j(k);
                     f32x4 acc = S[k];
-                    if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs)
                         acc = O::mma(frag_tr(KS, DK, SH::SWK, 16 * it, cs), vfrag(jt, cs), acc);
-                    if constexpr (KG) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
+                    if constexpr (FG && !SO) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
                     if constexpr (OG) acc *= sEGV[buf][16 * jt + x];
                     S[k] = acc;
                 }
@@ -913,10 +890,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 if (z_ok(m)) {
                     const int it = c + NC * m;
                     f32x4 acc = Z[m];
-                    if constexpr (GATE == kGateScalar) acc *= sEG[buf][0];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs) acc = O::mma(frag_tr(KS, DK, SH::SWK, 16 * it, cs), ones[cs], acc);
-                    if constexpr (KG) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
+                    if constexpr (FG) acc *= *(const f32x4 *)(sEG[buf] + 16 * it + 4 * grp);
                     Z[m] = acc;
                 }
             }
@@ -981,7 +957,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         lds_barrier();
         const SlowStage<T> st{(float *)&sQ[0][0], OG ? &sEV[0][0] : nullptr, &sK[0][0], &sK[0][0] + SR * DK,
                               &sV[0][0]};
-        slow_chunk_lds<T, DK, DVT, SR, 64 * NC, ELU1, !SO, NM, OG>(
+        slow_chunk_lds<T, DK, DVT, SR, 64 * NC, ELU1, !SO, NM, OG, GATE == kGateScalar>(
             PS, PZ, st, rq, rk, rvv, rg, rgv, t0, nvalid, DV, vt * DVT, SO ? nullptr : oh + (size_t)t0 * DV, tid - 64 * NP);
         lds_barrier();
 #pragma unroll
@@ -998,7 +974,15 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         }
         lds_barrier();
     };
-    constexpr bool KD = KG;                          // chunks may leave the factorised range
+    // chunks may leave the factorised range (not in the state-only pass, whose key
+    // exponents are <= 0)
+    constexpr bool KD = FG && !SO;
+    // first row of the n-th chunk in processing order: the state-only pass walks its
+    // segment last chunk first; past the last chunk, rows beyond the end (zeros)
+    auto row_of = [&](int n) __attribute__((always_inline)) -> int {
+        if constexpr (SO) return n < nchunks ? (nchunks - 1 - n) * C : n * C;
+        else return n * C;
+    };
 
     // ---------------- pipeline ---------------------------------------------------------
     // The two roles run separate loops (so their registers are not live at the same
@@ -1012,9 +996,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
             const int npairs = (nchunks + 1) / 2;
             // operands one chunk ahead of the consumers, raw rows two chunks ahead
             if (nchunks > 0) {
-                load_raw(R[0], 0);
-                load_raw(R[1], C);
-                produce(R[0], 0, 0, 2 * C);
+                load_raw(R[0], row_of(0));
+                load_raw(R[1], row_of(1));
+                produce(R[0], row_of(0), 0, row_of(2));
             }
             lds_barrier();
             for (int n = 0; n < 2 * npairs; n += 2) {
@@ -1022,18 +1006,18 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 if constexpr (KD) {
                     if (n < nchunks && chunk_far(0)) slow_barriers(n * C);
                 }
-                produce(R[1], (n + 1) * C, 1, (n + 3) * C);
+                produce(R[1], row_of(n + 1), 1, row_of(n + 3));
                 lds_barrier();
                 if constexpr (KD) {
                     if (n + 1 < nchunks && chunk_far(1)) slow_barriers((n + 1) * C);
                 }
-                produce(R[0], (n + 2) * C, 0, (n + 4) * C);
+                produce(R[0], row_of(n + 2), 0, row_of(n + 4));
                 lds_barrier();
             }
         } else {
-            if (nchunks > 0) load_raw(R[0], 0);
+            if (nchunks > 0) load_raw(R[0], row_of(0));
             for (int n = 0; n < nchunks; ++n) {
-                produce(R[0], n * C, 0, (n + 1) * C);
+                produce(R[0], row_of(n), 0, row_of(n + 1));
                 lds_barrier();
                 if constexpr (KD) {
                     if (chunk_far(0)) slow_barriers(n * C);

@@ -62,9 +62,10 @@ template <typename T> struct SlowStage {
 };
 
 // Stage rows [row, row + SR) of the views (rows past the end read as zeros) with
-// all NT threads.  Key-side rows are DK long; value-side rows are the dvt columns
-// of this tile, starting at column vcol of rows DV long.
-template <typename T, int DK, int SR, int NT, bool ELU1, bool OUT, bool VG>
+// all NT threads.  Key-side rows are DK long (SG: one gate per row, the same for
+// every key dimension); value-side rows are the dvt columns of this tile, starting at
+// column vcol of rows DV long.
+template <typename T, int DK, int SR, int NT, bool ELU1, bool OUT, bool VG, bool SG = false>
 __device__ __forceinline__ void slow_stage(const SlowStage<T> &st, Rsrc rq, Rsrc rk, Rsrc rv, Rsrc rg,
                                            Rsrc rgv, int row, int DV, int vcol, int dvt, int tid)
 {
@@ -73,7 +74,13 @@ __device__ __forceinline__ void slow_stage(const SlowStage<T> &st, Rsrc rq, Rsrc
 #pragma unroll 1
     for (int p = tid; p < SR * DK / 4; p += NT) {
         const int r = p / (DK / 4), c = (p % (DK / 4)) * 4;
-        const f32x4 g = buf_load16<f32x4>(rg, ((row + r) * DK + c) * 4);
+        f32x4 g;
+        if constexpr (SG) {
+            const float gs = buf_load4(rg, (row + r) * 4);
+            g = f32x4{gs, gs, gs, gs};
+        } else {
+            g = buf_load16<f32x4>(rg, ((row + r) * DK + c) * 4);
+        }
         f32x4 al;
 #pragma unroll
         for (int e = 0; e < 4; ++e) al[e] = exp2_fast(g[e] * kLog2e);
@@ -174,7 +181,7 @@ __device__ __forceinline__ void slow_tokens(const SlowStage<T> &st, f32x4 (&S)[N
 // the token loop runs on the first slow_waves(DVT, NTS / 64, DK) of those waves, in
 // passes over the tile's columns.  Every staging thread passes 2 * ceil(nvalid / SR)
 // workgroup barriers here; the caller passes one more before it reads PS or PZ.
-template <typename T, int DK, int DVT, int SR, int NTS, bool ELU1, bool OUT, bool NM, bool VG>
+template <typename T, int DK, int DVT, int SR, int NTS, bool ELU1, bool OUT, bool NM, bool VG, bool SG = false>
 __device__ __forceinline__ void slow_chunk_lds(float *PS, float *PZ, const SlowStage<T> &st, Rsrc rq, Rsrc rk,
                                                Rsrc rv, Rsrc rg, Rsrc rgv, int t0, int nvalid, int DV, int vcol,
                                                T *out, int sw)
@@ -186,7 +193,7 @@ __device__ __forceinline__ void slow_chunk_lds(float *PS, float *PZ, const SlowS
     const bool tl = tw < NTL;                      // wave-uniform
     const int jl = lane % JPW, isub = lane / JPW;
     for (int r0 = 0; r0 < nvalid; r0 += SR) {
-        slow_stage<T, DK, SR, NTS, ELU1, OUT, VG>(st, rq, rk, rv, rg, rgv, t0 + r0, DV, vcol, DVT, sw);
+        slow_stage<T, DK, SR, NTS, ELU1, OUT, VG, SG>(st, rq, rk, rv, rg, rgv, t0 + r0, DV, vcol, DVT, sw);
         lds_barrier();
         f32x4 Z[NG];                               // normaliser rows: the same in every pass
         const int rb = isub * RPL;                 // first key row of this lane

@@ -38,7 +38,8 @@
  *    log-gate <= 0 is exact up to rounding, however strong: the chunkwise
  *    form scales keys by exp(-(sum of the chunk's log-gates up to that token)), and a
  *    chunk whose log-gates sum below -100 / log2(e) (about -69.3) in some key
- *    dimension is computed token by token instead, inside the same launch.  Such
+ *    dimension (a scalar gate counts in every key dimension) is computed token by
+ *    token instead, inside the same launch.  Such
  *    chunks cost several times a regular chunk; the result does not depend on which
  *    form a chunk took beyond rounding.
  *  - q, k, v and o share one dtype (GLA_F32 or GLA_BF16); bf16 results are rounded

@@ -228,3 +228,81 @@ def test_outer_vanishing_gate_closed_form():
 
 def test_outer_tau1_headline_shape_all_heads():
     _check_outer(torch.bfloat16, 8, 16, 4096, 128, 128, 64, "tau1", "tau1", seed=4500)
+
+
+# ---- the scalar gate (one log-gate per token and head, the Mamba2-style case) ----
+# It takes the same factorised chunk form with one factor per row, so a chunk whose
+# log2 total falls below -100 runs token by token too.
+
+def _check_scalar(dtype, B, H, L, dk, dv, chunk, kind, seed, feature_map=None, norm=False):
+    w = inputs.Workload("strong_scalar_" + kind, dtype, B, H, L, dk, dv, chunk, "scalar", feature_map, True,
+                        seed=seed)
+    inp = inputs.draw(w)
+    inp["g"] = inputs.draw_strong_gate(kind, B, H, L, 1, seed=seed + 17)[..., 0].contiguous()
+    s0 = inputs.draw_state(B, H, dk, dv, seed=seed + 1, scale=0.5)
+    d = _dev(inp)
+    tol = util.TOL[dtype]
+    if norm:
+        z0 = torch.rand(B, H, dk, generator=torch.Generator().manual_seed(seed + 2)) + 0.25
+        o, s, z = api.prefill_norm(d["q"], d["k"], d["v"], log_gate=d["g"], gate="scalar", initial_state=s0.to(DEV),
+                                   initial_norm=z0.to(DEV), chunk=chunk, feature_map=feature_map)
+        torch.cuda.synchronize()
+        ro, rs, rz = oracle.forward_norm(inp["q"], inp["k"], inp["v"], g=inp["g"], gate="scalar",
+                                         feature_map=feature_map, s0=s0, z0=z0)
+        util.assert_close(z, rz, tol, "scalar %s norm z_final" % kind)
+    else:
+        o, s = api.prefill(d["q"], d["k"], d["v"], log_gate=d["g"], gate="scalar", initial_state=s0.to(DEV),
+                           chunk=chunk, feature_map=feature_map)
+        torch.cuda.synchronize()
+        ro, rs = oracle.forward(inp["q"], inp["k"], inp["v"], g=inp["g"], gate="scalar", feature_map=feature_map,
+                                s0=s0)
+    eo = util.assert_close(o, ro, tol, "scalar %s o (chunk %d)" % (kind, chunk))
+    es = util.assert_close(s, rs, tol, "scalar %s s_final (chunk %d)" % (kind, chunk))
+    print("scalar %s %s L=%d dk=%d dv=%d chunk=%d phi=%s norm=%s: err o %.2e s %.2e" % (
+        kind, dtype, L, dk, dv, chunk, feature_map, norm, eo, es))
+
+
+@pytest.mark.parametrize("kind", ["tau1", "const3", "vanish", "bursts"])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_scalar_strong(kind, chunk, dtype):
+    _check_scalar(dtype, 2, 2, 3 * chunk + 37, 64 if dtype == torch.float32 else 128, 64, chunk, kind,
+                  seed=4200 + chunk + len(kind))
+
+
+@pytest.mark.parametrize("kind", ["tau1", "vanish", "bursts"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 16), (16, 128)])
+def test_scalar_strong_dims(kind, dk, dv):
+    _check_scalar(torch.bfloat16, 2, 2, 150, dk, dv, 64, kind, seed=4300 + dk + dv + len(kind))
+
+
+@pytest.mark.parametrize("kind", ["tau1", "const3", "vanish"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_scalar_strong_elu1_and_norm(kind, dtype):
+    _check_scalar(dtype, 2, 2, 200, 64, 64, 64, kind, seed=4400 + len(kind), feature_map="elu1")
+    _check_scalar(dtype, 2, 2, 180, 64, 64, 64, kind, seed=4450 + len(kind), feature_map="elu1", norm=True)
+
+
+@pytest.mark.parametrize("kind", ["tau1", "bursts", "const3"])
+def test_scalar_strong_segmented(kind):
+    """Few long sequences with a scalar gate are segmented; both passes meet chunks
+    out of range and the scan carries totals below the fp32 range."""
+    B, H, L, d = 1, 2, 64 * 70 + 13, 128
+    assert api.workspace_bytes(B, H, L, d, d, 64, torch.bfloat16) > 0
+    _check_scalar(torch.bfloat16, B, H, L, d, d, 64, kind, seed=4500 + len(kind))
+
+
+def test_scalar_vanishing_gate_closed_form():
+    """A scalar gate of 0 keeps only the current write: o_t = (q_t . k_t) v_t."""
+    B, H, L, d = 2, 2, 200, 64
+    w = inputs.Workload("scalar_vanish", torch.bfloat16, B, H, L, d, d, 64, "scalar", None, True, seed=4600)
+    inp = inputs.draw(w)
+    g = torch.full((B, H, L), -1000.0)
+    dd = _dev(inp)
+    o, s = api.prefill(dd["q"], dd["k"], dd["v"], log_gate=g.to(DEV), gate="scalar", chunk=64)
+    torch.cuda.synchronize()
+    q, k, v = (inp[x].double().numpy() for x in ("q", "k", "v"))
+    util.assert_close(o, np.einsum("bhti,bhti->bht", q, k)[..., None] * v, util.TOL[torch.bfloat16],
+                      "scalar vanishing-gate o vs closed form")
+    util.assert_close(s, k[:, :, -1, :, None] * v[:, :, -1, None, :], util.TOL[torch.bfloat16],
+                      "scalar vanishing-gate s_final vs closed form")
