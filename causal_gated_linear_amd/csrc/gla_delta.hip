@@ -536,7 +536,7 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
     };
     // C: the block below the diagonal (two blocks): X_10 = -X_11 N_10 X_00
     auto solveC = [&]() {
-        if (NB == 2 && w == 0) {
+        if (NB == 2 && w == 3) {
             // R = N_10 X_00: A = N_10 rows, B = X_00 columns = X_00^T rows (masked)
             f32x4 b0 = lds_frag(sNX + x * LDC, 0, grp);       // X^T[x][4 grp + e] = X[4 grp + e][x]
 #pragma unroll
@@ -547,7 +547,8 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
             *(f32x4 *)(sNX + x * LDC + 16 + 4 * grp) = -xr;  // X^T block (0, 1)
         }
     };
-    // D: -W and U~ of chunk m into its buffer
+    // D: -W and U~ of chunk m into its buffer, by all eight waves (the state waves
+    // would otherwise wait for it); the fragments of X diag(beta) are formed once
     auto solveD = [&](int m) {
         const T *sK = bK(m), *sV = sVr[m & 1];
         T *sW = bW(m), *sU = bU(m);
@@ -555,24 +556,30 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
         auto xb = [&](int tb, int sb) -> F4 {
             return cvt4<T>(xrow(tb, sb) * *(const f32x4 *)(bt + 16 * sb + 4 * grp));
         };
+        const F4 x00 = xb(0, 0);
+        F4 x10 = x00, x11 = x00;
+        if (NB == 2) {
+            x10 = xb(1, 0);
+            x11 = xb(1, 1);
+        }
         const int nvb = DVT / 16;
-        for (int id = w; id < (NKB + nvb) * NB; id += 4) {
+        for (int id = w; id < (NKB + nvb) * NB; id += 8) {
             const int tb = id % NB, cb = id / NB;
             f32x4 acc = zero;
             if (cb < NKB) {       // lane (x, grp) element e: W[16 tb + x][16 cb + 4 grp + e]
                 if (tb == 1)
                     acc = mac2(col_frag(sK, LDK, 4 * grp, 16 * cb, x), col_frag(sK, LDK, 16 + 4 * grp, 16 * cb, x),
-                               xb(1, 0), xb(1, 1), acc);
+                               x10, x11, acc);
                 else
-                    acc = mac1(col_frag(sK, LDK, 4 * grp, 16 * cb, x), xb(0, 0), acc);
+                    acc = mac1(col_frag(sK, LDK, 4 * grp, 16 * cb, x), x00, acc);
                 store4(sW + (16 * tb + x) * LDK + 16 * cb + 4 * grp, -acc);
             } else {              // lane (x, grp) element e: U~[16 tb + 4 grp + e][16 jb + x]
                 const int jb = cb - NKB;
                 if (tb == 1)
-                    acc = mac2(xb(1, 0), xb(1, 1), col_frag(sV, LDV, 4 * grp, 16 * jb, x),
+                    acc = mac2(x10, x11, col_frag(sV, LDV, 4 * grp, 16 * jb, x),
                                col_frag(sV, LDV, 16 + 4 * grp, 16 * jb, x), acc);
                 else
-                    acc = mac1(xb(0, 0), col_frag(sV, LDV, 4 * grp, 16 * jb, x), acc);
+                    acc = mac1(x00, col_frag(sV, LDV, 4 * grp, 16 * jb, x), acc);
                 store4(sU + (16 * jb + x) * LDU + 16 * tb + 4 * grp, acc);
             }
         }
@@ -650,26 +657,30 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
         lds_barrier();
         if (solver) solveC();
         lds_barrier();
-        if (solver) {
-            solveD(0);
-            if (nch > 1) fetch(1);
-        }
+        solveD(0);                                     // all eight waves
+        if (solver && nch > 1) fetch(1);
     }
+    // The rows of chunk n+2 are requested by each solver wave in a step where it has
+    // no part of the solve: waves NB.. while waves 0..NB-1 invert the diagonal blocks,
+    // waves 0..NB-1 while wave 3 forms the block below the diagonal.
+    const bool early = w >= NB;
     for (int n = 0; n < nch; ++n) {
         const bool more = solver && n + 1 < nch;       // wave-uniform
+        const bool ahead = solver && n + 2 < nch;
         if (more) stash(n + 1);
-        if (solver && n + 2 < nch) fetch(n + 2);
         lds_barrier();                                 // chunk n's -W, U~ and chunk n+1's rows visible
         if (more) solveA(n + 1);
         if (active) scanU(n);
         lds_barrier();
         if (more) solveB();
+        if (ahead && early) fetch(n + 2);
         if (active) scanO(n);
         lds_barrier();
         if (more) solveC();
+        if (ahead && !early) fetch(n + 2);
         if (active) scanS(n);
         lds_barrier();
-        if (more) solveD(n + 1);
+        if (n + 1 < nch) solveD(n + 1);
     }
 
     if (active && a.s_final) {
