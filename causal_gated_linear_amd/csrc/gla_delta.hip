@@ -562,8 +562,8 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
             x10 = xb(1, 0);
             x11 = xb(1, 1);
         }
-        const int nvb = DVT / 16;
-        for (int id = w; id < (NKB + nvb) * NB; id += 8) {
+        const int nvb = DVT / 16, ntile = (NKB + nvb) * NB;
+        auto tile = [&](int id) {
             const int tb = id % NB, cb = id / NB;
             f32x4 acc = zero;
             if (cb < NKB) {       // lane (x, grp) element e: W[16 tb + x][16 cb + 4 grp + e]
@@ -582,6 +582,17 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
                     acc = mac1(x00, col_frag(sV, LDV, 4 * grp, 16 * jb, x), acc);
                 store4(sU + (16 * jb + x) * LDU + 16 * tb + 4 * grp, acc);
             }
+        };
+        if constexpr (NB == 2) {
+            // at most (NKB + 4) * 2 tiles, dealt round-robin: a fixed trip count lets
+            // the compiler interleave the tiles' reads and products (with one 16-row
+            // block this measured slower than the plain loop)
+            constexpr int ROUNDS = ((NKB + 4) * NB + 7) / 8;
+#pragma unroll
+            for (int r = 0; r < ROUNDS; ++r)
+                if (w + 8 * r < ntile) tile(w + 8 * r);
+        } else {
+            for (int id = w; id < ntile; id += 8) tile(id);
         }
     };
 
