@@ -35,6 +35,8 @@
 // solves chunk n+1's system into the other LDS buffer (see its own comment).
 // bf16 inputs: bf16 matrix-core operands, fp32 accumulation and fp32 X; fp32 inputs:
 // fp32 matrix-core products throughout.
+#include <type_traits>
+
 #include "gla_device.hpp"
 #include "gla_launch.hpp"
 
@@ -493,17 +495,32 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
 
     // ---- the triangular solve of chunk m, in four steps ------------------------------
     // A: N = tril(diag(beta) K K^T, -1), strictly lower entries only
+    // With two blocks, the full block N_10 is split over its key blocks between waves
+    // 1 and 3: wave 3 stores its part transposed in the X^T block (0, 1), which is free
+    // until the off-diagonal step adds it back in and then overwrites it.
     auto solveA = [&](int m) {
         const T *sK = bK(m);
         const float *bt = sBt[m & 1];
-        for (int id = w; id < NB * (NB + 1) / 2; id += 4) {
-            const int tb = id > 0, sb = id == 2;       // tiles (0,0), (1,0), (1,1)
-            const f32x4 g = contract_rows(sK + (16 * tb + x) * LDK, sK + (16 * sb + x) * LDK, NKB, grp, zero);
+        // block (tb, sb) of N over key blocks [k0, k0 + NK); `tr`: store transposed
+        auto part = [&](int tb, int sb, int k0, auto nkc, bool tr) {
+            constexpr int NK = decltype(nkc)::value;
+            const f32x4 g = contract_rows(sK + (16 * tb + x) * LDK + 16 * k0, sK + (16 * sb + x) * LDK + 16 * k0,
+                                          NK, grp, zero);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * tb + 4 * grp + e, s = 16 * sb + x;
-                if (s < t) sNX[t * LDC + s] = bt[t] * g[e];
+                if (tr) sNX[s * LDC + t] = bt[t] * g[e];
+                else if (s < t) sNX[t * LDC + s] = bt[t] * g[e];
             }
+        };
+        if constexpr (NB == 2) {
+            constexpr int H1 = (NKB + 1) / 2;         // wave 1's key blocks of N_10
+            if (w == 0) part(0, 0, 0, std::integral_constant<int, NKB>{}, false);
+            else if (w == 1) part(1, 0, 0, std::integral_constant<int, H1>{}, false);
+            else if (w == 2) part(1, 1, 0, std::integral_constant<int, NKB>{}, false);
+            else part(1, 0, H1, std::integral_constant<int, NKB - H1>{}, true);
+        } else {
+            if (w == 0) part(0, 0, 0, std::integral_constant<int, NKB>{}, false);
         }
     };
     // B: the diagonal blocks' inverses, stored transposed (upper triangle with diagonal)
@@ -542,7 +559,9 @@ __global__ __launch_bounds__(512) void delta_fused_kernel(const DeltaArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (4 * grp + e < x) b0[e] = 0.f;            // X_00 is zero above its diagonal
-            const f32x4 r = mma1(lds_frag(sNX + (16 + x) * LDC, 0, grp), b0, zero);
+            // N_10 = the part in place + wave 3's part, stored transposed in block (0, 1)
+            const f32x4 n10 = lds_frag(sNX + (16 + x) * LDC, 0, grp) + col_frag(sNX, LDC, 4 * grp, 16, x);
+            const f32x4 r = mma1(n10, b0, zero);
             const f32x4 xr = mma1(xrow(1, 1), r, zero);       // X_11 R
             *(f32x4 *)(sNX + x * LDC + 16 + 4 * grp) = -xr;  // X^T block (0, 1)
         }
