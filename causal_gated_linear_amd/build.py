@@ -33,7 +33,6 @@ def _units():
             units.append(("gla_prefill_inst.hip", "prefill_%d_%d.o" % (bf, dk),
                           ["-DGLA_INST_BF16=%d" % bf, "-DGLA_INST_DK=%d" % dk]))
     units.append(("gla_decode.hip", "decode.o", []))
-    units.append(("gla_scan.hip", "scan.o", []))
     units.append(("gla_delta.hip", "delta.o", []))
     units.append(("gla_gate.hip", "gate.o", []))
     units.append(("gla_outer.hip", "outer.o", []))

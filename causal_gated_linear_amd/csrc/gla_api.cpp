@@ -74,12 +74,12 @@ int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes, bool outer
 // Few long sequences: rather than narrowing the value tile (which repeats the per-
 // token gate and score work in every tile of a head), split each sequence into
 // segments at the widest tile.  A state-only pass computes every segment's state
-// from zero, a scan over segments turns those into each segment's initial state,
-// and the full pass then runs all segments in parallel.  Used when the widest tile
-// gives fewer than 256 workgroups and the sequences have at least 64 chunks;
-// segments keep at least 16 chunks.  Sequences of 32 to 63 chunks are split too when
-// even the narrowest tile leaves CUs idle (fewer than 256 workgroups), into segments
-// of at least 4 chunks, so that each tile's chain of chunks is short.
+// from zero, and the full pass then runs all segments in parallel, each workgroup
+// first scanning the earlier segments' states into its own initial state.  Used when
+// the widest tile gives fewer than 256 workgroups and the sequences have at least 64
+// chunks; segments keep at least 16 chunks.  Sequences of 32 to 63 chunks are split
+// too when even the narrowest tile leaves CUs idle (fewer than 256 workgroups), at a
+// 32-column tile into at most four segments of at least 4 chunks.
 // gla_testing_set_plan can force the count.
 constexpr int kSegMinChunks = 16, kSegMinSeqChunks = 64;
 constexpr int kSegShortMinChunks = 4, kSegShortSeqChunks = 32;
@@ -98,7 +98,12 @@ PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_by
     if (nchunks >= kSegMinSeqChunks) {
         while (wgs * nseg < 256 && nchunks / (2 * nseg) >= kSegMinChunks) nseg *= 2;
     } else if (nchunks >= kSegShortSeqChunks && (long)BH * (d_v / 16) < 256) {
-        while (wgs * nseg * 2 <= 256 && nchunks / (2 * nseg) >= kSegShortMinChunks) nseg *= 2;
+        // a 32-column tile with at most four segments: each workgroup scans the earlier
+        // segments' states before its first chunk, and with chains this short a deeper
+        // split costs more than the repeated per-token work of a narrower tile
+        if (tile_usable(32, d_k, d_v, chunk, elem_bytes)) dvt = 32;
+        const long w32 = (long)BH * (d_v / dvt);
+        while (w32 * nseg * 2 <= 256 && nseg < 4 && nchunks / (2 * nseg) >= kSegShortMinChunks) nseg *= 2;
     }
     const int forced = g_force_prefill_segments;
     if (forced >= 1) nseg = forced < nchunks ? forced : (nchunks > 0 ? nchunks : 1);
@@ -116,8 +121,8 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v)
 {
     if (p.nseg <= 1) return 0;
-    const size_t states = (size_t)BH * p.nseg * d_k * d_v * 4;
-    return 2 * round256(states) + round256((size_t)BH * p.nseg * d_k * 4);
+    const size_t states = (size_t)BH * (p.nseg - 1) * d_k * d_v * 4;
+    return round256(states) + round256((size_t)BH * (p.nseg - 1) * d_k * 4);
 }
 }  // namespace gla
 
@@ -380,11 +385,10 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
     if (plan.nseg == 1) {
         e = gla::launch_prefill(a, dt, d_k, chunk, plan.dvt, false, hs);
     } else {
-        // workspace: segment states from zero, segment initial states, gate totals
-        const size_t states = (size_t)BH * plan.nseg * d_k * d_v * 4;
-        char *w = (char *)workspace;
-        float *ds = (float *)w, *sin = (float *)(w + gla::round256(states));
-        float *gam = (float *)(w + 2 * gla::round256(states));
+        // workspace: the states from zero and gate totals of all segments but the last
+        const size_t states = (size_t)BH * (plan.nseg - 1) * d_k * d_v * 4;
+        float *ds = (float *)workspace;
+        float *gam = (float *)((char *)workspace + gla::round256(states));
         // pass 1: the states from zero of every segment but the last (whose state
         // only feeds s_final, which pass 2 writes)
         gla::PrefillArgs a1 = a;
@@ -392,11 +396,11 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
         a1.nseg = plan.nseg - 1;
         a1.xcd_remap = (a1.n_vt > 1 && ((long)BH * a1.nseg * a1.n_vt) % 8 == 0) ? 1 : 0;
         e = gla::launch_prefill(a1, dt, d_k, chunk, plan.dvt, true, hs);
-        if (e == hipSuccess)                       // scan over segments: initial states
-            e = gla::launch_segment_scan(ds, gate == GLA_GATE_NONE ? nullptr : gam, s0, sin,
-                                         (int)BH, plan.nseg, d_k, d_v, hs);
-        gla::PrefillArgs a2 = a;                   // pass 2: outputs of every segment
-        a2.s0 = sin; a2.s_final = s_final; a2.final_last_seg = 1;
+        // pass 2: outputs of every segment, each workgroup scanning the earlier
+        // segments' states into its own initial state
+        gla::PrefillArgs a2 = a;
+        a2.s_final = s_final; a2.final_last_seg = 1;
+        a2.seg_ds = ds; a2.seg_gam = gate == GLA_GATE_NONE ? nullptr : gam;
         if (e == hipSuccess) e = gla::launch_prefill(a2, dt, d_k, chunk, plan.dvt, false, hs);
     }
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

@@ -36,6 +36,11 @@ struct PrefillArgs {
     float *z_final;          // [B][H][d_k] or null
     // outer-product gate: value-dimension log-gates (natural log) [B][H][L][d_v]
     const float *gv = nullptr;
+    // full pass of a segmented prefill: the states from zero of segments 0 .. nseg-2
+    // ([BH][nseg - 1][d_k][d_v]) and their log2 gate totals ([BH][nseg - 1][d_k], null
+    // without gates); each workgroup scans them into its segment's initial state, and
+    // s0 is then the sequence's own initial state [BH][d_k][d_v] (or null)
+    const float *seg_ds = nullptr, *seg_gam = nullptr;
 };
 
 struct DecodeArgs {
@@ -77,9 +82,9 @@ struct PrefillPlan {
 };
 PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes);
 
-// Device workspace of a segmented prefill: segment states from zero, segment
-// initial states (both fp32 [BH][nseg][d_k][d_v]) and segment gate totals
-// (fp32 [BH][nseg][d_k]); 0 when nseg == 1.
+// Device workspace of a segmented prefill: the states from zero of all segments but
+// the last (fp32 [BH][nseg - 1][d_k][d_v]) and their gate totals (fp32
+// [BH][nseg - 1][d_k]); 0 when nseg == 1.
 size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v);
 
 // Enqueue the prefill kernel.  dtype: 0 fp32, 1 bf16.  state_only: compute only
@@ -87,13 +92,6 @@ size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v);
 // outputs.  Sizes must already be valid.
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int d_k, int chunk, int dvt,
                           bool state_only, hipStream_t stream);
-
-// Enqueue the scan over segments: for every head and state element, in segment
-// order, sin[seg] = S; S = exp2(gam[seg]) * S + ds[seg], from S = s0 (or 0).  ds and
-// gam hold the nseg - 1 first segments ([BH][nseg - 1][...]); the last segment's
-// final state comes from the full pass.  gam may be null (no gate).
-hipError_t launch_segment_scan(const float *ds, const float *gam, const float *s0, float *sin,
-                               int BH, int nseg, int d_k, int d_v, hipStream_t stream);
 
 // Enqueue one decode step.  Sizes must already be valid.
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int d_k, int d_v, hipStream_t stream);

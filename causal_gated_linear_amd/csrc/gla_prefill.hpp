@@ -632,18 +632,58 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     auto z_ok = [&](int m) __attribute__((always_inline)) -> bool { return c + NC * m < NKB; };
     // initial state (consumers, inside their own branch below, so that these loads
     // are never pending on the producers' path)
+    // In the full pass of a segmented prefill (a.seg_ds set) the segment's initial
+    // state is the weighted scan over the earlier segments' states from zero:
+    // S = s0, then S = Diag(exp2(gam_p)) S + ds_p for p = 0 .. seg-1.
     auto load_s0 = [&]() __attribute__((always_inline)) {
-        if (a.s0) {
+        if (SO || !a.seg_ds) {
+            if (a.s0) {
+#pragma unroll
+                for (int k = 0; k < NSLOT; ++k) {
+                    const bool ok = tile_ok(k);
+                    const int it = ok ? tile_i(k) : 0, jt = ok ? tile_j(k) : 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * it + 4 * grp + r;
+                        const float v = a.s0[((size_t)bhs * DK + i) * DV + vt * DVT + 16 * jt + x];
+                        S[k][r] = ok ? v : 0.f;
+                    }
+                }
+            }
+        } else {
 #pragma unroll
             for (int k = 0; k < NSLOT; ++k) {
                 const bool ok = tile_ok(k);
                 const int it = ok ? tile_i(k) : 0, jt = ok ? tile_j(k) : 0;
+                const int j = vt * DVT + 16 * jt + x;
+                f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (a.s0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * it + 4 * grp + r;
-                    const float v = a.s0[((size_t)bhs * DK + i) * DV + vt * DVT + 16 * jt + x];
-                    S[k][r] = ok ? v : 0.f;
+                    for (int r = 0; r < 4; ++r) v[r] = a.s0[((size_t)bh * DK + 16 * it + 4 * grp + r) * DV + j];
                 }
+                // segments four at a time, all their loads requested before the steps
+                for (int sp0 = 0; sp0 < seg; sp0 += 4) {
+                    f32x4 d[4], gm[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        d[u] = gm[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (sp0 + u < seg) {
+                            const size_t hp = (size_t)bh * (a.nseg - 1) + sp0 + u;
+                            const float *ds = a.seg_ds + (hp * DK + 16 * it + 4 * grp) * DV + j;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) d[u][r] = ds[(size_t)r * DV];
+                            if (a.seg_gam) gm[u] = *(const f32x4 *)(a.seg_gam + hp * DK + 16 * it + 4 * grp);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (sp0 + u < seg) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) v[r] = fmaf(exp2_fast(gm[u][r]), v[r], d[u][r]);
+                        }
+                    }
+                }
+                S[k] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
     };

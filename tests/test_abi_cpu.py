@@ -188,11 +188,12 @@ def test_state_alloc_rejects(lib):
 
 
 def test_workspace_for_few_long_sequences(lib):
-    """Few long sequences are split into segments, which need a workspace: two fp32
-    state arrays [B*H][segments][d_k][d_v] and the segment gate totals."""
+    """Few long sequences are split into segments, which need a workspace: the fp32
+    states from zero [B*H][segments - 1][d_k][d_v] of all segments but the last and
+    their gate totals [B*H][segments - 1][d_k]."""
     n = lib.gla_prefill_workspace_bytes(1, 32, 32768, 128, 128, 64, 1)
     rnd = lambda x: (x + 255) // 256 * 256
-    assert n == 2 * rnd(32 * 4 * 128 * 128 * 4) + rnd(32 * 4 * 128 * 4)   # 4 segments of 8192 tokens
+    assert n == rnd(32 * 3 * 128 * 128 * 4) + rnd(32 * 3 * 128 * 4)   # 4 segments of 8192 tokens
     assert lib.gla_prefill_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 0   # enough heads
     assert lib.gla_prefill_workspace_bytes(1, 2, 64 * 31, 64, 64, 64, 1) == 0   # too short
     # 32 to 63 chunks on too few heads for even the narrowest tile: short segments
@@ -432,7 +433,7 @@ def test_decode_outer_rejects(lib):
 
 def test_prefill_noalloc_rejects_sizes_beyond_its_scratch(lib):
     """The allocation-free prefill holds 32 MiB of scratch, which covers every size the
-    automatic plan segments (at most about 254 head-segments of 128 KiB of states).  A
+    automatic plan segments (at most about 254 head-segments of a 64 KiB state).  A
     plan forced through the test hook to more segments needs more and is rejected on
     the host, before any HIP call."""
     P = ctypes.c_void_p
