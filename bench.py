@@ -609,7 +609,7 @@ def summarize_traffic_all(dirs, command):
     fg, wg = groups(fdir, "FETCH_SIZE"), groups(wdir, "WRITE_SIZE")
     lines = ["# HBM traffic of the library's kernels for the bench.py workloads, per dispatch",
              "# (the workloads and their algorithmic bytes per launch are those of bench.py's JSON line:",
-             "#  bytes_per_launch / bytes_per_step; the segmented scalar_long prefill runs three kernels)",
+             "#  bytes_per_launch / bytes_per_step; the segmented prefills run two kernels)",
              "# commands (run from the repository root, each a rocprofv3 --pmc pass of its own):"] + \
             ["#   " + c for c in command.split(" ;; ")] + \
             ["# calibration: copy kernel reads and writes %d bytes per launch; fetch scale %.2f, "
@@ -652,7 +652,7 @@ def summarize_stats(d, command):
              "#   decode:  B=256 H=32 d=128 bf16, fp32 state; its state comes from a 512-token prefill "
              "(prefill grid 16384)",
              "#   other prefills: linear_elu1 (4x8x2048, d=64), scalar_long (1x32x32768, segmented: state-only "
-             "pass, segment scan, full pass), fp32_single_head, and the normalised form at the headline shape",
+             "pass, then the full pass), fp32_single_head, and the normalised form at the headline shape",
              "#   delta rule at the headline shape, chunk 32: delta_fused_kernel (grid 256); "
              "delta decode at the decode shape",
              "#   gate producer: 8x4096 tokens, d_model 2048 -> 16 heads x 128 (grid 256, persistent: 2 blocks of 64 tokens each)",
