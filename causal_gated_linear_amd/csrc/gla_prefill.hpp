@@ -164,13 +164,7 @@ struct PrefillShape {
     // dealt to the 64*NP producer lanes in order, NVL per lane
     static constexpr int NVP = C * VCH;
     static constexpr int NVL = NVP >= 64 * NP ? NVP / (64 * NP) : 1;
-    // consumer state tiles: with NKB % NC == 0 consumer c owns i-tiles c + NC*a
-    // (a < IPC) for every j-tile, so its fragments are shared across tiles;
-    // otherwise tiles are dealt round-robin
-    static constexpr int NU = NKB * NJT;
-    static constexpr bool BLOCKED = NKB % NC == 0;
-    static constexpr int IPC = BLOCKED ? NKB / NC : 1;
-    static constexpr int NSLOT = BLOCKED ? IPC * NJT : (NU + NC - 1) / NC;
+    static constexpr int NU = NKB * NJT;          // 16x16 state tiles
     // output staging: 16 rows x DVS, stored by 64 lanes in 16-byte chunks
     static constexpr int SCH = DVS / CE, SWS = SCH >= 16 ? kSwz16 : (SCH == 8 ? kSwzO8 : SCH - 1);
     static constexpr int OCH = 16 * SCH;           // chunks per staged block
@@ -290,7 +284,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     constexpr int NP = SH::NP, NC = SH::NC, NBUF = SH::NBUF, CE = SH::CE;
     constexpr int NTB = SH::NTB, NKB = SH::NKB, NJT = SH::NJT;
     constexpr int CW = SH::CW, RSEG = SH::RSEG, RPS = SH::RPS;
-    constexpr int NVL = SH::NVL, NSLOT = SH::NSLOT, NU = SH::NU;
+    constexpr int NVL = SH::NVL, NU = SH::NU;
 
     __shared__ __attribute__((aligned(16))) T sQ[NBUF][C * DK];      // Q~ [t][i]
     __shared__ __attribute__((aligned(16))) T sK[NBUF][C * DK];      // K^ [s][i]
@@ -361,8 +355,14 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     float gsum[CE];                                // state-only pass: gate totals so far
 #pragma unroll
     for (int e = 0; e < CE; ++e) gsum[e] = 0.f;
-    // raw register sets: rows are requested two chunks ahead with two operand buffers
-    constexpr int NRAW = NBUF == 2 ? 2 : 1;
+    // Who holds the fp32 state (see "state owners" below): the producers (POWN) where
+    // that measured faster -- scalar gates, the normalised form, the outer gate at
+    // 64-row chunks -- else the consumers.
+    constexpr bool POWN = !SO && (GATE == kGateScalar || NM || (OG && C == 64));
+    // raw register sets: with two operand buffers the rows are requested two chunks
+    // ahead, except where the producers also hold the state and per-key-dimension
+    // gates (one chunk ahead, which leaves room in their registers)
+    constexpr int NRAW = NBUF == 2 && !(POWN && KG) ? 2 : 1;
     Raw R[NRAW];
 
     // Raw rows of the chunk starting at t0, requested in three parts so that each
@@ -606,32 +606,44 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         }
     };
 
-    // ---------------- consumers -------------------------------------------------------
+    // ---------------- state owners and consumers ----------------------------------------
+    // The fp32 state tiles sit in the registers of their owner waves.  With POWN these
+    // are the producers: while the consumers compute chunk n's outputs from the bf16
+    // copy of the state before it, the producers prepare chunk n+1's operands and
+    // update S with chunk n's K^ and V, then write the next copy.  Otherwise the
+    // consumers update S after their outputs (and alone in the state-only pass).
+    // Owner ow holds the 16x16 tiles (key block ow + NOW a, every value tile) when
+    // NKB % NOW == 0, so that its key fragments are shared across value tiles;
+    // otherwise tiles are dealt round-robin.
     const int c = w - NP;
+    constexpr int NOW = POWN ? NP : NC;              // owner waves
+    const int ow = POWN ? w : c;                      // this wave's index among them
+    constexpr bool BLK = NKB % NOW == 0;
+    constexpr int IPC = BLK ? NKB / NOW : 1;
+    constexpr int NSLOT = BLK ? IPC * NJT : (NU + NOW - 1) / NOW;
     auto tile_i = [&](int k) __attribute__((always_inline)) -> int {
-        if constexpr (SH::BLOCKED) return c + NC * (k % SH::IPC);
-        else return (k * NC + c) % NKB;
+        if constexpr (BLK) return ow + NOW * (k % IPC);
+        else return (k * NOW + ow) % NKB;
     };
     auto tile_j = [&](int k) __attribute__((always_inline)) -> int {
-        if constexpr (SH::BLOCKED) return k / SH::IPC;
-        else return (k * NC + c) / NKB;
+        if constexpr (BLK) return k / IPC;
+        else return (k * NOW + ow) / NKB;
     };
     auto tile_ok = [&](int k) __attribute__((always_inline)) -> bool {
-        if constexpr (SH::BLOCKED) return true;
-        else return k * NC + c < NU;
+        if constexpr (BLK) return true;
+        else return k * NOW + ow < NU;
     };
 
     f32x4 S[NSLOT];
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // normaliser tiles: consumer c holds z rows 16 it + 4 grp + r for it = c + NC m
-    constexpr int NZ = NM ? (NKB + NC - 1) / NC : 0;
+    // normaliser tiles: owner ow holds z rows 16 it + 4 grp + r for it = ow + NOW m
+    constexpr int NZ = NM ? (NKB + NOW - 1) / NOW : 0;
     f32x4 Z[NZ > 0 ? NZ : 1];
 #pragma unroll
     for (int m = 0; m < NZ; ++m) Z[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto z_ok = [&](int m) __attribute__((always_inline)) -> bool { return c + NC * m < NKB; };
-    // initial state (consumers, inside their own branch below, so that these loads
-    // are never pending on the producers' path)
+    auto z_ok = [&](int m) __attribute__((always_inline)) -> bool { return ow + NOW * m < NKB; };
+    // initial state (by the owners)
     // In the full pass of a segmented prefill (a.seg_ds set) the segment's initial
     // state is the weighted scan over the earlier segments' states from zero:
     // S = s0, then S = Diag(exp2(gam_p)) S + ds_p for p = 0 .. seg-1.
@@ -695,7 +707,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 for (int m = 0; m < NZ; ++m) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int i = 16 * (z_ok(m) ? c + NC * m : 0) + 4 * grp + r;
+                        const int i = 16 * (z_ok(m) ? ow + NOW * m : 0) + 4 * grp + r;
                         const float v = a.z0[(size_t)bhs * DK + i];
                         Z[m][r] = z_ok(m) ? v : 0.f;
                     }
@@ -707,7 +719,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         if constexpr (NM) {
 #pragma unroll
             for (int m = 0; m < NZ; ++m)
-                if (z_ok(m) && x == 0) *(f32x4 *)(sZ[par] + 16 * (c + NC * m) + 4 * grp) = Z[m];
+                if (z_ok(m) && x == 0) *(f32x4 *)(sZ[par] + 16 * (ow + NOW * m) + 4 * grp) = Z[m];
         }
     };
 
@@ -857,43 +869,33 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         }
     };
 
-    // Outputs of chunk starting at t0 from operand buffer `buf`, then the state step.
-    auto consume = [&](int t0, int buf, int par) __attribute__((always_inline)) {
+    // State step of the chunk starting at t0 in operand buffer `buf`, by the owners:
+    // S <- Diag(exp Gamma) (S + K^^T V) (outer gate: times Diag(exp GB) on the right;
+    // state-only pass: S += K'^T V, the keys already decayed to the segment end).
+    auto state_step = [&](int t0, int buf) __attribute__((always_inline)) {
         const int nvalid = min(L - t0, C);
-        const T *Q = sQ[buf], *K = sK[buf], *V = sV[buf], *SS = sS[par];
-        const T *KS = K;                           // keys of the state update
+        const T *KS = sK[buf], *V = sV[buf];
         auto vfrag = [&](int jt, int cs) __attribute__((always_inline)) -> F {
             return frag_tr(V, DVT, SH::SWV, 16 * jt, cs);
         };
-        // consumer c owns t-block c % NTB (value tiles from (c / NTB) * NJC), or the
-        // t-blocks tb with tb % NC == c when there are more t-blocks than consumers
-        if constexpr (!SO) static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
-            constexpr int TB = decltype(tbc)::value;
-            if constexpr (NTB <= NC) {
-                if (c < NTB * SH::JS && TB == c % NTB) out_block(tbc, (c / NTB) * SH::NJC, t0, nvalid, buf, par, Q, K, V, SS);
-            } else {
-                if (TB % NC == c) out_block(tbc, 0, t0, nvalid, buf, par, Q, K, V, SS);
-            }
-        });
-        // state tiles: S <- Diag(exp Gamma) (S + K^^T V)  (scalar gate: exp(Gamma) S + K~^T V)
-        if constexpr (SH::BLOCKED) {
-            F af[SH::IPC][SH::CSTEPS];
+        if constexpr (BLK) {
+            F af[IPC][SH::CSTEPS];
 #pragma unroll
-            for (int ia = 0; ia < SH::IPC; ++ia)
+            for (int ia = 0; ia < IPC; ++ia)
 #pragma unroll
-                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_tr(KS, DK, SH::SWK, 16 * (c + NC * ia), cs);
+                for (int cs = 0; cs < SH::CSTEPS; ++cs) af[ia][cs] = frag_tr(KS, DK, SH::SWK, 16 * (ow + NOW * ia), cs);
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt) {
                 F bfr[SH::CSTEPS];
 #pragma unroll
                 for (int cs = 0; cs < SH::CSTEPS; ++cs) bfr[cs] = vfrag(jt, cs);
 #pragma unroll
-                for (int ia = 0; ia < SH::IPC; ++ia) {
-                    const int k = jt * SH::IPC + ia;
+                for (int ia = 0; ia < IPC; ++ia) {
+                    const int k = jt * IPC + ia;
                     f32x4 acc = S[k];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs) acc = O::mma(af[ia][cs], bfr[cs], acc);
-                    if constexpr (FG && !SO) acc *= *(const f32x4 *)(sEG[buf] + 16 * (c + NC * ia) + 4 * grp);
+                    if constexpr (FG && !SO) acc *= *(const f32x4 *)(sEG[buf] + 16 * (ow + NOW * ia) + 4 * grp);
                     if constexpr (OG) acc *= sEGV[buf][16 * jt + x];
                     S[k] = acc;
                 }
@@ -928,7 +930,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
 #pragma unroll
             for (int m = 0; m < NZ; ++m) {
                 if (z_ok(m)) {
-                    const int it = c + NC * m;
+                    const int it = ow + NOW * m;
                     f32x4 acc = Z[m];
 #pragma unroll
                     for (int cs = 0; cs < SH::CSTEPS; ++cs) acc = O::mma(frag_tr(KS, DK, SH::SWK, 16 * it, cs), ones[cs], acc);
@@ -936,9 +938,32 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     Z[m] = acc;
                 }
             }
+        }
+    };
+
+    // Outputs of the chunk starting at t0 from operand buffer `buf` and state copy `par`
+    // (consumers), then, where the consumers own the state, its step and next copy.
+    auto consume = [&](int t0, int buf, int par) __attribute__((always_inline)) {
+        if constexpr (!SO) {
+            const int nvalid = min(L - t0, C);
+            const T *Q = sQ[buf], *K = sK[buf], *V = sV[buf], *SS = sS[par];
+            // consumer c owns t-block c % NTB (value tiles from (c / NTB) * NJC), or the
+            // t-blocks tb with tb % NC == c when there are more t-blocks than consumers
+            static_for<NTB>([&](auto tbc) __attribute__((always_inline)) {
+                constexpr int TB = decltype(tbc)::value;
+                if constexpr (NTB <= NC) {
+                    if (c < NTB * SH::JS && TB == c % NTB)
+                        out_block(tbc, (c / NTB) * SH::NJC, t0, nvalid, buf, par, Q, K, V, SS);
+                } else {
+                    if (TB % NC == c) out_block(tbc, 0, t0, nvalid, buf, par, Q, K, V, SS);
+                }
+            });
+        }
+        if constexpr (!POWN) {
+            state_step(t0, buf);
+            if constexpr (!SO) write_state(par ^ 1);
             write_z(par ^ 1);
         }
-        if constexpr (!SO) write_state(par ^ 1);
     };
 
     // ---------------- chunks out of the factorised form's range -------------------------
@@ -961,26 +986,22 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         }
         return __builtin_amdgcn_readfirstlane(f) != 0;
     };
-    // The chunk starting at t0, token by token (gla_slow.hpp), by the consumer waves;
-    // the producers pass the same barriers (slow_barriers) and keep the rows they hold
-    // for the next chunks.  The consumers hand their fp32 state tiles over through the
-    // space of the bf16 state copies (as [j][i]) and take them back at the end; the
-    // operand buffers stage the rows.  Neither is needed otherwise at this point: the
-    // chunk's own operands are not used, and the producers fill the next chunk's buffer
-    // only afterwards.
+    // The chunk starting at t0, token by token (gla_slow.hpp), by the consumer waves.
+    // The state's owners hand their fp32 tiles over through the space of the bf16
+    // state copies (as [j][i]) before the first barrier and take them back after the
+    // last, then write the next copy; the operand buffers stage the rows.  Neither is
+    // needed otherwise at this point: the chunk's own operands are not used, and the
+    // producers fill the next chunk's buffer only afterwards.  Barriers: A, 2 per
+    // staged group, B, C, on both roles (slow_run, slow_pass).  (The state-only pass
+    // has no such chunks.)
     constexpr int SR = NBUF == 2 ? C : C / 2;        // rows staged at a time
     static_assert(SR * DK * 4 <= (int)sizeof(sQ) && 2 * SR * DK * ES <= (int)sizeof(sK) &&
                   SR * DVT * ES <= (int)sizeof(sV) && DVT * DK * 4 <= (int)sizeof(sS) &&
                   (!NM || DK * 4 <= (int)sizeof(sZ)) && (!OG || SR * DVT * 4 <= (int)sizeof(sEV)),
                   "token-loop staging within the operand buffers");
-    auto slow_barriers = [&](int t0) __attribute__((always_inline)) {
-        const int groups = (min(L - t0, C) + SR - 1) / SR;
-        for (int i = 0; i < 2 * groups + 3; ++i) lds_barrier();
-    };
-    auto slow_chunk = [&](int t0) __attribute__((always_inline)) {
-        float *const PS = (float *)&sS[0][0];
-        float *const PZ = &sZ[0][0];
-        const int nvalid = min(L - t0, C);
+    float *const PS = (float *)&sS[0][0];
+    float *const PZ = &sZ[0][0];
+    auto slow_give = [&]() __attribute__((always_inline)) {          // owners
         // S[16it + 4grp + r][16jt + x] -> PS[16jt + x][16it + 4grp + r]
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) {
@@ -992,14 +1013,12 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         if constexpr (NM) {
 #pragma unroll
             for (int m = 0; m < NZ; ++m)
-                if (z_ok(m) && x == 0) *(f32x4 *)(PZ + 16 * (c + NC * m) + 4 * grp) = Z[m];
+                if (z_ok(m) && x == 0) *(f32x4 *)(PZ + 16 * (ow + NOW * m) + 4 * grp) = Z[m];
         }
-        lds_barrier();
-        const SlowStage<T> st{(float *)&sQ[0][0], OG ? &sEV[0][0] : nullptr, &sK[0][0], &sK[0][0] + SR * DK,
-                              &sV[0][0]};
-        slow_chunk_lds<T, DK, DVT, SR, 64 * NC, ELU1, !SO, NM, OG, GATE == kGateScalar>(
-            PS, PZ, st, rq, rk, rvv, rg, rgv, t0, nvalid, DV, vt * DVT, SO ? nullptr : oh + (size_t)t0 * DV, tid - 64 * NP);
-        lds_barrier();
+    };
+    // (PS lies over the bf16 state copies: every owner has read its tiles back, barrier
+    // C, before any writes the next copy)
+    auto slow_take = [&](int par) __attribute__((always_inline)) {   // owners
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) {
             if (tile_ok(k)) {
@@ -1010,9 +1029,64 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         if constexpr (NM) {
 #pragma unroll
             for (int m = 0; m < NZ; ++m)
-                if (z_ok(m)) Z[m] = *(const f32x4 *)(PZ + 16 * (c + NC * m) + 4 * grp);
+                if (z_ok(m)) Z[m] = *(const f32x4 *)(PZ + 16 * (ow + NOW * m) + 4 * grp);
         }
-        lds_barrier();
+        lds_barrier();                                               // C
+        write_state(par);
+        write_z(par);
+    };
+    // consumers: the token loop between barriers A and B
+    auto slow_run = [&](int t0, int par) __attribute__((always_inline)) {
+        const int nvalid = min(L - t0, C);
+        if constexpr (!POWN) slow_give();
+        lds_barrier();                                               // A: state handed over
+        const SlowStage<T> st{(float *)&sQ[0][0], OG ? &sEV[0][0] : nullptr, &sK[0][0], &sK[0][0] + SR * DK,
+                              &sV[0][0]};
+        slow_chunk_lds<T, DK, DVT, SR, 64 * NC, ELU1, !SO, NM, OG, GATE == kGateScalar>(
+            PS, PZ, st, rq, rk, rvv, rg, rgv, t0, nvalid, DV, vt * DVT, SO ? nullptr : oh + (size_t)t0 * DV, tid - 64 * NP);
+        lds_barrier();                                               // B: state back in PS / PZ
+        if constexpr (!POWN) slow_take(par);
+        else lds_barrier();                                          // C
+    };
+    // producers: the same barriers
+    auto slow_pass = [&](int t0, int par) __attribute__((always_inline)) {
+        if constexpr (POWN) slow_give();
+        lds_barrier();                                               // A
+        const int groups = (min(L - t0, C) + SR - 1) / SR;
+        for (int i = 0; i < 2 * groups; ++i) lds_barrier();
+        lds_barrier();                                               // B
+        if constexpr (POWN) slow_take(par);
+        else lds_barrier();                                          // C
+    };
+    // the owners' step for the chunk starting at t0 in buffer `buf`, then the copy of
+    // the new state for the next chunk (parity `par`)
+    auto own_step = [&](int t0, int buf, int par) __attribute__((always_inline)) {
+        state_step(t0, buf);
+        write_state(par);
+        write_z(par);
+    };
+    auto store_final = [&]() __attribute__((always_inline)) {        // owners
+        if (a.s_final && (!a.final_last_seg || seg == a.nseg - 1)) {
+            const size_t sh = a.final_last_seg ? (size_t)bh : (size_t)bhs;
+#pragma unroll
+            for (int k = 0; k < NSLOT; ++k) {
+                if (tile_ok(k)) {
+                    const int it = tile_i(k), jt = tile_j(k);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * it + 4 * grp + r;
+                        a.s_final[(sh * DK + i) * DV + vt * DVT + 16 * jt + x] = S[k][r];
+                    }
+                }
+            }
+        }
+        if constexpr (NM) {
+            if (a.z_final && vt == 0 && x == 0) {
+#pragma unroll
+                for (int m = 0; m < NZ; ++m)
+                    if (z_ok(m)) *(f32x4 *)(a.z_final + (size_t)bhs * DK + 16 * (ow + NOW * m) + 4 * grp) = Z[m];
+            }
+        }
     };
     // chunks may leave the factorised range (not in the state-only pass, whose key
     // exponents are <= 0)
@@ -1032,36 +1106,58 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     // has no branch around its global loads.  With one buffer: 2 * nchunks barriers.
     // A chunk out of the factorised range adds the same barriers on both sides.
     if (producer) {
+        if constexpr (POWN) {                      // the producers own the state
+            load_s0();
+            load_z0();
+        }
         if constexpr (NBUF == 2) {
             const int npairs = (nchunks + 1) / 2;
-            // operands one chunk ahead of the consumers, raw rows two chunks ahead
+            // operands one chunk ahead of the consumers, raw rows NRAW chunks ahead (raw
+            // set n % NRAW holds chunk n)
             if (nchunks > 0) {
                 load_raw(R[0], row_of(0));
-                load_raw(R[1], row_of(1));
-                produce(R[0], row_of(0), 0, row_of(2));
+                if constexpr (NRAW == 2) load_raw(R[NRAW - 1], row_of(1));
+                produce(R[0], row_of(0), 0, row_of(NRAW));
+            }
+            if constexpr (POWN) {
+                write_state(0);
+                write_z(0);
             }
             lds_barrier();
             for (int n = 0; n < 2 * npairs; n += 2) {
                 // chunk n (buffer 0) out of range: the consumers compute it token by token
+                bool far = false;
                 if constexpr (KD) {
-                    if (n < nchunks && chunk_far(0)) slow_barriers(n * C);
+                    far = n < nchunks && chunk_far(0);
+                    if (far) slow_pass(n * C, 1);
                 }
-                produce(R[1], row_of(n + 1), 1, row_of(n + 3));
+                produce(R[1 % NRAW], row_of(n + 1), 1, row_of(n + 1 + NRAW));
+                if constexpr (POWN) {
+                    if (n < nchunks && !far) own_step(n * C, 0, 1);
+                }
                 lds_barrier();
+                far = false;
                 if constexpr (KD) {
-                    if (n + 1 < nchunks && chunk_far(1)) slow_barriers((n + 1) * C);
+                    far = n + 1 < nchunks && chunk_far(1);
+                    if (far) slow_pass((n + 1) * C, 0);
                 }
-                produce(R[0], row_of(n + 2), 0, row_of(n + 4));
+                produce(R[0], row_of(n + 2), 0, row_of(n + 2 + NRAW));
+                if constexpr (POWN) {
+                    if (n + 1 < nchunks && !far) own_step((n + 1) * C, 1, 0);
+                }
                 lds_barrier();
             }
         } else {
             if (nchunks > 0) load_raw(R[0], row_of(0));
+            if constexpr (POWN) {
+                write_state(0);
+                write_z(0);
+            }
             for (int n = 0; n < nchunks; ++n) {
                 produce(R[0], row_of(n), 0, row_of(n + 1));
                 lds_barrier();
-                if constexpr (KD) {
-                    if (chunk_far(0)) slow_barriers(n * C);
-                }
+                if (KD && chunk_far(0)) slow_pass(n * C, (n & 1) ^ 1);
+                else if constexpr (POWN) own_step(n * C, 0, (n & 1) ^ 1);
                 lds_barrier();
             }
         }
@@ -1071,11 +1167,14 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 for (int e = 0; e < CE; ++e) a.gam[(size_t)bhs * DK + ic + e] = gsum[e];
             }
         }
+        if constexpr (POWN) store_final();
     } else {
-        load_s0();
-        load_z0();
-        if constexpr (!SO) write_state(0);
-        write_z(0);
+        if constexpr (!POWN) {                     // the consumers own the state
+            load_s0();
+            load_z0();
+            if constexpr (!SO) write_state(0);
+            write_z(0);
+        }
         if constexpr (NBUF == 2) {
             const int npairs = (nchunks + 1) / 2;
             lds_barrier();
@@ -1091,9 +1190,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     lds_barrier();
                 }
                 if (n >= 2 * npairs) break;
-                slow_chunk(n * C);
-                if constexpr (!SO) write_state((n & 1) ^ 1);
-                write_z((n & 1) ^ 1);
+                slow_run(n * C, (n & 1) ^ 1);
                 lds_barrier();
                 ++n;
             }
@@ -1107,34 +1204,12 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     lds_barrier();
                 }
                 if (n >= nchunks) break;
-                slow_chunk(n * C);
-                if constexpr (!SO) write_state((n & 1) ^ 1);
-                write_z((n & 1) ^ 1);
+                slow_run(n * C, (n & 1) ^ 1);
                 lds_barrier();
                 ++n;
             }
         }
-        if (a.s_final && (!a.final_last_seg || seg == a.nseg - 1)) {
-            const size_t sh = a.final_last_seg ? (size_t)bh : (size_t)bhs;
-#pragma unroll
-            for (int k = 0; k < NSLOT; ++k) {
-                if (tile_ok(k)) {
-                    const int it = tile_i(k), jt = tile_j(k);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = 16 * it + 4 * grp + r;
-                        a.s_final[(sh * DK + i) * DV + vt * DVT + 16 * jt + x] = S[k][r];
-                    }
-                }
-            }
-        }
-        if constexpr (NM) {
-            if (a.z_final && vt == 0 && x == 0) {
-#pragma unroll
-                for (int m = 0; m < NZ; ++m)
-                    if (z_ok(m)) *(f32x4 *)(a.z_final + (size_t)bhs * DK + 16 * (c + NC * m) + 4 * grp) = Z[m];
-            }
-        }
+        if constexpr (!POWN) store_final();
     }
 }
 
