@@ -83,10 +83,14 @@ int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes, bool outer
 // gla_testing_set_plan can force the count.
 constexpr int kSegMinChunks = 16, kSegMinSeqChunks = 64;
 constexpr int kSegShortMinChunks = 4, kSegShortSeqChunks = 32;
+// The state-only pass runs alone ahead of the full pass: it splits each segment into
+// equal pieces (each at least kPieceMinChunks chunks) until up to two of its
+// workgroups share each CU, and the full pass scans the pieces' states.
+constexpr int kPieceMinChunks = 4, kPieceMaxWorkgroups = 512;
 
 PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes)
 {
-    PrefillPlan p{prefill_tile(BH, d_k, d_v, chunk, elem_bytes), 1, L};
+    PrefillPlan p{prefill_tile(BH, d_k, d_v, chunk, elem_bytes), 1, L, 1};
     const int nchunks = (L + chunk - 1) / chunk;
     int dvt = 16;
     for (int t : {64, 32})
@@ -112,6 +116,10 @@ PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_by
         p.nseg = (nchunks + cps - 1) / cps;
         p.seg_len = cps * chunk;
         p.dvt = dvt;
+        const long pass1 = (long)BH * (d_v / dvt) * (p.nseg - 1);
+        while (pass1 * p.sub * 2 <= kPieceMaxWorkgroups && cps % (2 * p.sub) == 0 &&
+               cps / (2 * p.sub) >= kPieceMinChunks)
+            p.sub *= 2;
     }
     return p;
 }
@@ -121,8 +129,8 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v)
 {
     if (p.nseg <= 1) return 0;
-    const size_t states = (size_t)BH * (p.nseg - 1) * d_k * d_v * 4;
-    return round256(states) + round256((size_t)BH * (p.nseg - 1) * d_k * 4);
+    const size_t pieces = (size_t)BH * (p.nseg - 1) * p.sub;
+    return round256(pieces * d_k * d_v * 4) + round256(pieces * d_k * 4);
 }
 }  // namespace gla
 
@@ -363,7 +371,7 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
         return fail(GLA_ERR_ALIAS, "z_final overlaps z0 (in-place normaliser state is not supported)");
 
     gla::PrefillPlan plan = gla::prefill_plan((int)BH, L, d_k, d_v, chunk, (int)es);
-    if (norm) plan = {gla::prefill_tile((int)BH, d_k, d_v, chunk, (int)es), 1, L};
+    if (norm) plan = {gla::prefill_tile((int)BH, d_k, d_v, chunk, (int)es), 1, L, 1};
     gla::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s0 = s0; a.o = o; a.s_final = s_final;
     a.BH = (int)BH; a.L = L; a.d_v = d_v;
@@ -385,15 +393,17 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
     if (plan.nseg == 1) {
         e = gla::launch_prefill(a, dt, d_k, chunk, plan.dvt, false, hs);
     } else {
-        // workspace: the states from zero and gate totals of all segments but the last
-        const size_t states = (size_t)BH * (plan.nseg - 1) * d_k * d_v * 4;
+        // workspace: the states from zero and gate totals of the pieces of all segments
+        // but the last
+        const size_t states = (size_t)BH * (plan.nseg - 1) * plan.sub * d_k * d_v * 4;
         float *ds = (float *)workspace;
         float *gam = (float *)((char *)workspace + gla::round256(states));
-        // pass 1: the states from zero of every segment but the last (whose state
-        // only feeds s_final, which pass 2 writes)
+        // pass 1: the states from zero of the pieces of every segment but the last
+        // (whose state only feeds s_final, which pass 2 writes)
         gla::PrefillArgs a1 = a;
         a1.s0 = nullptr; a1.s_final = ds; a1.o = nullptr; a1.gam = gam;
-        a1.nseg = plan.nseg - 1;
+        a1.nseg = (plan.nseg - 1) * plan.sub;
+        a1.seg_len = plan.seg_len / plan.sub;
         a1.xcd_remap = (a1.n_vt > 1 && ((long)BH * a1.nseg * a1.n_vt) % 8 == 0) ? 1 : 0;
         e = gla::launch_prefill(a1, dt, d_k, chunk, plan.dvt, true, hs);
         // pass 2: outputs of every segment, each workgroup scanning the earlier
@@ -401,6 +411,7 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
         gla::PrefillArgs a2 = a;
         a2.s_final = s_final; a2.final_last_seg = 1;
         a2.seg_ds = ds; a2.seg_gam = gate == GLA_GATE_NONE ? nullptr : gam;
+        a2.seg_sub = plan.sub;
         if (e == hipSuccess) e = gla::launch_prefill(a2, dt, d_k, chunk, plan.dvt, false, hs);
     }
     if (e != hipSuccess) return fail(GLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

@@ -36,11 +36,14 @@ struct PrefillArgs {
     float *z_final;          // [B][H][d_k] or null
     // outer-product gate: value-dimension log-gates (natural log) [B][H][L][d_v]
     const float *gv = nullptr;
-    // full pass of a segmented prefill: the states from zero of segments 0 .. nseg-2
-    // ([BH][nseg - 1][d_k][d_v]) and their log2 gate totals ([BH][nseg - 1][d_k], null
-    // without gates); each workgroup scans them into its segment's initial state, and
-    // s0 is then the sequence's own initial state [BH][d_k][d_v] (or null)
+    // full pass of a segmented prefill: the states from zero of the pieces that cover
+    // segments 0 .. nseg-2, seg_sub equal pieces per segment ([BH][(nseg - 1) seg_sub]
+    // [d_k][d_v]), and their log2 gate totals ([BH][(nseg - 1) seg_sub][d_k], null
+    // without gates); each workgroup scans the pieces before its segment into its
+    // initial state, and s0 is then the sequence's own initial state [BH][d_k][d_v]
+    // (or null)
     const float *seg_ds = nullptr, *seg_gam = nullptr;
+    int seg_sub = 1;
 };
 
 struct DecodeArgs {
@@ -76,15 +79,16 @@ constexpr int prefill_nbuf(int es, int dk, int c, int dvt, bool outer = false)
 }
 
 // Launch plan of a prefill: value columns per workgroup (16, 32 or 64) and, for
-// few long sequences, the number of sequence segments and their length in rows.
+// few long sequences, the number of sequence segments, their length in rows, and into
+// how many equal pieces the state-only pass splits each segment but the last.
 struct PrefillPlan {
-    int dvt, nseg, seg_len;
+    int dvt, nseg, seg_len, sub;
 };
 PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes);
 
-// Device workspace of a segmented prefill: the states from zero of all segments but
-// the last (fp32 [BH][nseg - 1][d_k][d_v]) and their gate totals (fp32
-// [BH][nseg - 1][d_k]); 0 when nseg == 1.
+// Device workspace of a segmented prefill: the states from zero of the pieces of all
+// segments but the last (fp32 [BH][(nseg - 1) sub][d_k][d_v]) and their gate totals
+// (fp32 [BH][(nseg - 1) sub][d_k]); 0 when nseg == 1.
 size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v);
 
 // Enqueue the prefill kernel.  dtype: 0 fp32, 1 bf16.  state_only: compute only

@@ -645,8 +645,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     auto z_ok = [&](int m) __attribute__((always_inline)) -> bool { return ow + NOW * m < NKB; };
     // initial state (by the owners)
     // In the full pass of a segmented prefill (a.seg_ds set) the segment's initial
-    // state is the weighted scan over the earlier segments' states from zero:
-    // S = s0, then S = Diag(exp2(gam_p)) S + ds_p for p = 0 .. seg-1.
+    // state is the weighted scan over the states from zero of the pieces before it
+    // (a.seg_sub per segment): S = s0, then S = Diag(exp2(gam_p)) S + ds_p for
+    // p = 0 .. seg * seg_sub - 1.
     auto load_s0 = [&]() __attribute__((always_inline)) {
         if (SO || !a.seg_ds) {
             if (a.s0) {
@@ -665,37 +666,57 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
         } else {
 #pragma unroll
             for (int k = 0; k < NSLOT; ++k) {
-                const bool ok = tile_ok(k);
-                const int it = ok ? tile_i(k) : 0, jt = ok ? tile_j(k) : 0;
-                const int j = vt * DVT + 16 * jt + x;
-                f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (a.s0) {
+                S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (a.s0 && tile_ok(k)) {
+                    const int it = tile_i(k), j = vt * DVT + 16 * tile_j(k) + x;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = a.s0[((size_t)bh * DK + 16 * it + 4 * grp + r) * DV + j];
+                    for (int r = 0; r < 4; ++r) S[k][r] = a.s0[((size_t)bh * DK + 16 * it + 4 * grp + r) * DV + j];
                 }
-                // segments four at a time, all their loads requested before the steps
-                for (int sp0 = 0; sp0 < seg; sp0 += 4) {
-                    f32x4 d[4], gm[4];
+            }
+            // pieces two at a time, their loads for every tile requested before the steps
+            // (one memory round trip per two pieces); the gate totals depend on the key
+            // block only, shared by the tiles of one key block
+            const int np = seg * a.seg_sub;
+            const size_t hp0 = (size_t)bh * (a.nseg - 1) * a.seg_sub;
+            constexpr int PB = 2, NG = BLK ? IPC : NSLOT;
+            auto gidx = [&](int k) __attribute__((always_inline)) -> int { return BLK ? k % IPC : k; };
+            for (int sp0 = 0; sp0 < np; sp0 += PB) {
+                f32x4 d[PB][NSLOT], gm[PB][NG];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        d[u] = gm[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (sp0 + u < seg) {
-                            const size_t hp = (size_t)bh * (a.nseg - 1) + sp0 + u;
+                for (int u = 0; u < PB; ++u) {
+                    const size_t hp = hp0 + sp0 + u;
+#pragma unroll
+                    for (int k = 0; k < NSLOT; ++k) {
+                        d[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (sp0 + u < np && tile_ok(k)) {
+                            const int it = tile_i(k), j = vt * DVT + 16 * tile_j(k) + x;
                             const float *ds = a.seg_ds + (hp * DK + 16 * it + 4 * grp) * DV + j;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) d[u][r] = ds[(size_t)r * DV];
-                            if (a.seg_gam) gm[u] = *(const f32x4 *)(a.seg_gam + hp * DK + 16 * it + 4 * grp);
+                            for (int r = 0; r < 4; ++r) d[u][k][r] = ds[(size_t)r * DV];
                         }
                     }
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        if (sp0 + u < seg) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) v[r] = fmaf(exp2_fast(gm[u][r]), v[r], d[u][r]);
+                    for (int g = 0; g < NG; ++g) {
+                        gm[u][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (a.seg_gam && sp0 + u < np && tile_ok(g)) {
+                            const int it = tile_i(g);
+                            gm[u][g] = *(const f32x4 *)(a.seg_gam + hp * DK + 16 * it + 4 * grp);
                         }
                     }
                 }
-                S[k] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < PB; ++u) {
+                    if (sp0 + u < np) {
+#pragma unroll
+                        for (int g = 0; g < NG; ++g)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) gm[u][g][r] = exp2_fast(gm[u][g][r]);
+#pragma unroll
+                        for (int k = 0; k < NSLOT; ++k)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) S[k][r] = fmaf(gm[u][gidx(k)][r], S[k][r], d[u][k][r]);
+                    }
+                }
             }
         }
     };
@@ -1106,14 +1127,14 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     // has no branch around its global loads.  With one buffer: 2 * nchunks barriers.
     // A chunk out of the factorised range adds the same barriers on both sides.
     if (producer) {
-        if constexpr (POWN) {                      // the producers own the state
-            load_s0();
-            load_z0();
-        }
         if constexpr (NBUF == 2) {
             const int npairs = (nchunks + 1) / 2;
             // operands one chunk ahead of the consumers, raw rows NRAW chunks ahead (raw
             // set n % NRAW holds chunk n)
+            if constexpr (POWN) {                  // the producers own the state
+                load_s0();
+                load_z0();
+            }
             if (nchunks > 0) {
                 load_raw(R[0], row_of(0));
                 if constexpr (NRAW == 2) load_raw(R[NRAW - 1], row_of(1));
@@ -1148,6 +1169,10 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                 lds_barrier();
             }
         } else {
+            if constexpr (POWN) {
+                load_s0();
+                load_z0();
+            }
             if (nchunks > 0) load_raw(R[0], row_of(0));
             if constexpr (POWN) {
                 write_state(0);
