@@ -84,9 +84,10 @@ int prefill_tile(int BH, int d_k, int d_v, int chunk, int elem_bytes, bool outer
 constexpr int kSegMinChunks = 16, kSegMinSeqChunks = 64;
 constexpr int kSegShortMinChunks = 4, kSegShortSeqChunks = 32;
 // The state-only pass runs alone ahead of the full pass: it splits each segment into
-// equal pieces (each at least kPieceMinChunks chunks) until up to two of its
-// workgroups share each CU, and the full pass scans the pieces' states.
-constexpr int kPieceMinChunks = 4, kPieceMaxWorkgroups = 512;
+// equal pieces (each at least kPieceMinChunks chunks) until up to three of its
+// workgroups share each CU (as many as its registers allow without gates or with a
+// scalar gate), and the full pass scans the pieces' states.
+constexpr int kPieceMinChunks = 4, kPieceMaxWorkgroups = 768;
 
 PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes)
 {

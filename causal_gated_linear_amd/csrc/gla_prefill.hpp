@@ -362,7 +362,8 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     // raw register sets: with two operand buffers the rows are requested two chunks
     // ahead, except where the producers also hold the state and per-key-dimension
     // gates (one chunk ahead, which leaves room in their registers)
-    constexpr int NRAW = NBUF == 2 && !(POWN && KG) ? 2 : 1;
+    constexpr int NRAW = NBUF == 2 && !(POWN && KG) && !SO ? 2 : 1;   // (state-only: one set,
+                                                                      // so three workgroups fit a CU)
     Raw R[NRAW];
 
     // Raw rows of the chunk starting at t0, requested in three parts so that each
