@@ -225,11 +225,15 @@ def run_other_prefills(args, torch, api, inputs, baselines=None):
         inp = inputs.draw(w, device="cuda")
         o = torch.empty(w.B, w.H, w.L, w.d_v, dtype=w.dtype, device="cuda")
         s = torch.empty(w.B, w.H, w.d_k, w.d_v, dtype=torch.float32, device="cuda")
+        # the segmented workloads' workspace, allocated once as a caller running many
+        # prefills would (as for the headline)
+        ws_n = api.workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, w.dtype)
+        ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
         stream = torch.cuda.current_stream()
 
         def step():
             api.prefill(inp["q"], inp["k"], inp["v"], log_gate=inp["g"], gate=w.gate, chunk=w.chunk,
-                        feature_map=w.feature_map, out=o, final_state=s, stream=stream)
+                        feature_map=w.feature_map, out=o, final_state=s, workspace=ws, stream=stream)
 
         _settle(torch, step, args.settle_s / 4)
         for _ in range(3):
@@ -250,7 +254,7 @@ def run_other_prefills(args, torch, api, inputs, baselines=None):
                      "shape": "B=%d H=%d L=%d d_k=%d d_v=%d chunk=%d %s gate=%s phi=%s" % (
                          w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, str(w.dtype).replace("torch.", ""), w.gate,
                          w.feature_map or "identity")}
-        del inp, o, s
+        del inp, o, s, ws
     # the normalised form (normaliser state z beside S) at the headline shape, elu+1
     w = inputs.WORKLOADS["gla_prefill"]
     inp = inputs.draw(w, device="cuda")

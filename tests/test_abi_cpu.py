@@ -436,7 +436,8 @@ def test_decode_outer_rejects(lib):
 
 def test_prefill_noalloc_rejects_sizes_beyond_its_scratch(lib):
     """The allocation-free prefill holds 32 MiB of scratch, which covers every size the
-    automatic plan segments (at most about 254 head-segments of a 64 KiB state).  A
+    automatic plan segments (at most 768 state-pass pieces of one value tile's state,
+    24 MiB at d_k = 128 and 64-column tiles).  A
     plan forced through the test hook to more segments needs more and is rejected on
     the host, before any HIP call."""
     P = ctypes.c_void_p
