@@ -131,7 +131,7 @@ size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v)
 {
     if (p.nseg <= 1) return 0;
     const size_t pieces = (size_t)BH * (p.nseg - 1) * p.sub;
-    return round256(pieces * d_k * d_v * 4) + round256(pieces * d_k * 4);
+    return round256(pieces * d_k * d_v * 4) + round256(pieces * d_k * 4) + round256((size_t)BH * d_k * d_v * 4);
 }
 }  // namespace gla
 
@@ -363,6 +363,9 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
         if (overlap(ssf, x)) return fail(GLA_ERR_ALIAS, "s_final overlaps %s", x.name);
     if (overlap(ssf, ss0) && s_final != s0)
         return fail(GLA_ERR_ALIAS, "s_final partially overlaps s0");
+    const Span w_forbidden[] = {sq, sk, sv, sg, ss0, sz0};
+    for (const Span &x : w_forbidden)
+        if (overlap(sw, x)) return fail(GLA_ERR_ALIAS, "workspace overlaps %s", x.name);
     const Span zf_forbidden[] = {sq, sk, sv, sg, sw, ss0};
     for (const Span &x : zf_forbidden)
         if (overlap(szf, x)) return fail(GLA_ERR_ALIAS, "z_final overlaps %s", x.name);
@@ -395,10 +398,20 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
         e = gla::launch_prefill(a, dt, d_k, chunk, plan.dvt, false, hs);
     } else {
         // workspace: the states from zero and gate totals of the pieces of all segments
-        // but the last
-        const size_t states = (size_t)BH * (plan.nseg - 1) * plan.sub * d_k * d_v * 4;
+        // but the last, then room for a copy of s0
+        const size_t pieces = (size_t)BH * (plan.nseg - 1) * plan.sub;
         float *ds = (float *)workspace;
-        float *gam = (float *)((char *)workspace + gla::round256(states));
+        float *gam = (float *)((char *)ds + gla::round256(pieces * d_k * d_v * 4));
+        float *s0c = (float *)((char *)gam + gla::round256(pieces * d_k * 4));
+        // in place (s_final == s0): every segment's workgroups read s0 while the last
+        // segment's write s_final, and they need not all be running at once, so the
+        // full pass reads a copy taken before either launch
+        const float *s0_full = s0;
+        e = hipSuccess;
+        if (s0 && s_final == s0) {
+            e = hipMemcpyAsync(s0c, s0, sbytes, hipMemcpyDeviceToDevice, hs);
+            s0_full = s0c;
+        }
         // pass 1: the states from zero of the pieces of every segment but the last
         // (whose state only feeds s_final, which pass 2 writes)
         gla::PrefillArgs a1 = a;
@@ -406,11 +419,11 @@ static int prefill_impl(const void *q, const void *k, const void *v, const float
         a1.nseg = (plan.nseg - 1) * plan.sub;
         a1.seg_len = plan.seg_len / plan.sub;
         a1.xcd_remap = (a1.n_vt > 1 && ((long)BH * a1.nseg * a1.n_vt) % 8 == 0) ? 1 : 0;
-        e = gla::launch_prefill(a1, dt, d_k, chunk, plan.dvt, true, hs);
+        if (e == hipSuccess) e = gla::launch_prefill(a1, dt, d_k, chunk, plan.dvt, true, hs);
         // pass 2: outputs of every segment, each workgroup scanning the earlier
         // segments' states into its own initial state
         gla::PrefillArgs a2 = a;
-        a2.s_final = s_final; a2.final_last_seg = 1;
+        a2.s0 = s0_full; a2.s_final = s_final; a2.final_last_seg = 1;
         a2.seg_ds = ds; a2.seg_gam = gate == GLA_GATE_NONE ? nullptr : gam;
         a2.seg_sub = plan.sub;
         if (e == hipSuccess) e = gla::launch_prefill(a2, dt, d_k, chunk, plan.dvt, false, hs);

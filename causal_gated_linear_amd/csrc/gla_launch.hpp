@@ -87,8 +87,10 @@ struct PrefillPlan {
 PrefillPlan prefill_plan(int BH, int L, int d_k, int d_v, int chunk, int elem_bytes);
 
 // Device workspace of a segmented prefill: the states from zero of the pieces of all
-// segments but the last (fp32 [BH][(nseg - 1) sub][d_k][d_v]) and their gate totals
-// (fp32 [BH][(nseg - 1) sub][d_k]); 0 when nseg == 1.
+// segments but the last (fp32 [BH][(nseg - 1) sub][d_k][d_v]), their gate totals
+// (fp32 [BH][(nseg - 1) sub][d_k]) and room for a copy of s0 (fp32 [BH][d_k][d_v],
+// used when the state is updated in place), each rounded up to 256 bytes; 0 when
+// nseg == 1.
 size_t prefill_workspace(const PrefillPlan &p, int BH, int d_k, int d_v);
 
 // Enqueue the prefill kernel.  dtype: 0 fp32, 1 bf16.  state_only: compute only

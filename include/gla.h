@@ -138,11 +138,13 @@ size_t gla_prefill_workspace_bytes(int B, int H, int L, int d_k, int d_v, int ch
  *   o         out  [B][H][L][d_v], dtype
  *   s_final   out  fp32 [B][H][d_k][d_v] state after the last token, or NULL;
  *                  may equal s0 (update in place) but must not partially overlap it
+ *                  (in place with a workspace, s0 is first copied into it)
  *   workspace      device scratch of at least gla_prefill_workspace_bytes(...)
  *                  bytes (NULL allowed when that is 0); contents are clobbered
  *
  * o must not overlap q, k, v, g, s0, s_final or the workspace; s_final must not
- * overlap q, k, v, g or the workspace.  Errors: GLA_ERR_NULL, GLA_ERR_SHAPE,
+ * overlap q, k, v, g or the workspace; the workspace must not overlap any argument.
+ * Errors: GLA_ERR_NULL, GLA_ERR_SHAPE,
  * GLA_ERR_UNSUPPORTED, GLA_ERR_ALIGN, GLA_ERR_ALIAS, GLA_ERR_WORKSPACE, GLA_ERR_HIP.
  */
 int gla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,

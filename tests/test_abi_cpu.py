@@ -116,6 +116,10 @@ PREFILL_BAD = {
     "o_overlaps_s_final": (dict(s_final=A + 96 * MB + 64), _lib.GLA_ERR_ALIAS),
     "s_final_overlaps_q": (dict(s_final=A + 1024), _lib.GLA_ERR_ALIAS),
     "s_final_partially_overlaps_s0": (dict(s0=A + 200 * MB, s_final=A + 200 * MB + 256), _lib.GLA_ERR_ALIAS),
+    # a segmented plan (workspace in use) whose workspace overlaps an input
+    "workspace_overlaps_s0": (dict(L=64 * 65, s0=A + 400 * MB + 4096, ws=A + 400 * MB, ws_bytes=64 * MB),
+                              _lib.GLA_ERR_ALIAS),
+    "workspace_overlaps_k": (dict(L=64 * 65, ws=A + 16 * MB + 4096, ws_bytes=64 * MB), _lib.GLA_ERR_ALIAS),
 }
 
 
@@ -189,14 +193,15 @@ def test_state_alloc_rejects(lib):
 
 def test_workspace_for_few_long_sequences(lib):
     """Few long sequences are split into segments, which need a workspace: the fp32
-    states from zero [B*H][pieces][d_k][d_v] of the pieces of all segments but the last
-    and their gate totals [B*H][pieces][d_k].  The state-only pass splits each such
+    states from zero [B*H][pieces][d_k][d_v] of the pieces of all segments but the last,
+    their gate totals [B*H][pieces][d_k], and room for a copy of s0 [B*H][d_k][d_v]
+    (taken when the state is updated in place).  The state-only pass splits each such
     segment into equal pieces until up to three of its workgroups share a CU."""
     n = lib.gla_prefill_workspace_bytes(1, 32, 32768, 128, 128, 64, 1)
     rnd = lambda x: (x + 255) // 256 * 256
     # 4 segments of 8192 tokens; 32 heads x 2 value tiles x 3 segments = 192 workgroups
-    # in the state-only pass, so 4 pieces per segment (768)
-    assert n == rnd(32 * 12 * 128 * 128 * 4) + rnd(32 * 12 * 128 * 4)
+    # in the state-only pass, so 4 pieces per segment (768); then room for a copy of s0
+    assert n == rnd(32 * 12 * 128 * 128 * 4) + rnd(32 * 12 * 128 * 4) + rnd(32 * 128 * 128 * 4)
     assert lib.gla_prefill_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 0   # enough heads
     assert lib.gla_prefill_workspace_bytes(1, 2, 64 * 31, 64, 64, 64, 1) == 0   # too short
     # 32 to 63 chunks on too few heads for even the narrowest tile: short segments

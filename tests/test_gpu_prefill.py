@@ -283,7 +283,7 @@ def test_prefill_segmented_weak_gates_carry_state(gate):
 
 
 def test_prefill_segmented_in_place_state():
-    """s_final may be s0 on the segmented path too (the scan reads s0 before it writes)."""
+    """s_final may be s0 on the segmented path too."""
     w = W["gla_prefill"]
     B, H, L = 1, 2, 64 * 66
     inp = inputs.draw(w, B=B, H=H, L=L, seed=801)
@@ -294,6 +294,28 @@ def test_prefill_segmented_in_place_state():
     ro, rs = oracle.forward(inp["q"], inp["k"], inp["v"], g=inp["g"], gate=w.gate, s0=s0)
     util.assert_close(o, ro, util.TOL[w.dtype], "o")
     util.assert_close(s, rs, util.TOL[w.dtype], "s_final in place")
+
+
+def test_prefill_segmented_in_place_state_with_more_workgroups_than_cus():
+    """In place on a segmented plan whose full pass has more workgroups (3 heads x 64
+    segments x 2 value tiles = 384) than one round of the CUs runs at once: a segment's
+    workgroups may start after the last segment's have written s_final, so the full
+    pass reads a copy of s0 taken before its launches.  The result equals the
+    out-of-place run bit for bit and meets the oracle on every head."""
+    w = W["gla_prefill"]
+    B, H, L = 1, 3, 64 * 2048
+    assert api.workspace_bytes(B, H, L, w.d_k, w.d_v, w.chunk, w.dtype) > 0
+    inp = inputs.draw(w, B=B, H=H, L=L, seed=803)
+    s0 = inputs.draw_state(B, H, w.d_k, w.d_v, seed=804, scale=0.5)
+    d = _to(inp, DEV)
+    o1, s1 = _run_gpu(w, d, s0=s0.to(DEV))
+    st = s0.to(DEV)
+    o2, s2 = _run_gpu(w, d, s0=st, final_state=st)
+    assert s2.data_ptr() == st.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    ro, rs = oracle.forward(inp["q"], inp["k"], inp["v"], g=inp["g"], gate=w.gate, s0=s0)
+    util.assert_close(o2, ro, util.TOL[w.dtype], "o")
+    util.assert_close(s2, rs, util.TOL[w.dtype], "s_final in place")
 
 
 def test_prefill_on_side_stream_with_binding_workspace():
