@@ -501,14 +501,15 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                             SO ? tot[e] - (excl[e] + bc[r][e]) + gsum[e] : -(excl[e] + bc[r][e]);
                         if constexpr (ELU1 && FG) {
                             // phi(x) 2^(+-b) with one exponential: (x + 1) 2^(+-b) for
-                            // x > 0, else 2^(x log2(e) +- b)
+                            // x > 0, else 2^(x log2(e) +- b), i.e. (max(x, 0) + 1) times
+                            // 2^(min(x, 0) log2(e) +- b) (no compare-and-select)
                             const float b = excl[e] + bc[r][e];
                             if constexpr (!SO) {
                                 const float x = q[e];
-                                q[e] = (x > 0.f ? x + 1.f : 1.f) * exp2_fast(x > 0.f ? b : fmaf(x, kLog2e, b));
+                                q[e] = (fmaxf(x, 0.f) + 1.f) * exp2_fast(fmaf(fminf(x, 0.f), kLog2e, b));
                             }
                             const float x = kk[e];
-                            kk[e] = (x > 0.f ? x + 1.f : 1.f) * exp2_fast(x > 0.f ? kb : fmaf(x, kLog2e, kb));
+                            kk[e] = (fmaxf(x, 0.f) + 1.f) * exp2_fast(fmaf(fminf(x, 0.f), kLog2e, kb));
                         } else {
                             if constexpr (ELU1) {
                                 if constexpr (!SO) q[e] = feature(q[e], true);
