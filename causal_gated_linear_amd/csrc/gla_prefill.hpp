@@ -262,14 +262,15 @@ __device__ __forceinline__ float group_scan(float v, int lane)
 }
 
 
-// SO (state only): the first pass of a segmented prefill.  Each workgroup computes its
-// segment's state from a zero start and the segment's gate totals; no outputs, no Q~.
-// It walks the segment's chunks last to first and adds each chunk's writes already
-// decayed to the segment's end, S += (phi(K) * exp(Gamma_c - B + later))^T V, with
-// `later` the gate total of the chunks after it: every exponent is <= 0, so no chunk
-// leaves the factorised range and this pass needs no token-by-token chunks.
+// SO (state only): the first pass of a segmented prefill, launched over pieces of the
+// segments (its own "segments").  Each workgroup computes its piece's state from a
+// zero start and the piece's gate totals; no outputs, no Q~.  It walks the piece's
+// chunks last to first and adds each chunk's writes already decayed to the piece's
+// end, S += (phi(K) * exp(Gamma_c - B + later))^T V, with `later` the gate total of
+// the chunks after it: every exponent is <= 0, so no chunk leaves the factorised
+// range and this pass needs no token-by-token chunks.
 // NM (normalised, "Transformers are RNNs" notes: the weighted sum of values over the
-// sum of the same weights): the consumers also carry the normaliser state z, the
+// sum of the same weights): the state's owners also carry the normaliser state z, the
 // state of a value that is 1 in every token, z <- Diag(e^Gamma)(z + K^^T 1), with the
 // matrix cores (a fragment of ones as the value operand); each output row is divided
 // by its denominator Q~_t . z + sum_{s<=t} P_ts.
@@ -361,9 +362,9 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     constexpr bool POWN = !SO && (GATE == kGateScalar || NM || (OG && C == 64));
     // raw register sets: with two operand buffers the rows are requested two chunks
     // ahead, except where the producers also hold the state and per-key-dimension
-    // gates (one chunk ahead, which leaves room in their registers)
-    constexpr int NRAW = NBUF == 2 && !(POWN && KG) && !SO ? 2 : 1;   // (state-only: one set,
-                                                                      // so three workgroups fit a CU)
+    // gates (one chunk ahead, which leaves room in their registers) and in the
+    // state-only pass (one set, so that three of its workgroups fit a CU)
+    constexpr int NRAW = NBUF == 2 && !(POWN && KG) && !SO ? 2 : 1;
     Raw R[NRAW];
 
     // Raw rows of the chunk starting at t0, requested in three parts so that each
