@@ -502,15 +502,18 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                             SO ? tot[e] - (excl[e] + bc[r][e]) + gsum[e] : -(excl[e] + bc[r][e]);
                         if constexpr (ELU1 && FG) {
                             // phi(x) 2^(+-b) with one exponential: (x + 1) 2^(+-b) for
-                            // x > 0, else 2^(x log2(e) +- b), i.e. (max(x, 0) + 1) times
-                            // 2^(min(x, 0) log2(e) +- b) (no compare-and-select)
+                            // x > 0, else 2^(x log2(e) +- b), i.e. with
+                            // f = 2^(min(x, 0) log2(e) +- b), max(x, 0) f + f (no
+                            // compare-and-select, one fused multiply-add)
                             const float b = excl[e] + bc[r][e];
                             if constexpr (!SO) {
                                 const float x = q[e];
-                                q[e] = (fmaxf(x, 0.f) + 1.f) * exp2_fast(fmaf(fminf(x, 0.f), kLog2e, b));
+                                const float f = exp2_fast(fmaf(fminf(x, 0.f), kLog2e, b));
+                                q[e] = fmaf(fmaxf(x, 0.f), f, f);
                             }
                             const float x = kk[e];
-                            kk[e] = (fmaxf(x, 0.f) + 1.f) * exp2_fast(fmaf(fminf(x, 0.f), kLog2e, kb));
+                            const float f = exp2_fast(fmaf(fminf(x, 0.f), kLog2e, kb));
+                            kk[e] = fmaf(fmaxf(x, 0.f), f, f);
                         } else {
                             if constexpr (ELU1) {
                                 if constexpr (!SO) q[e] = feature(q[e], true);
