@@ -261,6 +261,45 @@ __device__ __forceinline__ float group_scan(float v, int lane)
     return v;
 }
 
+// The same scan for NE columns at once, with the group totals: v[e] becomes the
+// inclusive scan and tot[e] the total over all RSEG segments.  Inside each 16-lane row
+// DPP row shifts as above; the rows' totals then go through a small LDS area of this
+// wave (scr, STRIDE * NE * 4 floats): the last segment of each row writes its row
+// total, and every lane reads the (at most four) totals of its column group in one
+// access, so all columns take one LDS round trip instead of one shuffle per row step.
+// (A wave's LDS accesses complete in order, so the reads see this wave's writes.)
+template <int RSEG, int STRIDE, int NE>
+__device__ __forceinline__ void group_scan_tot(float (&v)[NE], float (&tot)[NE], int lane, float *scr)
+{
+    constexpr int SPR = 16 / STRIDE;                   // segments per 16-lane row
+    constexpr int NR = (RSEG * STRIDE + 15) / 16;      // rows of the group
+    static_assert(NR <= 4 && (RSEG * STRIDE) % 16 == 0, "group scan: whole 16-lane rows");
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        if constexpr (SPR > 1) v[e] += row_shr<STRIDE>(v[e]);
+        if constexpr (SPR > 2) v[e] += row_shr<2 * STRIDE>(v[e]);
+        if constexpr (SPR > 4) v[e] += row_shr<4 * STRIDE>(v[e]);
+        if constexpr (SPR > 8) v[e] += row_shr<8 * STRIDE>(v[e]);
+    }
+    const int row = lane >> 4, cg = lane & (STRIDE - 1);
+    if ((lane & 15) >= 16 - STRIDE) {                  // the row's last segment
+#pragma unroll
+        for (int e = 0; e < NE; ++e) scr[(cg * NE + e) * 4 + row] = v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const f32x4 t = *(const f32x4 *)(scr + (cg * NE + e) * 4);
+        float before = 0.f, all = 0.f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            all += t[r];
+            before += r < row ? t[r] : 0.f;
+        }
+        v[e] += before;
+        tot[e] = all;
+    }
+}
+
 
 // SO (state only): the first pass of a segmented prefill, launched over pieces of the
 // segments (its own "segments").  Each workgroup computes its piece's state from a
@@ -298,6 +337,8 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     __shared__ __attribute__((aligned(16))) float sEG[NBUF][DK];     // exp(Gamma_i)
     __shared__ __attribute__((aligned(16))) float sZ[NM ? 2 : 1][NM ? DK : 4];   // normaliser z, by parity
     __shared__ __attribute__((aligned(16))) int sFlag[NBUF][4];      // per producer: chunk out of range
+    // outer gate, per producer: the gate scan's row totals
+    __shared__ __attribute__((aligned(16))) float sScan[OG ? SH::NP : 1][OG ? SH::CG * SH::CE * 4 : 4];
     // outer-product gate: exp(Bv) [t][j] for the outputs, exp of the value-side chunk
     // totals, and per producer the lowest key-side and value-side log2 totals
     __shared__ __attribute__((aligned(16))) float sEV[OG ? NBUF : 1][OG ? C * SH::LEV : 4];
@@ -454,11 +495,24 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     }
                 }
                 load_g(r_, t_next);                // gates consumed: refill them now
+                if constexpr (OG) {
+                    // outer gate (measured faster there): the rows' totals through LDS
+                    float incl[NE], totn[NE];
 #pragma unroll
-                for (int e = 0; e < NE; ++e) {
-                    const float incl = group_scan<RSEG, SH::CG>(run[e], lane);
-                    excl[e] = incl - run[e];
-                    tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64);
+                    for (int e = 0; e < NE; ++e) incl[e] = run[e];
+                    group_scan_tot<RSEG, SH::CG, NE>(incl, totn, lane, sScan[OG ? p : 0]);
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) {
+                        excl[e] = incl[e] - run[e];
+                        tot[e] = totn[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) {
+                        const float incl = group_scan<RSEG, SH::CG>(run[e], lane);
+                        excl[e] = incl - run[e];
+                        tot[e] = __shfl(incl, (RSEG - 1) * SH::CG + cg, 64);
+                    }
                 }
                 if constexpr (GATE == kGateScalar) {     // one gate per row: the same in every column
 #pragma unroll
