@@ -338,7 +338,7 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
     __shared__ __attribute__((aligned(16))) float sZ[NM ? 2 : 1][NM ? DK : 4];   // normaliser z, by parity
     __shared__ __attribute__((aligned(16))) int sFlag[NBUF][4];      // per producer: chunk out of range
     // outer gate, per producer: the gate scan's row totals
-    __shared__ __attribute__((aligned(16))) float sScan[OG ? SH::NP : 1][OG ? SH::CG * SH::CE * 4 : 4];
+    __shared__ __attribute__((aligned(16))) float sScan[OG || NM ? SH::NP : 1][OG || NM ? SH::CG * SH::CE * 4 : 4];
     // outer-product gate: exp(Bv) [t][j] for the outputs, exp of the value-side chunk
     // totals, and per producer the lowest key-side and value-side log2 totals
     __shared__ __attribute__((aligned(16))) float sEV[OG ? NBUF : 1][OG ? C * SH::LEV : 4];
@@ -495,12 +495,13 @@ __global__ __launch_bounds__((PrefillShape<T, DK, C, DVT>::NT)) void prefill_ker
                     }
                 }
                 load_g(r_, t_next);                // gates consumed: refill them now
-                if constexpr (OG) {
-                    // outer gate (measured faster there): the rows' totals through LDS
+                if constexpr (OG || NM) {
+                    // outer gate and normalised form (their producers carry the
+                    // longer role; measured faster there): the rows' totals through LDS
                     float incl[NE], totn[NE];
 #pragma unroll
                     for (int e = 0; e < NE; ++e) incl[e] = run[e];
-                    group_scan_tot<RSEG, SH::CG, NE>(incl, totn, lane, sScan[OG ? p : 0]);
+                    group_scan_tot<RSEG, SH::CG, NE>(incl, totn, lane, sScan[OG || NM ? p : 0]);
 #pragma unroll
                     for (int e = 0; e < NE; ++e) {
                         excl[e] = incl[e] - run[e];
