@@ -318,6 +318,25 @@ def test_prefill_segmented_in_place_state_with_more_workgroups_than_cus():
     util.assert_close(s2, rs, util.TOL[w.dtype], "s_final in place")
 
 
+def test_prefill_noalloc_segmented_in_place_state():
+    """The allocation-free prefill in place on a segmented plan: the copy of s0 goes to
+    the library's scratch array; the result equals the out-of-place run bit for bit."""
+    w = W["gla_prefill"]
+    B, H, L = 1, 3, 64 * 2048
+    assert api.workspace_bytes(B, H, L, w.d_k, w.d_v, w.chunk, w.dtype) > 0
+    inp = inputs.draw(w, B=B, H=H, L=L, seed=805)
+    s0 = inputs.draw_state(B, H, w.d_k, w.d_v, seed=806, scale=0.5)
+    d = _to(inp, DEV)
+    o1, s1 = _run_gpu(w, d, s0=s0.to(DEV))
+    st = s0.to(DEV)
+    o2 = torch.empty_like(o1)
+    _, s2 = api.prefill_noalloc(d["q"], d["k"], d["v"], log_gate=d["g"], gate=w.gate, initial_state=st,
+                                chunk=w.chunk, out=o2, final_state=st)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == st.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
 def test_prefill_on_side_stream_with_binding_workspace():
     """A segmented prefill on a side stream, whose workspace the binding allocates:
     the workspace stays reserved for that stream until its work is done, although the
